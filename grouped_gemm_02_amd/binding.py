@@ -1,0 +1,221 @@
+"""Thin ctypes binding of libmoe.so (declared in include/moe.h).
+
+Functions keep the C names and only marshal arguments: torch tensors become
+device pointers, the current torch stream becomes the hipStream_t, and a
+non-OK status becomes :class:`MoEError`. Every step of the layer runs in the
+library's HIP kernels; if the library is missing this module raises, it never
+falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+PRECISIONS = {"bf16": 0, "fp8_block": 1, "mxfp8": 2, "fp8_bwd": 3}
+
+STATUS_NAMES = {
+    0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
+    4: "MOE_ERR_PRECISION", 5: "MOE_ERR_ARCH", 6: "MOE_ERR_WORKSPACE",
+    7: "MOE_ERR_LAUNCH", 8: "MOE_ERR_ROUTING", 9: "MOE_ERR_UNSUPPORTED",
+}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {moe_status_string(status)}")
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
+                ("E", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("precision", ctypes.c_int32), ("num_cus", ctypes.c_int32)]
+
+
+class moe_saved_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("counts", "offsets", "row_of", "src_of", "h13", "act", "total")]
+
+
+class moe_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "moe_workspace_size": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_get_saved_layout": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.POINTER(moe_saved_layout)]),
+    "moe_permute_scratch_bytes": (ctypes.c_size_t, [ctypes.POINTER(moe_shape)]),
+    "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P]),
+    "moe_fwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                               ctypes.c_size_t, _P]),
+    "moe_bwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                               _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32), _P]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_set_kernel_timing": (ctypes.c_int, [ctypes.c_int]),
+    "moe_kernel_timing_collect": (ctypes.c_int, [ctypes.POINTER(moe_kernel_time), ctypes.c_int32,
+                                                 ctypes.POINTER(ctypes.c_int32)]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libmoe.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m grouped_gemm_02_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def exported_symbols() -> list[str]:
+    return list(_SIGS)
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise MoEError(status, what)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_shape(T, H, I, E, k, precision="bf16", num_cus=0) -> moe_shape:
+    p = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
+    return moe_shape(int(T), int(H), int(I), int(E), int(k), p, int(num_cus))
+
+
+# ------------------------------------------------------------ C entry points
+
+def moe_status_string(status: int) -> str:
+    try:
+        return lib().moe_status_string(int(status)).decode()
+    except RuntimeError:
+        return STATUS_NAMES.get(int(status), f"status {status}")
+
+
+def moe_workspace_size(shape: moe_shape):
+    f, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().moe_workspace_size(ctypes.byref(shape), ctypes.byref(f), ctypes.byref(s), ctypes.byref(b)),
+           "moe_workspace_size")
+    return f.value, s.value, b.value
+
+
+def moe_get_saved_layout(shape: moe_shape) -> dict:
+    out = moe_saved_layout()
+    _check(lib().moe_get_saved_layout(ctypes.byref(shape), ctypes.byref(out)), "moe_get_saved_layout")
+    return {n: getattr(out, n) for n, _ in moe_saved_layout._fields_}
+
+
+def moe_permute_scratch_bytes(shape: moe_shape) -> int:
+    return int(lib().moe_permute_scratch_bytes(ctypes.byref(shape)))
+
+
+def moe_permute(shape, topk_idx, counts, offsets, row_of, src_of, scratch, stream=None) -> None:
+    _check(lib().moe_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(row_of),
+                             _ptr(src_of), _ptr(scratch), _stream(stream)), "moe_permute")
+
+
+def moe_fwd(shape, x, topk_idx, topk_w, W13, W2, W13_scale, W2_scale, y, saved, ws, stream=None) -> None:
+    _check(lib().moe_fwd(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W13), _ptr(W2),
+                         _ptr(W13_scale), _ptr(W2_scale), _ptr(y), _ptr(saved), _ptr(ws),
+                         ws.numel() * ws.element_size(), _stream(stream)), "moe_fwd")
+
+
+def moe_bwd(shape, dy, x, topk_idx, topk_w, W13, W2, W13_scale, W2_scale, saved, dx, d_topk_w, dW13, dW2,
+            ws, stream=None) -> None:
+    _check(lib().moe_bwd(ctypes.byref(shape), _ptr(dy), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W13),
+                         _ptr(W2), _ptr(W13_scale), _ptr(W2_scale), _ptr(saved), _ptr(dx), _ptr(d_topk_w),
+                         _ptr(dW13), _ptr(dW2), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_bwd")
+
+
+def moe_read_status(ws, stream=None) -> int:
+    out = ctypes.c_int32()
+    _check(lib().moe_read_status(_ptr(ws), ctypes.byref(out), _stream(stream)), "moe_read_status")
+    return out.value
+
+
+def moe_set_kernel_timing(enable: bool) -> None:
+    _check(lib().moe_set_kernel_timing(1 if enable else 0), "moe_set_kernel_timing")
+
+
+def moe_kernel_timing_collect(max_entries: int = 64) -> dict:
+    arr = (moe_kernel_time * max_entries)()
+    n = ctypes.c_int32()
+    _check(lib().moe_kernel_timing_collect(arr, max_entries, ctypes.byref(n)), "moe_kernel_timing_collect")
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+# ------------------------------------------------------------ buffer plumbing
+
+@dataclasses.dataclass
+class LayerBuffers:
+    """Device buffers of one layer shape (allocated once with torch)."""
+    shape: moe_shape
+    fwd_ws: torch.Tensor
+    saved: torch.Tensor
+    bwd_ws: torch.Tensor
+    layout: dict
+
+    @classmethod
+    def allocate(cls, shape: moe_shape, device="cuda") -> "LayerBuffers":
+        f, s, b = moe_workspace_size(shape)
+        mk = lambda n: torch.empty(max(n, 256), dtype=torch.uint8, device=device)  # noqa: E731
+        return cls(shape, mk(f), mk(s), mk(b), moe_get_saved_layout(shape))
+
+    def saved_view(self, name: str, dtype, count: int) -> torch.Tensor:
+        off = self.layout[name]
+        esz = torch.empty((), dtype=dtype).element_size()
+        return self.saved[off:off + count * esz].view(dtype)
+
+
+def forward(buf: LayerBuffers, x, topk_idx, topk_w, W13, W2, y=None, training=True, stream=None):
+    s = buf.shape
+    if y is None:
+        y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=x.device)
+    moe_fwd(s, x, topk_idx, topk_w, W13, W2, None, None, y, buf.saved if training else None, buf.fwd_ws,
+            stream)
+    return y
+
+
+def backward(buf: LayerBuffers, dy, x, topk_idx, topk_w, W13, W2, grads=None, stream=None):
+    s = buf.shape
+    if grads is None:
+        dev = dy.device
+        grads = (torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev),
+                 torch.empty((s.T, s.k), dtype=torch.float32, device=dev),
+                 torch.empty((s.E, 2 * s.I, s.H), dtype=torch.bfloat16, device=dev),
+                 torch.empty((s.E, s.H, s.I), dtype=torch.bfloat16, device=dev))
+    dx, dw, dW13, dW2 = grads
+    moe_bwd(s, dy, x, topk_idx, topk_w, W13, W2, None, None, buf.saved, dx, dw, dW13, dW2, buf.bwd_ws, stream)
+    return grads

@@ -1,0 +1,70 @@
+// Host-side launcher declarations for the MoE layer's HIP kernels, and the
+// optional per-kernel event timer used by the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Records one (start, stop) HIP event pair per launch when enabled.
+struct KernelTimer {
+  virtual void begin(const char* name, hipStream_t st) = 0;
+  virtual void end(hipStream_t st) = 0;
+  virtual ~KernelTimer() {}
+};
+
+struct TimedLaunch {
+  KernelTimer* t;
+  hipStream_t st;
+  TimedLaunch(KernelTimer* timer, const char* name, hipStream_t s) : t(timer), st(s) {
+    if (t) t->begin(name, st);
+  }
+  ~TimedLaunch() {
+    if (t) t->end(st);
+  }
+};
+
+// ---------------------------------------------------------------- permute
+int permute_num_chunks(int64_t n);
+size_t permute_scratch_bytes(int64_t n, int E);
+hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
+                          int32_t* offsets, int32_t* row_of, int32_t* src_of, void* scratch,
+                          hipStream_t st, KernelTimer* timer);
+
+// ---------------------------------------------------------------- combine
+// y[t] = sum_j rows[row_of[t*k+j]]  (bf16 rows of width H, fp32 sum, ascending j)
+// and, when dwpart != nullptr, d_topk_w[f] = sum_c dwpart[row_of[f]*nparts + c].
+hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of, int64_t T, int k, int64_t H,
+                          uint16_t* out, const float* dwpart, int nparts, float* d_topk_w,
+                          hipStream_t st, KernelTimer* timer, const char* name);
+
+// ---------------------------------------------------------------- grouped GEMMs
+struct GemmProblem {
+  int64_t T, H, I, E, k;
+  int num_cus;  // persistent grid cap in CUs
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* src_of;
+  const float* topk_w;
+};
+
+// forward
+hipError_t launch_gemm1_swiglu(const GemmProblem& p, const uint16_t* x, const uint16_t* W13,
+                               uint16_t* h13, uint16_t* act, hipStream_t st, KernelTimer* timer);
+hipError_t launch_gemm2_scale(const GemmProblem& p, const uint16_t* act, const uint16_t* W2,
+                              uint16_t* out_rows, hipStream_t st, KernelTimer* timer);
+// backward
+int dh_num_parts(int64_t I);
+hipError_t launch_gemm_dh(const GemmProblem& p, const uint16_t* dy, const uint16_t* W2,
+                          const uint16_t* h13, uint16_t* dh13, float* dwpart, hipStream_t st,
+                          KernelTimer* timer);
+hipError_t launch_gemm_dx(const GemmProblem& p, const uint16_t* dh13, const uint16_t* W13,
+                          uint16_t* dx_rows, hipStream_t st, KernelTimer* timer);
+hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x,
+                            uint16_t* dW13, hipStream_t st, KernelTimer* timer);
+hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint16_t* act,
+                           uint16_t* dW2, hipStream_t st, KernelTimer* timer);
+
+}  // namespace moe

@@ -1,0 +1,365 @@
+// C ABI of the MoE expert layer: validation, buffer layout, launch order.
+// Declarations and the contract of every entry point are in include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// ------------------------------------------------------------ shape checks
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_NULL;
+  if (s->precision < MOE_BF16 || s->precision > MOE_FP8_BWD) return MOE_ERR_PRECISION;
+  if (s->T < 0 || s->E < 1 || s->E > 1024 || s->k < 1 || s->k > s->E) return MOE_ERR_SHAPE;
+  if (s->H < 256 || s->H > 16384 || s->H % 256 != 0) return MOE_ERR_SHAPE;
+  if (s->I < 128 || s->I > 8192 || s->I % 128 != 0) return MOE_ERR_SHAPE;
+  if (s->T * s->k >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (s->num_cus < 0) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------------ buffer layouts
+
+struct FwdLayout {
+  size_t perm;     // permutation scratch (status word first)
+  size_t rows;     // bf16 [Tk, H] weighted expert outputs
+  size_t inf;      // saved-like area used when no saved buffer is given
+  size_t total;
+};
+
+moe_saved_layout saved_layout(const moe_shape& s) {
+  const int64_t Tk = s.T * s.k;
+  moe_saved_layout L;
+  size_t o = 0;
+  L.counts = o;  o = align_up(o + size_t(s.E) * 4);
+  L.offsets = o; o = align_up(o + size_t(s.E + 1) * 4);
+  L.row_of = o;  o = align_up(o + size_t(Tk) * 4);
+  L.src_of = o;  o = align_up(o + size_t(Tk) * 4);
+  L.h13 = o;     o = align_up(o + size_t(Tk) * size_t(2 * s.I) * 2);
+  L.act = o;     o = align_up(o + size_t(Tk) * size_t(s.I) * 2);
+  L.total = o;
+  return L;
+}
+
+FwdLayout fwd_layout(const moe_shape& s) {
+  const int64_t Tk = s.T * s.k;
+  FwdLayout L;
+  size_t o = 0;
+  L.perm = o; o = align_up(o + permute_scratch_bytes(Tk, int(s.E)));
+  L.rows = o; o = align_up(o + size_t(Tk) * size_t(s.H) * 2);
+  L.inf = o;  o = align_up(o + saved_layout(s).total);
+  L.total = o;
+  return L;
+}
+
+struct BwdLayout {
+  size_t dh13, dwpart, dxrows, total;
+};
+
+BwdLayout bwd_layout(const moe_shape& s) {
+  const int64_t Tk = s.T * s.k;
+  BwdLayout L;
+  size_t o = 0;
+  L.dh13 = o;   o = align_up(o + size_t(Tk) * size_t(2 * s.I) * 2);
+  L.dwpart = o; o = align_up(o + size_t(Tk) * size_t(dh_num_parts(s.I)) * 4);
+  L.dxrows = o; o = align_up(o + size_t(Tk) * size_t(s.H) * 2);
+  L.total = o;
+  return L;
+}
+
+// ------------------------------------------------------------ device info
+
+struct DevInfo {
+  bool checked = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+moe_status device_info(int* cus_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_LAUNCH;
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.checked = true;
+  }
+  if (!d.gfx950) return MOE_ERR_ARCH;
+  *cus_out = d.cus;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ kernel timing
+
+struct EventTimer : KernelTimer {
+  struct Rec {
+    std::string name;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void begin(const char* name, hipStream_t st) override {
+    Rec r{name, get(), get()};
+    if (r.a) (void)hipEventRecord(r.a, st);
+    recs.push_back(r);
+  }
+  void end(hipStream_t st) override {
+    if (!recs.empty() && recs.back().b) (void)hipEventRecord(recs.back().b, st);
+  }
+};
+
+std::mutex g_timer_mu;
+bool g_timing = false;
+EventTimer g_timer;
+
+KernelTimer* timer() { return g_timing ? &g_timer : nullptr; }
+
+moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+template <class T>
+const T* at(const void* base, size_t off) {
+  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+int effective_cus(const moe_shape& s, int dev_cus) {
+  return (s.num_cus > 0 && s.num_cus < dev_cus) ? s.num_cus : dev_cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: shape violates H%256, I%128, 1<=k<=E or size limits";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case MOE_ERR_PRECISION: return "MOE_ERR_PRECISION: unknown precision";
+    case MOE_ERR_ARCH: return "MOE_ERR_ARCH: current device is not gfx950";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than required";
+    case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: HIP launch or runtime call failed";
+    case MOE_ERR_ROUTING: return "MOE_ERR_ROUTING: an expert id was outside [0, E)";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: not implemented in this build";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_workspace_size(const moe_shape* s, size_t* fwd_ws, size_t* saved_bytes,
+                              size_t* bwd_ws) {
+  const moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (fwd_ws) *fwd_ws = fwd_layout(*s).total;
+  if (saved_bytes) *saved_bytes = saved_layout(*s).total;
+  if (bwd_ws) *bwd_ws = bwd_layout(*s).total;
+  return MOE_OK;
+}
+
+moe_status moe_get_saved_layout(const moe_shape* s, moe_saved_layout* out) {
+  const moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_ERR_NULL;
+  *out = saved_layout(*s);
+  return MOE_OK;
+}
+
+size_t moe_permute_scratch_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return permute_scratch_bytes(s->T * s->k, int(s->E));
+}
+
+moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* row_of, int32_t* src_of, void* scratch,
+                       void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  const int64_t Tk = s->T * s->k;
+  if (!counts || !offsets || !scratch || (Tk > 0 && (!topk_idx || !row_of || !src_of)))
+    return MOE_ERR_NULL;
+  if (!aligned16(scratch)) return MOE_ERR_ALIGN;
+  int cus = 0;
+  if ((st = device_info(&cus)) != MOE_OK) return st;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  return launch_status(launch_permute(topk_idx, Tk, int(s->E), counts, offsets, row_of, src_of,
+                                      scratch, static_cast<hipStream_t>(stream), timer()));
+}
+
+moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                   const float* topk_w, const void* W13, const void* W2, const void* W13_scale,
+                   const void* W2_scale, void* y, void* saved, void* ws, size_t ws_bytes,
+                   void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->precision != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (W13_scale || W2_scale) return MOE_ERR_PRECISION;
+  const int64_t Tk = s->T * s->k;
+  if (!W13 || !W2 || !ws || (s->T > 0 && (!x || !topk_idx || !topk_w || !y))) return MOE_ERR_NULL;
+  const void* ptrs[] = {x, topk_idx, topk_w, W13, W2, y, saved, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+  const FwdLayout FL = fwd_layout(*s);
+  if (ws_bytes < FL.total) return MOE_ERR_WORKSPACE;
+  int cus = 0;
+  if ((st = device_info(&cus)) != MOE_OK) return st;
+
+  const moe_saved_layout SL = saved_layout(*s);
+  void* sv = saved ? saved : at<char>(ws, FL.inf);
+  int32_t* counts = at<int32_t>(sv, SL.counts);
+  int32_t* offsets = at<int32_t>(sv, SL.offsets);
+  int32_t* row_of = at<int32_t>(sv, SL.row_of);
+  int32_t* src_of = at<int32_t>(sv, SL.src_of);
+  uint16_t* h13 = saved ? at<uint16_t>(sv, SL.h13) : nullptr;
+  uint16_t* act = at<uint16_t>(sv, SL.act);
+  uint16_t* rows = at<uint16_t>(ws, FL.rows);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  KernelTimer* tm = timer();
+  hipError_t e = launch_permute(topk_idx, Tk, int(s->E), counts, offsets, row_of, src_of,
+                                at<char>(ws, FL.perm), hs, tm);
+  if (e != hipSuccess || s->T == 0) return launch_status(e);
+  GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w};
+  if ((e = launch_gemm1_swiglu(gp, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W13),
+                               h13, act, hs, tm)) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  if ((e = launch_gemm2_scale(gp, act, static_cast<const uint16_t*>(W2), rows, hs, tm)) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  e = launch_combine(rows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(y), nullptr, 0,
+                     nullptr, hs, tm, "combine_y");
+  return launch_status(e);
+}
+
+moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int32_t* topk_idx,
+                   const float* topk_w, const void* W13, const void* W2, const void* W13_scale,
+                   const void* W2_scale, const void* saved, void* dx, float* d_topk_w,
+                   void* dW13, void* dW2, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->precision != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (W13_scale || W2_scale) return MOE_ERR_PRECISION;
+  (void)topk_idx;  // the permutation comes from `saved`
+  if (!W13 || !W2 || !saved || !dW13 || !dW2 || !ws ||
+      (s->T > 0 && (!dy || !x || !topk_w || !dx || !d_topk_w)))
+    return MOE_ERR_NULL;
+  const void* ptrs[] = {dy, x, topk_idx, topk_w, W13, W2, saved, dx, d_topk_w, dW13, dW2, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+  const BwdLayout BL = bwd_layout(*s);
+  if (ws_bytes < BL.total) return MOE_ERR_WORKSPACE;
+  int cus = 0;
+  if ((st = device_info(&cus)) != MOE_OK) return st;
+
+  const moe_saved_layout SL = saved_layout(*s);
+  const int32_t* counts = at<int32_t>(saved, SL.counts);
+  const int32_t* offsets = at<int32_t>(saved, SL.offsets);
+  const int32_t* row_of = at<int32_t>(saved, SL.row_of);
+  const int32_t* src_of = at<int32_t>(saved, SL.src_of);
+  const uint16_t* h13 = at<uint16_t>(saved, SL.h13);
+  const uint16_t* act = at<uint16_t>(saved, SL.act);
+  uint16_t* dh13 = at<uint16_t>(ws, BL.dh13);
+  float* dwpart = at<float>(ws, BL.dwpart);
+  uint16_t* dxrows = at<uint16_t>(ws, BL.dxrows);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const uint16_t* dy16 = static_cast<const uint16_t*>(dy);
+  const uint16_t* x16 = static_cast<const uint16_t*>(x);
+
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  KernelTimer* tm = timer();
+  GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w};
+  hipError_t e = hipSuccess;
+  if (s->T > 0) {
+    if ((e = launch_gemm_dh(gp, dy16, static_cast<const uint16_t*>(W2), h13, dh13, dwpart, hs, tm)) !=
+        hipSuccess)
+      return MOE_ERR_LAUNCH;
+    if ((e = launch_gemm_dx(gp, dh13, static_cast<const uint16_t*>(W13), dxrows, hs, tm)) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    if ((e = launch_combine(dxrows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(dx), dwpart,
+                            dh_num_parts(s->I), d_topk_w, hs, tm, "combine_dx_dw")) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+  }
+  if ((e = launch_gemm_dw13(gp, dh13, x16, static_cast<uint16_t*>(dW13), hs, tm)) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  e = launch_gemm_dw2(gp, dy16, act, static_cast<uint16_t*>(dW2), hs, tm);
+  return launch_status(e);
+}
+
+moe_status moe_read_status(const void* fwd_ws, int32_t* out, void* stream) {
+  if (!fwd_ws || !out) return MOE_ERR_NULL;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(out, fwd_ws, sizeof(int32_t), hipMemcpyDeviceToHost, hs) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  if (hipStreamSynchronize(hs) != hipSuccess) return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}
+
+moe_status moe_set_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_timing = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_kernel_timing_collect(moe_kernel_time* out, int32_t max, int32_t* n_out) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  std::vector<moe_kernel_time> agg;
+  moe_status st = MOE_OK;
+  for (auto& r : g_timer.recs) {
+    float ms = 0.f;
+    if (!r.a || !r.b || hipEventSynchronize(r.b) != hipSuccess ||
+        hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = MOE_ERR_LAUNCH;
+    }
+    size_t i = 0;
+    for (; i < agg.size(); ++i)
+      if (r.name == agg[i].name) break;
+    if (i == agg.size()) {
+      moe_kernel_time kt;
+      std::memset(&kt, 0, sizeof(kt));
+      std::strncpy(kt.name, r.name.c_str(), sizeof(kt.name) - 1);
+      agg.push_back(kt);
+    }
+    agg[i].launches += 1;
+    agg[i].total_ms += ms;
+    if (r.a) g_timer.pool.push_back(r.a);
+    if (r.b) g_timer.pool.push_back(r.b);
+  }
+  g_timer.recs.clear();
+  int32_t n = 0;
+  for (size_t i = 0; i < agg.size() && n < max; ++i) out[n++] = agg[i];
+  if (n_out) *n_out = n;
+  return st;
+}
+
+}  // extern "C"

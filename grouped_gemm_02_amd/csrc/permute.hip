@@ -1,0 +1,187 @@
+// Expert-contiguous permutation of the routed (token, slot) pairs.
+//
+// Routing indices become a token reorder in which every expert's rows are
+// contiguous and indexed by group offsets, the first stage of the fused
+// pipeline (kongchang.com explainer, grouped-GEMM note). Integer work, so
+// the result is exact and deterministic: the rows of one expert keep the
+// ascending order of the flat pair index f = t*k + j.
+//
+// Three launches:
+//   permute_hist    per chunk of kChunk pairs, per-expert counts (LDS integer
+//                   atomics: the totals do not depend on their order); column E
+//                   counts ids outside [0, E)
+//   permute_scan    one workgroup: per-expert totals, exclusive prefix over
+//                   experts (offsets) and each chunk's starting row per expert
+//   permute_scatter per chunk again, in pair order: the rank of a pair among
+//                   the equal ids before it comes from wavefront ballots
+//                   (lanes with the same id found bit by bit), per-wave counts
+//                   in LDS and a running per-chunk count, then
+//                   row_of[f] = start + rank and src_of[row] = f.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kPermThreads = 256;
+constexpr int kPermItems = 16;
+constexpr int kChunk = kPermThreads * kPermItems;  // 4096 pairs per workgroup
+constexpr int kPermWaves = kPermThreads / kWave;
+
+__global__ __launch_bounds__(kPermThreads) void permute_hist(const int32_t* __restrict__ idx,
+                                                             int64_t n, int E,
+                                                             int32_t* __restrict__ chunk_hist) {
+  extern __shared__ int32_t hist[];  // E + 1
+  for (int e = threadIdx.x; e <= E; e += kPermThreads) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = int64_t(blockIdx.x) * kChunk;
+  for (int it = 0; it < kPermItems; ++it) {
+    const int64_t f = base + int64_t(it) * kPermThreads + threadIdx.x;
+    if (f < n) {
+      int e = idx[f];
+      if (e < 0 || e >= E) e = E;
+      atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* out = chunk_hist + int64_t(blockIdx.x) * (E + 1);
+  for (int e = threadIdx.x; e <= E; e += kPermThreads) out[e] = hist[e];
+}
+
+// One workgroup of 1024 threads. chunk_hist [nchunk][E+1] is turned in place
+// into each chunk's first row per expert; counts/offsets written; status word
+// set when any id was out of range.
+__global__ __launch_bounds__(1024) void permute_scan(int32_t* __restrict__ chunk_hist, int nchunk,
+                                                     int E, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ status) {
+  __shared__ int32_t tot[1025];
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  // per-expert running sums over chunks (column E = invalid ids)
+  for (int e = tid; e <= E; e += 1024) {
+    int32_t run = 0;
+    for (int c = 0; c < nchunk; ++c) {
+      int32_t* p = chunk_hist + int64_t(c) * (E + 1) + e;
+      const int32_t v = *p;
+      *p = run;
+      run += v;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  // exclusive scan of tot[0..E) (E <= 1024): Hillis-Steele on a copy
+  int32_t v = tid < E ? tot[tid] : 0;
+  part[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  const int32_t excl = part[tid] - v;  // exclusive prefix at tid
+  if (tid < E) {
+    counts[tid] = v;
+    offsets[tid] = excl;
+  }
+  if (tid == E - 1) offsets[E] = part[tid];
+  if (tid == 0) status[0] = tot[E] > 0 ? 8 /* MOE_ERR_ROUTING */ : 0;
+  __syncthreads();
+  // add each expert's offset to its per-chunk starts
+  for (int e = tid; e < E; e += 1024) {
+    const int32_t o = offsets[e];
+    for (int c = 0; c < nchunk; ++c) chunk_hist[int64_t(c) * (E + 1) + e] += o;
+  }
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_scatter(
+    const int32_t* __restrict__ idx, int64_t n, int E, int id_bits,
+    const int32_t* __restrict__ chunk_start, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ src_of) {
+  extern __shared__ int32_t sm[];
+  int32_t* running = sm;                // [E+1]  rows already placed in this chunk
+  int32_t* wave_cnt = sm + (E + 1);     // [kPermWaves][E+1]
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = lane_id();
+  for (int i = tid; i < (E + 1) * (1 + kPermWaves); i += kPermThreads) sm[i] = 0;
+  const int32_t* start = chunk_start + int64_t(blockIdx.x) * (E + 1);
+  const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  __syncthreads();
+  const int64_t base = int64_t(blockIdx.x) * kChunk;
+  for (int it = 0; it < kPermItems; ++it) {
+    const int64_t f = base + int64_t(it) * kPermThreads + tid;
+    const bool in_range = f < n;
+    int e = E;
+    if (in_range) {
+      e = idx[f];
+      if (e < 0 || e >= E) e = E;
+    }
+    // peers: lanes of this wave holding the same id (and in range)
+    uint64_t peers = __ballot(in_range);
+    if (!in_range) peers = ~peers;
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      peers &= bit ? ones : ~ones;
+    }
+    const int rank_in_wave = __popcll(peers & lanes_below);
+    const bool leader = rank_in_wave == 0;
+    if (in_range && leader) wave_cnt[wave * (E + 1) + e] = __popcll(peers);
+    __syncthreads();
+    if (in_range) {
+      int32_t before = running[e];
+      for (int w = 0; w < wave; ++w) before += wave_cnt[w * (E + 1) + e];
+      if (e < E) {
+        const int32_t row = start[e] + before + rank_in_wave;
+        row_of[f] = row;
+        src_of[row] = static_cast<int32_t>(f);
+      } else {
+        row_of[f] = -1;
+      }
+    }
+    __syncthreads();
+    if (in_range && leader) {
+      atomicAdd(&running[e], __popcll(peers));
+      wave_cnt[wave * (E + 1) + e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+int permute_num_chunks(int64_t n) { return int((n + kChunk - 1) / kChunk); }
+
+size_t permute_scratch_bytes(int64_t n, int E) {
+  // [status word, padded to 256 B][chunk table nchunk x (E+1) int32]
+  const int64_t nchunk = permute_num_chunks(n);
+  return 256 + size_t(nchunk > 0 ? nchunk : 1) * size_t(E + 1) * 4;
+}
+
+hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
+                          int32_t* offsets, int32_t* row_of, int32_t* src_of, void* scratch,
+                          hipStream_t st, KernelTimer* timer) {
+  int32_t* status = static_cast<int32_t*>(scratch);
+  int32_t* chunk_tab = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + 256);
+  const int nchunk = permute_num_chunks(n);
+  int id_bits = 0;
+  while ((1 << id_bits) <= E) ++id_bits;  // ids 0..E (E marks invalid) fit
+  if (nchunk > 0) {
+    TimedLaunch t(timer, "permute_hist", st);
+    hipLaunchKernelGGL(permute_hist, dim3(nchunk), dim3(kPermThreads), (E + 1) * 4, st, idx, n,
+                       E, chunk_tab);
+  }
+  {
+    TimedLaunch t(timer, "permute_scan", st);
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, st, chunk_tab, nchunk, E, counts,
+                       offsets, status);
+  }
+  if (nchunk > 0) {
+    TimedLaunch t(timer, "permute_scatter", st);
+    hipLaunchKernelGGL(permute_scatter, dim3(nchunk), dim3(kPermThreads),
+                       (E + 1) * (1 + kPermWaves) * 4, st, idx, n, E, id_bits, chunk_tab, row_of,
+                       src_of);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -77,6 +77,8 @@ def _gen(seed: int, device) -> torch.Generator:
 
 def _normal_bf16(shape, std, g, device) -> torch.Tensor:
     out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    if out.numel() == 0:
+        return out
     # draw slab by slab along the first axis to bound fp32 temporaries
     flat = out.view(shape[0], -1)
     step = max(1, (1 << 26) // max(1, flat.shape[1]))

@@ -1,0 +1,192 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) trainable MoE expert layer.
+ *
+ * One GPU's share of a fused mixture-of-experts layer, forward and backward.
+ * The computation follows the pages that describe Prime Mega MoE:
+ *   - MarkTechPost article "Prime Intellect Releases Prime Mega MoE: Trainable
+ *     Fused MoE Kernel, 3.11x Faster Forward Pass", section "How does the
+ *     fused kernel work?": one call covers the two expert linear layers with
+ *     SwiGLU between them and the weighted combine; the backward adds the
+ *     missing gradient pass.
+ *   - kongchang.com explainer, grouped-GEMM note: routing indices become a
+ *     token reorder, then one grouped GEMM call indexes each expert's
+ *     differently-sized matrix product by group offsets, then activation and
+ *     routing-weighted aggregation.
+ *   - ic.work analysis, section on hardware constraints: bias-free gated
+ *     experts only, hidden size divisible by 256, intermediate size divisible
+ *     by 128; precisions BF16, MXFP8 and blockwise FP8.
+ * The router is outside the call (ic.work analysis, section on idealised
+ * assumptions: the single-layer benchmark excludes the router), so routing
+ * arrives as (topk_idx, topk_w). There is no cross-GPU dispatch.
+ *
+ * Notation: T tokens, H hidden, I expert intermediate, E experts, k experts
+ * per token, M = T*k routed (token, slot) pairs, f = t*k + j the flat pair.
+ *
+ * Math (fp32 accumulation; SwiGLU a = silu(g)*u, silu(g) = g*sigmoid(g)):
+ *   g = W13[e][0:I] x[t],  u = W13[e][I:2I] x[t],  o = W2[e] (silu(g)*u)
+ *   y[t] = sum_j topk_w[t,j] * o(t, j)
+ * Backward of L = <dY, y>:
+ *   d_topk_w[t,j] = <dY[t], o>,  dO = w dY[t],  dA = W2[e]^T dO,
+ *   dg = dA*u*sig(g)*(1 + g*(1 - sig(g))),  du = dA*silu(g),
+ *   dx[t] += W13[e]^T [dg;du],  dW13[e] += [dg;du] x[t]^T,  dW2[e] += dO a^T.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are device memory owned by the caller; the library
+ *     never allocates, frees or synchronises on the forward/backward path.
+ *     Tensors are dense and row-major with the shapes given below; every
+ *     tensor pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream); all work is
+ *     enqueued on it in order. Results are ready when the stream says so.
+ *   - Host-checkable preconditions are checked before anything is launched;
+ *     on error the call returns a status and enqueues nothing.
+ *   - Expert ids outside [0, E) are dropped (the pair contributes nothing and
+ *     gets d_topk_w = 0); the forward records this in a device status word
+ *     read back by moe_read_status.
+ *   - Calls that share a workspace or saved buffer must not overlap.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  MOE_ERR_SHAPE = 2,       /* H%256, I%128, k<1, k>E, T<0, E<1 or size limits */
+  MOE_ERR_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned          */
+  MOE_ERR_PRECISION = 4,   /* unknown precision value                          */
+  MOE_ERR_ARCH = 5,        /* current device is not gfx950                     */
+  MOE_ERR_WORKSPACE = 6,   /* workspace or saved buffer smaller than required  */
+  MOE_ERR_LAUNCH = 7,      /* a HIP launch or runtime call failed              */
+  MOE_ERR_ROUTING = 8,     /* device: some expert id was outside [0, E)        */
+  MOE_ERR_UNSUPPORTED = 9  /* valid request this build does not implement      */
+} moe_status;
+
+/* Precision of the expert GEMMs (ic.work analysis, hardware constraints;
+ * MarkTechPost article, "How do developers use it?": bf16, mxfp8, fp8 and
+ * fp8_bwd = BF16 forward with FP8 backward). */
+typedef enum moe_precision {
+  MOE_BF16 = 0,
+  MOE_FP8_BLOCK = 1,
+  MOE_MXFP8 = 2,
+  MOE_FP8_BWD = 3
+} moe_precision;
+
+/* Problem description. Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= E,
+ * T*k < 2^31, H%256 == 0, I%128 == 0, 256 <= H <= 16384, 128 <= I <= 8192.
+ * num_cus caps how many compute units the persistent GEMMs occupy
+ * (0 = all), so that concurrent kernels (e.g. collectives) keep CUs. */
+typedef struct moe_shape {
+  int64_t T, H, I, E, k;
+  int32_t precision; /* moe_precision */
+  int32_t num_cus;
+} moe_shape;
+
+/* Byte sizes of the three caller-provided buffers for `s`:
+ *   fwd_ws      scratch of moe_fwd (also holds its status word)
+ *   saved_bytes what moe_fwd keeps for moe_bwd (permutation, gate/up
+ *               pre-activations, activations)
+ *   bwd_ws      scratch of moe_bwd
+ * Any output pointer may be NULL. Pure host function. */
+moe_status moe_workspace_size(const moe_shape* s, size_t* fwd_ws, size_t* saved_bytes,
+                              size_t* bwd_ws);
+
+/* Layout of the saved buffer (byte offsets from its start). Pure host. */
+typedef struct moe_saved_layout {
+  size_t counts;    /* int32 [E]      rows per expert                         */
+  size_t offsets;   /* int32 [E+1]    exclusive prefix of counts              */
+  size_t row_of;    /* int32 [T*k]    permuted row of pair f, -1 if dropped   */
+  size_t src_of;    /* int32 [T*k]    pair f of permuted row r (first M used) */
+  size_t h13;       /* bf16 [T*k,2I]  per permuted row: [g | u] (bf16)        */
+  size_t act;       /* bf16 [T*k, I]  per permuted row: silu(g)*u (bf16)      */
+  size_t total;
+} moe_saved_layout;
+moe_status moe_get_saved_layout(const moe_shape* s, moe_saved_layout* out);
+
+/* Expert-contiguous permutation of the routed pairs (kongchang.com explainer,
+ * grouped-GEMM note: routing index -> token reorder -> grouped GEMM indexed
+ * by group offsets). Integer work, deterministic:
+ *   counts[e]  = #{f : topk_idx[f] == e}
+ *   offsets    = exclusive prefix sum of counts, offsets[E] = number of
+ *                valid pairs
+ *   row_of[f]  = offsets[e] + #{f' < f : topk_idx[f'] == e}; -1 if the id
+ *                is outside [0, E)
+ *   src_of[r]  = f with row_of[f] == r, for r < offsets[E]
+ * topk_idx: int32 [T,k]. Outputs: counts int32[E], offsets int32[E+1],
+ * row_of int32[T*k], src_of int32[T*k] (entries past offsets[E] unspecified).
+ * `scratch` must hold moe_permute_scratch_bytes(s) bytes; its first int32 is
+ * the status word (0 or MOE_ERR_ROUTING) after the call. */
+size_t moe_permute_scratch_bytes(const moe_shape* s);
+moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* row_of, int32_t* src_of, void* scratch,
+                       void* stream);
+
+/* Forward of the layer (MarkTechPost article, "How does the fused kernel
+ * work?"; kongchang.com explainer, grouped-GEMM note).
+ *   x        bf16  [T, H]
+ *   topk_idx int32 [T, k]       expert of each pair
+ *   topk_w   fp32  [T, k]       routing weight of each pair, used as given
+ *   W13      bf16  [E, 2I, H]   rows [0,I) gate (W1), rows [I,2I) up (W3)
+ *   W2       bf16  [E, H, I]
+ *   W13_scale, W2_scale         must be NULL for MOE_BF16
+ *   y        bf16  [T, H]       output (written, not accumulated)
+ *   saved    moe_workspace_size().saved_bytes, or NULL for inference only;
+ *            when given it is what moe_bwd reads
+ *   ws       moe_workspace_size().fwd_ws bytes of scratch
+ * Steps: permutation; gate/up grouped GEMM with SwiGLU epilogue; down grouped
+ * GEMM with routing-weight epilogue; gather-reduce combine (fp32 sum over
+ * ascending j, one bf16 rounding). */
+moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                   const float* topk_w, const void* W13, const void* W2, const void* W13_scale,
+                   const void* W2_scale, void* y, void* saved, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Backward of the layer for L = <dY, y> (ic.work analysis, "From 3.11x to
+ * 1.32x": the backward produces activation and weight gradients).
+ *   dy       bf16 [T, H]
+ *   x, topk_idx, topk_w, W13, W2, scales: as passed to moe_fwd
+ *   saved    filled by moe_fwd with the same inputs
+ *   dx       bf16 [T, H]        written
+ *   d_topk_w fp32 [T, k]        written (0 for dropped pairs)
+ *   dW13     bf16 [E, 2I, H]    written (exact zeros for experts with no rows)
+ *   dW2      bf16 [E, H, I]     written (exact zeros for experts with no rows)
+ *   ws       moe_workspace_size().bwd_ws bytes of scratch
+ * Steps: dH grouped GEMM (K = H) with SwiGLU-backward and routing-weight
+ * gradient partials fused in its epilogue; dX grouped GEMM (K = 2I);
+ * gather-reduce of dx and d_topk_w; per-expert dW13 and dW2 GEMMs whose
+ * reduction dimension is that expert's row count. */
+moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int32_t* topk_idx,
+                   const float* topk_w, const void* W13, const void* W2, const void* W13_scale,
+                   const void* W2_scale, const void* saved, void* dx, float* d_topk_w,
+                   void* dW13, void* dW2, void* ws, size_t ws_bytes, void* stream);
+
+/* Copies the routing status word that moe_fwd left in `fwd_ws` (or that
+ * moe_permute left in its scratch) to *out (MOE_OK or MOE_ERR_ROUTING).
+ * Synchronises `stream`. */
+moe_status moe_read_status(const void* fwd_ws, int32_t* out, void* stream);
+
+/* Human-readable name of a status value (static storage). */
+const char* moe_status_string(moe_status st);
+
+/* Optional per-kernel timing. While enabled, every kernel that moe_fwd /
+ * moe_bwd / moe_permute launches is bracketed by HIP events recorded on the
+ * call's stream. moe_kernel_timing_collect waits for those events, adds up
+ * the elapsed times per kernel name, writes at most `max` entries and clears
+ * the record. Not for use under graph capture. */
+typedef struct moe_kernel_time {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} moe_kernel_time;
+moe_status moe_set_kernel_timing(int enable);
+moe_status moe_kernel_timing_collect(moe_kernel_time* out, int32_t max, int32_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/moe.h declares, and rejects bad requests before any
+launch (nothing here reaches a HIP call)."""
+import ctypes
+import json
+import os
+
+import pytest
+
+from tests.helpers import LIB, ROOT, header_symbols
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmoe.so not built")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from grouped_gemm_02_amd import binding
+    binding.lib()
+    return binding
+
+
+def test_library_exports_every_declared_function(B):
+    h = ctypes.CDLL(LIB)
+    names = header_symbols()
+    assert "moe_fwd" in names and "moe_bwd" in names and "moe_permute" in names
+    for n in names:
+        assert hasattr(h, n), f"{n} declared in include/moe.h but not exported"
+    assert sorted(B.exported_symbols()) == names
+
+
+def test_status_strings(B):
+    for code, name in B.STATUS_NAMES.items():
+        assert B.moe_status_string(code).startswith(name)
+
+
+def _shape(B, **kw):
+    d = dict(T=16384, H=2048, I=768, E=128, k=8, precision="bf16", num_cus=0)
+    d.update(kw)
+    return B.make_shape(**d)
+
+
+def test_page_shapes_accepted_and_divisibility_enforced(B):
+    page = json.load(open(os.path.join(ROOT, "tests", "golden", "page_constraints.json")))
+    hd, idv = page["hidden_divisor"], page["intermediate_divisor"]
+    for H, I in ((2048, 768), (4096, 1536)):
+        B.moe_workspace_size(_shape(B, H=H, I=I, E=page["experts"], k=page["top_k"], T=page["tokens_per_gpu"]))
+    for H, I in ((2048 + hd // 2, 768), (2048, 768 + idv // 2), (2048 - hd, 768)):
+        bad = _shape(B, H=H, I=I)
+        if H % hd == 0 and I % idv == 0 and H >= 256:
+            continue
+        with pytest.raises(B.MoEError) as ei:
+            B.moe_workspace_size(bad)
+        assert ei.value.status == 2
+
+
+@pytest.mark.parametrize("kw", [dict(k=0), dict(k=129), dict(E=0), dict(T=-1), dict(E=2000, k=8),
+                                dict(H=128), dict(I=64), dict(T=1 << 28, k=8), dict(num_cus=-1)])
+def test_bad_shapes_rejected(B, kw):
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_workspace_size(_shape(B, **kw))
+    assert ei.value.status == 2
+
+
+def test_bad_precision_rejected(B):
+    s = _shape(B)
+    s.precision = 7
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_workspace_size(s)
+    assert ei.value.status == 4
+
+
+def test_workspace_sizes_cover_the_buffers(B):
+    s = _shape(B)
+    f, sv, b = B.moe_workspace_size(s)
+    Tk, H, I = 16384 * 8, 2048, 768
+    L = B.moe_get_saved_layout(s)
+    assert L["total"] == sv
+    assert L["act"] >= L["h13"] + Tk * 2 * I * 2
+    assert sv >= L["act"] + Tk * I * 2
+    assert f >= Tk * H * 2 + sv            # weighted rows + inference area
+    assert b >= Tk * 2 * I * 2 + Tk * H * 2  # dH13 + dX rows
+
+
+class _Fake:
+    """Stands in for a tensor: only data_ptr / numel / element_size are read."""
+    def __init__(self, ptr, nbytes=1 << 40):
+        self.p, self.n = ptr, nbytes
+
+    def data_ptr(self):
+        return self.p
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+def _fwd_args(ptr=0x10000):
+    return [_Fake(ptr + 0x1000 * i) for i in range(8)]
+
+
+def test_fwd_null_pointer_rejected(B):
+    x, idx, w, W13, W2, y, saved, ws = _fwd_args()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_fwd(_shape(B), x, idx, w, None, W2, None, None, y, saved, ws, stream=0)
+    assert ei.value.status == 1
+
+
+def test_fwd_misaligned_pointer_rejected(B):
+    x, idx, w, W13, W2, y, saved, ws = _fwd_args()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_fwd(_shape(B), _Fake(0x10008), idx, w, W13, W2, None, None, y, saved, ws, stream=0)
+    assert ei.value.status == 3
+
+
+def test_fwd_small_workspace_rejected(B):
+    x, idx, w, W13, W2, y, saved, _ = _fwd_args()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_fwd(_shape(B), x, idx, w, W13, W2, None, None, y, saved, _Fake(0x90000, 1024), stream=0)
+    assert ei.value.status == 6
+
+
+def test_fwd_scales_with_bf16_rejected(B):
+    x, idx, w, W13, W2, y, saved, ws = _fwd_args()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_fwd(_shape(B), x, idx, w, W13, W2, _Fake(0x80000), None, y, saved, ws, stream=0)
+    assert ei.value.status == 4
+
+
+def test_bwd_requires_saved(B):
+    a = _fwd_args()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_bwd(_shape(B), a[0], a[1], a[2], a[3], a[4], a[5], None, None, None, a[6], a[7], a[0], a[1],
+                  _Fake(0x70000), stream=0)
+    assert ei.value.status == 1
+
+
+def test_bwd_small_workspace_rejected(B):
+    a = _fwd_args()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_bwd(_shape(B), a[0], a[1], a[2], a[3], a[4], a[5], None, None, a[6], a[7], a[0], a[1], a[2],
+                  _Fake(0x70000, 4096), stream=0)
+    assert ei.value.status == 6

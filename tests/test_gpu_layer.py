@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Indices (counts, offsets, row_of, src_of) must match bit-exactly; floating
+outputs and gradients must be within the bf16 max-relative-error bound
+(normwise by the reference maximum). Small layers are compared element by
+element; the Qwen3-30B-A3B-shaped layer is compared on sampled tokens and
+experts that the oracle computes one by one.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from grouped_gemm_02_amd import inputs
+from oracle import moe_oracle as orc
+from tests.helpers import TOL_BF16, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from grouped_gemm_02_amd import binding
+    binding.lib()
+    return binding
+
+
+def run_layer(B, cfg, d, num_cus=0):
+    """Forward + backward through the C ABI. Returns host tensors."""
+    shape = B.make_shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, "bf16", num_cus)
+    buf = B.LayerBuffers.allocate(shape)
+    buf.fwd_ws.fill_(0xFF)   # poison scratch: reads of unwritten memory show up
+    buf.bwd_ws.fill_(0xFF)
+    buf.saved.fill_(0xFF)
+    y = B.forward(buf, d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
+    dx, dw, dW13, dW2 = B.backward(buf, d["dy"], d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
+    torch.cuda.synchronize()
+    Tk = cfg.T * cfg.k
+    out = {
+        "y": y, "dx": dx, "dw": dw, "dW13": dW13, "dW2": dW2,
+        "counts": buf.saved_view("counts", torch.int32, cfg.E).clone(),
+        "offsets": buf.saved_view("offsets", torch.int32, cfg.E + 1).clone(),
+        "row_of": buf.saved_view("row_of", torch.int32, Tk).clone(),
+        "src_of": buf.saved_view("src_of", torch.int32, Tk).clone(),
+        "h13": buf.saved_view("h13", torch.bfloat16, Tk * 2 * cfg.I).view(Tk, 2 * cfg.I).clone(),
+        "act": buf.saved_view("act", torch.bfloat16, Tk * cfg.I).view(Tk, cfg.I).clone(),
+        "status": B.moe_read_status(buf.fwd_ws),
+    }
+    return out
+
+
+def check_permutation(out, idx, E):
+    counts, offsets, row_of, src_of = orc.permute(idx, E)
+    M = int(offsets[E])
+    assert np.array_equal(out["counts"].cpu().numpy(), counts)
+    assert np.array_equal(out["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(out["row_of"].cpu().numpy(), row_of)
+    assert np.array_equal(out["src_of"].cpu().numpy()[:M], src_of)
+
+
+def check_full(out, cfg, d, tol=TOL_BF16):
+    """Element-by-element comparison of every output against the oracle."""
+    idx = d["topk_idx"]
+    check_permutation(out, idx, cfg.E)
+    y_ref, pairs = orc.forward(d["x"], idx, d["topk_w"], d["W13"], d["W2"], return_pairs=True)
+    dx_ref, dw_ref, dW13_ref, dW2_ref = orc.backward(d["dy"], d["x"], idx, d["topk_w"], d["W13"], d["W2"])
+    errs = {
+        "y": max_rel_err(orc.as_f64(out["y"]), y_ref),
+        "dx": max_rel_err(orc.as_f64(out["dx"]), dx_ref),
+        "d_topk_w": max_rel_err(orc.as_f64(out["dw"]), dw_ref),
+        "dW13": max_rel_err(orc.as_f64(out["dW13"]), dW13_ref),
+        "dW2": max_rel_err(orc.as_f64(out["dW2"]), dW2_ref),
+    }
+    # saved intermediates, per permuted row
+    _, _, row_of, src_of = orc.permute(idx, cfg.E)
+    M = src_of.size
+    I = cfg.I
+    h13 = orc.as_f64(out["h13"])[:M]
+    errs["g"] = max_rel_err(h13[:, :I], pairs["g"][src_of])
+    errs["u"] = max_rel_err(h13[:, I:], pairs["u"][src_of])
+    errs["a"] = max_rel_err(orc.as_f64(out["act"])[:M], pairs["a"][src_of])
+    _say(f"{cfg.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    # empty experts: exactly zero weight gradients
+    counts = orc.permute(idx, cfg.E)[0]
+    for e in np.nonzero(counts == 0)[0]:
+        assert not out["dW13"][e].any() and not out["dW2"][e].any()
+    assert np.all(np.isfinite(orc.as_f64(out["dx"])))
+
+
+SMALL = [
+    inputs.CONFIGS["tiny"],
+    # several m-tiles per expert with a ragged tail, several n-tiles, K loop > 1
+    inputs.LayerConfig("mid", 600, 512, 384, 7, 3, "uniform", "bf16", 10),
+    # skewed: empty experts and one hot expert; ragged everything
+    inputs.LayerConfig("skew", 333, 256, 128, 16, 4, "zipf", "bf16", 11, zipf_s=1.2, zipf_cold=5),
+    # one expert, top-1: a dense GEMM pair through the grouped path
+    inputs.LayerConfig("one_expert", 300, 256, 256, 1, 1, "uniform", "bf16", 12),
+    # top-1 routing over many experts with short segments
+    inputs.LayerConfig("top1", 257, 768, 128, 40, 1, "uniform", "bf16", 13),
+    # a single token
+    inputs.LayerConfig("one_token", 1, 256, 128, 8, 8, "uniform", "bf16", 14),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_layer_matches_oracle_elementwise(B, cfg):
+    _say(f"case {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    out = run_layer(B, cfg, d)
+    assert out["status"] == 0
+    check_full(out, cfg, d)
+
+
+def test_layer_deterministic_bitwise(B):
+    cfg = SMALL[1]
+    _say(f"case determinism {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    a = run_layer(B, cfg, d)
+    b = run_layer(B, cfg, d)
+    for k in ("y", "dx", "dw", "dW13", "dW2", "h13", "act"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_invalid_expert_ids_are_dropped_and_reported(B):
+    cfg = inputs.LayerConfig("invalid_ids", 200, 256, 128, 8, 2, "uniform", "bf16", 15)
+    _say(f"case {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    idx = d["topk_idx"].clone()
+    idx[3, 1] = 8
+    idx[17, 0] = -1
+    idx[199, 1] = 1 << 20
+    d["topk_idx"] = idx
+    out = run_layer(B, cfg, d)
+    assert out["status"] == 8  # MOE_ERR_ROUTING
+    check_full(out, cfg, d)
+    dw = out["dw"].cpu()
+    assert dw[3, 1] == 0 and dw[17, 0] == 0 and dw[199, 1] == 0
+
+
+def test_zero_tokens_gives_zero_weight_grads(B):
+    cfg = inputs.LayerConfig("empty", 0, 256, 128, 4, 2, "uniform", "bf16", 16)
+    d = inputs.make_layer_inputs(cfg, DEV)
+    out = run_layer(B, cfg, d)
+    assert out["counts"].sum().item() == 0
+    assert not out["dW13"].any() and not out["dW2"].any()
+
+
+def test_num_cus_cap_gives_identical_results(B):
+    cfg = SMALL[1]
+    d = inputs.make_layer_inputs(cfg, DEV)
+    a = run_layer(B, cfg, d)
+    b = run_layer(B, cfg, d, num_cus=13)
+    for k in ("y", "dx", "dw", "dW13", "dW2"):
+        assert torch.equal(a[k], b[k]), k
+
+
+# --------------------------------------------------------------- full size
+
+def _sampled_check(B, cfg, n_tokens=24, experts=None):
+    _say(f"case full-size {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    out = run_layer(B, cfg, d)
+    assert out["status"] == 0
+    check_permutation(out, d["topk_idx"], cfg.E)
+    g = np.random.default_rng(cfg.seed)
+    toks = np.sort(g.choice(cfg.T, n_tokens, replace=False))
+    idx_h = d["topk_idx"].cpu()
+    ys, yr, dxs, dxr, dws, dwr = [], [], [], [], [], []
+    for t in toks:
+        ex = idx_h[t].long()
+        sub = dict(x=d["x"][t:t + 1], idx=torch.arange(cfg.k).view(1, -1), w=d["topk_w"][t:t + 1],
+                   W13=d["W13"][ex], W2=d["W2"][ex], dy=d["dy"][t:t + 1])
+        yr.append(orc.forward(sub["x"], sub["idx"], sub["w"], sub["W13"], sub["W2"])[0])
+        gx, gw, _, _ = orc.backward(sub["dy"], sub["x"], sub["idx"], sub["w"], sub["W13"], sub["W2"])
+        dxr.append(gx[0])
+        dwr.append(gw[0])
+        ys.append(orc.as_f64(out["y"][t]))
+        dxs.append(orc.as_f64(out["dx"][t]))
+        dws.append(orc.as_f64(out["dw"][t]))
+    errs = {"y": max_rel_err(np.array(ys), np.array(yr)),
+            "dx": max_rel_err(np.array(dxs), np.array(dxr)),
+            "d_topk_w": max_rel_err(np.array(dws), np.array(dwr))}
+    counts = out["counts"].cpu().numpy()
+    if experts is None:
+        experts = [int(np.argmax(counts)), int(np.argmin(counts)), cfg.E // 2]
+    for e in experts:
+        f, xe, ie, we, dye = orc.restrict_to_expert(d["x"], d["topk_idx"], d["topk_w"], d["dy"], e)
+        if f.size == 0:
+            assert not out["dW13"][e].any() and not out["dW2"][e].any()
+            continue
+        _, _, r13, r2 = orc.backward(dye, xe, ie, we, d["W13"][e:e + 1], d["W2"][e:e + 1])
+        errs[f"dW13[{e}]"] = max_rel_err(orc.as_f64(out["dW13"][e]), r13[0])
+        errs[f"dW2[{e}]"] = max_rel_err(orc.as_f64(out["dW2"][e]), r2[0])
+    _say(f"{cfg.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL_BF16, (k, v)
+    for k in ("y", "dx", "dW13", "dW2"):
+        assert torch.isfinite(out[k].float()).all(), k
+
+
+def test_qwen3_30b_shape_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["qwen3_30b"])
+
+
+def test_qwen3_30b_shape_zipf_routing_bf16_sampled(B):
+    cfg = inputs.CONFIGS["zipf"].scaled(name="zipf_bf16", precision="bf16")
+    _sampled_check(B, cfg)
