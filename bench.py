@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0
 
 # algorithmic flops per launch of each GEMM, as a multiple of M*H*I
 GEMM_FLOP_FACTOR = {
-    "gemm1_swiglu": 4, "gemm2_scale": 2, "gemm_dh_dswiglu": 2, "gemm_dx": 4, "gemm_dw13": 4, "gemm_dw2": 2,
+    "gemm1_swiglu": 4, "gemm2": 2, "gemm_dh_dswiglu": 2, "gemm_dx": 4, "gemm_dw13": 4, "gemm_dw2": 2,
 }
 
 

@@ -3,29 +3,33 @@
 // One grouped GEMM call runs many differently-sized per-expert matrix
 // products, each indexed by the expert's group offset into the permuted rows
 // (kongchang.com explainer, grouped-GEMM note). Six products make up the
-// layer: the gate/up GEMM with SwiGLU in its epilogue and the down GEMM with
-// the routing-weight scale in its epilogue (MarkTechPost article, "How does
-// the fused kernel work?"), and in the backward the dH GEMM with the SwiGLU
-// derivative and routing-weight-gradient partials in its epilogue, the dX
-// GEMM, and the two weight-gradient GEMMs whose reduction dimension is each
-// expert's row count.
+// layer: the gate/up GEMM with SwiGLU in its epilogue and the down GEMM
+// (MarkTechPost article, "How does the fused kernel work?"), and in the
+// backward the dH GEMM with the SwiGLU derivative and routing-weight-gradient
+// partials in its epilogue, the dX GEMM, and the two weight-gradient GEMMs
+// whose reduction dimension is each expert's row count.
 //
 // Structure shared by all six:
-//   * Output tile C[m][n] of BM x BN, m on the "P" operand, n on the "Q"
-//     operand, C = sum_k P[m][k] Q[n][k], fp32 accumulation in MFMA
-//     registers. Workgroup of 256 threads = 4 waves in a 2 x 2 grid, each wave
-//     a (BM/2) x (BN/2) block of 32x32 MFMA sub-tiles
-//     (v_mfma_f32_32x32x16_bf16). The MFMA's A operand is the Q fragment and
-//     its B operand the P fragment, so each lane ends up holding one row m and
-//     16 columns n of a sub-tile (4 runs of 4 consecutive n): per-row
-//     epilogue scalars (routing weight, row sums) live in one lane.
-//   * Both operands are staged through LDS as rows of BK = 64 k-values with
-//     a 16-byte pad per row (conflict-free 16-byte fragment reads), double
-//     buffered: the global loads of k-tile kt+1 are in flight while tile kt
-//     is multiplied. Operands whose k runs along rows in global memory are
-//     copied as 16-byte chunks; operands whose k runs across rows (weights
-//     read transposed, and both operands of the weight gradients) are loaded
-//     as 8 k-rows x V entities per thread and transposed in registers.
+//   * Output tile C[m][n] of 256 x 256, C = sum_k P[m][k] Q[n][k], fp32
+//     accumulation in MFMA registers. 256 threads = 4 waves in a 2 x 2 grid,
+//     each wave a 128 x 128 block of 4 x 4 sub-tiles of
+//     v_mfma_f32_32x32x16_bf16 (256 accumulator registers per lane). The
+//     MFMA's A operand is the Q fragment and its B operand the P fragment, so
+//     each lane holds one row m and 16 columns n of a sub-tile (4 runs of 4
+//     consecutive n): per-row epilogue scalars live in one lane.
+//   * Both operands are staged through LDS in k-slabs of BK = 64, double
+//     buffered: the global loads of slab kt+1 are in flight (in registers)
+//     while slab kt is multiplied. Every global load is a 16-byte chunk of a
+//     contiguous row:
+//       - "k-major" operands (k contiguous in memory: activations as GEMM
+//         rows, weights in the forward) sit in LDS as [entity][64 + 8 pad]
+//         and are read with 16-byte ds_read_b128 fragments;
+//       - "mn-major" operands (entities contiguous, one memory row per k:
+//         weights in the backward data-gradient GEMMs and both operands of
+//         the weight-gradient GEMMs, whose k is the token row) sit in LDS as
+//         [k][entities + 32 pad] and are read with the gfx950 LDS transpose
+//         read ds_read_b64_tr_b16, which hands every lane 4 consecutive k of
+//         one entity. No register transposes.
 //   * Persistent grid: each workgroup walks tiles blockIdx, +grid, ...; tile
 //     ids are remapped so that the eight XCDs each take a contiguous range
 //     (tiles of one expert share its weight panel in that XCD's L2).
@@ -35,107 +39,117 @@
 namespace moe {
 
 constexpr int BK = 64;
-constexpr int LDS_LD = BK + 8;  // bf16 elements per LDS row: 128 B of data + 16 B pad
+constexpr int BM = 256;   // tile rows (P entities)
+constexpr int BN = 256;   // tile columns (Q entities)
 constexpr int kThreads = 256;
+constexpr int LDK = BK + 8;          // k-major LDS row: 64 k + 8 pad (bf16 elements)
+constexpr int LDN = 256 + 32;        // mn-major LDS row: 256 entities + 32 pad
+constexpr int kOperandLds = 256 * LDK;  // == 64 * LDN: both layouts take 36 KiB
+static_assert(256 * LDK == 64 * LDN, "operand layouts must have the same LDS size");
+constexpr int kStageLds = 2 * kOperandLds;  // P + Q
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // ------------------------------------------------------------------ loaders
 
-// A tile of ROWS entities whose k-values are contiguous in global memory.
-// Thread t copies the 16-byte chunk (t % 8) of rows t/8 + 32*i.
-template <int ROWS>
+// k-major operand: 256 entity rows, each with its k-values contiguous.
+// Thread t copies chunk (t % 8) of rows t/8 + 32*i, i < 8. Row addresses are
+// a tile-uniform base plus a 32-bit element offset per row (-1 = zero row),
+// which keeps the loader at 8 address registers.
 struct KMajorLoader {
-  static constexpr int kPer = ROWS / 32;
-  const uint16_t* ptr[kPer];  // row start (k = 0), nullptr = zero row
+  static constexpr int kPer = 8;
+  const uint16_t* base;
+  int32_t off[kPer];
   u32x4 reg[kPer];
 
-  __device__ __forceinline__ void set_row(int i, const uint16_t* row) {
-    ptr[i] = row ? row + (threadIdx.x & 7) * 8 : nullptr;
-  }
   __device__ __forceinline__ static int row_of_thread(int i) { return (threadIdx.x >> 3) + 32 * i; }
-
+  // row_off: element offset of the row start from `base`, or -1
+  __device__ __forceinline__ void set_row(int i, int64_t row_off) {
+    off[i] = row_off >= 0 ? int32_t(row_off) + (threadIdx.x & 7) * 8 : -1;
+  }
   __device__ __forceinline__ void fetch(int kt) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (ptr[i]) {
-        reg[i] = *reinterpret_cast<const u32x4*>(ptr[i] + kt * BK);
-      } else {
-        reg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int i = 0; i < kPer; ++i)
+      reg[i] = off[i] >= 0 ? *reinterpret_cast<const u32x4*>(base + off[i] + kt * BK) : u32x4{0u, 0u, 0u, 0u};
   }
   __device__ __forceinline__ void store(uint16_t* lds) const {
     const int r0 = threadIdx.x >> 3, c = threadIdx.x & 7;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<u32x4*>(lds + (r0 + 32 * i) * LDS_LD + c * 8) = reg[i];
+      *reinterpret_cast<u32x4*>(lds + (r0 + 32 * i) * LDK + c * 8) = reg[i];
   }
 };
 
-// A tile of MN entities x BK k-values where each k is one row in global
-// memory holding the MN entities contiguously. Thread t loads k-rows
-// kb*8 .. kb*8+7 (kb = t / 32) at entities mb*V .. mb*V+V-1 (mb = t % 32) and
-// writes them transposed: LDS row (entity) gets 8 consecutive k-values.
-// RowFn gives, for an absolute k, the global address of entity 0 of that
-// k-row (nullptr = zeros) and a scale (applied in fp32 when SCALED).
-template <int MN, bool SCALED, class RowFn>
+// mn-major operand: 64 k-rows per slab, each holding the tile's 256 entities
+// contiguously. Thread t copies chunk (t % 32) of k-rows t/32 + 8*i, i < 8.
+// RowFn::index(k) names the memory row of absolute k (-1 = zero row; it may
+// read an index array, so the indices of slab kt+1 are fetched one slab
+// ahead) and RowFn::ptr(index) its address at entity 0 of the tile.
+template <class RowFn>
 struct MNMajorLoader {
-  static constexpr int V = MN / 32;  // 4 or 8 entities per thread
-  static_assert(V == 4 || V == 8, "MN must be 128 or 256");
+  static constexpr int kPer = 8;
   RowFn fn;
-  uint32_t reg[8][V / 2];
-  float scl[8];
+  int nchunks = 32;   // 16-byte chunks of the tile that exist (partial last n-tile)
+  int32_t nxt[kPer];  // memory rows of the next slab
+  u32x4 reg[kPer];
 
-  __device__ __forceinline__ void fetch(int kt) {
-    const int kb = threadIdx.x >> 5, mb = threadIdx.x & 31;
+  __device__ __forceinline__ void prime(int kt) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = kt * BK + kb * 8 + i;
-      float s = 1.f;
-      const uint16_t* p = fn.row(k, s);
-      if (SCALED) scl[i] = s;
-      if (p) {
-        if constexpr (V == 8) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(p + mb * V);
-          reg[i][0] = v[0]; reg[i][1] = v[1]; reg[i][2] = v[2]; reg[i][3] = v[3];
-        } else {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(p + mb * V);
-          reg[i][0] = v[0]; reg[i][1] = v[1];
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < V / 2; ++d) reg[i][d] = 0u;
-      }
-    }
+    for (int i = 0; i < kPer; ++i) nxt[i] = fn.index(kt * BK + (threadIdx.x >> 5) + 8 * i);
   }
-
-  __device__ __forceinline__ void store(uint16_t* lds) const {
-    const int kb = threadIdx.x >> 5, mb = threadIdx.x & 31;
+  __device__ __forceinline__ void fetch(int kt) {
+    const int c = threadIdx.x & 31;
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-      u32x4 out;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t a = reg[2 * p][v >> 1];
-        const uint32_t b = reg[2 * p + 1][v >> 1];
-        if (SCALED) {
-          const float fa = (v & 1) ? bf16_hi(a) : bf16_lo(a);
-          const float fb = (v & 1) ? bf16_hi(b) : bf16_lo(b);
-          out[p] = pack_bf16x2(fa * scl[2 * p], fb * scl[2 * p + 1]);
-        } else {
-          out[p] = (v & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-        }
-      }
-      *reinterpret_cast<u32x4*>(lds + (mb * V + v) * LDS_LD + kb * 8) = out;
+    for (int i = 0; i < kPer; ++i) {
+      const int32_t row = nxt[i];
+      reg[i] = (row >= 0 && c < nchunks) ? *reinterpret_cast<const u32x4*>(fn.ptr(row) + c * 8)
+                                         : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) nxt[i] = fn.index((kt + 1) * BK + (threadIdx.x >> 5) + 8 * i);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+    const int r0 = threadIdx.x >> 5, c = threadIdx.x & 31;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      *reinterpret_cast<u32x4*>(lds + (r0 + 8 * i) * LDN + c * 8) = reg[i];
   }
 };
+
+// ------------------------------------------------------------------ fragments
+
+// 32 entities x 16 k of a k-major tile: lane holds entity (lane % 32),
+// k = kk*16 + 8*(lane/32) + 0..7.
+__device__ __forceinline__ bf16x8 frag_k(const uint16_t* lds, int ent0, int kk) {
+  const int lane = lane_id();
+  return *reinterpret_cast<const bf16x8*>(lds + (ent0 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
+}
+
+// The same fragment from an mn-major tile with two transpose reads. In each
+// 16-lane group, ds_read_b64_tr_b16 gives lane p element (p % 4) of the
+// 8-byte chunk addressed by lane 4j + p/4, for j = 0..3. Lane p therefore
+// addresses k-row k0 + p/4 at entities n0 + 4*(p % 4), and receives the
+// 4 consecutive k of entity n0 + p.
+__device__ __forceinline__ bf16x8 frag_mn(const uint16_t* lds, int ent0, int kk) {
+  const int lane = lane_id();
+  const int g = lane >> 4, p = lane & 15;
+  const int n = ent0 + 16 * (g & 1) + 4 * (p & 3);
+  const int k = kk * 16 + 8 * (g >> 1) + (p >> 2);
+  const uint16_t* a = lds + k * LDN + n;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 4 * LDN));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 // ------------------------------------------------------------------ MFMA core
 
-template <int BM, int BN>
+constexpr int TM = 4;  // 32-row sub-tiles per wave
+constexpr int TN = 4;  // 32-column sub-tiles per wave
+
 struct Acc {
-  static constexpr int TM = BM / 64;
-  static constexpr int TN = BN / 64;
   f32x16 c[TM][TN];
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -150,67 +164,88 @@ struct Acc {
 __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) & 1; }
 __device__ __forceinline__ int wave_n() { return threadIdx.x >> 7; }
 
-// row (within the tile) held by this lane for sub-tile tm
-template <int BM>
-__device__ __forceinline__ int lane_row(int tm) {
-  return wave_m() * (BM / 2) + tm * 32 + (lane_id() & 31);
-}
-// first of 4 consecutive columns (within the tile) held in registers 4*g..4*g+3
-template <int BN>
+// tile row held by this lane in sub-tile tm
+__device__ __forceinline__ int lane_row(int tm) { return wave_m() * 128 + tm * 32 + (lane_id() & 31); }
+// first of 4 consecutive tile columns held in registers 4g .. 4g+3 of sub-tile tn
 __device__ __forceinline__ int lane_col(int tn, int g) {
-  return wave_n() * (BN / 2) + tn * 32 + 8 * g + 4 * (lane_id() >> 5);
+  return wave_n() * 128 + tn * 32 + 8 * g + 4 * (lane_id() >> 5);
 }
 
-template <int BM, int BN>
-__device__ __forceinline__ void mma_ktile(const uint16_t* ldsP, const uint16_t* ldsQ,
-                                          Acc<BM, BN>& acc) {
-  constexpr int TM = BM / 64, TN = BN / 64;
-  const int lane = lane_id();
-  const uint16_t* pb = ldsP + (wave_m() * (BM / 2) + (lane & 31)) * LDS_LD + (lane >> 5) * 8;
-  const uint16_t* qb = ldsQ + (wave_n() * (BN / 2) + (lane & 31)) * LDS_LD + (lane >> 5) * 8;
+// One k-slab of MFMAs for this wave; sub-tiles i >= ACT (rows past the end of
+// a ragged m-tile) are skipped.
+template <bool P_MN, bool Q_MN, int ACT>
+__device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
+  const int pm0 = wave_m() * 128, qn0 = wave_n() * 128;
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
-    bf16x8 pf[TM], qf[TN];
+    bf16x8 qf[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) pf[i] = *reinterpret_cast<const bf16x8*>(pb + i * 32 * LDS_LD + kk * 16);
+    for (int j = 0; j < TN; ++j) qf[j] = Q_MN ? frag_mn(ldsQ, qn0 + 32 * j, kk) : frag_k(ldsQ, qn0 + 32 * j, kk);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) qf[j] = *reinterpret_cast<const bf16x8*>(qb + j * 32 * LDS_LD + kk * 16);
+    for (int i = 0; i < ACT; ++i) {
+      const bf16x8 pf = P_MN ? frag_mn(ldsP, pm0 + 32 * i, kk) : frag_k(ldsP, pm0 + 32 * i, kk);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc.c[i][j] = mfma_32x32x16(qf[j], pf[i], acc.c[i][j]);
+      for (int j = 0; j < TN; ++j) acc.c[i][j] = mfma_32x32x16(qf[j], pf, acc.c[i][j]);
+    }
   }
 }
 
-template <int BM, int BN, class LP, class LQ>
-__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc<BM, BN>& acc) {
-  constexpr int kStage = (BM + BN) * LDS_LD;
+// Runs the k loop of one tile.
+template <bool P_MN, bool Q_MN, class LP, class LQ>
+__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, int rows, uint16_t* lds, Acc& acc) {
+  (void)rows;
   if (nk <= 0) return;
   lp.fetch(0);
   lq.fetch(0);
   lp.store(lds);
-  lq.store(lds + BM * LDS_LD);
+  lq.store(lds + kOperandLds);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    uint16_t* cur = lds + (kt & 1) * kStage;
-    uint16_t* nxt = lds + ((kt + 1) & 1) * kStage;
+    uint16_t* cur = lds + (kt & 1) * kStageLds;
+    uint16_t* nxt = lds + ((kt + 1) & 1) * kStageLds;
     const bool more = kt + 1 < nk;
     if (more) {
       lp.fetch(kt + 1);
       lq.fetch(kt + 1);
     }
-    mma_ktile<BM, BN>(cur, cur + BM * LDS_LD, acc);
+    mma_slab<P_MN, Q_MN, TM>(cur, cur + kOperandLds, acc);
     if (more) {
       lp.store(nxt);
-      lq.store(nxt + BM * LDS_LD);
+      lq.store(nxt + kOperandLds);
     }
     __syncthreads();
   }
 }
 
+// ------------------------------------------------------------------ LDS-staged epilogue
+// After the k loop the operand buffers are free. The accumulators of the two
+// waves of one column half (wave_n() == half) are written there as fp32
+// F[m][c], m < 256, c < 128 (this half's columns), then every thread works on
+// whole 16-byte row pieces, so the epilogue's global loads and stores are
+// coalesced and its register footprint is independent of the accumulators.
+constexpr int FLD = 128 + 4;  // fp32 row stride (the pad spreads rows over banks)
+static_assert(256 * FLD * 4 <= 2 * kStageLds * 2, "fp32 staging must fit the operand buffers");
+
+__device__ __forceinline__ void stage_half(const Acc& acc, float* F, int half) {
+  if (wave_n() != half) return;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = lane_row(tm);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = tn * 32 + 8 * g + 4 * (lane_id() >> 5);
+        const f32x16& a = acc.c[tm][tn];
+        const f32x4 v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        *reinterpret_cast<f32x4*>(F + m * FLD + c) = v;
+      }
+  }
+}
+
 // ------------------------------------------------------------------ scheduling
 
-// Tile t of a persistent walk, remapped so that XCD x (= blockIdx % 8 under
+// Tile of a persistent walk, remapped so that XCD x (= blockIdx % 8 under
 // round-robin dispatch) owns a contiguous block of tile ids in every round.
 __device__ __forceinline__ int64_t first_tile() {
   const int G = gridDim.x, b = blockIdx.x;
@@ -219,8 +254,7 @@ __device__ __forceinline__ int64_t first_tile() {
 }
 
 // s_pref[e] = sum_{e' < e} ceil(counts[e'] / BM), e = 0..E (E <= 1024).
-__device__ void tile_prefix(const int32_t* counts, int E, int BM, int32_t* s_pref,
-                            int32_t* s_tmp) {
+__device__ void tile_prefix(const int32_t* counts, int E, int32_t* s_pref, int32_t* s_tmp) {
   const int tid = threadIdx.x;
   int32_t loc[4];
   int32_t sum = 0;
@@ -251,7 +285,7 @@ __device__ void tile_prefix(const int32_t* counts, int E, int BM, int32_t* s_pre
 
 // expert e with s_pref[e] <= gm < s_pref[e+1]
 __device__ __forceinline__ int find_expert(const int32_t* s_pref, int E, int32_t gm) {
-  int lo = 0, hi = E;  // answer in [lo, hi)
+  int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (s_pref[mid] <= gm) lo = mid; else hi = mid;
@@ -266,7 +300,6 @@ struct RowTile {
   int nt;        // n-tile index
 };
 
-template <int BM>
 __device__ __forceinline__ RowTile decode_row_tile(int64_t t, int NT, const int32_t* s_pref, int E,
                                                    const int32_t* counts, const int32_t* offsets) {
   RowTile r;
@@ -291,19 +324,48 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* o) {
   o[0] = bf16_lo(v[0]); o[1] = bf16_hi(v[0]); o[2] = bf16_lo(v[1]); o[3] = bf16_hi(v[1]);
 }
 
+// Plain bf16 store of the tile into a row-major [*, ld] output starting at
+// (row0, col0); rows beyond `rows` and columns beyond `cols` are not written.
+__device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* out, int64_t ld, int64_t row0,
+                                           int64_t col0, int rows, int cols) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = lane_row(tm);
+    if (m >= rows) continue;
+    uint16_t* o = out + (row0 + m) * ld + col0;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = lane_col(tn, g);
+        if (n >= cols) continue;
+        const f32x16& c = acc.c[tm][tn];
+        store4_bf16(o + n, c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
+      }
+  }
+}
+
+#define MOE_GEMM_SMEM                                                          \
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStageLds];
+
+#define MOE_ROW_SCHED                                                          \
+  __shared__ int32_t s_pref[1025];                                             \
+  __shared__ int32_t s_tmp[kThreads];                                          \
+  tile_prefix(p.counts, E, s_pref, s_tmp);
+
 // ================================================================== forward GEMM1
 // C[r][q] = x[tok(r)] . W13[e][wrow(q)],  K = H. Q rows are arranged so that
-// every wave holds gate and up columns of the same intermediate index in
-// paired sub-tiles; the epilogue forms a = silu(g) * u and stores g, u (for
-// the backward) and a, all as bf16.
+// each wave's sub-tiles come in (gate, up) pairs of the same intermediate
+// indices; the epilogue forms a = silu(g) * u and stores g and u (for the
+// backward) and w * a (routing weight folded in: the down GEMM then needs no
+// scale, and the dW2 GEMM reads the weighted activation directly).
 namespace g1 {
-constexpr int BM = 256, BN = 128;
-constexpr int TN = BN / 64;                 // sub-tiles per wave along n (pairs of g/u)
-constexpr int IPT = BN / 2;                 // intermediate indices per tile
-__device__ __forceinline__ int q_to_w13_row(int q, int nt, int I) {
-  const int wn = q / (BN / 2);
-  const int s = (q % (BN / 2)) / 32;        // sub-tile within the wave
-  const int i = nt * IPT + wn * (BN / 4) + (s >> 1) * 32 + (q & 31);
+constexpr int IPT = BN / 2;  // intermediate indices per tile
+// Q row q -> row of W13[e]
+__device__ __forceinline__ int w13_row(int q, int nt, int I) {
+  const int wn = q >> 7;          // wave column
+  const int s = (q & 127) >> 5;   // sub-tile within the wave: 0 g, 1 u, 2 g, 3 u
+  const int i = nt * IPT + wn * 64 + (s >> 1) * 32 + (q & 31);
   return (s & 1) * I + i;
 }
 }  // namespace g1
@@ -312,301 +374,233 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, c
                                                                 const uint16_t* __restrict__ W13,
                                                                 uint16_t* __restrict__ h13,
                                                                 uint16_t* __restrict__ act) {
-  using namespace g1;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * LDS_LD];
-  __shared__ int32_t s_pref[1025];
-  __shared__ int32_t s_tmp[kThreads];
+  MOE_GEMM_SMEM
   const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
+  MOE_ROW_SCHED
   const int NT = (2 * I) / BN;
-  tile_prefix(p.counts, E, BM, s_pref, s_tmp);
   const int64_t total = int64_t(s_pref[E]) * NT;
-  const int nk = H / BK;
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
-    const RowTile rt = decode_row_tile<BM>(t, NT, s_pref, E, p.counts, p.offsets);
-    KMajorLoader<BM> lp;
+    const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
+    KMajorLoader lp, lq;
+    lp.base = x;
+    lq.base = W13 + int64_t(rt.e) * 2 * I * H;
 #pragma unroll
-    for (int i = 0; i < lp.kPer; ++i) {
-      const int m = lp.row_of_thread(i);
-      const uint16_t* row = nullptr;
-      if (m < rt.rows) row = x + int64_t(p.src_of[rt.row0 + m] / k) * H;
-      lp.set_row(i, row);
+    for (int i = 0; i < KMajorLoader::kPer; ++i) {
+      const int m = KMajorLoader::row_of_thread(i);
+      lp.set_row(i, m < rt.rows ? int64_t(p.src_of[rt.row0 + m] / k) * H : -1);
+      lq.set_row(i, int64_t(g1::w13_row(m, rt.nt, I)) * H);
     }
-    KMajorLoader<BN> lq;
-#pragma unroll
-    for (int i = 0; i < lq.kPer; ++i) {
-      const int q = lq.row_of_thread(i);
-      lq.set_row(i, W13 + (int64_t(rt.e) * 2 * I + q_to_w13_row(q, rt.nt, I)) * H);
-    }
-    Acc<BM, BN> acc;
+    Acc acc;
     acc.zero();
-    mainloop<BM, BN>(lp, lq, nk, lds, acc);
-    // epilogue: pairs (2p, 2p+1) of sub-tiles are (gate, up)
+    mainloop<false, false>(lp, lq, H / BK, rt.rows, lds, acc);
+    // half h holds g and u of intermediate indices nt*128 + h*64 + [0, 64):
+    // staged column (i/32)*64 + i%32 is g, +32 is u.
+    float* F = reinterpret_cast<float*>(lds);
+    for (int h = 0; h < 2; ++h) {
+      stage_half(acc, F, h);
+      __syncthreads();
+      const int io = (threadIdx.x & 15) * 4;            // 4 intermediate indices per thread
+      const int gc = (io >> 5) * 64 + (io & 31);
+      const int i = rt.nt * g1::IPT + h * 64 + io;
+      for (int m = threadIdx.x >> 4; m < rt.rows; m += 16) {
+        const int64_t r = rt.row0 + m;
+        const float w = p.topk_w[p.src_of[r]];
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(F + m * FLD + gc);
+        const f32x4 uv = *reinterpret_cast<const f32x4*>(F + m * FLD + gc + 32);
+        float av[4];
 #pragma unroll
-    for (int tm = 0; tm < acc.TM; ++tm) {
-      const int m = lane_row<BM>(tm);
-      if (m >= rt.rows) continue;
-      const int64_t r = rt.row0 + m;
-#pragma unroll
-      for (int pr = 0; pr < TN / 2; ++pr) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // column of the gate sub-tile 2*pr -> intermediate index
-          const int i = rt.nt * IPT + wave_n() * (BN / 4) + pr * 32 + 8 * g + 4 * (lane_id() >> 5);
-          float gv[4], uv[4], av[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            gv[q] = acc.c[tm][2 * pr][4 * g + q];
-            uv[q] = acc.c[tm][2 * pr + 1][4 * g + q];
-            av[q] = gv[q] * sigmoidf_fast(gv[q]) * uv[q];
-          }
-          if (h13) {
-            store4_bf16(h13 + r * 2 * I + i, gv[0], gv[1], gv[2], gv[3]);
-            store4_bf16(h13 + r * 2 * I + I + i, uv[0], uv[1], uv[2], uv[3]);
-          }
-          store4_bf16(act + r * I + i, av[0], av[1], av[2], av[3]);
+        for (int q = 0; q < 4; ++q) av[q] = w * (gv[q] * sigmoidf_fast(gv[q]) * uv[q]);
+        if (h13) {
+          store4_bf16(h13 + r * 2 * I + i, gv[0], gv[1], gv[2], gv[3]);
+          store4_bf16(h13 + r * 2 * I + I + i, uv[0], uv[1], uv[2], uv[3]);
         }
+        store4_bf16(act + r * I + i, av[0], av[1], av[2], av[3]);
       }
+      __syncthreads();
     }
   }
 }
 
 // ================================================================== forward GEMM2
-// O[r][h] = topk_w[src_of[r]] * (a[r] . W2[e][h]),  K = I.
-namespace g2 {
-constexpr int BM = 256, BN = 128;
-}
-
-__global__ __launch_bounds__(kThreads) void gemm2_scale_kernel(GemmProblem p, const uint16_t* __restrict__ act,
-                                                               const uint16_t* __restrict__ W2,
-                                                               uint16_t* __restrict__ out) {
-  using namespace g2;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * LDS_LD];
-  __shared__ int32_t s_pref[1025];
-  __shared__ int32_t s_tmp[kThreads];
+// O[r][h] = (w a)[r] . W2[e][h],  K = I.
+__global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, const uint16_t* __restrict__ act,
+                                                         const uint16_t* __restrict__ W2,
+                                                         uint16_t* __restrict__ out) {
+  MOE_GEMM_SMEM
   const int E = int(p.E), H = int(p.H), I = int(p.I);
+  MOE_ROW_SCHED
   const int NT = H / BN;
-  tile_prefix(p.counts, E, BM, s_pref, s_tmp);
   const int64_t total = int64_t(s_pref[E]) * NT;
-  const int nk = I / BK;
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
-    const RowTile rt = decode_row_tile<BM>(t, NT, s_pref, E, p.counts, p.offsets);
-    KMajorLoader<BM> lp;
+    const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
+    KMajorLoader lp, lq;
+    lp.base = act + rt.row0 * I;
+    lq.base = W2 + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * I;
 #pragma unroll
-    for (int i = 0; i < lp.kPer; ++i) {
-      const int m = lp.row_of_thread(i);
-      lp.set_row(i, m < rt.rows ? act + (rt.row0 + m) * I : nullptr);
+    for (int i = 0; i < KMajorLoader::kPer; ++i) {
+      const int m = KMajorLoader::row_of_thread(i);
+      lp.set_row(i, m < rt.rows ? int64_t(m) * I : -1);
+      lq.set_row(i, int64_t(m) * I);
     }
-    KMajorLoader<BN> lq;
-#pragma unroll
-    for (int i = 0; i < lq.kPer; ++i) {
-      const int q = lq.row_of_thread(i);
-      lq.set_row(i, W2 + (int64_t(rt.e) * H + int64_t(rt.nt) * BN + q) * I);
-    }
-    Acc<BM, BN> acc;
+    Acc acc;
     acc.zero();
-    mainloop<BM, BN>(lp, lq, nk, lds, acc);
-#pragma unroll
-    for (int tm = 0; tm < acc.TM; ++tm) {
-      const int m = lane_row<BM>(tm);
-      if (m >= rt.rows) continue;
-      const int64_t r = rt.row0 + m;
-      const float w = p.topk_w[p.src_of[r]];
-#pragma unroll
-      for (int tn = 0; tn < acc.TN; ++tn)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = rt.nt * BN + lane_col<BN>(tn, g);
-          const f32x16& c = acc.c[tm][tn];
-          store4_bf16(out + r * H + n, w * c[4 * g], w * c[4 * g + 1], w * c[4 * g + 2], w * c[4 * g + 3]);
-        }
-    }
+    mainloop<false, false>(lp, lq, I / BK, rt.rows, lds, acc);
+    store_tile(acc, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
   }
 }
 
+// ------------------------------------------------------------------ row functions
+
+struct DirectRows {  // memory row k of a row-major tensor
+  const uint16_t* base;  // entity 0 of the tile in row 0
+  int64_t ld;
+  int32_t nrows;         // rows beyond this read as zero
+  __device__ __forceinline__ int32_t index(int k) const { return k < nrows ? k : -1; }
+  __device__ __forceinline__ const uint16_t* ptr(int32_t row) const { return base + int64_t(row) * ld; }
+};
+
+struct TokenRows {  // k-th row of an expert segment -> its token's row
+  const uint16_t* base;  // entity 0 of the tile in token row 0
+  int64_t ld;
+  const int32_t* src;    // src_of + segment start
+  int rows;
+  int kk;                // experts per token
+  __device__ __forceinline__ int32_t index(int k) const { return k < rows ? src[k] / kk : -1; }
+  __device__ __forceinline__ const uint16_t* ptr(int32_t row) const { return base + int64_t(row) * ld; }
+};
+
 // ================================================================== backward dH
-// dA_u[r][i] = dY[tok(r)] . W2[e][:, i]  (K = H; W2 read transposed), then per
+// dA_u[r][i] = dY[tok(r)] . W2[e][:, i]  (K = H; W2 read mn-major), then per
 // element, with g, u from the saved [g | u]:
 //   a = silu(g) u,  dw partial += dA_u a,  dA = w dA_u,
 //   dg = dA u sig(g) (1 + g (1 - sig(g))),  du = dA silu(g).
-// dwpart[r][2*nt + wave_n] holds this wave's partial sum of dA_u * a.
-namespace gdh {
-constexpr int BM = 256, BN = 128;
-struct W2Rows {  // k = h: row h of W2[e], entities i from n0
-  const uint16_t* base;
-  int64_t ld;
-  __device__ __forceinline__ const uint16_t* row(int k, float&) const { return base + int64_t(k) * ld; }
-};
-}  // namespace gdh
-
-int dh_num_parts(int64_t I) { return int(I / gdh::BN) * 2; }
+// dwpart[r][2*nt + wave_n] holds one wave's partial sum of dA_u * a.
+int dh_num_parts(int64_t I) { return int((I + BN - 1) / BN) * 2; }
 
 __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const uint16_t* __restrict__ dy,
                                                            const uint16_t* __restrict__ W2,
                                                            const uint16_t* __restrict__ h13,
                                                            uint16_t* __restrict__ dh13,
                                                            float* __restrict__ dwpart) {
-  using namespace gdh;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * LDS_LD];
-  __shared__ int32_t s_pref[1025];
-  __shared__ int32_t s_tmp[kThreads];
+  MOE_GEMM_SMEM
   const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
-  const int NT = I / BN;
+  MOE_ROW_SCHED
+  const int NT = (I + BN - 1) / BN;  // the last n-tile may hold 128 columns
   const int nparts = 2 * NT;
-  tile_prefix(p.counts, E, BM, s_pref, s_tmp);
   const int64_t total = int64_t(s_pref[E]) * NT;
-  const int nk = H / BK;
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
-    const RowTile rt = decode_row_tile<BM>(t, NT, s_pref, E, p.counts, p.offsets);
-    KMajorLoader<BM> lp;
+    const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
+    KMajorLoader lp;
+    lp.base = dy;
 #pragma unroll
-    for (int i = 0; i < lp.kPer; ++i) {
-      const int m = lp.row_of_thread(i);
-      const uint16_t* row = nullptr;
-      if (m < rt.rows) row = dy + int64_t(p.src_of[rt.row0 + m] / k) * H;
-      lp.set_row(i, row);
+    for (int i = 0; i < KMajorLoader::kPer; ++i) {
+      const int m = KMajorLoader::row_of_thread(i);
+      lp.set_row(i, m < rt.rows ? int64_t(p.src_of[rt.row0 + m] / k) * H : -1);
     }
-    MNMajorLoader<BN, false, W2Rows> lq;
+    MNMajorLoader<DirectRows> lq;
     lq.fn.base = W2 + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN;
     lq.fn.ld = I;
-    Acc<BM, BN> acc;
+    lq.fn.nrows = H;
+    const int ncols = min(BN, I - rt.nt * BN);
+    lq.nchunks = ncols / 8;
+    lq.prime(0);
+    Acc acc;
     acc.zero();
-    mainloop<BM, BN>(lp, lq, nk, lds, acc);
+    mainloop<false, true>(lp, lq, H / BK, rt.rows, lds, acc);
+    // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128)
+    float* F = reinterpret_cast<float*>(lds);
+    for (int h = 0; h < 2; ++h) {
+      stage_half(acc, F, h);
+      __syncthreads();
+      const int c = (threadIdx.x & 15) * 8;             // 8 intermediate indices per thread
+      const bool col_ok = h * 128 + c < ncols;
+      const int i = rt.nt * BN + h * 128 + c;
+      for (int m0 = 0; m0 < rt.rows; m0 += 16) {
+        const int m = m0 + (threadIdx.x >> 4);
+        const bool row_ok = m < rt.rows;
+        float dws = 0.f;
+        if (row_ok && col_ok) {
+          const int64_t r = rt.row0 + m;
+          const float w = p.topk_w[p.src_of[r]];
+          const u32x4 gq = *reinterpret_cast<const u32x4*>(h13 + r * 2 * I + i);
+          const u32x4 uq = *reinterpret_cast<const u32x4*>(h13 + r * 2 * I + I + i);
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(F + m * FLD + c);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(F + m * FLD + c + 4);
+          u32x4 dgq, duq;
 #pragma unroll
-    for (int tm = 0; tm < acc.TM; ++tm) {
-      const int m = lane_row<BM>(tm);
-      const bool valid = m < rt.rows;
-      const int64_t r = rt.row0 + (valid ? m : 0);
-      const float w = valid ? p.topk_w[p.src_of[r]] : 0.f;
-      float dws = 0.f;
-      if (valid) {
+          for (int q = 0; q < 4; ++q) {
+            float dgp[2], dup[2];
 #pragma unroll
-        for (int tn = 0; tn < acc.TN; ++tn)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int i = rt.nt * BN + lane_col<BN>(tn, g);
-            float gv[4], uv[4], dg[4], du[4];
-            load4_bf16(h13 + r * 2 * I + i, gv);
-            load4_bf16(h13 + r * 2 * I + I + i, uv);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float dau = acc.c[tm][tn][4 * g + q];
-              const float s = sigmoidf_fast(gv[q]);
-              const float sg = gv[q] * s;  // silu(g)
-              dws += dau * sg * uv[q];
+            for (int hh = 0; hh < 2; ++hh) {
+              const float gv = hh ? bf16_hi(gq[q]) : bf16_lo(gq[q]);
+              const float uv = hh ? bf16_hi(uq[q]) : bf16_lo(uq[q]);
+              const int e8 = 2 * q + hh;
+              const float dau = e8 < 4 ? d0[e8] : d1[e8 - 4];
+              const float s = sigmoidf_fast(gv);
+              const float sg = gv * s;  // silu(g)
+              dws += dau * sg * uv;
               const float da = w * dau;
-              dg[q] = da * uv[q] * s * (1.f + gv[q] * (1.f - s));
-              du[q] = da * sg;
+              dgp[hh] = da * uv * s * (1.f + gv * (1.f - s));
+              dup[hh] = da * sg;
             }
-            store4_bf16(dh13 + r * 2 * I + i, dg[0], dg[1], dg[2], dg[3]);
-            store4_bf16(dh13 + r * 2 * I + I + i, du[0], du[1], du[2], du[3]);
+            dgq[q] = pack_bf16x2(dgp[0], dgp[1]);
+            duq[q] = pack_bf16x2(dup[0], dup[1]);
           }
+          *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i) = dgq;
+          *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i) = duq;
+        }
+        // sum over the 16 threads of this row (lanes 16g .. 16g+15)
+        dws += __shfl_xor(dws, 8);
+        dws += __shfl_xor(dws, 4);
+        dws += __shfl_xor(dws, 2);
+        dws += __shfl_xor(dws, 1);
+        if (row_ok && (threadIdx.x & 15) == 0) dwpart[(rt.row0 + m) * nparts + 2 * rt.nt + h] = dws;
       }
-      dws += __shfl_xor(dws, 32);
-      if (valid && lane_id() < 32) dwpart[r * nparts + 2 * rt.nt + wave_n()] = dws;
+      __syncthreads();
     }
   }
 }
 
 // ================================================================== backward dX
-// dXr[r][h] = [dg | du][r] . W13[e][:, h]  (K = 2I; W13 read transposed).
-namespace gdx {
-constexpr int BM = 256, BN = 128;
-struct W13Rows {  // k = c: row c of W13[e], entities h from n0
-  const uint16_t* base;
-  int64_t ld;
-  __device__ __forceinline__ const uint16_t* row(int k, float&) const { return base + int64_t(k) * ld; }
-};
-}  // namespace gdx
-
+// dXr[r][h] = [dg | du][r] . W13[e][:, h]  (K = 2I; W13 read mn-major).
 __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, const uint16_t* __restrict__ dh13,
                                                            const uint16_t* __restrict__ W13,
                                                            uint16_t* __restrict__ out) {
-  using namespace gdx;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * LDS_LD];
-  __shared__ int32_t s_pref[1025];
-  __shared__ int32_t s_tmp[kThreads];
+  MOE_GEMM_SMEM
   const int E = int(p.E), H = int(p.H), I = int(p.I);
+  MOE_ROW_SCHED
   const int NT = H / BN;
-  tile_prefix(p.counts, E, BM, s_pref, s_tmp);
   const int64_t total = int64_t(s_pref[E]) * NT;
-  const int nk = (2 * I) / BK;
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
-    const RowTile rt = decode_row_tile<BM>(t, NT, s_pref, E, p.counts, p.offsets);
-    KMajorLoader<BM> lp;
+    const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
+    KMajorLoader lp;
+    lp.base = dh13 + rt.row0 * 2 * I;
 #pragma unroll
-    for (int i = 0; i < lp.kPer; ++i) {
-      const int m = lp.row_of_thread(i);
-      lp.set_row(i, m < rt.rows ? dh13 + (rt.row0 + m) * 2 * I : nullptr);
+    for (int i = 0; i < KMajorLoader::kPer; ++i) {
+      const int m = KMajorLoader::row_of_thread(i);
+      lp.set_row(i, m < rt.rows ? int64_t(m) * 2 * I : -1);
     }
-    MNMajorLoader<BN, false, W13Rows> lq;
+    MNMajorLoader<DirectRows> lq;
     lq.fn.base = W13 + int64_t(rt.e) * 2 * I * H + int64_t(rt.nt) * BN;
     lq.fn.ld = H;
-    Acc<BM, BN> acc;
+    lq.fn.nrows = 2 * I;
+    lq.prime(0);
+    Acc acc;
     acc.zero();
-    mainloop<BM, BN>(lp, lq, nk, lds, acc);
-#pragma unroll
-    for (int tm = 0; tm < acc.TM; ++tm) {
-      const int m = lane_row<BM>(tm);
-      if (m >= rt.rows) continue;
-      const int64_t r = rt.row0 + m;
-#pragma unroll
-      for (int tn = 0; tn < acc.TN; ++tn)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = rt.nt * BN + lane_col<BN>(tn, g);
-          const f32x16& c = acc.c[tm][tn];
-          store4_bf16(out + r * H + n, c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
-        }
-    }
+    mainloop<false, true>(lp, lq, (2 * I) / BK, rt.rows, lds, acc);
+    store_tile(acc, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
   }
 }
 
 // ================================================================== weight gradients
 // dW13[e][c][h] = sum_{r in seg e} dH13[r][c] x[tok(r)][h]
-// dW2[e][h][i]  = sum_{r in seg e} (w_r dY[tok(r)][h]) a[r][i]
-// The reduction runs over the expert's rows (K = rows_e, ragged tail
-// zero-filled); an expert without rows produces an exact-zero tile.
-namespace gw {
-constexpr int BM = 256, BN = 128;
-struct SegRows {  // k = r within the segment: direct rows
-  const uint16_t* base;  // row 0 of the segment, column offset applied
-  int64_t ld;
-  int rows;
-  __device__ __forceinline__ const uint16_t* row(int k, float&) const {
-    return k < rows ? base + int64_t(k) * ld : nullptr;
-  }
-};
-struct GatherRows {  // k = r within the segment: token row tok(r) of a [T, ld] tensor
-  const uint16_t* base;  // column offset applied
-  int64_t ld;
-  const int32_t* src;    // src_of + segment start
-  int rows;
-  int kk;
-  __device__ __forceinline__ const uint16_t* row(int k, float&) const {
-    return k < rows ? base + int64_t(src[k] / kk) * ld : nullptr;
-  }
-};
-struct GatherRowsScaled {  // as GatherRows, scaled by topk_w of the pair
-  const uint16_t* base;
-  int64_t ld;
-  const int32_t* src;
-  const float* w;
-  int rows;
-  int kk;
-  __device__ __forceinline__ const uint16_t* row(int k, float& s) const {
-    if (k >= rows) return nullptr;
-    const int32_t f = src[k];
-    s = w[f];
-    return base + int64_t(f / kk) * ld;
-  }
-};
-}  // namespace gw
-
+// dW2[e][h][i]  = sum_{r in seg e} dY[tok(r)][h] (w a)[r][i]
+// The reduction runs over the expert's rows (K = rows_e, the ragged last
+// slab zero-filled); an expert without rows produces an exact-zero tile.
 __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, const uint16_t* __restrict__ dh13,
                                                              const uint16_t* __restrict__ x,
                                                              uint16_t* __restrict__ dW13) {
-  using namespace gw;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * LDS_LD];
+  MOE_GEMM_SMEM
   const int H = int(p.H), I = int(p.I);
   const int MT = (2 * I) / BM, NT = H / BN;
   const int64_t total = p.E * MT * NT;
@@ -616,42 +610,31 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     const int e = int(t / (int64_t(NT) * MT));
     const int rows = p.counts[e];
     const int64_t off = p.offsets[e];
-    MNMajorLoader<BM, false, SegRows> lp;
+    MNMajorLoader<DirectRows> lp;
     lp.fn.base = dh13 + off * 2 * I + int64_t(mt) * BM;
     lp.fn.ld = 2 * I;
-    lp.fn.rows = rows;
-    MNMajorLoader<BN, false, GatherRows> lq;
+    lp.fn.nrows = rows;
+    lp.prime(0);
+    MNMajorLoader<TokenRows> lq;
     lq.fn.base = x + int64_t(nt) * BN;
     lq.fn.ld = H;
     lq.fn.src = p.src_of + off;
     lq.fn.rows = rows;
     lq.fn.kk = int(p.k);
-    Acc<BM, BN> acc;
+    lq.prime(0);
+    Acc acc;
     acc.zero();
-    mainloop<BM, BN>(lp, lq, (rows + BK - 1) / BK, lds, acc);
-    uint16_t* o = dW13 + int64_t(e) * 2 * I * H;
-#pragma unroll
-    for (int tm = 0; tm < acc.TM; ++tm) {
-      const int64_t c = int64_t(mt) * BM + lane_row<BM>(tm);
-#pragma unroll
-      for (int tn = 0; tn < acc.TN; ++tn)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int h = nt * BN + lane_col<BN>(tn, g);
-          const f32x16& a = acc.c[tm][tn];
-          store4_bf16(o + c * H + h, a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
-        }
-    }
+    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, BM, lds, acc);
+    store_tile(acc, dW13 + int64_t(e) * 2 * I * H, H, int64_t(mt) * BM, int64_t(nt) * BN, BM, BN);
   }
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const uint16_t* __restrict__ dy,
                                                             const uint16_t* __restrict__ act,
                                                             uint16_t* __restrict__ dW2) {
-  using namespace gw;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * LDS_LD];
+  MOE_GEMM_SMEM
   const int H = int(p.H), I = int(p.I);
-  const int MT = H / BM, NT = I / BN;
+  const int MT = H / BM, NT = (I + BN - 1) / BN;  // the last n-tile may hold 128 columns
   const int64_t total = p.E * MT * NT;
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
     const int nt = int(t % NT);
@@ -659,33 +642,24 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     const int e = int(t / (int64_t(NT) * MT));
     const int rows = p.counts[e];
     const int64_t off = p.offsets[e];
-    MNMajorLoader<BM, true, GatherRowsScaled> lp;
+    MNMajorLoader<TokenRows> lp;
     lp.fn.base = dy + int64_t(mt) * BM;
     lp.fn.ld = H;
     lp.fn.src = p.src_of + off;
-    lp.fn.w = p.topk_w;
     lp.fn.rows = rows;
     lp.fn.kk = int(p.k);
-    MNMajorLoader<BN, false, SegRows> lq;
+    lp.prime(0);
+    MNMajorLoader<DirectRows> lq;
     lq.fn.base = act + off * I + int64_t(nt) * BN;
     lq.fn.ld = I;
-    lq.fn.rows = rows;
-    Acc<BM, BN> acc;
+    lq.fn.nrows = rows;
+    const int ncols = min(BN, I - nt * BN);
+    lq.nchunks = ncols / 8;
+    lq.prime(0);
+    Acc acc;
     acc.zero();
-    mainloop<BM, BN>(lp, lq, (rows + BK - 1) / BK, lds, acc);
-    uint16_t* o = dW2 + int64_t(e) * H * I;
-#pragma unroll
-    for (int tm = 0; tm < acc.TM; ++tm) {
-      const int64_t h = int64_t(mt) * BM + lane_row<BM>(tm);
-#pragma unroll
-      for (int tn = 0; tn < acc.TN; ++tn)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int i = nt * BN + lane_col<BN>(tn, g);
-          const f32x16& a = acc.c[tm][tn];
-          store4_bf16(o + h * I + i, a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
-        }
-    }
+    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, BM, lds, acc);
+    store_tile(acc, dW2 + int64_t(e) * H * I, I, int64_t(mt) * BM, int64_t(nt) * BN, BM, ncols);
   }
 }
 
@@ -698,33 +672,28 @@ static int grid_for(int64_t tiles, int num_cus) {
   return int(g);
 }
 
-static int64_t row_tiles_upper(const GemmProblem& p, int BM) {
-  return (p.T * p.k + BM - 1) / BM + p.E;
-}
+static int64_t row_tiles_upper(const GemmProblem& p) { return (p.T * p.k + BM - 1) / BM + p.E; }
 
 hipError_t launch_gemm1_swiglu(const GemmProblem& p, const uint16_t* x, const uint16_t* W13,
                                uint16_t* h13, uint16_t* act, hipStream_t st, KernelTimer* timer) {
-  const int NT = int(2 * p.I / g1::BN);
-  const int grid = grid_for(row_tiles_upper(p, g1::BM) * NT, p.num_cus);
+  const int grid = grid_for(row_tiles_upper(p) * (2 * p.I / BN), p.num_cus);
   TimedLaunch tl(timer, "gemm1_swiglu", st);
   hipLaunchKernelGGL(gemm1_swiglu_kernel, dim3(grid), dim3(kThreads), 0, st, p, x, W13, h13, act);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm2_scale(const GemmProblem& p, const uint16_t* act, const uint16_t* W2,
-                              uint16_t* out_rows, hipStream_t st, KernelTimer* timer) {
-  const int NT = int(p.H / g2::BN);
-  const int grid = grid_for(row_tiles_upper(p, g2::BM) * NT, p.num_cus);
-  TimedLaunch tl(timer, "gemm2_scale", st);
-  hipLaunchKernelGGL(gemm2_scale_kernel, dim3(grid), dim3(kThreads), 0, st, p, act, W2, out_rows);
+hipError_t launch_gemm2(const GemmProblem& p, const uint16_t* act, const uint16_t* W2, uint16_t* out_rows,
+                        hipStream_t st, KernelTimer* timer) {
+  const int grid = grid_for(row_tiles_upper(p) * (p.H / BN), p.num_cus);
+  TimedLaunch tl(timer, "gemm2", st);
+  hipLaunchKernelGGL(gemm2_kernel, dim3(grid), dim3(kThreads), 0, st, p, act, W2, out_rows);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dh(const GemmProblem& p, const uint16_t* dy, const uint16_t* W2,
                           const uint16_t* h13, uint16_t* dh13, float* dwpart, hipStream_t st,
                           KernelTimer* timer) {
-  const int NT = int(p.I / gdh::BN);
-  const int grid = grid_for(row_tiles_upper(p, gdh::BM) * NT, p.num_cus);
+  const int grid = grid_for(row_tiles_upper(p) * ((p.I + BN - 1) / BN), p.num_cus);
   TimedLaunch tl(timer, "gemm_dh_dswiglu", st);
   hipLaunchKernelGGL(gemm_dh_kernel, dim3(grid), dim3(kThreads), 0, st, p, dy, W2, h13, dh13, dwpart);
   return hipGetLastError();
@@ -732,8 +701,7 @@ hipError_t launch_gemm_dh(const GemmProblem& p, const uint16_t* dy, const uint16
 
 hipError_t launch_gemm_dx(const GemmProblem& p, const uint16_t* dh13, const uint16_t* W13,
                           uint16_t* dx_rows, hipStream_t st, KernelTimer* timer) {
-  const int NT = int(p.H / gdx::BN);
-  const int grid = grid_for(row_tiles_upper(p, gdx::BM) * NT, p.num_cus);
+  const int grid = grid_for(row_tiles_upper(p) * (p.H / BN), p.num_cus);
   TimedLaunch tl(timer, "gemm_dx", st);
   hipLaunchKernelGGL(gemm_dx_kernel, dim3(grid), dim3(kThreads), 0, st, p, dh13, W13, dx_rows);
   return hipGetLastError();
@@ -741,8 +709,7 @@ hipError_t launch_gemm_dx(const GemmProblem& p, const uint16_t* dh13, const uint
 
 hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x,
                             uint16_t* dW13, hipStream_t st, KernelTimer* timer) {
-  const int64_t tiles = p.E * (2 * p.I / gw::BM) * (p.H / gw::BN);
-  const int grid = grid_for(tiles, p.num_cus);
+  const int grid = grid_for(p.E * (2 * p.I / BM) * (p.H / BN), p.num_cus);
   TimedLaunch tl(timer, "gemm_dw13", st);
   hipLaunchKernelGGL(gemm_dw13_kernel, dim3(grid), dim3(kThreads), 0, st, p, dh13, x, dW13);
   return hipGetLastError();
@@ -750,8 +717,7 @@ hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const ui
 
 hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint16_t* act,
                            uint16_t* dW2, hipStream_t st, KernelTimer* timer) {
-  const int64_t tiles = p.E * (p.H / gw::BM) * (p.I / gw::BN);
-  const int grid = grid_for(tiles, p.num_cus);
+  const int grid = grid_for(p.E * (p.H / BM) * ((p.I + BN - 1) / BN), p.num_cus);
   TimedLaunch tl(timer, "gemm_dw2", st);
   hipLaunchKernelGGL(gemm_dw2_kernel, dim3(grid), dim3(kThreads), 0, st, p, dy, act, dW2);
   return hipGetLastError();

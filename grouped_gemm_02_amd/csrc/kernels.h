@@ -53,8 +53,8 @@ struct GemmProblem {
 // forward
 hipError_t launch_gemm1_swiglu(const GemmProblem& p, const uint16_t* x, const uint16_t* W13,
                                uint16_t* h13, uint16_t* act, hipStream_t st, KernelTimer* timer);
-hipError_t launch_gemm2_scale(const GemmProblem& p, const uint16_t* act, const uint16_t* W2,
-                              uint16_t* out_rows, hipStream_t st, KernelTimer* timer);
+hipError_t launch_gemm2(const GemmProblem& p, const uint16_t* act, const uint16_t* W2, uint16_t* out_rows,
+                        hipStream_t st, KernelTimer* timer);
 // backward
 int dh_num_parts(int64_t I);
 hipError_t launch_gemm_dh(const GemmProblem& p, const uint16_t* dy, const uint16_t* W2,

@@ -26,6 +26,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->H < 256 || s->H > 16384 || s->H % 256 != 0) return MOE_ERR_SHAPE;
   if (s->I < 128 || s->I > 8192 || s->I % 128 != 0) return MOE_ERR_SHAPE;
   if (s->T * s->k >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (s->T * s->H >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;  // 32-bit row offsets into x, dY
   if (s->num_cus < 0) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
@@ -255,7 +256,7 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
   if ((e = launch_gemm1_swiglu(gp, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W13),
                                h13, act, hs, tm)) != hipSuccess)
     return MOE_ERR_LAUNCH;
-  if ((e = launch_gemm2_scale(gp, act, static_cast<const uint16_t*>(W2), rows, hs, tm)) != hipSuccess)
+  if ((e = launch_gemm2(gp, act, static_cast<const uint16_t*>(W2), rows, hs, tm)) != hipSuccess)
     return MOE_ERR_LAUNCH;
   e = launch_combine(rows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(y), nullptr, 0,
                      nullptr, hs, tm, "combine_y");

@@ -78,7 +78,8 @@ typedef enum moe_precision {
 } moe_precision;
 
 /* Problem description. Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= E,
- * T*k < 2^31, H%256 == 0, I%128 == 0, 256 <= H <= 16384, 128 <= I <= 8192.
+ * T*k < 2^31, T*H < 2^31, H%256 == 0, I%128 == 0, 256 <= H <= 16384,
+ * 128 <= I <= 8192.
  * num_cus caps how many compute units the persistent GEMMs occupy
  * (0 = all), so that concurrent kernels (e.g. collectives) keep CUs. */
 typedef struct moe_shape {
@@ -103,7 +104,8 @@ typedef struct moe_saved_layout {
   size_t row_of;    /* int32 [T*k]    permuted row of pair f, -1 if dropped   */
   size_t src_of;    /* int32 [T*k]    pair f of permuted row r (first M used) */
   size_t h13;       /* bf16 [T*k,2I]  per permuted row: [g | u] (bf16)        */
-  size_t act;       /* bf16 [T*k, I]  per permuted row: silu(g)*u (bf16)      */
+  size_t act;       /* bf16 [T*k, I]  per permuted row: w*silu(g)*u, with w   */
+                    /*                the pair's routing weight (bf16)        */
   size_t total;
 } moe_saved_layout;
 moe_status moe_get_saved_layout(const moe_shape* s, moe_saved_layout* out);
@@ -138,9 +140,10 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* cou
  *   saved    moe_workspace_size().saved_bytes, or NULL for inference only;
  *            when given it is what moe_bwd reads
  *   ws       moe_workspace_size().fwd_ws bytes of scratch
- * Steps: permutation; gate/up grouped GEMM with SwiGLU epilogue; down grouped
- * GEMM with routing-weight epilogue; gather-reduce combine (fp32 sum over
- * ascending j, one bf16 rounding). */
+ * Steps: permutation; gate/up grouped GEMM whose epilogue forms
+ * w * silu(g) * u (SwiGLU with the routing weight folded in); down grouped
+ * GEMM; gather-reduce combine (fp32 sum over ascending j, one bf16
+ * rounding). */
 moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
                    const float* topk_w, const void* W13, const void* W2, const void* W13_scale,
                    const void* W2_scale, void* y, void* saved, void* ws, size_t ws_bytes,

@@ -89,7 +89,9 @@ def check_full(out, cfg, d, tol=TOL_BF16):
     h13 = orc.as_f64(out["h13"])[:M]
     errs["g"] = max_rel_err(h13[:, :I], pairs["g"][src_of])
     errs["u"] = max_rel_err(h13[:, I:], pairs["u"][src_of])
-    errs["a"] = max_rel_err(orc.as_f64(out["act"])[:M], pairs["a"][src_of])
+    # the saved activation carries the routing weight: w * silu(g) * u
+    wf = orc.as_f64(d["topk_w"]).reshape(-1)
+    errs["wa"] = max_rel_err(orc.as_f64(out["act"])[:M], pairs["a"][src_of] * wf[src_of][:, None])
     _say(f"{cfg.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= tol, (k, v)
