@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "MoE layer fwd+bwd ms and TFLOP/s (frac of MFMA peak), Qwen3-30B-A3B shape, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+COPY_CALIB_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 
 # algorithmic flops per launch of each GEMM, as a multiple of M*H*I
 GEMM_FLOP_FACTOR = {
@@ -99,6 +100,16 @@ def main():
         B.backward(buf, d["dy"], d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], grads=grads)
         if evs:
             evs[2].record()
+
+    # A plain device-to-device copy of known size: rocprofv3 counter runs
+    # (FETCH_SIZE / WRITE_SIZE) use it to calibrate the layer kernels' HBM
+    # traffic. Outside the timed region.
+    calib = torch.empty(COPY_CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    calib.zero_()
+    torch.cuda.synchronize()
+    calib_out = calib.clone()
+    torch.cuda.synchronize()
+    del calib, calib_out
 
     for _ in range(args.warmup):
         step()

@@ -40,7 +40,7 @@ class moe_shape(ctypes.Structure):
 
 class moe_saved_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("counts", "offsets", "row_of", "src_of", "h13", "act", "total")]
+                ("counts", "offsets", "row_of", "src_of", "wrow", "h13", "act", "total")]
 
 
 class moe_kernel_time(ctypes.Structure):

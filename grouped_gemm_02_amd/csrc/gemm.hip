@@ -53,67 +53,84 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // ------------------------------------------------------------------ loaders
 
+// Register stage of one operand's k-slab: 8 16-byte chunks per thread plus
+// a zero-fill mask (bit i set: chunk i is real data).
+struct Stage {
+  u32x4 r[8];
+  uint32_t ok;
+};
+
 // k-major operand: 256 entity rows, each with its k-values contiguous.
 // Thread t copies chunk (t % 8) of rows t/8 + 32*i, i < 8. Row addresses are
-// a tile-uniform base plus a 32-bit element offset per row (-1 = zero row),
-// which keeps the loader at 8 address registers.
+// a tile-uniform base plus a 32-bit element offset per row. Every offset
+// must address a real row: rows of the token side past the end of a ragged
+// tile are pointed at a valid row and their results are never stored, so the
+// loads need no predicate.
 struct KMajorLoader {
   static constexpr int kPer = 8;
   const uint16_t* base;
   int32_t off[kPer];
-  u32x4 reg[kPer];
 
   __device__ __forceinline__ static int row_of_thread(int i) { return (threadIdx.x >> 3) + 32 * i; }
-  // row_off: element offset of the row start from `base`, or -1
   __device__ __forceinline__ void set_row(int i, int64_t row_off) {
-    off[i] = row_off >= 0 ? int32_t(row_off) + (threadIdx.x & 7) * 8 : -1;
+    off[i] = int32_t(row_off) + (threadIdx.x & 7) * 8;
   }
-  __device__ __forceinline__ void fetch(int kt) {
+  __device__ __forceinline__ void prime(int) {}
+  __device__ __forceinline__ void fetch(int kt, Stage& st) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      reg[i] = off[i] >= 0 ? *reinterpret_cast<const u32x4*>(base + off[i] + kt * BK) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < kPer; ++i) st.r[i] = *reinterpret_cast<const u32x4*>(base + off[i] + kt * BK);
+    st.ok = 0xffu;
   }
-  __device__ __forceinline__ void store(uint16_t* lds) const {
+  __device__ __forceinline__ void store(uint16_t* lds, const Stage& st) const {
     const int r0 = threadIdx.x >> 3, c = threadIdx.x & 7;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<u32x4*>(lds + (r0 + 32 * i) * LDK + c * 8) = reg[i];
+      *reinterpret_cast<u32x4*>(lds + (r0 + 32 * i) * LDK + c * 8) = st.r[i];
   }
 };
 
 // mn-major operand: 64 k-rows per slab, each holding the tile's 256 entities
 // contiguously. Thread t copies chunk (t % 32) of k-rows t/32 + 8*i, i < 8.
-// RowFn::index(k) names the memory row of absolute k (-1 = zero row; it may
-// read an index array, so the indices of slab kt+1 are fetched one slab
-// ahead) and RowFn::ptr(index) its address at entity 0 of the tile.
+// RowFn::index(k) gives the memory row of absolute k, always a real row, and
+// RowFn::valid(k) whether k contributes (k-rows past the end read as zeros:
+// they are loaded from a real row and replaced by zero when stored). Slabs
+// are fetched in order; each fetch also works out the rows of the next slab,
+// since they may come from an index array.
 template <class RowFn>
 struct MNMajorLoader {
   static constexpr int kPer = 8;
   RowFn fn;
-  int nchunks = 32;   // 16-byte chunks of the tile that exist (partial last n-tile)
-  int32_t nxt[kPer];  // memory rows of the next slab
-  u32x4 reg[kPer];
+  int nchunks = 32;  // 16-byte chunks of the tile that exist (partial last n-tile)
+  int32_t nxt[kPer];
+  uint32_t nxt_ok;   // bit i: k-row i of the next slab contributes
 
   __device__ __forceinline__ void prime(int kt) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) nxt[i] = fn.index(kt * BK + (threadIdx.x >> 5) + 8 * i);
-  }
-  __device__ __forceinline__ void fetch(int kt) {
-    const int c = threadIdx.x & 31;
+    uint32_t ok = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int32_t row = nxt[i];
-      reg[i] = (row >= 0 && c < nchunks) ? *reinterpret_cast<const u32x4*>(fn.ptr(row) + c * 8)
-                                         : u32x4{0u, 0u, 0u, 0u};
+      const int k = kt * BK + (threadIdx.x >> 5) + 8 * i;
+      nxt[i] = fn.index(k);
+      ok |= uint32_t(fn.valid(k)) << i;
     }
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) nxt[i] = fn.index((kt + 1) * BK + (threadIdx.x >> 5) + 8 * i);
+    nxt_ok = ok;
   }
-  __device__ __forceinline__ void store(uint16_t* lds) const {
+  __device__ __forceinline__ void fetch(int kt, Stage& st) {
+    const int c = threadIdx.x & 31;
+    const bool col_ok = c < nchunks;
+    const int cc = col_ok ? c : 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) st.r[i] = *reinterpret_cast<const u32x4*>(fn.ptr(nxt[i]) + cc * 8);
+    st.ok = col_ok ? nxt_ok : 0u;
+    prime(kt + 1);
+  }
+  // The zero-fill is applied when the stage is written to LDS, after the
+  // MFMAs, so that nothing right after the loads waits for them.
+  __device__ __forceinline__ void store(uint16_t* lds, const Stage& st) const {
     const int r0 = threadIdx.x >> 5, c = threadIdx.x & 31;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<u32x4*>(lds + (r0 + 8 * i) * LDN + c * 8) = reg[i];
+      *reinterpret_cast<u32x4*>(lds + (r0 + 8 * i) * LDN + c * 8) =
+          ((st.ok >> i) & 1u) ? st.r[i] : u32x4{0u, 0u, 0u, 0u};
   }
 };
 
@@ -171,47 +188,71 @@ __device__ __forceinline__ int lane_col(int tn, int g) {
   return wave_n() * 128 + tn * 32 + 8 * g + 4 * (lane_id() >> 5);
 }
 
-// One k-slab of MFMAs for this wave; sub-tiles i >= ACT (rows past the end of
-// a ragged m-tile) are skipped.
-template <bool P_MN, bool Q_MN, int ACT>
-__device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
+template <bool P_MN, bool Q_MN>
+__device__ __forceinline__ void load_frags(const uint16_t* ldsP, const uint16_t* ldsQ, int kk,
+                                           bf16x8 (&pf)[TM], bf16x8 (&qf)[TN]) {
   const int pm0 = wave_m() * 128, qn0 = wave_n() * 128;
 #pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    bf16x8 qf[TN];
+  for (int j = 0; j < TN; ++j) qf[j] = Q_MN ? frag_mn(ldsQ, qn0 + 32 * j, kk) : frag_k(ldsQ, qn0 + 32 * j, kk);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) qf[j] = Q_MN ? frag_mn(ldsQ, qn0 + 32 * j, kk) : frag_k(ldsQ, qn0 + 32 * j, kk);
-#pragma unroll
-    for (int i = 0; i < ACT; ++i) {
-      const bf16x8 pf = P_MN ? frag_mn(ldsP, pm0 + 32 * i, kk) : frag_k(ldsP, pm0 + 32 * i, kk);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc.c[i][j] = mfma_32x32x16(qf[j], pf, acc.c[i][j]);
-    }
-  }
+  for (int i = 0; i < TM; ++i) pf[i] = P_MN ? frag_mn(ldsP, pm0 + 32 * i, kk) : frag_k(ldsP, pm0 + 32 * i, kk);
 }
 
-// Runs the k loop of one tile.
+__device__ __forceinline__ void mma_step(const bf16x8 (&pf)[TM], const bf16x8 (&qf)[TN], Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc.c[i][j] = mfma_32x32x16(qf[j], pf[i], acc.c[i][j]);
+}
+
+// One k-slab (4 steps of 16) of MFMAs for this wave. Fragments are double
+// buffered: the LDS reads of step s+1 are issued before the 16 MFMAs of step
+// s, and scheduling barriers keep the compiler from sinking them, so LDS
+// latency hides under the MFMA pipe.
+template <bool P_MN, bool Q_MN>
+__device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
+  bf16x8 pa[TM], qa[TN], pb[TM], qb[TN];
+  load_frags<P_MN, Q_MN>(ldsP, ldsQ, 0, pa, qa);
+  load_frags<P_MN, Q_MN>(ldsP, ldsQ, 1, pb, qb);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(pa, qa, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<P_MN, Q_MN>(ldsP, ldsQ, 2, pa, qa);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(pb, qb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<P_MN, Q_MN>(ldsP, ldsQ, 3, pb, qb);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(pa, qa, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(pb, qb, acc);
+}
+
+// Runs the k loop of one tile: the global loads of slab kt+1 are in flight
+// (in registers) while slab kt is multiplied out of one LDS buffer; then they
+// are written to the other buffer.
 template <bool P_MN, bool Q_MN, class LP, class LQ>
 __device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, int rows, uint16_t* lds, Acc& acc) {
   (void)rows;
   if (nk <= 0) return;
-  lp.fetch(0);
-  lq.fetch(0);
-  lp.store(lds);
-  lq.store(lds + kOperandLds);
+  Stage sp, sq;
+  lp.fetch(0, sp);
+  lq.fetch(0, sq);
+  lp.store(lds, sp);
+  lq.store(lds + kOperandLds, sq);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     uint16_t* cur = lds + (kt & 1) * kStageLds;
     uint16_t* nxt = lds + ((kt + 1) & 1) * kStageLds;
     const bool more = kt + 1 < nk;
     if (more) {
-      lp.fetch(kt + 1);
-      lq.fetch(kt + 1);
+      lp.fetch(kt + 1, sp);
+      lq.fetch(kt + 1, sq);
     }
-    mma_slab<P_MN, Q_MN, TM>(cur, cur + kOperandLds, acc);
+    mma_slab<P_MN, Q_MN>(cur, cur + kOperandLds, acc);
     if (more) {
-      lp.store(nxt);
-      lq.store(nxt + kOperandLds);
+      lp.store(nxt, sp);
+      lq.store(nxt + kOperandLds, sq);
     }
     __syncthreads();
   }
@@ -375,6 +416,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, c
                                                                 uint16_t* __restrict__ h13,
                                                                 uint16_t* __restrict__ act) {
   MOE_GEMM_SMEM
+  __shared__ float s_w[BM];
   const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
   MOE_ROW_SCHED
   const int NT = (2 * I) / BN;
@@ -387,12 +429,16 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, c
 #pragma unroll
     for (int i = 0; i < KMajorLoader::kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
-      lp.set_row(i, m < rt.rows ? int64_t(p.src_of[rt.row0 + m] / k) * H : -1);
+      const int mc = m < rt.rows ? m : rt.rows - 1;  // past-the-end rows reuse a real row
+      lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * H);
       lq.set_row(i, int64_t(g1::w13_row(m, rt.nt, I)) * H);
     }
+    // routing weight of tile row threadIdx.x: loaded now, used after the k loop
+    const float w_row = p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)];
     Acc acc;
     acc.zero();
     mainloop<false, false>(lp, lq, H / BK, rt.rows, lds, acc);
+    s_w[threadIdx.x] = w_row;
     // half h holds g and u of intermediate indices nt*128 + h*64 + [0, 64):
     // staged column (i/32)*64 + i%32 is g, +32 is u.
     float* F = reinterpret_cast<float*>(lds);
@@ -404,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, c
       const int i = rt.nt * g1::IPT + h * 64 + io;
       for (int m = threadIdx.x >> 4; m < rt.rows; m += 16) {
         const int64_t r = rt.row0 + m;
-        const float w = p.topk_w[p.src_of[r]];
+        const float w = s_w[m];
         const f32x4 gv = *reinterpret_cast<const f32x4*>(F + m * FLD + gc);
         const f32x4 uv = *reinterpret_cast<const f32x4*>(F + m * FLD + gc + 32);
         float av[4];
@@ -439,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, const ui
 #pragma unroll
     for (int i = 0; i < KMajorLoader::kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
-      lp.set_row(i, m < rt.rows ? int64_t(m) * I : -1);
+      lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * I);
       lq.set_row(i, int64_t(m) * I);
     }
     Acc acc;
@@ -454,8 +500,9 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, const ui
 struct DirectRows {  // memory row k of a row-major tensor
   const uint16_t* base;  // entity 0 of the tile in row 0
   int64_t ld;
-  int32_t nrows;         // rows beyond this read as zero
-  __device__ __forceinline__ int32_t index(int k) const { return k < nrows ? k : -1; }
+  int32_t nrows;         // k-rows past this contribute zeros (nrows >= 1)
+  __device__ __forceinline__ int32_t index(int k) const { return k < nrows ? k : nrows - 1; }
+  __device__ __forceinline__ bool valid(int k) const { return k < nrows; }
   __device__ __forceinline__ const uint16_t* ptr(int32_t row) const { return base + int64_t(row) * ld; }
 };
 
@@ -463,9 +510,10 @@ struct TokenRows {  // k-th row of an expert segment -> its token's row
   const uint16_t* base;  // entity 0 of the tile in token row 0
   int64_t ld;
   const int32_t* src;    // src_of + segment start
-  int rows;
+  int rows;              // segment length (>= 1)
   int kk;                // experts per token
-  __device__ __forceinline__ int32_t index(int k) const { return k < rows ? src[k] / kk : -1; }
+  __device__ __forceinline__ int32_t index(int k) const { return src[k < rows ? k : rows - 1] / kk; }
+  __device__ __forceinline__ bool valid(int k) const { return k < rows; }
   __device__ __forceinline__ const uint16_t* ptr(int32_t row) const { return base + int64_t(row) * ld; }
 };
 
@@ -483,6 +531,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const 
                                                            uint16_t* __restrict__ dh13,
                                                            float* __restrict__ dwpart) {
   MOE_GEMM_SMEM
+  __shared__ float s_w[BM];
   const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
   MOE_ROW_SCHED
   const int NT = (I + BN - 1) / BN;  // the last n-tile may hold 128 columns
@@ -495,7 +544,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const 
 #pragma unroll
     for (int i = 0; i < KMajorLoader::kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
-      lp.set_row(i, m < rt.rows ? int64_t(p.src_of[rt.row0 + m] / k) * H : -1);
+      const int mc = m < rt.rows ? m : rt.rows - 1;
+      lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * H);
     }
     MNMajorLoader<DirectRows> lq;
     lq.fn.base = W2 + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN;
@@ -506,55 +556,81 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const 
     lq.prime(0);
     Acc acc;
     acc.zero();
+    const float w_row = p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)];
     mainloop<false, true>(lp, lq, H / BK, rt.rows, lds, acc);
-    // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128)
+    s_w[threadIdx.x] = w_row;
+    // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
+    // Thread t works on 8 of them (c) for tile rows t/16 + 16*j, j < 16, in
+    // four batches of four rows; the [g | u] pieces of the next batch are
+    // requested before the current batch is computed (the first batch's before
+    // the staging barrier), so their latency overlaps other work.
     float* F = reinterpret_cast<float*>(lds);
     for (int h = 0; h < 2; ++h) {
-      stage_half(acc, F, h);
-      __syncthreads();
-      const int c = (threadIdx.x & 15) * 8;             // 8 intermediate indices per thread
+      const int c = (threadIdx.x & 15) * 8;
       const bool col_ok = h * 128 + c < ncols;
-      const int i = rt.nt * BN + h * 128 + c;
-      for (int m0 = 0; m0 < rt.rows; m0 += 16) {
-        const int m = m0 + (threadIdx.x >> 4);
-        const bool row_ok = m < rt.rows;
-        float dws = 0.f;
-        if (row_ok && col_ok) {
-          const int64_t r = rt.row0 + m;
-          const float w = p.topk_w[p.src_of[r]];
-          const u32x4 gq = *reinterpret_cast<const u32x4*>(h13 + r * 2 * I + i);
-          const u32x4 uq = *reinterpret_cast<const u32x4*>(h13 + r * 2 * I + I + i);
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(F + m * FLD + c);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(F + m * FLD + c + 4);
-          u32x4 dgq, duq;
+      const int i = rt.nt * BN + h * 128 + (col_ok ? c : 0);
+      auto fetch_gu = [&](int j, u32x4& gq, u32x4& uq) {
+        const int m = min((int(threadIdx.x) >> 4) + 16 * j, rt.rows - 1);
+        const uint16_t* src = h13 + (rt.row0 + m) * 2 * I + i;
+        gq = *reinterpret_cast<const u32x4*>(src);
+        uq = *reinterpret_cast<const u32x4*>(src + I);
+      };
+      u32x4 ga[4], ua[4], gb[4], ub[4];
+      stage_half(acc, F, h);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float dgp[2], dup[2];
+      for (int j = 0; j < 4; ++j) fetch_gu(j, ga[j], ua[j]);
+      __syncthreads();
+#pragma unroll 1
+      for (int bt = 0; bt < 4; ++bt) {
+        if (bt < 3) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const float gv = hh ? bf16_hi(gq[q]) : bf16_lo(gq[q]);
-              const float uv = hh ? bf16_hi(uq[q]) : bf16_lo(uq[q]);
-              const int e8 = 2 * q + hh;
-              const float dau = e8 < 4 ? d0[e8] : d1[e8 - 4];
-              const float s = sigmoidf_fast(gv);
-              const float sg = gv * s;  // silu(g)
-              dws += dau * sg * uv;
-              const float da = w * dau;
-              dgp[hh] = da * uv * s * (1.f + gv * (1.f - s));
-              dup[hh] = da * sg;
-            }
-            dgq[q] = pack_bf16x2(dgp[0], dgp[1]);
-            duq[q] = pack_bf16x2(dup[0], dup[1]);
+          for (int j = 0; j < 4; ++j) {
+            if (bt & 1) fetch_gu(4 * (bt + 1) + j, ga[j], ua[j]);
+            else fetch_gu(4 * (bt + 1) + j, gb[j], ub[j]);
           }
-          *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i) = dgq;
-          *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i) = duq;
         }
-        // sum over the 16 threads of this row (lanes 16g .. 16g+15)
-        dws += __shfl_xor(dws, 8);
-        dws += __shfl_xor(dws, 4);
-        dws += __shfl_xor(dws, 2);
-        dws += __shfl_xor(dws, 1);
-        if (row_ok && (threadIdx.x & 15) == 0) dwpart[(rt.row0 + m) * nparts + 2 * rt.nt + h] = dws;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 gq = (bt & 1) ? gb[j] : ga[j];
+          const u32x4 uq = (bt & 1) ? ub[j] : ua[j];
+          const int m = (threadIdx.x >> 4) + 16 * (4 * bt + j);
+          const bool row_ok = m < rt.rows;
+          float dws = 0.f;
+          if (row_ok && col_ok) {
+            const int64_t r = rt.row0 + m;
+            const float w = s_w[m];
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(F + m * FLD + c);
+            const f32x4 d1 = *reinterpret_cast<const f32x4*>(F + m * FLD + c + 4);
+            u32x4 dgq, duq;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float dgp[2], dup[2];
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const float gv = hh ? bf16_hi(gq[q]) : bf16_lo(gq[q]);
+                const float uv = hh ? bf16_hi(uq[q]) : bf16_lo(uq[q]);
+                const int e8 = 2 * q + hh;
+                const float dau = e8 < 4 ? d0[e8] : d1[e8 - 4];
+                const float sg_ = sigmoidf_fast(gv);
+                const float sl = gv * sg_;  // silu(g)
+                dws += dau * sl * uv;
+                const float da = w * dau;
+                dgp[hh] = da * uv * sg_ * (1.f + gv * (1.f - sg_));
+                dup[hh] = da * sl;
+              }
+              dgq[q] = pack_bf16x2(dgp[0], dgp[1]);
+              duq[q] = pack_bf16x2(dup[0], dup[1]);
+            }
+            *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i) = dgq;
+            *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i) = duq;
+          }
+          // sum over the 16 threads of this row (lanes 16g .. 16g+15)
+          dws += __shfl_xor(dws, 8);
+          dws += __shfl_xor(dws, 4);
+          dws += __shfl_xor(dws, 2);
+          dws += __shfl_xor(dws, 1);
+          if (row_ok && (threadIdx.x & 15) == 0) dwpart[(rt.row0 + m) * nparts + 2 * rt.nt + h] = dws;
+        }
       }
       __syncthreads();
     }
@@ -578,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, const 
 #pragma unroll
     for (int i = 0; i < KMajorLoader::kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
-      lp.set_row(i, m < rt.rows ? int64_t(m) * 2 * I : -1);
+      lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * 2 * I);
     }
     MNMajorLoader<DirectRows> lq;
     lq.fn.base = W13 + int64_t(rt.e) * 2 * I * H + int64_t(rt.nt) * BN;
@@ -614,14 +690,16 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     lp.fn.base = dh13 + off * 2 * I + int64_t(mt) * BM;
     lp.fn.ld = 2 * I;
     lp.fn.nrows = rows;
-    lp.prime(0);
     MNMajorLoader<TokenRows> lq;
     lq.fn.base = x + int64_t(nt) * BN;
     lq.fn.ld = H;
     lq.fn.src = p.src_of + off;
     lq.fn.rows = rows;
     lq.fn.kk = int(p.k);
-    lq.prime(0);
+    if (rows > 0) {  // an empty expert runs no k loop and stores zeros
+      lp.prime(0);
+      lq.prime(0);
+    }
     Acc acc;
     acc.zero();
     mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, BM, lds, acc);
@@ -648,14 +726,16 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     lp.fn.src = p.src_of + off;
     lp.fn.rows = rows;
     lp.fn.kk = int(p.k);
-    lp.prime(0);
     MNMajorLoader<DirectRows> lq;
     lq.fn.base = act + off * I + int64_t(nt) * BN;
     lq.fn.ld = I;
     lq.fn.nrows = rows;
     const int ncols = min(BN, I - nt * BN);
     lq.nchunks = ncols / 8;
-    lq.prime(0);
+    if (rows > 0) {  // an empty expert runs no k loop and stores zeros
+      lp.prime(0);
+      lq.prime(0);
+    }
     Acc acc;
     acc.zero();
     mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, BM, lds, acc);

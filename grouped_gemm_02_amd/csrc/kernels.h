@@ -29,9 +29,11 @@ struct TimedLaunch {
 // ---------------------------------------------------------------- permute
 int permute_num_chunks(int64_t n);
 size_t permute_scratch_bytes(int64_t n, int E);
+// When wrow != nullptr also wrow[row_of[f]] = topk_w[f].
 hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
                           int32_t* offsets, int32_t* row_of, int32_t* src_of, void* scratch,
-                          hipStream_t st, KernelTimer* timer);
+                          hipStream_t st, KernelTimer* timer, const float* topk_w = nullptr,
+                          float* wrow = nullptr);
 
 // ---------------------------------------------------------------- combine
 // y[t] = sum_j rows[row_of[t*k+j]]  (bf16 rows of width H, fp32 sum, ascending j)
@@ -48,6 +50,7 @@ struct GemmProblem {
   const int32_t* offsets;
   const int32_t* src_of;
   const float* topk_w;
+  const float* wrow;  // routing weight of each permuted row
 };
 
 // forward

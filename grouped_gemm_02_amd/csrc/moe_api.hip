@@ -50,6 +50,7 @@ moe_saved_layout saved_layout(const moe_shape& s) {
   L.offsets = o; o = align_up(o + size_t(s.E + 1) * 4);
   L.row_of = o;  o = align_up(o + size_t(Tk) * 4);
   L.src_of = o;  o = align_up(o + size_t(Tk) * 4);
+  L.wrow = o;    o = align_up(o + size_t(Tk) * 4);
   L.h13 = o;     o = align_up(o + size_t(Tk) * size_t(2 * s.I) * 2);
   L.act = o;     o = align_up(o + size_t(Tk) * size_t(s.I) * 2);
   L.total = o;
@@ -242,6 +243,7 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
   int32_t* offsets = at<int32_t>(sv, SL.offsets);
   int32_t* row_of = at<int32_t>(sv, SL.row_of);
   int32_t* src_of = at<int32_t>(sv, SL.src_of);
+  float* wrow = at<float>(sv, SL.wrow);
   uint16_t* h13 = saved ? at<uint16_t>(sv, SL.h13) : nullptr;
   uint16_t* act = at<uint16_t>(sv, SL.act);
   uint16_t* rows = at<uint16_t>(ws, FL.rows);
@@ -250,9 +252,9 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
   std::lock_guard<std::mutex> lk(g_timer_mu);
   KernelTimer* tm = timer();
   hipError_t e = launch_permute(topk_idx, Tk, int(s->E), counts, offsets, row_of, src_of,
-                                at<char>(ws, FL.perm), hs, tm);
+                                at<char>(ws, FL.perm), hs, tm, topk_w, wrow);
   if (e != hipSuccess || s->T == 0) return launch_status(e);
-  GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w};
+  GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w, wrow};
   if ((e = launch_gemm1_swiglu(gp, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W13),
                                h13, act, hs, tm)) != hipSuccess)
     return MOE_ERR_LAUNCH;
@@ -288,6 +290,7 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
   const int32_t* offsets = at<int32_t>(saved, SL.offsets);
   const int32_t* row_of = at<int32_t>(saved, SL.row_of);
   const int32_t* src_of = at<int32_t>(saved, SL.src_of);
+  const float* wrow = at<float>(saved, SL.wrow);
   const uint16_t* h13 = at<uint16_t>(saved, SL.h13);
   const uint16_t* act = at<uint16_t>(saved, SL.act);
   uint16_t* dh13 = at<uint16_t>(ws, BL.dh13);
@@ -299,7 +302,7 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
 
   std::lock_guard<std::mutex> lk(g_timer_mu);
   KernelTimer* tm = timer();
-  GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w};
+  GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w, wrow};
   hipError_t e = hipSuccess;
   if (s->T > 0) {
     if ((e = launch_gemm_dh(gp, dy16, static_cast<const uint16_t*>(W2), h13, dh13, dwpart, hs, tm)) !=

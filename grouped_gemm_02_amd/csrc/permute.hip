@@ -16,7 +16,8 @@
 //                   the equal ids before it comes from wavefront ballots
 //                   (lanes with the same id found bit by bit), per-wave counts
 //                   in LDS and a running per-chunk count, then
-//                   row_of[f] = start + rank and src_of[row] = f.
+//                   row_of[f] = start + rank and src_of[row] = f (and, for
+//                   the layer, the pair's routing weight at its row).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(1024) void permute_scan(int32_t* __restrict__ chunk
 __global__ __launch_bounds__(kPermThreads) void permute_scatter(
     const int32_t* __restrict__ idx, int64_t n, int E, int id_bits,
     const int32_t* __restrict__ chunk_start, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ src_of) {
+    int32_t* __restrict__ src_of, const float* __restrict__ topk_w, float* __restrict__ wrow) {
   extern __shared__ int32_t sm[];
   int32_t* running = sm;                // [E+1]  rows already placed in this chunk
   int32_t* wave_cnt = sm + (E + 1);     // [kPermWaves][E+1]
@@ -136,6 +137,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter(
         const int32_t row = start[e] + before + rank_in_wave;
         row_of[f] = row;
         src_of[row] = static_cast<int32_t>(f);
+        if (wrow) wrow[row] = topk_w[f];
       } else {
         row_of[f] = -1;
       }
@@ -159,7 +161,7 @@ size_t permute_scratch_bytes(int64_t n, int E) {
 
 hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
                           int32_t* offsets, int32_t* row_of, int32_t* src_of, void* scratch,
-                          hipStream_t st, KernelTimer* timer) {
+                          hipStream_t st, KernelTimer* timer, const float* topk_w, float* wrow) {
   int32_t* status = static_cast<int32_t*>(scratch);
   int32_t* chunk_tab = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + 256);
   const int nchunk = permute_num_chunks(n);
@@ -179,7 +181,7 @@ hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
     TimedLaunch t(timer, "permute_scatter", st);
     hipLaunchKernelGGL(permute_scatter, dim3(nchunk), dim3(kPermThreads),
                        (E + 1) * (1 + kPermWaves) * 4, st, idx, n, E, id_bits, chunk_tab, row_of,
-                       src_of);
+                       src_of, topk_w, wrow);
   }
   return hipGetLastError();
 }

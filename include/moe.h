@@ -103,6 +103,7 @@ typedef struct moe_saved_layout {
   size_t offsets;   /* int32 [E+1]    exclusive prefix of counts              */
   size_t row_of;    /* int32 [T*k]    permuted row of pair f, -1 if dropped   */
   size_t src_of;    /* int32 [T*k]    pair f of permuted row r (first M used) */
+  size_t wrow;      /* fp32 [T*k]     routing weight of permuted row r        */
   size_t h13;       /* bf16 [T*k,2I]  per permuted row: [g | u] (bf16)        */
   size_t act;       /* bf16 [T*k, I]  per permuted row: w*silu(g)*u, with w   */
                     /*                the pair's routing weight (bf16)        */
