@@ -11,12 +11,13 @@
 //
 // Structure shared by all six:
 //   * Output tile C[m][n] of 256 x 256, C = sum_k P[m][k] Q[n][k], fp32
-//     accumulation in MFMA registers. 256 threads = 4 waves in a 2 x 2 grid,
-//     each wave a 128 x 128 block of 4 x 4 sub-tiles of
-//     v_mfma_f32_32x32x16_bf16 (256 accumulator registers per lane). The
+//     accumulation in MFMA registers. 512 threads = 8 waves in a 2 x 4 grid
+//     (two waves per SIMD, so one wave's LDS and memory waits overlap the
+//     other's MFMAs), each wave a 128 x 64 block of 4 x 2 sub-tiles of
+//     v_mfma_f32_32x32x16_bf16 (128 accumulator registers per lane). The
 //     MFMA's A operand is the Q fragment and its B operand the P fragment, so
 //     each lane holds one row m and 16 columns n of a sub-tile (4 runs of 4
-//     consecutive n): per-row epilogue scalars live in one lane.
+//     consecutive n): per-row scalars of the epilogue live in one lane.
 //   * Both operands are staged through LDS in k-slabs of BK = 64, double
 //     buffered: the global loads of slab kt+1 are in flight (in registers)
 //     while slab kt is multiplied. Every global load is a 16-byte chunk of a
@@ -30,6 +31,9 @@
 //         [k][entities + 32 pad] and are read with the gfx950 LDS transpose
 //         read ds_read_b64_tr_b16, which hands every lane 4 consecutive k of
 //         one entity. No register transposes.
+//   * Epilogues go through LDS: the accumulators of one column half are
+//     written there in fp32, then every thread handles 16-byte row pieces,
+//     so global stores (and the loads some epilogues need) are coalesced.
 //   * Persistent grid: each workgroup walks tiles blockIdx, +grid, ...; tile
 //     ids are remapped so that the eight XCDs each take a contiguous range
 //     (tiles of one expert share its weight panel in that XCD's L2).
@@ -41,64 +45,68 @@ namespace moe {
 constexpr int BK = 64;
 constexpr int BM = 256;   // tile rows (P entities)
 constexpr int BN = 256;   // tile columns (Q entities)
-constexpr int kThreads = 256;
-constexpr int LDK = BK + 8;          // k-major LDS row: 64 k + 8 pad (bf16 elements)
-constexpr int LDN = 256 + 32;        // mn-major LDS row: 256 entities + 32 pad
+constexpr int kThreads = 512;
+constexpr int kWavesM = 2;
+constexpr int kWavesN = 4;
+constexpr int WTM = BM / kWavesM;  // 128 rows per wave
+constexpr int WTN = BN / kWavesN;  // 64 columns per wave
+constexpr int TM = WTM / 32;       // 4 sub-tiles
+constexpr int TN = WTN / 32;       // 2 sub-tiles
+constexpr int LDK = BK + 8;        // k-major LDS row: 64 k + 8 pad (bf16 elements)
+constexpr int LDN = 256 + 32;      // mn-major LDS row: 256 entities + 32 pad
 constexpr int kOperandLds = 256 * LDK;  // == 64 * LDN: both layouts take 36 KiB
 static_assert(256 * LDK == 64 * LDN, "operand layouts must have the same LDS size");
 constexpr int kStageLds = 2 * kOperandLds;  // P + Q
+constexpr int kPer = 256 * 8 / kThreads;   // 16-byte chunks per thread per operand slab
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // ------------------------------------------------------------------ loaders
 
-// Register stage of one operand's k-slab: 8 16-byte chunks per thread plus
-// a zero-fill mask (bit i set: chunk i is real data).
+// Register stage of one operand's k-slab plus a zero-fill mask (bit i set:
+// chunk i is real data).
 struct Stage {
-  u32x4 r[8];
+  u32x4 r[kPer];
   uint32_t ok;
 };
 
 // k-major operand: 256 entity rows, each with its k-values contiguous.
-// Thread t copies chunk (t % 8) of rows t/8 + 32*i, i < 8. Row addresses are
-// a tile-uniform base plus a 32-bit element offset per row. Every offset
-// must address a real row: rows of the token side past the end of a ragged
-// tile are pointed at a valid row and their results are never stored, so the
+// Thread t copies chunk (t % 8) of rows t/8 + 64*i. Row addresses are a
+// tile-uniform base plus a 32-bit element offset per row. Every offset must
+// address a real row: rows of the token side past the end of a ragged tile
+// are pointed at a valid row and their results are never stored, so the
 // loads need no predicate.
 struct KMajorLoader {
-  static constexpr int kPer = 8;
   const uint16_t* base;
   int32_t off[kPer];
 
-  __device__ __forceinline__ static int row_of_thread(int i) { return (threadIdx.x >> 3) + 32 * i; }
+  __device__ __forceinline__ static int row_of_thread(int i) { return (threadIdx.x >> 3) + 64 * i; }
   __device__ __forceinline__ void set_row(int i, int64_t row_off) {
     off[i] = int32_t(row_off) + (threadIdx.x & 7) * 8;
   }
-  __device__ __forceinline__ void prime(int) {}
   __device__ __forceinline__ void fetch(int kt, Stage& st) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) st.r[i] = *reinterpret_cast<const u32x4*>(base + off[i] + kt * BK);
-    st.ok = 0xffu;
+    st.ok = ~0u;
   }
   __device__ __forceinline__ void store(uint16_t* lds, const Stage& st) const {
     const int r0 = threadIdx.x >> 3, c = threadIdx.x & 7;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<u32x4*>(lds + (r0 + 32 * i) * LDK + c * 8) = st.r[i];
+      *reinterpret_cast<u32x4*>(lds + (r0 + 64 * i) * LDK + c * 8) = st.r[i];
   }
 };
 
 // mn-major operand: 64 k-rows per slab, each holding the tile's 256 entities
-// contiguously. Thread t copies chunk (t % 32) of k-rows t/32 + 8*i, i < 8.
+// contiguously. Thread t copies chunk (t % 32) of k-rows t/32 + 16*i.
 // RowFn::index(k) gives the memory row of absolute k, always a real row, and
-// RowFn::valid(k) whether k contributes (k-rows past the end read as zeros:
-// they are loaded from a real row and replaced by zero when stored). Slabs
-// are fetched in order; each fetch also works out the rows of the next slab,
-// since they may come from an index array.
+// RowFn::valid(k) whether k contributes (k-rows past the end are loaded from
+// a real row and replaced by zero when stored). Slabs are fetched in order;
+// each fetch also works out the rows of the next slab, since they may come
+// from an index array.
 template <class RowFn>
 struct MNMajorLoader {
-  static constexpr int kPer = 8;
   RowFn fn;
   int nchunks = 32;  // 16-byte chunks of the tile that exist (partial last n-tile)
   int32_t nxt[kPer];
@@ -108,7 +116,7 @@ struct MNMajorLoader {
     uint32_t ok = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int k = kt * BK + (threadIdx.x >> 5) + 8 * i;
+      const int k = kt * BK + (threadIdx.x >> 5) + 16 * i;
       nxt[i] = fn.index(k);
       ok |= uint32_t(fn.valid(k)) << i;
     }
@@ -129,7 +137,7 @@ struct MNMajorLoader {
     const int r0 = threadIdx.x >> 5, c = threadIdx.x & 31;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<u32x4*>(lds + (r0 + 8 * i) * LDN + c * 8) =
+      *reinterpret_cast<u32x4*>(lds + (r0 + 16 * i) * LDN + c * 8) =
           ((st.ok >> i) & 1u) ? st.r[i] : u32x4{0u, 0u, 0u, 0u};
   }
 };
@@ -163,9 +171,6 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t* lds, int ent0, int kk)
 
 // ------------------------------------------------------------------ MFMA core
 
-constexpr int TM = 4;  // 32-row sub-tiles per wave
-constexpr int TN = 4;  // 32-column sub-tiles per wave
-
 struct Acc {
   f32x16 c[TM][TN];
   __device__ __forceinline__ void zero() {
@@ -178,20 +183,21 @@ struct Acc {
   }
 };
 
-__device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) & 1; }
-__device__ __forceinline__ int wave_n() { return threadIdx.x >> 7; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int wave_m() { return wave_id() % kWavesM; }
+__device__ __forceinline__ int wave_n() { return wave_id() / kWavesM; }
 
 // tile row held by this lane in sub-tile tm
-__device__ __forceinline__ int lane_row(int tm) { return wave_m() * 128 + tm * 32 + (lane_id() & 31); }
+__device__ __forceinline__ int lane_row(int tm) { return wave_m() * WTM + tm * 32 + (lane_id() & 31); }
 // first of 4 consecutive tile columns held in registers 4g .. 4g+3 of sub-tile tn
 __device__ __forceinline__ int lane_col(int tn, int g) {
-  return wave_n() * 128 + tn * 32 + 8 * g + 4 * (lane_id() >> 5);
+  return wave_n() * WTN + tn * 32 + 8 * g + 4 * (lane_id() >> 5);
 }
 
 template <bool P_MN, bool Q_MN>
 __device__ __forceinline__ void load_frags(const uint16_t* ldsP, const uint16_t* ldsQ, int kk,
                                            bf16x8 (&pf)[TM], bf16x8 (&qf)[TN]) {
-  const int pm0 = wave_m() * 128, qn0 = wave_n() * 128;
+  const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
 #pragma unroll
   for (int j = 0; j < TN; ++j) qf[j] = Q_MN ? frag_mn(ldsQ, qn0 + 32 * j, kk) : frag_k(ldsQ, qn0 + 32 * j, kk);
 #pragma unroll
@@ -205,35 +211,24 @@ __device__ __forceinline__ void mma_step(const bf16x8 (&pf)[TM], const bf16x8 (&
     for (int j = 0; j < TN; ++j) acc.c[i][j] = mfma_32x32x16(qf[j], pf[i], acc.c[i][j]);
 }
 
-// One k-slab (4 steps of 16) of MFMAs for this wave. Fragments are double
-// buffered: the LDS reads of step s+1 are issued before the 16 MFMAs of step
-// s, and scheduling barriers keep the compiler from sinking them, so LDS
-// latency hides under the MFMA pipe.
+// One k-slab (4 steps of 16) of MFMAs for this wave. With two waves per SIMD
+// the other wave's MFMAs cover this wave's fragment reads, so fragments are
+// single buffered (register budget: 128 accumulators share the 256 VGPRs).
 template <bool P_MN, bool Q_MN>
 __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
-  bf16x8 pa[TM], qa[TN], pb[TM], qb[TN];
-  load_frags<P_MN, Q_MN>(ldsP, ldsQ, 0, pa, qa);
-  load_frags<P_MN, Q_MN>(ldsP, ldsQ, 1, pb, qb);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_step(pa, qa, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  load_frags<P_MN, Q_MN>(ldsP, ldsQ, 2, pa, qa);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_step(pb, qb, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  load_frags<P_MN, Q_MN>(ldsP, ldsQ, 3, pb, qb);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_step(pa, qa, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_step(pb, qb, acc);
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    bf16x8 pf[TM], qf[TN];
+    load_frags<P_MN, Q_MN>(ldsP, ldsQ, kk, pf, qf);
+    mma_step(pf, qf, acc);
+  }
 }
 
 // Runs the k loop of one tile: the global loads of slab kt+1 are in flight
 // (in registers) while slab kt is multiplied out of one LDS buffer; then they
 // are written to the other buffer.
 template <bool P_MN, bool Q_MN, class LP, class LQ>
-__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, int rows, uint16_t* lds, Acc& acc) {
-  (void)rows;
+__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc) {
   if (nk <= 0) return;
   Stage sp, sq;
   lp.fetch(0, sp);
@@ -259,16 +254,15 @@ __device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, int rows, uint1
 }
 
 // ------------------------------------------------------------------ LDS-staged epilogue
-// After the k loop the operand buffers are free. The accumulators of the two
-// waves of one column half (wave_n() == half) are written there as fp32
-// F[m][c], m < 256, c < 128 (this half's columns), then every thread works on
-// whole 16-byte row pieces, so the epilogue's global loads and stores are
-// coalesced and its register footprint is independent of the accumulators.
+// After the k loop the operand buffers are free. The accumulators of the
+// waves of one column half (wave_n() in {2h, 2h+1}) are written there as fp32
+// F[m][c], m < 256, c < 128 (this half's columns, in tile order).
 constexpr int FLD = 128 + 4;  // fp32 row stride (the pad spreads rows over banks)
 static_assert(256 * FLD * 4 <= 2 * kStageLds * 2, "fp32 staging must fit the operand buffers");
+constexpr int kRowPass = kThreads / 16;  // rows per pass when 16 threads share a row
 
 __device__ __forceinline__ void stage_half(const Acc& acc, float* F, int half) {
-  if (wave_n() != half) return;
+  if ((wave_n() >> 1) != half) return;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int m = lane_row(tm);
@@ -276,11 +270,34 @@ __device__ __forceinline__ void stage_half(const Acc& acc, float* F, int half) {
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = tn * 32 + 8 * g + 4 * (lane_id() >> 5);
+        const int c = lane_col(tn, g) - half * 128;
         const f32x16& a = acc.c[tm][tn];
         const f32x4 v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
         *reinterpret_cast<f32x4*>(F + m * FLD + c) = v;
       }
+  }
+}
+
+// Plain bf16 store of the tile into a row-major [*, ld] output starting at
+// (row0, col0); rows beyond `rows` and columns beyond `cols` are not written.
+// Each thread writes 16-byte pieces (8 columns) of rows t/16 + 32*j.
+__device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* lds, uint16_t* out, int64_t ld,
+                                           int64_t row0, int64_t col0, int rows, int cols) {
+  float* F = reinterpret_cast<float*>(lds);
+  const int c = (threadIdx.x & 15) * 8;
+  for (int h = 0; h < 2; ++h) {
+    stage_half(acc, F, h);
+    __syncthreads();
+    if (h * 128 + c < cols) {
+      for (int m = threadIdx.x >> 4; m < rows; m += kRowPass) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(F + m * FLD + c);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(F + m * FLD + c + 4);
+        const u32x4 v = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                         pack_bf16x2(b[2], b[3])};
+        *reinterpret_cast<u32x4*>(out + (row0 + m) * ld + col0 + h * 128 + c) = v;
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -296,12 +313,13 @@ __device__ __forceinline__ int64_t first_tile() {
 
 // s_pref[e] = sum_{e' < e} ceil(counts[e'] / BM), e = 0..E (E <= 1024).
 __device__ void tile_prefix(const int32_t* counts, int E, int32_t* s_pref, int32_t* s_tmp) {
+  constexpr int kPerT = (1024 + kThreads - 1) / kThreads;
   const int tid = threadIdx.x;
-  int32_t loc[4];
+  int32_t loc[kPerT];
   int32_t sum = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid * 4 + q;
+  for (int q = 0; q < kPerT; ++q) {
+    const int e = tid * kPerT + q;
     loc[q] = e < E ? (counts[e] + BM - 1) / BM : 0;
     sum += loc[q];
   }
@@ -315,8 +333,8 @@ __device__ void tile_prefix(const int32_t* counts, int E, int32_t* s_pref, int32
   }
   int32_t run = s_tmp[tid] - sum;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid * 4 + q;
+  for (int q = 0; q < kPerT; ++q) {
+    const int e = tid * kPerT + q;
     if (e < E) s_pref[e] = run;
     run += loc[q];
   }
@@ -353,37 +371,9 @@ __device__ __forceinline__ RowTile decode_row_tile(int64_t t, int NT, const int3
   return r;
 }
 
-// ------------------------------------------------------------------ epilogue helpers
-
 __device__ __forceinline__ void store4_bf16(uint16_t* p, float a, float b, float c, float d) {
   u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
   *reinterpret_cast<u32x2*>(p) = v;
-}
-
-__device__ __forceinline__ void load4_bf16(const uint16_t* p, float* o) {
-  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-  o[0] = bf16_lo(v[0]); o[1] = bf16_hi(v[0]); o[2] = bf16_lo(v[1]); o[3] = bf16_hi(v[1]);
-}
-
-// Plain bf16 store of the tile into a row-major [*, ld] output starting at
-// (row0, col0); rows beyond `rows` and columns beyond `cols` are not written.
-__device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* out, int64_t ld, int64_t row0,
-                                           int64_t col0, int rows, int cols) {
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int m = lane_row(tm);
-    if (m >= rows) continue;
-    uint16_t* o = out + (row0 + m) * ld + col0;
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = lane_col(tn, g);
-        if (n >= cols) continue;
-        const f32x16& c = acc.c[tm][tn];
-        store4_bf16(o + n, c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
-      }
-  }
 }
 
 #define MOE_GEMM_SMEM                                                          \
@@ -396,18 +386,18 @@ __device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* out, int64_
 
 // ================================================================== forward GEMM1
 // C[r][q] = x[tok(r)] . W13[e][wrow(q)],  K = H. Q rows are arranged so that
-// each wave's sub-tiles come in (gate, up) pairs of the same intermediate
+// each wave's two sub-tiles are (gate, up) of the same 32 intermediate
 // indices; the epilogue forms a = silu(g) * u and stores g and u (for the
 // backward) and w * a (routing weight folded in: the down GEMM then needs no
 // scale, and the dW2 GEMM reads the weighted activation directly).
 namespace g1 {
-constexpr int IPT = BN / 2;  // intermediate indices per tile
+constexpr int IPT = BN / 2;  // intermediate indices per tile (128)
 // Q row q -> row of W13[e]
 __device__ __forceinline__ int w13_row(int q, int nt, int I) {
-  const int wn = q >> 7;          // wave column
-  const int s = (q & 127) >> 5;   // sub-tile within the wave: 0 g, 1 u, 2 g, 3 u
-  const int i = nt * IPT + wn * 64 + (s >> 1) * 32 + (q & 31);
-  return (s & 1) * I + i;
+  const int wn = q / WTN;         // wave column
+  const int s = (q % WTN) >> 5;   // 0 gate, 1 up
+  const int i = nt * IPT + wn * 32 + (q & 31);
+  return s * I + i;
 }
 }  // namespace g1
 
@@ -427,28 +417,28 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, c
     lp.base = x;
     lq.base = W13 + int64_t(rt.e) * 2 * I * H;
 #pragma unroll
-    for (int i = 0; i < KMajorLoader::kPer; ++i) {
+    for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
       const int mc = m < rt.rows ? m : rt.rows - 1;  // past-the-end rows reuse a real row
       lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * H);
       lq.set_row(i, int64_t(g1::w13_row(m, rt.nt, I)) * H);
     }
-    // routing weight of tile row threadIdx.x: loaded now, used after the k loop
-    const float w_row = p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)];
+    // routing weight of tile row t: loaded now, used after the k loop
+    const float w_row = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
     Acc acc;
     acc.zero();
-    mainloop<false, false>(lp, lq, H / BK, rt.rows, lds, acc);
-    s_w[threadIdx.x] = w_row;
+    mainloop<false, false>(lp, lq, H / BK, lds, acc);
+    if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds g and u of intermediate indices nt*128 + h*64 + [0, 64):
     // staged column (i/32)*64 + i%32 is g, +32 is u.
     float* F = reinterpret_cast<float*>(lds);
+    const int io = (threadIdx.x & 15) * 4;  // 4 intermediate indices per thread
+    const int gc = (io >> 5) * 64 + (io & 31);
     for (int h = 0; h < 2; ++h) {
       stage_half(acc, F, h);
       __syncthreads();
-      const int io = (threadIdx.x & 15) * 4;            // 4 intermediate indices per thread
-      const int gc = (io >> 5) * 64 + (io & 31);
       const int i = rt.nt * g1::IPT + h * 64 + io;
-      for (int m = threadIdx.x >> 4; m < rt.rows; m += 16) {
+      for (int m = threadIdx.x >> 4; m < rt.rows; m += kRowPass) {
         const int64_t r = rt.row0 + m;
         const float w = s_w[m];
         const f32x4 gv = *reinterpret_cast<const f32x4*>(F + m * FLD + gc);
@@ -483,15 +473,15 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, const ui
     lp.base = act + rt.row0 * I;
     lq.base = W2 + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * I;
 #pragma unroll
-    for (int i = 0; i < KMajorLoader::kPer; ++i) {
+    for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
       lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * I);
       lq.set_row(i, int64_t(m) * I);
     }
     Acc acc;
     acc.zero();
-    mainloop<false, false>(lp, lq, I / BK, rt.rows, lds, acc);
-    store_tile(acc, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
+    mainloop<false, false>(lp, lq, I / BK, lds, acc);
+    store_tile(acc, lds, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
   }
 }
 
@@ -522,7 +512,7 @@ struct TokenRows {  // k-th row of an expert segment -> its token's row
 // element, with g, u from the saved [g | u]:
 //   a = silu(g) u,  dw partial += dA_u a,  dA = w dA_u,
 //   dg = dA u sig(g) (1 + g (1 - sig(g))),  du = dA silu(g).
-// dwpart[r][2*nt + wave_n] holds one wave's partial sum of dA_u * a.
+// dwpart[r][2*nt + h] holds the partial sum of dA_u * a over column half h.
 int dh_num_parts(int64_t I) { return int((I + BN - 1) / BN) * 2; }
 
 __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const uint16_t* __restrict__ dy,
@@ -542,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const 
     KMajorLoader lp;
     lp.base = dy;
 #pragma unroll
-    for (int i = 0; i < KMajorLoader::kPer; ++i) {
+    for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
       const int mc = m < rt.rows ? m : rt.rows - 1;
       lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * H);
@@ -554,46 +544,34 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const 
     const int ncols = min(BN, I - rt.nt * BN);
     lq.nchunks = ncols / 8;
     lq.prime(0);
+    const float w_row = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
     Acc acc;
     acc.zero();
-    const float w_row = p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)];
-    mainloop<false, true>(lp, lq, H / BK, rt.rows, lds, acc);
-    s_w[threadIdx.x] = w_row;
+    mainloop<false, true>(lp, lq, H / BK, lds, acc);
+    if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
-    // Thread t works on 8 of them (c) for tile rows t/16 + 16*j, j < 16, in
-    // four batches of four rows; the [g | u] pieces of the next batch are
-    // requested before the current batch is computed (the first batch's before
-    // the staging barrier), so their latency overlaps other work.
+    // Thread t works on 8 of them (c) for tile rows t/16 + 32*j, j < 8, in
+    // two batches of four rows; each batch's [g | u] pieces are requested
+    // together (the first batch's before the staging barrier).
     float* F = reinterpret_cast<float*>(lds);
+    const int c = (threadIdx.x & 15) * 8;
     for (int h = 0; h < 2; ++h) {
-      const int c = (threadIdx.x & 15) * 8;
       const bool col_ok = h * 128 + c < ncols;
       const int i = rt.nt * BN + h * 128 + (col_ok ? c : 0);
-      auto fetch_gu = [&](int j, u32x4& gq, u32x4& uq) {
-        const int m = min((int(threadIdx.x) >> 4) + 16 * j, rt.rows - 1);
-        const uint16_t* src = h13 + (rt.row0 + m) * 2 * I + i;
-        gq = *reinterpret_cast<const u32x4*>(src);
-        uq = *reinterpret_cast<const u32x4*>(src + I);
-      };
-      u32x4 ga[4], ua[4], gb[4], ub[4];
       stage_half(acc, F, h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fetch_gu(j, ga[j], ua[j]);
-      __syncthreads();
-#pragma unroll 1
-      for (int bt = 0; bt < 4; ++bt) {
-        if (bt < 3) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (bt & 1) fetch_gu(4 * (bt + 1) + j, ga[j], ua[j]);
-            else fetch_gu(4 * (bt + 1) + j, gb[j], ub[j]);
-          }
-        }
+      for (int bt = 0; bt < 2; ++bt) {
+        u32x4 gq[4], uq[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const u32x4 gq = (bt & 1) ? gb[j] : ga[j];
-          const u32x4 uq = (bt & 1) ? ub[j] : ua[j];
-          const int m = (threadIdx.x >> 4) + 16 * (4 * bt + j);
+          const int m = min((int(threadIdx.x) >> 4) + kRowPass * (4 * bt + j), rt.rows - 1);
+          const uint16_t* src = h13 + (rt.row0 + m) * 2 * I + i;
+          gq[j] = *reinterpret_cast<const u32x4*>(src);
+          uq[j] = *reinterpret_cast<const u32x4*>(src + I);
+        }
+        if (bt == 0) __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int m = (threadIdx.x >> 4) + kRowPass * (4 * bt + j);
           const bool row_ok = m < rt.rows;
           float dws = 0.f;
           if (row_ok && col_ok) {
@@ -607,8 +585,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const 
               float dgp[2], dup[2];
 #pragma unroll
               for (int hh = 0; hh < 2; ++hh) {
-                const float gv = hh ? bf16_hi(gq[q]) : bf16_lo(gq[q]);
-                const float uv = hh ? bf16_hi(uq[q]) : bf16_lo(uq[q]);
+                const float gv = hh ? bf16_hi(gq[j][q]) : bf16_lo(gq[j][q]);
+                const float uv = hh ? bf16_hi(uq[j][q]) : bf16_lo(uq[j][q]);
                 const int e8 = 2 * q + hh;
                 const float dau = e8 < 4 ? d0[e8] : d1[e8 - 4];
                 const float sg_ = sigmoidf_fast(gv);
@@ -652,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, const 
     KMajorLoader lp;
     lp.base = dh13 + rt.row0 * 2 * I;
 #pragma unroll
-    for (int i = 0; i < KMajorLoader::kPer; ++i) {
+    for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
       lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * 2 * I);
     }
@@ -663,8 +641,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, const 
     lq.prime(0);
     Acc acc;
     acc.zero();
-    mainloop<false, true>(lp, lq, (2 * I) / BK, rt.rows, lds, acc);
-    store_tile(acc, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
+    mainloop<false, true>(lp, lq, (2 * I) / BK, lds, acc);
+    store_tile(acc, lds, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
   }
 }
 
@@ -702,8 +680,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     }
     Acc acc;
     acc.zero();
-    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, BM, lds, acc);
-    store_tile(acc, dW13 + int64_t(e) * 2 * I * H, H, int64_t(mt) * BM, int64_t(nt) * BN, BM, BN);
+    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, lds, acc);
+    store_tile(acc, lds, dW13 + int64_t(e) * 2 * I * H, H, int64_t(mt) * BM, int64_t(nt) * BN, BM, BN);
   }
 }
 
@@ -738,15 +716,15 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     }
     Acc acc;
     acc.zero();
-    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, BM, lds, acc);
-    store_tile(acc, dW2 + int64_t(e) * H * I, I, int64_t(mt) * BM, int64_t(nt) * BN, BM, ncols);
+    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, lds, acc);
+    store_tile(acc, lds, dW2 + int64_t(e) * H * I, I, int64_t(mt) * BM, int64_t(nt) * BN, BM, ncols);
   }
 }
 
 // ================================================================== launchers
 
 static int grid_for(int64_t tiles, int num_cus) {
-  int64_t g = int64_t(num_cus);  // one 256-thread workgroup per CU (LDS-bound)
+  int64_t g = int64_t(num_cus);  // one 512-thread workgroup per CU (LDS-bound)
   if (tiles < g) g = tiles;
   if (g < 1) g = 1;
   return int(g);
