@@ -33,6 +33,27 @@ COPY_CALIB_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 GEMM_FLOP_FACTOR = {
     "gemm1_swiglu": 4, "gemm2": 2, "gemm_dh_dswiglu": 2, "gemm_dx": 4, "gemm_dw13": 4, "gemm_dw2": 2,
 }
+# timer name -> kernel function name in rocprofv3 output
+KERNEL_FN = {
+    "gemm1_swiglu": "gemm1_swiglu_kernel", "gemm2": "gemm2_kernel", "gemm_dh_dswiglu": "gemm_dh_kernel",
+    "gemm_dx": "gemm_dx_kernel", "gemm_dw13": "gemm_dw13_kernel", "gemm_dw2": "gemm_dw2_kernel",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_qwen3_30b_bf16.json")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when there is none or the kernels changed since it was taken."""
+    from grouped_gemm_02_amd import profile_summary
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    d = json.load(open(TRAFFIC_FILE))
+    if d.get("source_sha256") != profile_summary.source_hash():
+        return None
+    k = d.get("kernels", {}).get(KERNEL_FN.get(kernel, kernel))
+    if not k or "fetch_size_bytes" not in k or "write_size_bytes" not in k:
+        return None
+    return k["fetch_size_bytes"] + k["write_size_bytes"]
 
 
 def parse():
@@ -42,7 +63,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_30b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     return ap.parse_args()
 
 
@@ -52,6 +73,7 @@ def cpu_baseline(cfg, d, n_tok):
     from threadpoolctl import threadpool_info
 
     from oracle import moe_oracle as orc
+    n_tok = min(n_tok, cfg.T)
     sub = {k: d[k][:n_tok].cpu() for k in ("x", "topk_idx", "topk_w", "dy")}
     W13 = d["W13"].cpu()
     W2 = d["W2"].cpu()
@@ -174,7 +196,8 @@ def main():
         "wall_s": round(wall, 3),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample_tokens)

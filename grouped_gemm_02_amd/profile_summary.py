@@ -1,0 +1,115 @@
+"""Summaries of rocprofv3 output for the layer's kernels.
+
+    python -m grouped_gemm_02_amd.profile_summary stats <kernel_stats.csv> <out.txt> --cmd "<command>"
+    python -m grouped_gemm_02_amd.profile_summary traffic <fetch_counter_collection.csv> \
+        <write_counter_collection.csv> <out.json> --cmd "<command>"
+
+`stats` turns the --kernel-trace --stats table into a short text table.
+`traffic` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE, both in KiB per
+dispatch) into HBM bytes per launch of each layer kernel. Both counters are
+calibrated against the largest device-to-device copy in the same run, whose
+size is known (it reads and writes `--copy-bytes` bytes): factor =
+known bytes / counter reading. The JSON records the sha256 of the GEMM
+sources it was measured with, so a reader can tell when it has gone stale.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/device_common.h", "csrc/combine.hip", "csrc/permute.hip")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str:
+    n = name.split("(")[0]
+    if n.startswith("void "):
+        n = n[5:]
+    return n.replace("moe::", "")
+
+
+def stats(csv_path: str, out_path: str, cmd: str) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = [f"# rocprofv3 --kernel-trace --stats summary", f"# command: {cmd}", "#",
+             f"{'kernel':34s} {'calls':>6s} {'avg_us':>10s} {'total_us':>12s} {'pct':>6s}"]
+    for r in rows:
+        name = r.get("Name") or r.get("KERNEL_NAME") or ""
+        if "moe::" not in name:
+            continue
+        calls = int(float(r.get("Calls", r.get("TotalCalls", 0))))
+        tot = float(r.get("TotalDurationNs", 0)) / 1e3
+        avg = float(r.get("AverageNs", 0)) / 1e3
+        pct = float(r.get("Percentage", 0))
+        lines.append(f"{short_name(name):34s} {calls:6d} {avg:10.1f} {tot:12.1f} {pct:6.2f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(csv_path: str, counter: str):
+    vals = collections.defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = r["Dispatch_Id"]
+        vals[d] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    return vals, names
+
+
+def traffic(fetch_csv: str, write_csv: str, out_path: str, cmd: str, copy_bytes: int) -> None:
+    res = {"command": cmd, "source_sha256": source_hash(), "copy_bytes": copy_bytes, "kernels": {}}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals, names = _per_dispatch(path, counter)
+        copies = [d for d, n in names.items() if "copy" in n.lower() and "moe::" not in n]
+        if not copies:
+            raise SystemExit(f"no copy kernel found in {path}")
+        cal = max(copies, key=lambda d: vals[d])
+        factor = copy_bytes / (vals[cal] * 1024.0)
+        res[f"{counter.lower()}_calibration"] = {"copy_kib": vals[cal], "factor": factor}
+        agg = collections.defaultdict(list)
+        for d, v in vals.items():
+            if "moe::" in names[d]:
+                agg[short_name(names[d])].append(v * 1024.0 * factor)
+        for k, vs in agg.items():
+            ent = res["kernels"].setdefault(k, {})
+            ent[f"{counter.lower()}_bytes"] = sum(vs) / len(vs)
+            ent["dispatches"] = len(vs)
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("out")
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--copy-bytes", type=int, default=1 << 30)
+    a = ap.parse_args()
+    if a.what == "stats":
+        stats(a.csv, a.out, a.cmd)
+    else:
+        traffic(a.fetch_csv, a.write_csv, a.out, a.cmd, a.copy_bytes)
+
+
+if __name__ == "__main__":
+    main()
