@@ -1,0 +1,242 @@
+"""FP8 emulation for the CPU oracle: TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import this module. It shares no code with the HIP
+path.
+
+The pages name the precisions (ic.work analysis, section on hardware
+constraints: BF16, MXFP8 and blockwise FP8; MarkTechPost article, "How do
+developers use it?": bf16, mxfp8, fp8 and fp8_bwd = BF16 forward with FP8
+backward) but not the number format, block shapes, scale rule or which
+tensors are quantized. The readings used here (listed in the design doc):
+
+* FP8 is OCP E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7,
+  3 mantissa bits, subnormals, no infinities, largest finite value 448.
+  Values are rounded to nearest, ties to the even code, and saturate at +-448.
+* Every block has one power-of-two scale 2^e (stored as an E8M0 exponent
+  byte e + 127); a value v is stored as code(v / 2^e).
+  - "fp8_block" (blockwise): activations in 1x128 blocks along the GEMM's
+    reduction axis, weights in 128x128 blocks; e is the smallest integer with
+    448 * 2^e >= amax (no value saturates).
+  - "mxfp8": 1x32 blocks along the reduction axis for every operand, weights
+    included; e = floor(log2 amax) - 8 (the OCP MX rule; values up to just
+    under 2 * 2^(e+8) saturate at 448).
+  - an all-zero block gets e = 0.
+* Quantization points: forward x (along H) and the weighted activation
+  w * silu(g) * u (along I), gate/up and down weights; backward dY (along H)
+  and [dg | du] (along 2I), and the weights again for the transposed use
+  (blockwise: the same 128x128 blocks; mxfp8: re-blocked along the new
+  reduction axis). The two weight-gradient GEMMs run on the unquantized
+  (bf16) operands.
+* Quantization is applied to the exact (float64) value at each point; the
+  result is dequantized (code * 2^e) and the math continues exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import moe_oracle as base
+
+E4M3_MAX = 448.0
+MODES = ("fp8_block", "mxfp8", "fp8_bwd")
+
+
+# --------------------------------------------------------------- E4M3 codes
+
+def e4m3_decode_table() -> np.ndarray:
+    """float64 value of each of the 256 codes (NaN for the two NaN codes)."""
+    vals = np.empty(256)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        ex = (c >> 3) & 0xF
+        m = c & 0x7
+        if ex == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif ex == 0:
+            vals[c] = s * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[c] = s * (1.0 + m / 8.0) * 2.0 ** (ex - 7)
+    return vals
+
+
+_TABLE = e4m3_decode_table()
+_POS = _TABLE[:0x7F]                    # codes 0x00..0x7E: 0 .. 448, increasing
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code (ties to the even code), saturating at +-448."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(_POS, a, side="left")          # first value >= a
+    hi = np.minimum(hi, len(_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _POS[lo]
+    d_hi = _POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a == _POS[hi], hi, code).astype(np.uint8)
+    neg = (v < 0) & (code != 0)
+    return (code | (neg.astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+# --------------------------------------------------------------- block scales
+
+def scale_exponent(amax, rule: str) -> np.ndarray:
+    """Integer e of the block scale 2^e for block maxima `amax` (float64)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    out = np.zeros(amax.shape, dtype=np.int64)
+    nz = amax > 0
+    if rule == "pow2_ceil":
+        # smallest e with 448 * 2^e >= amax, found exactly (448 * 2^e is exact)
+        e = np.ceil(np.log2(amax[nz] / E4M3_MAX)).astype(np.int64)
+        e = np.where(np.ldexp(E4M3_MAX, e) < amax[nz], e + 1, e)
+        e = np.where(np.ldexp(E4M3_MAX, e - 1) >= amax[nz], e - 1, e)
+        out[nz] = e
+    elif rule == "mx_floor":
+        _, ex = np.frexp(amax[nz])            # amax = f * 2^ex, f in [0.5, 1)
+        out[nz] = (ex - 1) - 8                # floor(log2 amax) - emax(E4M3)
+    else:
+        raise ValueError(rule)
+    return out
+
+
+def quantize_along_last(v, block: int, rule: str):
+    """Blocks of `block` consecutive values along the last axis. Returns
+    (codes uint8, e int64 per block, dequantized float64)."""
+    v = np.asarray(v, dtype=np.float64)
+    *lead, n = v.shape
+    assert n % block == 0
+    vb = v.reshape(*lead, n // block, block)
+    e = scale_exponent(np.max(np.abs(vb), axis=-1), rule)
+    codes = e4m3_encode(vb / np.ldexp(1.0, e)[..., None])
+    deq = e4m3_decode(codes) * np.ldexp(1.0, e)[..., None]
+    return codes.reshape(v.shape), e, deq.reshape(v.shape)
+
+
+def quantize_tiles(w, tile: int, rule: str):
+    """tile x tile blocks over the last two axes. Returns (codes, e, deq)."""
+    w = np.asarray(w, dtype=np.float64)
+    *lead, r, c = w.shape
+    assert r % tile == 0 and c % tile == 0
+    wb = w.reshape(*lead, r // tile, tile, c // tile, tile)
+    e = scale_exponent(np.max(np.abs(wb), axis=(-3, -1)), rule)
+    sc = np.ldexp(1.0, e)[..., :, None, :, None]
+    codes = e4m3_encode(wb / sc)
+    deq = e4m3_decode(codes) * sc
+    return codes.reshape(w.shape), e, deq.reshape(w.shape)
+
+
+def _act(v, mode):
+    """Quantize-dequantize an activation along its last (reduction) axis."""
+    if mode == "mxfp8":
+        return quantize_along_last(v, 32, "mx_floor")[2]
+    return quantize_along_last(v, 128, "pow2_ceil")[2]
+
+
+def _weight(w, mode, reduce_axis_last: bool):
+    """Quantize-dequantize a weight matrix stack [E, R, C]; the GEMM reduces
+    over its last axis (reduce_axis_last) or over the middle axis."""
+    if mode == "mxfp8":
+        if reduce_axis_last:
+            return quantize_along_last(w, 32, "mx_floor")[2]
+        return np.swapaxes(quantize_along_last(np.swapaxes(w, -1, -2), 32, "mx_floor")[2], -1, -2)
+    return quantize_tiles(w, 128, "pow2_ceil")[2]
+
+
+# --------------------------------------------------------------- layer
+
+def forward(x, topk_idx, topk_w, W13, W2, mode: str, return_pairs: bool = False):
+    """Forward with the quantization points of `mode` ("fp8_bwd" runs the
+    forward in full precision)."""
+    if mode == "fp8_bwd":
+        return base.forward(x, topk_idx, topk_w, W13, W2, return_pairs=return_pairs)
+    x = base.as_f64(x)
+    W13 = base.as_f64(W13)
+    W2 = base.as_f64(W2)
+    w = base.as_f64(topk_w)
+    idx = base.as_i64(topk_idx)
+    T, H = x.shape
+    E, I2, _ = W13.shape
+    I = I2 // 2
+    k = idx.shape[1]
+    wf = w.reshape(-1)
+    xq = _act(x, mode)
+    W13q = _weight(W13, mode, True)
+    W2q = _weight(W2, mode, True)
+    y = np.zeros((T, H))
+    pairs = {"g": np.zeros((T * k, I)), "u": np.zeros((T * k, I)), "wa": np.zeros((T * k, I))} \
+        if return_pairs else None
+    for e in range(E):
+        f = base.expert_pairs(idx, e)
+        if f.size == 0:
+            continue
+        t = f // k
+        X = xq[t]
+        G = X @ W13q[e, :I].T
+        U = X @ W13q[e, I:].T
+        WA = wf[f][:, None] * (base.silu(G) * U)
+        O = _act(WA, mode) @ W2q[e].T
+        np.add.at(y, t, O)
+        if return_pairs:
+            pairs["g"][f] = G
+            pairs["u"][f] = U
+            pairs["wa"][f] = WA
+    if return_pairs:
+        return y, pairs
+    return y
+
+
+def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str):
+    """Gradients of L = <dY, y> with the backward quantization points of
+    `mode`: dY and W2 quantized for the dH product, [dg | du] and W13 for the
+    dX product; the weight gradients use unquantized operands. g and u come
+    from the forward of the same mode."""
+    dy = base.as_f64(dy)
+    x = base.as_f64(x)
+    W13 = base.as_f64(W13)
+    W2 = base.as_f64(W2)
+    w = base.as_f64(topk_w)
+    idx = base.as_i64(topk_idx)
+    T, H = x.shape
+    E, I2, _ = W13.shape
+    I = I2 // 2
+    k = idx.shape[1]
+    wf = w.reshape(-1)
+    if mode == "fp8_bwd":
+        xf, W13f = x, W13
+    else:
+        xf, W13f = _act(x, mode), _weight(W13, mode, True)
+    dyq = _act(dy, mode)
+    W2b = _weight(W2, mode, False)      # dH product reduces over H = W2's rows
+    W13b = _weight(W13, mode, False)    # dX product reduces over 2I = W13's rows
+    dx = np.zeros((T, H))
+    dwf = np.zeros(T * k)
+    dW13 = np.zeros((E, I2, H))
+    dW2 = np.zeros((E, H, I))
+    for e in range(E):
+        f = base.expert_pairs(idx, e)
+        if f.size == 0:
+            continue
+        t = f // k
+        G = xf[t] @ W13f[e, :I].T
+        U = xf[t] @ W13f[e, I:].T
+        S = base.sigmoid(G)
+        A = G * S * U
+        dAu = dyq[t] @ W2b[e]
+        dwf[f] = np.sum(dAu * A, axis=1)
+        dA = wf[f][:, None] * dAu
+        dG = dA * U * S * (1.0 + G * (1.0 - S))
+        dU = dA * G * S
+        dHm = np.concatenate([dG, dU], axis=1)
+        np.add.at(dx, t, _act(dHm, mode) @ W13b[e])
+        dW13[e] = dHm.T @ x[t]
+        dW2[e] = dy[t].T @ (wf[f][:, None] * A)
+    return dx, dwf.reshape(T, k), dW13, dW2
+
+
+__all__ = ["MODES", "E4M3_MAX", "e4m3_decode_table", "e4m3_encode", "e4m3_decode", "scale_exponent",
+           "quantize_along_last", "quantize_tiles", "forward", "backward"]

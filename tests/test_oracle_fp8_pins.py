@@ -1,0 +1,234 @@
+"""Pins for the oracle's FP8 emulation (oracle/moe_fp8.py).
+
+Independent references: E4M3 values observed on the MI355X matrix cores
+(code 0x38 multiplies as 1.0, 0x40 as 2.0, and the scale byte 127 + 1
+doubles a product), the defining properties of the scale rules and of
+round-to-nearest-even, and a per-token loop implementation of the quantized
+layer with its own scalar rounding (math.frexp based) on tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import moe_fp8 as f8
+from oracle import moe_oracle as orc
+
+
+def test_e4m3_anchor_values():
+    t = f8.e4m3_decode_table()
+    assert t[0x38] == 1.0 and t[0x40] == 2.0          # as multiplied by the MI355X MFMA
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0     # largest finite magnitude
+    assert t[0x08] == 2.0 ** -6                       # smallest normal
+    assert t[0x01] == 2.0 ** -9                       # smallest subnormal
+    assert t[0x00] == 0.0 and t[0x80] == 0.0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert np.isfinite(t[np.r_[0:0x7F, 0x80:0xFF]]).all()
+
+
+def test_e4m3_monotone_and_round_trip():
+    t = f8.e4m3_decode_table()
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    codes = np.r_[0:0x7F, 0x81:0xFF].astype(np.uint8)
+    assert np.array_equal(f8.e4m3_encode(t[codes]), codes)
+
+
+def test_e4m3_ties_to_even_and_saturation():
+    t = f8.e4m3_decode_table()
+    for c in range(0, 0x7E):
+        lo, hi = t[c], t[c + 1]
+        mid = (lo + hi) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert f8.e4m3_encode(mid) == even, c
+        assert f8.e4m3_encode(np.nextafter(mid, hi)) == c + 1
+        assert f8.e4m3_encode(np.nextafter(mid, lo)) == c
+        assert f8.e4m3_encode(-mid) == (even | 0x80 if even else 0)
+    assert f8.e4m3_encode(1e9) == 0x7E and f8.e4m3_encode(-1e9) == 0xFE
+    assert f8.e4m3_encode(460.0) == 0x7E
+
+
+def test_scale_exponent_rules():
+    rng = np.random.default_rng(0)
+    amax = np.exp(rng.uniform(-40, 40, size=20000))
+    amax = np.concatenate([amax, [448.0, 449.0, 224.0, 1.0, 2.0 ** -30, 256.0, 512.0]])
+    e = f8.scale_exponent(amax, "pow2_ceil")
+    assert np.all(448.0 * np.ldexp(1.0, e) >= amax)
+    assert np.all(448.0 * np.ldexp(1.0, e - 1) < amax)
+    e = f8.scale_exponent(amax, "mx_floor")
+    assert np.all(np.ldexp(1.0, e + 8) <= amax)
+    assert np.all(np.ldexp(1.0, e + 9) > amax)
+    assert f8.scale_exponent(np.zeros(3), "pow2_ceil").tolist() == [0, 0, 0]
+    assert f8.scale_exponent(np.zeros(3), "mx_floor").tolist() == [0, 0, 0]
+
+
+@pytest.mark.parametrize("block,rule", [(128, "pow2_ceil"), (32, "mx_floor")])
+def test_quantization_error_bounds(block, rule):
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal((64, 512)) * np.exp(rng.uniform(-6, 6, size=(64, 1)))
+    v[3, :block] = 0.0                                 # an all-zero block
+    codes, e, deq = f8.quantize_along_last(v, block, rule)
+    sc = np.repeat(np.ldexp(1.0, e), block, axis=-1)
+    q = deq / sc
+    if rule == "pow2_ceil":
+        assert np.all(np.abs(q) <= 448.0)
+        bound = np.abs(v) * 2.0 ** -4 + sc * 2.0 ** -10
+        assert np.all(np.abs(deq - v) <= bound)
+    else:
+        unsat = np.abs(v / sc) <= 448.0
+        bound = np.abs(v) * 2.0 ** -4 + sc * 2.0 ** -10
+        assert np.all(np.abs(deq - v)[unsat] <= bound[unsat])
+        assert np.all(np.abs(q[~unsat]) == 448.0)
+    assert not deq[3, :block].any()
+
+
+def test_weight_tiles_share_one_scale():
+    rng = np.random.default_rng(2)
+    w = rng.standard_normal((2, 256, 384)) * 0.02
+    codes, e, deq = f8.quantize_tiles(w, 128, "pow2_ceil")
+    assert e.shape == (2, 2, 3)
+    blk = np.abs(w[1, 128:256, 256:384]).max()
+    assert 448 * 2.0 ** e[1, 1, 2] >= blk > 224 * 2.0 ** e[1, 1, 2]
+
+
+# ----------------------------------------------------- loop reference, tiny layer
+
+def _q_scalar(v, e):
+    """Round v / 2^e to E4M3 (ties to even, saturating) with math.frexp and
+    return the dequantized value."""
+    a = abs(v) / 2.0 ** e
+    s = -1.0 if v < 0 else 1.0
+    if a >= 448.0:
+        return s * 448.0 * 2.0 ** e
+    if a == 0.0:
+        return 0.0
+    m, ex = math.frexp(a)            # a = m * 2^ex, m in [0.5, 1)
+    lsb = 2.0 ** (max(ex - 1, -6) - 3)   # spacing of representable values here
+    n = a / lsb
+    r = math.floor(n)
+    frac = n - r
+    if frac > 0.5 or (frac == 0.5 and r % 2 == 1):
+        r += 1
+    return s * min(r * lsb, 448.0) * 2.0 ** e
+
+
+def _q_block(vals, rule):
+    amax = max(abs(v) for v in vals)
+    if amax == 0.0:
+        e = 0
+    elif rule == "pow2_ceil":
+        e = 0
+        while 448.0 * 2.0 ** e < amax:
+            e += 1
+        while 448.0 * 2.0 ** (e - 1) >= amax:
+            e -= 1
+    else:
+        e = math.floor(math.log2(amax)) - 8
+        if 2.0 ** (e + 8) > amax:
+            e -= 1
+        if 2.0 ** (e + 9) <= amax:
+            e += 1
+    return [_q_scalar(v, e) for v in vals]
+
+
+def _q_rows(M, block, rule):
+    out = []
+    for row in M:
+        r = []
+        for s in range(0, len(row), block):
+            r += _q_block(list(row[s:s + block]), rule)
+        out.append(r)
+    return np.array(out)
+
+
+def _q_weight(W, mode, reduce_last):
+    if mode == "mxfp8":
+        if reduce_last:
+            return np.array([_q_rows(W[e], 32, "mx_floor") for e in range(W.shape[0])])
+        return np.array([_q_rows(W[e].T, 32, "mx_floor").T for e in range(W.shape[0])])
+    out = np.zeros_like(W)
+    for e in range(W.shape[0]):
+        for r in range(0, W.shape[1], 128):
+            for c in range(0, W.shape[2], 128):
+                blk = W[e, r:r + 128, c:c + 128]
+                out[e, r:r + 128, c:c + 128] = np.array(_q_block(list(blk.reshape(-1)), "pow2_ceil")).reshape(
+                    blk.shape)
+    return out
+
+
+def _layer_loops(x, idx, w, W13, W2, dy, mode):
+    """Forward and dx/d_topk_w of the quantized layer, token by token."""
+    blk, rule = (32, "mx_floor") if mode == "mxfp8" else (128, "pow2_ceil")
+    T, H = x.shape
+    I = W13.shape[1] // 2
+    k = idx.shape[1]
+    qa = lambda M: _q_rows(M, blk, rule)  # noqa: E731
+    if mode == "fp8_bwd":
+        xq, W13q, W2q = x, W13, W2
+        fwd_q = lambda M: M  # noqa: E731
+    else:
+        xq, W13q, W2q = qa(x), _q_weight(W13, mode, True), _q_weight(W2, mode, True)
+        fwd_q = qa
+    W2b = _q_weight(W2, mode, False)
+    W13b = _q_weight(W13, mode, False)
+    dyq = qa(dy)
+    y = np.zeros((T, H))
+    dx = np.zeros((T, H))
+    dw = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            g = W13q[e, :I] @ xq[t]
+            u = W13q[e, I:] @ xq[t]
+            sg = 1.0 / (1.0 + np.exp(-g))
+            a = g * sg * u
+            wa = fwd_q((w[t, j] * a)[None, :])[0]
+            y[t] += W2q[e] @ wa
+            dau = W2b[e].T @ dyq[t]
+            dw[t, j] = float(dau @ a)
+            da = w[t, j] * dau
+            dh = np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg])
+            dx[t] += W13b[e].T @ qa(dh[None, :])[0]
+    return y, dx, dw
+
+
+@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8", "fp8_bwd"])
+def test_quantized_layer_matches_per_token_loops(mode):
+    rng = np.random.default_rng(3)
+    T, H, I, E, k = 6, 256, 128, 3, 2
+    x = rng.standard_normal((T, H))
+    W13 = rng.standard_normal((E, 2 * I, H)) * 0.05
+    W2 = rng.standard_normal((E, H, I)) * 0.05
+    idx = np.array([rng.choice(E, k, replace=False) for _ in range(T)])
+    w = rng.uniform(0.1, 1.0, size=(T, k))
+    dy = rng.standard_normal((T, H))
+    y = f8.forward(x, idx, w, W13, W2, mode)
+    dx, dw, _, _ = f8.backward(dy, x, idx, w, W13, W2, mode)
+    ry, rdx, rdw = _layer_loops(x, idx, w, W13, W2, dy, mode)
+    np.testing.assert_allclose(y, ry, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(dx, rdx, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(dw, rdw, rtol=1e-9, atol=1e-9)
+
+
+@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8"])
+def test_quantized_layer_close_to_exact_layer(mode):
+    """Sanity scale of the quantization error (a few percent), not a pin."""
+    from grouped_gemm_02_amd import inputs
+    d = inputs.make_layer_inputs(inputs.CONFIGS["tiny"], "cpu")
+    y = f8.forward(d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], mode)
+    ref = orc.forward(d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
+    err = np.max(np.abs(y - ref)) / np.max(np.abs(ref))
+    assert err < 0.15, err
+
+
+def test_weight_gradients_use_unquantized_operands():
+    """With a full-precision forward, dW2 = dY^T (w a) involves no quantized
+    operand and equals the exact gradient; dW13 inherits the quantized dH
+    product through [dg | du] only."""
+    from grouped_gemm_02_amd import inputs
+    d = inputs.make_layer_inputs(inputs.CONFIGS["tiny"], "cpu")
+    args = (d["dy"], d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
+    _, _, dW13, dW2 = f8.backward(*args, mode="fp8_bwd")
+    _, _, rW13, rW2 = orc.backward(*args)
+    np.testing.assert_allclose(dW2, rW2, rtol=1e-12, atol=1e-12)
+    assert np.max(np.abs(dW13 - rW13)) / np.max(np.abs(rW13)) < 0.15
