@@ -43,6 +43,11 @@ class moe_saved_layout(ctypes.Structure):
                 ("counts", "offsets", "row_of", "src_of", "wrow", "h13", "act", "total")]
 
 
+class moe_wq_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("w13", "w13_scale", "w2", "w2_scale", "w2t", "w2t_scale", "w13t", "w13t_scale", "total")]
+
+
 class moe_kernel_time(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32),
                 ("total_ms", ctypes.c_double)]
@@ -55,12 +60,16 @@ _SIGS = {
     "moe_workspace_size": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.POINTER(ctypes.c_size_t),
                                           ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
     "moe_get_saved_layout": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.POINTER(moe_saved_layout)]),
+    "moe_get_wq_layout": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.POINTER(moe_wq_layout)]),
+    "moe_quantize_weights": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P]),
+    "moe_quantize_rows": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                         _P]),
     "moe_permute_scratch_bytes": (ctypes.c_size_t, [ctypes.POINTER(moe_shape)]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P]),
-    "moe_fwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+    "moe_fwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                ctypes.c_size_t, _P]),
     "moe_bwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                               _P, _P, _P, ctypes.c_size_t, _P]),
+                               _P, _P, ctypes.c_size_t, _P]),
     "moe_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32), _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_set_kernel_timing": (ctypes.c_int, [ctypes.c_int]),
@@ -136,6 +145,22 @@ def moe_get_saved_layout(shape: moe_shape) -> dict:
     return {n: getattr(out, n) for n, _ in moe_saved_layout._fields_}
 
 
+def moe_get_wq_layout(shape: moe_shape) -> dict:
+    out = moe_wq_layout()
+    _check(lib().moe_get_wq_layout(ctypes.byref(shape), ctypes.byref(out)), "moe_get_wq_layout")
+    return {n: getattr(out, n) for n, _ in moe_wq_layout._fields_}
+
+
+def moe_quantize_weights(shape, W13, W2, wq, stream=None) -> None:
+    _check(lib().moe_quantize_weights(ctypes.byref(shape), _ptr(W13), _ptr(W2), _ptr(wq), _stream(stream)),
+           "moe_quantize_weights")
+
+
+def moe_quantize_rows(shape, x, rows, K, codes, scales, stream=None) -> None:
+    _check(lib().moe_quantize_rows(ctypes.byref(shape), _ptr(x), int(rows), int(K), _ptr(codes), _ptr(scales),
+                                   _stream(stream)), "moe_quantize_rows")
+
+
 def moe_permute_scratch_bytes(shape: moe_shape) -> int:
     return int(lib().moe_permute_scratch_bytes(ctypes.byref(shape)))
 
@@ -145,18 +170,17 @@ def moe_permute(shape, topk_idx, counts, offsets, row_of, src_of, scratch, strea
                              _ptr(src_of), _ptr(scratch), _stream(stream)), "moe_permute")
 
 
-def moe_fwd(shape, x, topk_idx, topk_w, W13, W2, W13_scale, W2_scale, y, saved, ws, stream=None) -> None:
+def moe_fwd(shape, x, topk_idx, topk_w, W13, W2, wq, y, saved, ws, stream=None) -> None:
     _check(lib().moe_fwd(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W13), _ptr(W2),
-                         _ptr(W13_scale), _ptr(W2_scale), _ptr(y), _ptr(saved), _ptr(ws),
-                         ws.numel() * ws.element_size(), _stream(stream)), "moe_fwd")
+                         _ptr(wq), _ptr(y), _ptr(saved), _ptr(ws), ws.numel() * ws.element_size(),
+                         _stream(stream)), "moe_fwd")
 
 
-def moe_bwd(shape, dy, x, topk_idx, topk_w, W13, W2, W13_scale, W2_scale, saved, dx, d_topk_w, dW13, dW2,
-            ws, stream=None) -> None:
+def moe_bwd(shape, dy, x, topk_idx, topk_w, W13, W2, wq, saved, dx, d_topk_w, dW13, dW2, ws,
+            stream=None) -> None:
     _check(lib().moe_bwd(ctypes.byref(shape), _ptr(dy), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W13),
-                         _ptr(W2), _ptr(W13_scale), _ptr(W2_scale), _ptr(saved), _ptr(dx), _ptr(d_topk_w),
-                         _ptr(dW13), _ptr(dW2), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "moe_bwd")
+                         _ptr(W2), _ptr(wq), _ptr(saved), _ptr(dx), _ptr(d_topk_w), _ptr(dW13), _ptr(dW2),
+                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_bwd")
 
 
 def moe_read_status(ws, stream=None) -> int:
@@ -180,18 +204,23 @@ def moe_kernel_timing_collect(max_entries: int = 64) -> dict:
 
 @dataclasses.dataclass
 class LayerBuffers:
-    """Device buffers of one layer shape (allocated once with torch)."""
+    """Device buffers of one layer shape (allocated once with torch). `wq`
+    holds the quantized weights of the FP8 precisions (None for bf16)."""
     shape: moe_shape
     fwd_ws: torch.Tensor
     saved: torch.Tensor
     bwd_ws: torch.Tensor
     layout: dict
+    wq: torch.Tensor | None = None
+    wq_layout: dict | None = None
 
     @classmethod
     def allocate(cls, shape: moe_shape, device="cuda") -> "LayerBuffers":
         f, s, b = moe_workspace_size(shape)
         mk = lambda n: torch.empty(max(n, 256), dtype=torch.uint8, device=device)  # noqa: E731
-        return cls(shape, mk(f), mk(s), mk(b), moe_get_saved_layout(shape))
+        wl = moe_get_wq_layout(shape)
+        wq = mk(wl["total"]) if wl["total"] > 0 else None
+        return cls(shape, mk(f), mk(s), mk(b), moe_get_saved_layout(shape), wq, wl)
 
     def saved_view(self, name: str, dtype, count: int) -> torch.Tensor:
         off = self.layout[name]
@@ -199,12 +228,18 @@ class LayerBuffers:
         return self.saved[off:off + count * esz].view(dtype)
 
 
+def quantize_weights(buf: LayerBuffers, W13, W2, stream=None) -> None:
+    """Refreshes buf.wq from the bf16 weights (no-op for bf16)."""
+    if buf.wq is not None:
+        moe_quantize_weights(buf.shape, W13, W2, buf.wq, stream)
+
+
 def forward(buf: LayerBuffers, x, topk_idx, topk_w, W13, W2, y=None, training=True, stream=None):
+    """Forward; for FP8 precisions buf.wq must hold quantize_weights of W13, W2."""
     s = buf.shape
     if y is None:
         y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=x.device)
-    moe_fwd(s, x, topk_idx, topk_w, W13, W2, None, None, y, buf.saved if training else None, buf.fwd_ws,
-            stream)
+    moe_fwd(s, x, topk_idx, topk_w, W13, W2, buf.wq, y, buf.saved if training else None, buf.fwd_ws, stream)
     return y
 
 
@@ -217,5 +252,5 @@ def backward(buf: LayerBuffers, dy, x, topk_idx, topk_w, W13, W2, grads=None, st
                  torch.empty((s.E, 2 * s.I, s.H), dtype=torch.bfloat16, device=dev),
                  torch.empty((s.E, s.H, s.I), dtype=torch.bfloat16, device=dev))
     dx, dw, dW13, dW2 = grads
-    moe_bwd(s, dy, x, topk_idx, topk_w, W13, W2, None, None, buf.saved, dx, dw, dW13, dW2, buf.bwd_ws, stream)
+    moe_bwd(s, dy, x, topk_idx, topk_w, W13, W2, buf.wq, buf.saved, dx, dw, dW13, dW2, buf.bwd_ws, stream)
     return grads

@@ -37,6 +37,8 @@
 //   * Persistent grid: each workgroup walks tiles blockIdx, +grid, ...; tile
 //     ids are remapped so that the eight XCDs each take a contiguous range
 //     (tiles of one expert share its weight panel in that XCD's L2).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -63,6 +65,12 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // ------------------------------------------------------------------ loaders
+
+// Raw buffer resource over [base, base + bytes) (bytes < 2^32; dword 3 as
+// gfx9 parts expect for untyped loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(uint32_t(bytes)), 0x00020000);
+}
 
 // Register stage of one operand's k-slab plus a zero-fill mask (bit i set:
 // chunk i is real data).
@@ -253,6 +261,131 @@ __device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, 
   }
 }
 
+// ------------------------------------------------------------------ FP8 core
+// FP8 (E4M3) operands use the k-major LDS layout with bytes in place of bf16
+// elements: a k-slab is 128 codes = 128 bytes per row, the bytes of a bf16
+// slab, so the same 16-byte loads move it. The row's 4 scale bytes of the
+// slab (one per 32 codes) go into the row's LDS padding, at byte 128.
+//
+// Each 64-deep step is one v_mfma_scale_f32_32x32x64_f8f6f4 per sub-tile
+// pair. Operand layout (measured on gfx950): a lane of half h = lane / 32
+// holds row lane % 32 with k = 16h .. 16h+15 in its registers 0-3 and
+// k = 32+16h .. 32+16h+15 in registers 4-7, while its scale operand is the
+// scale of k-block h (k = 32h .. 32h+31) of that row. The registers are
+// filled so that register order is memory order; the lane then passes the
+// scale byte of memory block h of the step.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct Stage8 {
+  u32x4 r[kPer];
+  uint32_t s;  // the slab's 4 scale bytes of row t/8 + 64 * (t % 4)
+};
+
+// k-major E4M3 operand with scales [rows, K/32]. Loads go through buffer
+// resources (base and extent in scalar registers, a 32-bit byte offset per
+// row in a vector register): an address past the extent reads zero instead
+// of faulting, and no 64-bit per-row pointers occupy vector registers.
+// Offsets are set in 16-bit units like KMajorLoader's (K/2 units per row);
+// the scale row of a code row at byte offset o is at byte o/32 of the scales.
+// Of the 8 threads that share 4 rows, thread t also moves the scales of row
+// t/8 + 64 * (t % 4) (threads t and t+4 duplicate each other, which keeps
+// every load and LDS write unconditional).
+struct KMajorLoader8 {
+  __amdgpu_buffer_rsrc_t data, scale;
+  uint32_t off[kPer];  // byte offset of this thread's 16 bytes of row i in slab 0
+  uint32_t soff;       // byte offset of the scale row this thread moves
+
+  __device__ __forceinline__ static int row_of_thread(int i) { return KMajorLoader::row_of_thread(i); }
+  // base: codes of row 0 (as 16-bit units), units: extent in 16-bit units;
+  // sbase / sbytes: the matching scale bytes
+  __device__ __forceinline__ void set_base(const uint16_t* base, int64_t units, const uint8_t* sbase,
+                                           int64_t sbytes) {
+    data = make_rsrc(base, units * 2);
+    scale = make_rsrc(sbase, sbytes);
+  }
+  __device__ __forceinline__ void set_row(int i, int64_t row_off) {
+    off[i] = uint32_t(row_off * 2) + (threadIdx.x & 7) * 16;
+    if (int(threadIdx.x & 3) == i) soff = uint32_t(row_off * 2) >> 5;
+  }
+  __device__ __forceinline__ void fetch(int kt, Stage8& st) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) st.r[i] = __builtin_amdgcn_raw_buffer_load_b128(data, off[i], kt * 2 * BK, 0);
+    st.s = __builtin_amdgcn_raw_buffer_load_b32(scale, soff, kt * 4, 0);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, const Stage8& st) const {
+    const int r0 = threadIdx.x >> 3, c = threadIdx.x & 7;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4*>(lds + (r0 + 64 * i) * LDK + c * 8) = st.r[i];
+    *reinterpret_cast<uint32_t*>(lds + (r0 + 64 * (c & 3)) * LDK + BK) = st.s;
+  }
+};
+
+template <bool FP8>
+using KLoader = typename std::conditional<FP8, KMajorLoader8, KMajorLoader>::type;
+
+__device__ __forceinline__ i32x8 frag8(const uint16_t* lds, int ent0, int s) {
+  const int lane = lane_id();
+  const uint16_t* p = lds + (ent0 + (lane & 31)) * LDK + s * 32 + (lane >> 5) * 8;
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);       // codes 16h .. 16h+15 of the step
+  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);  // codes 32+16h .. 32+16h+15
+  return i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(b[0]), int(b[1]), int(b[2]), int(b[3])};
+}
+
+// scale byte of k-block 2s + lane/32 (codes 64s + 32h .. +31) of this lane's row
+__device__ __forceinline__ int scale8(const uint16_t* lds, int ent0, int s) {
+  const int lane = lane_id();
+  return reinterpret_cast<const uint8_t*>(lds + (ent0 + (lane & 31)) * LDK + BK)[2 * s + (lane >> 5)];
+}
+
+__device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
+  const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    i32x8 qf[TN];
+    int qs[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      qf[j] = frag8(ldsQ, qn0 + 32 * j, s);
+      qs[j] = scale8(ldsQ, qn0 + 32 * j, s);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const i32x8 pf = frag8(ldsP, pm0 + 32 * i, s);
+      const int ps = scale8(ldsP, pm0 + 32 * i, s);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[j], pf, acc.c[i][j], 0, 0, 0, qs[j], 0, ps);
+    }
+  }
+}
+
+__device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, uint16_t* lds,
+                                             Acc& acc) {
+  if (nk <= 0) return;
+  Stage8 sp, sq;
+  lp.fetch(0, sp);
+  lq.fetch(0, sq);
+  lp.store(lds, sp);
+  lq.store(lds + kOperandLds, sq);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    uint16_t* cur = lds + (kt & 1) * kStageLds;
+    uint16_t* nxt = lds + ((kt + 1) & 1) * kStageLds;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      lp.fetch(kt + 1, sp);
+      lq.fetch(kt + 1, sq);
+    }
+    mma_slab_fp8(cur, cur + kOperandLds, acc);
+    // unconditional (after the last slab it rewrites stale data into the idle
+    // buffer): a conditional block here lets the compiler sink the MFMAs
+    // below it, with every fragment of the slab live at once
+    lp.store(nxt, sp);
+    lq.store(nxt + kOperandLds, sq);
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ LDS-staged epilogue
 // After the k loop the operand buffers are free. The accumulators of the
 // waves of one column half (wave_n() in {2h, 2h+1}) are written there as fp32
@@ -364,8 +497,10 @@ __device__ __forceinline__ RowTile decode_row_tile(int64_t t, int NT, const int3
   RowTile r;
   r.nt = int(t % NT);
   const int32_t gm = int32_t(t / NT);
-  r.e = find_expert(s_pref, E, gm);
-  const int mt = gm - s_pref[r.e];
+  // the search reads LDS into vector registers; the result is the same in
+  // every lane, and saying so keeps the tile's bases in scalar registers
+  r.e = __builtin_amdgcn_readfirstlane(find_expert(s_pref, E, gm));
+  const int mt = __builtin_amdgcn_readfirstlane(gm - s_pref[r.e]);
   r.row0 = int64_t(offsets[r.e]) + int64_t(mt) * BM;
   r.rows = min(BM, counts[r.e] - mt * BM);
   return r;
@@ -401,8 +536,20 @@ __device__ __forceinline__ int w13_row(int q, int nt, int I) {
 }
 }  // namespace g1
 
-__global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ W13,
+// An operand in memory: bf16 elements (scales == nullptr) or E4M3 codes with
+// per-(row, 32-block) E8M0 scales.
+struct Operand {
+  const void* data;
+  const uint8_t* scales;
+};
+
+// Row length in 16-bit units (a bf16 element, or two E4M3 codes): the k loop
+// runs over slabs of 64 such units in both cases.
+template <bool FP8>
+__device__ __forceinline__ int row_units(int K) { return FP8 ? K / 2 : K; }
+
+template <bool FP8>
+__global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, Operand X, Operand W,
                                                                 uint16_t* __restrict__ h13,
                                                                 uint16_t* __restrict__ act) {
   MOE_GEMM_SMEM
@@ -410,24 +557,35 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, c
   const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
   MOE_ROW_SCHED
   const int NT = (2 * I) / BN;
+  const int KU = row_units<FP8>(H);
   const int64_t total = int64_t(s_pref[E]) * NT;
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
-    KMajorLoader lp, lq;
-    lp.base = x;
-    lq.base = W13 + int64_t(rt.e) * 2 * I * H;
+    KLoader<FP8> lp, lq;
+    if constexpr (FP8) {
+      lp.set_base(static_cast<const uint16_t*>(X.data), p.T * KU, X.scales, p.T * (H / 32));
+      lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * KU, 2 * I * KU,
+                  W.scales + int64_t(rt.e) * 2 * I * (H / 32), 2 * I * (H / 32));
+    } else {
+      lp.base = static_cast<const uint16_t*>(X.data);
+      lq.base = static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * KU;
+    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
       const int mc = m < rt.rows ? m : rt.rows - 1;  // past-the-end rows reuse a real row
-      lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * H);
-      lq.set_row(i, int64_t(g1::w13_row(m, rt.nt, I)) * H);
+      lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * KU);
+      lq.set_row(i, int64_t(g1::w13_row(m, rt.nt, I)) * KU);
     }
     // routing weight of tile row t: loaded now, used after the k loop
     const float w_row = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
     Acc acc;
     acc.zero();
-    mainloop<false, false>(lp, lq, H / BK, lds, acc);
+    if constexpr (FP8) {
+      mainloop_fp8(lp, lq, KU / 64, lds, acc);
+    } else {
+      mainloop<false, false>(lp, lq, KU / 64, lds, acc);
+    }
     if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds g and u of intermediate indices nt*128 + h*64 + [0, 64):
     // staged column (i/32)*64 + i%32 is g, +32 is u.
@@ -459,28 +617,41 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, c
 
 // ================================================================== forward GEMM2
 // O[r][h] = (w a)[r] . W2[e][h],  K = I.
-__global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, const uint16_t* __restrict__ act,
-                                                         const uint16_t* __restrict__ W2,
+template <bool FP8>
+__global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand A, Operand W,
                                                          uint16_t* __restrict__ out) {
   MOE_GEMM_SMEM
   const int E = int(p.E), H = int(p.H), I = int(p.I);
   MOE_ROW_SCHED
   const int NT = H / BN;
+  const int KU = row_units<FP8>(I);
   const int64_t total = int64_t(s_pref[E]) * NT;
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
-    KMajorLoader lp, lq;
-    lp.base = act + rt.row0 * I;
-    lq.base = W2 + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * I;
+    KLoader<FP8> lp, lq;
+    if constexpr (FP8) {
+      lp.set_base(static_cast<const uint16_t*>(A.data) + rt.row0 * KU, int64_t(rt.rows) * KU,
+                  A.scales + rt.row0 * (I / 32), int64_t(rt.rows) * (I / 32));
+      lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * KU,
+                  int64_t(BN) * KU, W.scales + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * (I / 32),
+                  int64_t(BN) * (I / 32));
+    } else {
+      lp.base = static_cast<const uint16_t*>(A.data) + rt.row0 * KU;
+      lq.base = static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * KU;
+    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
-      lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * I);
-      lq.set_row(i, int64_t(m) * I);
+      lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * KU);
+      lq.set_row(i, int64_t(m) * KU);
     }
     Acc acc;
     acc.zero();
-    mainloop<false, false>(lp, lq, I / BK, lds, acc);
+    if constexpr (FP8) {
+      mainloop_fp8(lp, lq, KU / 64, lds, acc);
+    } else {
+      mainloop<false, false>(lp, lq, KU / 64, lds, acc);
+    }
     store_tile(acc, lds, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
   }
 }
@@ -515,8 +686,9 @@ struct TokenRows {  // k-th row of an expert segment -> its token's row
 // dwpart[r][2*nt + h] holds the partial sum of dA_u * a over column half h.
 int dh_num_parts(int64_t I) { return int((I + BN - 1) / BN) * 2; }
 
-__global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const uint16_t* __restrict__ dy,
-                                                           const uint16_t* __restrict__ W2,
+// In the FP8 variant W2 arrives transposed, [E, I, H] (k-major rows i).
+template <bool FP8>
+__global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operand DY, Operand W,
                                                            const uint16_t* __restrict__ h13,
                                                            uint16_t* __restrict__ dh13,
                                                            float* __restrict__ dwpart) {
@@ -529,25 +701,42 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const 
   const int64_t total = int64_t(s_pref[E]) * NT;
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
-    KMajorLoader lp;
-    lp.base = dy;
+    const int KU = row_units<FP8>(H);
+    KLoader<FP8> lp;
+    if constexpr (FP8)
+      lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU, DY.scales, p.T * (H / 32));
+    else
+      lp.base = static_cast<const uint16_t*>(DY.data);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
       const int mc = m < rt.rows ? m : rt.rows - 1;
-      lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * H);
+      lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * KU);
     }
-    MNMajorLoader<DirectRows> lq;
-    lq.fn.base = W2 + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN;
-    lq.fn.ld = I;
-    lq.fn.nrows = H;
     const int ncols = min(BN, I - rt.nt * BN);
-    lq.nchunks = ncols / 8;
-    lq.prime(0);
     const float w_row = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
     Acc acc;
     acc.zero();
-    mainloop<false, true>(lp, lq, H / BK, lds, acc);
+    if constexpr (FP8) {
+      // rows i of W2^T past the (partial) last n-tile reuse row I-1; their
+      // columns are never stored
+      KMajorLoader8 lq;
+      lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * I + int64_t(rt.nt) * BN) * KU,
+                  int64_t(ncols) * KU, W.scales + (int64_t(rt.e) * I + int64_t(rt.nt) * BN) * (H / 32),
+                  int64_t(ncols) * (H / 32));
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        lq.set_row(i, int64_t(min(KMajorLoader::row_of_thread(i), ncols - 1)) * KU);
+      mainloop_fp8(lp, lq, KU / 64, lds, acc);
+    } else {
+      MNMajorLoader<DirectRows> lq;
+      lq.fn.base = static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN;
+      lq.fn.ld = I;
+      lq.fn.nrows = H;
+      lq.nchunks = ncols / 8;
+      lq.prime(0);
+      mainloop<false, true>(lp, lq, KU / 64, lds, acc);
+    }
     if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
     // Thread t works on 8 of them (c) for tile rows t/16 + 32*j, j < 8, in
@@ -617,31 +806,47 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, const 
 
 // ================================================================== backward dX
 // dXr[r][h] = [dg | du][r] . W13[e][:, h]  (K = 2I; W13 read mn-major).
-__global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, const uint16_t* __restrict__ dh13,
-                                                           const uint16_t* __restrict__ W13,
+// In the FP8 variant W13 arrives transposed, [E, H, 2I] (k-major rows h).
+template <bool FP8>
+__global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operand DH, Operand W,
                                                            uint16_t* __restrict__ out) {
   MOE_GEMM_SMEM
   const int E = int(p.E), H = int(p.H), I = int(p.I);
   MOE_ROW_SCHED
   const int NT = H / BN;
+  const int KU = row_units<FP8>(2 * I);
   const int64_t total = int64_t(s_pref[E]) * NT;
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
-    KMajorLoader lp;
-    lp.base = dh13 + rt.row0 * 2 * I;
+    KLoader<FP8> lp;
+    if constexpr (FP8)
+      lp.set_base(static_cast<const uint16_t*>(DH.data) + rt.row0 * KU, int64_t(rt.rows) * KU,
+                  DH.scales + rt.row0 * (2 * I / 32), int64_t(rt.rows) * (2 * I / 32));
+    else
+      lp.base = static_cast<const uint16_t*>(DH.data) + rt.row0 * KU;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
-      lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * 2 * I);
+      lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * KU);
     }
-    MNMajorLoader<DirectRows> lq;
-    lq.fn.base = W13 + int64_t(rt.e) * 2 * I * H + int64_t(rt.nt) * BN;
-    lq.fn.ld = H;
-    lq.fn.nrows = 2 * I;
-    lq.prime(0);
     Acc acc;
     acc.zero();
-    mainloop<false, true>(lp, lq, (2 * I) / BK, lds, acc);
+    if constexpr (FP8) {
+      KMajorLoader8 lq;
+      lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * KU,
+                  int64_t(BN) * KU, W.scales + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * (2 * I / 32),
+                  int64_t(BN) * (2 * I / 32));
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) lq.set_row(i, int64_t(KMajorLoader::row_of_thread(i)) * KU);
+      mainloop_fp8(lp, lq, KU / 64, lds, acc);
+    } else {
+      MNMajorLoader<DirectRows> lq;
+      lq.fn.base = static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * H + int64_t(rt.nt) * BN;
+      lq.fn.ld = H;
+      lq.fn.nrows = 2 * I;
+      lq.prime(0);
+      mainloop<false, true>(lp, lq, KU / 64, lds, acc);
+    }
     store_tile(acc, lds, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
   }
 }
@@ -732,36 +937,59 @@ static int grid_for(int64_t tiles, int num_cus) {
 
 static int64_t row_tiles_upper(const GemmProblem& p) { return (p.T * p.k + BM - 1) / BM + p.E; }
 
-hipError_t launch_gemm1_swiglu(const GemmProblem& p, const uint16_t* x, const uint16_t* W13,
-                               uint16_t* h13, uint16_t* act, hipStream_t st, KernelTimer* timer) {
+hipError_t launch_gemm1_swiglu(const GemmProblem& p, GemmOperand x, GemmOperand W13, uint16_t* h13,
+                               uint16_t* act, hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(row_tiles_upper(p) * (2 * p.I / BN), p.num_cus);
-  TimedLaunch tl(timer, "gemm1_swiglu", st);
-  hipLaunchKernelGGL(gemm1_swiglu_kernel, dim3(grid), dim3(kThreads), 0, st, p, x, W13, h13, act);
+  const Operand X{x.data, x.scales}, W{W13.data, W13.scales};
+  if (x.scales) {
+    TimedLaunch tl(timer, "gemm1_swiglu_fp8", st);
+    hipLaunchKernelGGL(gemm1_swiglu_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, X, W, h13, act);
+  } else {
+    TimedLaunch tl(timer, "gemm1_swiglu", st);
+    hipLaunchKernelGGL(gemm1_swiglu_kernel<false>, dim3(grid), dim3(kThreads), 0, st, p, X, W, h13, act);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm2(const GemmProblem& p, const uint16_t* act, const uint16_t* W2, uint16_t* out_rows,
+hipError_t launch_gemm2(const GemmProblem& p, GemmOperand act, GemmOperand W2, uint16_t* out_rows,
                         hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(row_tiles_upper(p) * (p.H / BN), p.num_cus);
-  TimedLaunch tl(timer, "gemm2", st);
-  hipLaunchKernelGGL(gemm2_kernel, dim3(grid), dim3(kThreads), 0, st, p, act, W2, out_rows);
+  const Operand A{act.data, act.scales}, W{W2.data, W2.scales};
+  if (act.scales) {
+    TimedLaunch tl(timer, "gemm2_fp8", st);
+    hipLaunchKernelGGL(gemm2_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, A, W, out_rows);
+  } else {
+    TimedLaunch tl(timer, "gemm2", st);
+    hipLaunchKernelGGL(gemm2_kernel<false>, dim3(grid), dim3(kThreads), 0, st, p, A, W, out_rows);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_dh(const GemmProblem& p, const uint16_t* dy, const uint16_t* W2,
-                          const uint16_t* h13, uint16_t* dh13, float* dwpart, hipStream_t st,
-                          KernelTimer* timer) {
+hipError_t launch_gemm_dh(const GemmProblem& p, GemmOperand dy, GemmOperand W2, const uint16_t* h13,
+                          uint16_t* dh13, float* dwpart, hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(row_tiles_upper(p) * ((p.I + BN - 1) / BN), p.num_cus);
-  TimedLaunch tl(timer, "gemm_dh_dswiglu", st);
-  hipLaunchKernelGGL(gemm_dh_kernel, dim3(grid), dim3(kThreads), 0, st, p, dy, W2, h13, dh13, dwpart);
+  const Operand D{dy.data, dy.scales}, W{W2.data, W2.scales};
+  if (dy.scales) {
+    TimedLaunch tl(timer, "gemm_dh_dswiglu_fp8", st);
+    hipLaunchKernelGGL(gemm_dh_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, D, W, h13, dh13, dwpart);
+  } else {
+    TimedLaunch tl(timer, "gemm_dh_dswiglu", st);
+    hipLaunchKernelGGL(gemm_dh_kernel<false>, dim3(grid), dim3(kThreads), 0, st, p, D, W, h13, dh13, dwpart);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_dx(const GemmProblem& p, const uint16_t* dh13, const uint16_t* W13,
-                          uint16_t* dx_rows, hipStream_t st, KernelTimer* timer) {
+hipError_t launch_gemm_dx(const GemmProblem& p, GemmOperand dh13, GemmOperand W13, uint16_t* dx_rows,
+                          hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(row_tiles_upper(p) * (p.H / BN), p.num_cus);
-  TimedLaunch tl(timer, "gemm_dx", st);
-  hipLaunchKernelGGL(gemm_dx_kernel, dim3(grid), dim3(kThreads), 0, st, p, dh13, W13, dx_rows);
+  const Operand D{dh13.data, dh13.scales}, W{W13.data, W13.scales};
+  if (dh13.scales) {
+    TimedLaunch tl(timer, "gemm_dx_fp8", st);
+    hipLaunchKernelGGL(gemm_dx_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, D, W, dx_rows);
+  } else {
+    TimedLaunch tl(timer, "gemm_dx", st);
+    hipLaunchKernelGGL(gemm_dx_kernel<false>, dim3(grid), dim3(kThreads), 0, st, p, D, W, dx_rows);
+  }
   return hipGetLastError();
 }
 

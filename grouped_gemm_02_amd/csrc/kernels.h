@@ -53,21 +53,37 @@ struct GemmProblem {
   const float* wrow;  // routing weight of each permuted row
 };
 
+// A GEMM operand: bf16 elements (scales == nullptr) or E4M3 codes with
+// E8M0 scales per (row, 32-block along the reduction axis).
+struct GemmOperand {
+  const void* data;
+  const uint8_t* scales;
+};
 // forward
-hipError_t launch_gemm1_swiglu(const GemmProblem& p, const uint16_t* x, const uint16_t* W13,
-                               uint16_t* h13, uint16_t* act, hipStream_t st, KernelTimer* timer);
-hipError_t launch_gemm2(const GemmProblem& p, const uint16_t* act, const uint16_t* W2, uint16_t* out_rows,
+hipError_t launch_gemm1_swiglu(const GemmProblem& p, GemmOperand x, GemmOperand W13, uint16_t* h13,
+                               uint16_t* act, hipStream_t st, KernelTimer* timer);
+hipError_t launch_gemm2(const GemmProblem& p, GemmOperand act, GemmOperand W2, uint16_t* out_rows,
                         hipStream_t st, KernelTimer* timer);
-// backward
+// backward (FP8: W2 as [E, I, H] and W13 as [E, H, 2I], i.e. transposed)
 int dh_num_parts(int64_t I);
-hipError_t launch_gemm_dh(const GemmProblem& p, const uint16_t* dy, const uint16_t* W2,
-                          const uint16_t* h13, uint16_t* dh13, float* dwpart, hipStream_t st,
-                          KernelTimer* timer);
-hipError_t launch_gemm_dx(const GemmProblem& p, const uint16_t* dh13, const uint16_t* W13,
-                          uint16_t* dx_rows, hipStream_t st, KernelTimer* timer);
+hipError_t launch_gemm_dh(const GemmProblem& p, GemmOperand dy, GemmOperand W2, const uint16_t* h13,
+                          uint16_t* dh13, float* dwpart, hipStream_t st, KernelTimer* timer);
+hipError_t launch_gemm_dx(const GemmProblem& p, GemmOperand dh13, GemmOperand W13, uint16_t* dx_rows,
+                          hipStream_t st, KernelTimer* timer);
 hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x,
                             uint16_t* dW13, hipStream_t st, KernelTimer* timer);
 hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint16_t* act,
                            uint16_t* dW2, hipStream_t st, KernelTimer* timer);
+
+// ---------------------------------------------------------------- FP8 quantization
+constexpr int kRulePow2 = 0;  // smallest 2^e with 448 * 2^e >= amax
+constexpr int kRuleMx = 1;    // 2^(floor(log2 amax) - 8)
+// bf16 [rows, K] -> E4M3 codes [rows, K] + E8M0 scales [rows, K/32]; block 32 or 128
+hipError_t launch_quant_rows(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                             int block, int rule, hipStream_t st, KernelTimer* timer, const char* name);
+// bf16 W [E, R, C] in 128x128 tiles -> codes [E, R, C] (or [E, C, R] when transpose) with scales
+// per (output row, 32-block); blockwise rule: one exponent per tile, MX rule: per 32 values
+hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* codes, uint8_t* scales,
+                                int transpose, int rule, hipStream_t st, KernelTimer* timer);
 
 }  // namespace moe

@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/moe.h.
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -33,14 +34,48 @@ moe_status check_shape(const moe_shape* s) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool fp8_forward(const moe_shape& s) { return s.precision == MOE_FP8_BLOCK || s.precision == MOE_MXFP8; }
+bool fp8_backward(const moe_shape& s) { return s.precision != MOE_BF16; }
+// activation block (32 or 128 values along the reduction axis) and scale rule
+int act_block(const moe_shape& s) { return s.precision == MOE_MXFP8 ? 32 : 128; }
+int scale_rule(const moe_shape& s) { return s.precision == MOE_MXFP8 ? kRuleMx : kRulePow2; }
+
+// bytes of E4M3 codes [rows, K] and of their scale bytes [rows, K/32]
+size_t codes_bytes(int64_t rows, int64_t K) { return align_up(size_t(rows) * size_t(K)); }
+size_t scale_bytes(int64_t rows, int64_t K) { return align_up(size_t(rows) * size_t(K / 32)); }
+
 // ------------------------------------------------------------ buffer layouts
 
 struct FwdLayout {
   size_t perm;     // permutation scratch (status word first)
   size_t rows;     // bf16 [Tk, H] weighted expert outputs
   size_t inf;      // saved-like area used when no saved buffer is given
+  size_t xq, xs;   // FP8 forward: x codes [T, H], scales [T, H/32]
+  size_t aq, as;   // FP8 forward: w*silu(g)*u codes [Tk, I], scales [Tk, I/32]
   size_t total;
 };
+
+moe_wq_layout wq_layout(const moe_shape& s) {
+  moe_wq_layout L;
+  L.w13 = L.w13_scale = L.w2 = L.w2_scale = SIZE_MAX;
+  L.w2t = L.w2t_scale = L.w13t = L.w13t_scale = SIZE_MAX;
+  size_t o = 0;
+  const int64_t E = s.E, H = s.H, I = s.I;
+  if (fp8_forward(s)) {
+    L.w13 = o;       o += codes_bytes(E * 2 * I, H);
+    L.w13_scale = o; o += scale_bytes(E * 2 * I, H);
+    L.w2 = o;        o += codes_bytes(E * H, I);
+    L.w2_scale = o;  o += scale_bytes(E * H, I);
+  }
+  if (fp8_backward(s)) {
+    L.w2t = o;        o += codes_bytes(E * I, H);
+    L.w2t_scale = o;  o += scale_bytes(E * I, H);
+    L.w13t = o;       o += codes_bytes(E * H, 2 * I);
+    L.w13t_scale = o; o += scale_bytes(E * H, 2 * I);
+  }
+  L.total = o;
+  return L;
+}
 
 moe_saved_layout saved_layout(const moe_shape& s) {
   const int64_t Tk = s.T * s.k;
@@ -64,12 +99,22 @@ FwdLayout fwd_layout(const moe_shape& s) {
   L.perm = o; o = align_up(o + permute_scratch_bytes(Tk, int(s.E)));
   L.rows = o; o = align_up(o + size_t(Tk) * size_t(s.H) * 2);
   L.inf = o;  o = align_up(o + saved_layout(s).total);
+  L.xq = L.xs = L.aq = L.as = 0;
+  if (fp8_forward(s)) {
+    L.xq = o; o += codes_bytes(s.T, s.H);
+    L.xs = o; o += scale_bytes(s.T, s.H);
+    L.aq = o; o += codes_bytes(Tk, s.I);
+    L.as = o; o += scale_bytes(Tk, s.I);
+  }
   L.total = o;
   return L;
 }
 
 struct BwdLayout {
-  size_t dh13, dwpart, dxrows, total;
+  size_t dh13, dwpart, dxrows;
+  size_t dyq, dys;  // FP8 backward: dY codes [T, H], scales [T, H/32]
+  size_t dhq, dhs;  // FP8 backward: [dg | du] codes [Tk, 2I], scales [Tk, 2I/32]
+  size_t total;
 };
 
 BwdLayout bwd_layout(const moe_shape& s) {
@@ -79,6 +124,13 @@ BwdLayout bwd_layout(const moe_shape& s) {
   L.dh13 = o;   o = align_up(o + size_t(Tk) * size_t(2 * s.I) * 2);
   L.dwpart = o; o = align_up(o + size_t(Tk) * size_t(dh_num_parts(s.I)) * 4);
   L.dxrows = o; o = align_up(o + size_t(Tk) * size_t(s.H) * 2);
+  L.dyq = L.dys = L.dhq = L.dhs = 0;
+  if (fp8_backward(s)) {
+    L.dyq = o; o += codes_bytes(s.T, s.H);
+    L.dys = o; o += scale_bytes(s.T, s.H);
+    L.dhq = o; o += codes_bytes(Tk, 2 * s.I);
+    L.dhs = o; o += scale_bytes(Tk, 2 * s.I);
+  }
   L.total = o;
   return L;
 }
@@ -219,17 +271,75 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* cou
                                       scratch, static_cast<hipStream_t>(stream), timer()));
 }
 
-moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
-                   const float* topk_w, const void* W13, const void* W2, const void* W13_scale,
-                   const void* W2_scale, void* y, void* saved, void* ws, size_t ws_bytes,
-                   void* stream) {
+moe_status moe_get_wq_layout(const moe_shape* s, moe_wq_layout* out) {
+  const moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_ERR_NULL;
+  *out = wq_layout(*s);
+  return MOE_OK;
+}
+
+moe_status moe_quantize_weights(const moe_shape* s, const void* W13, const void* W2, void* wq,
+                                void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (s->precision != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (W13_scale || W2_scale) return MOE_ERR_PRECISION;
+  if (s->precision == MOE_BF16) return MOE_OK;
+  if (!W13 || !W2 || !wq) return MOE_ERR_NULL;
+  if (!aligned16(W13) || !aligned16(W2) || !aligned16(wq)) return MOE_ERR_ALIGN;
+  int cus = 0;
+  if ((st = device_info(&cus)) != MOE_OK) return st;
+  const moe_wq_layout L = wq_layout(*s);
+  const uint16_t* w13 = static_cast<const uint16_t*>(W13);
+  const uint16_t* w2 = static_cast<const uint16_t*>(W2);
+  const int H = int(s->H), I = int(s->I), rule = scale_rule(*s);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  KernelTimer* tm = timer();
+  hipError_t e = hipSuccess;
+  if (fp8_forward(*s)) {
+    if ((e = launch_quant_weights(w13, s->E, 2 * I, H, at<uint8_t>(wq, L.w13), at<uint8_t>(wq, L.w13_scale), 0,
+                                  rule, hs, tm)) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    if ((e = launch_quant_weights(w2, s->E, H, I, at<uint8_t>(wq, L.w2), at<uint8_t>(wq, L.w2_scale), 0, rule, hs,
+                                  tm)) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+  }
+  if ((e = launch_quant_weights(w2, s->E, H, I, at<uint8_t>(wq, L.w2t), at<uint8_t>(wq, L.w2t_scale), 1, rule, hs,
+                                tm)) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  e = launch_quant_weights(w13, s->E, 2 * I, H, at<uint8_t>(wq, L.w13t), at<uint8_t>(wq, L.w13t_scale), 1, rule, hs,
+                           tm);
+  return launch_status(e);
+}
+
+moe_status moe_quantize_rows(const moe_shape* s, const void* in, int64_t rows, int64_t K, void* codes,
+                             void* scales, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->precision == MOE_BF16) return MOE_ERR_PRECISION;
+  if (rows < 0 || K < 128 || K > 65536 || K % 128 != 0 || rows * K >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!in || !codes || !scales) return MOE_ERR_NULL;
+  if (!aligned16(in) || !aligned16(codes)) return MOE_ERR_ALIGN;
+  int cus = 0;
+  if ((st = device_info(&cus)) != MOE_OK) return st;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  return launch_status(launch_quant_rows(static_cast<const uint16_t*>(in), rows, int(K), static_cast<uint8_t*>(codes),
+                                         static_cast<uint8_t*>(scales), act_block(*s), scale_rule(*s),
+                                         static_cast<hipStream_t>(stream), timer(), "quant_rows"));
+}
+
+moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                   const float* topk_w, const void* W13, const void* W2, const void* wq,
+                   void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->precision == MOE_BF16 && wq) return MOE_ERR_PRECISION;
+  const bool f8 = fp8_forward(*s);
   const int64_t Tk = s->T * s->k;
-  if (!W13 || !W2 || !ws || (s->T > 0 && (!x || !topk_idx || !topk_w || !y))) return MOE_ERR_NULL;
-  const void* ptrs[] = {x, topk_idx, topk_w, W13, W2, y, saved, ws};
+  if (!W13 || !W2 || !ws || (f8 && !wq) || (s->T > 0 && (!x || !topk_idx || !topk_w || !y)))
+    return MOE_ERR_NULL;
+  const void* ptrs[] = {x, topk_idx, topk_w, W13, W2, y, saved, ws, wq};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_ALIGN;
   const FwdLayout FL = fwd_layout(*s);
@@ -255,29 +365,47 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
                                 at<char>(ws, FL.perm), hs, tm, topk_w, wrow);
   if (e != hipSuccess || s->T == 0) return launch_status(e);
   GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w, wrow};
-  if ((e = launch_gemm1_swiglu(gp, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W13),
-                               h13, act, hs, tm)) != hipSuccess)
-    return MOE_ERR_LAUNCH;
-  if ((e = launch_gemm2(gp, act, static_cast<const uint16_t*>(W2), rows, hs, tm)) != hipSuccess)
-    return MOE_ERR_LAUNCH;
+  GemmOperand gx{x, nullptr}, gw13{W13, nullptr}, ga{act, nullptr}, gw2{W2, nullptr};
+  if (f8) {
+    const moe_wq_layout WL = wq_layout(*s);
+    const int blk = act_block(*s), rule = scale_rule(*s);
+    uint8_t* xq = at<uint8_t>(ws, FL.xq);
+    uint8_t* xs = at<uint8_t>(ws, FL.xs);
+    if ((e = launch_quant_rows(static_cast<const uint16_t*>(x), s->T, int(s->H), xq, xs, blk, rule, hs, tm,
+                               "quant_x")) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    gx = GemmOperand{xq, xs};
+    gw13 = GemmOperand{at<uint8_t>(wq, WL.w13), at<uint8_t>(wq, WL.w13_scale)};
+    gw2 = GemmOperand{at<uint8_t>(wq, WL.w2), at<uint8_t>(wq, WL.w2_scale)};
+  }
+  if ((e = launch_gemm1_swiglu(gp, gx, gw13, h13, act, hs, tm)) != hipSuccess) return MOE_ERR_LAUNCH;
+  if (f8) {
+    uint8_t* aq = at<uint8_t>(ws, FL.aq);
+    uint8_t* as = at<uint8_t>(ws, FL.as);
+    if ((e = launch_quant_rows(act, Tk, int(s->I), aq, as, act_block(*s), scale_rule(*s), hs, tm,
+                               "quant_act")) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    ga = GemmOperand{aq, as};
+  }
+  if ((e = launch_gemm2(gp, ga, gw2, rows, hs, tm)) != hipSuccess) return MOE_ERR_LAUNCH;
   e = launch_combine(rows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(y), nullptr, 0,
                      nullptr, hs, tm, "combine_y");
   return launch_status(e);
 }
 
 moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int32_t* topk_idx,
-                   const float* topk_w, const void* W13, const void* W2, const void* W13_scale,
-                   const void* W2_scale, const void* saved, void* dx, float* d_topk_w,
-                   void* dW13, void* dW2, void* ws, size_t ws_bytes, void* stream) {
+                   const float* topk_w, const void* W13, const void* W2, const void* wq,
+                   const void* saved, void* dx, float* d_topk_w, void* dW13, void* dW2, void* ws,
+                   size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (s->precision != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (W13_scale || W2_scale) return MOE_ERR_PRECISION;
+  if (s->precision == MOE_BF16 && wq) return MOE_ERR_PRECISION;
+  const bool f8 = fp8_backward(*s);
   (void)topk_idx;  // the permutation comes from `saved`
-  if (!W13 || !W2 || !saved || !dW13 || !dW2 || !ws ||
+  if (!W13 || !W2 || !saved || !dW13 || !dW2 || !ws || (f8 && !wq) ||
       (s->T > 0 && (!dy || !x || !topk_w || !dx || !d_topk_w)))
     return MOE_ERR_NULL;
-  const void* ptrs[] = {dy, x, topk_idx, topk_w, W13, W2, saved, dx, d_topk_w, dW13, dW2, ws};
+  const void* ptrs[] = {dy, x, topk_idx, topk_w, W13, W2, saved, dx, d_topk_w, dW13, dW2, ws, wq};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_ALIGN;
   const BwdLayout BL = bwd_layout(*s);
@@ -305,11 +433,28 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
   GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w, wrow};
   hipError_t e = hipSuccess;
   if (s->T > 0) {
-    if ((e = launch_gemm_dh(gp, dy16, static_cast<const uint16_t*>(W2), h13, dh13, dwpart, hs, tm)) !=
-        hipSuccess)
-      return MOE_ERR_LAUNCH;
-    if ((e = launch_gemm_dx(gp, dh13, static_cast<const uint16_t*>(W13), dxrows, hs, tm)) != hipSuccess)
-      return MOE_ERR_LAUNCH;
+    GemmOperand gdy{dy, nullptr}, gw2{W2, nullptr}, gdh{dh13, nullptr}, gw13{W13, nullptr};
+    if (f8) {
+      const moe_wq_layout WL = wq_layout(*s);
+      uint8_t* dyq = at<uint8_t>(ws, BL.dyq);
+      uint8_t* dys = at<uint8_t>(ws, BL.dys);
+      if ((e = launch_quant_rows(dy16, s->T, int(s->H), dyq, dys, act_block(*s), scale_rule(*s), hs, tm,
+                                 "quant_dy")) != hipSuccess)
+        return MOE_ERR_LAUNCH;
+      gdy = GemmOperand{dyq, dys};
+      gw2 = GemmOperand{at<uint8_t>(wq, WL.w2t), at<uint8_t>(wq, WL.w2t_scale)};
+      gw13 = GemmOperand{at<uint8_t>(wq, WL.w13t), at<uint8_t>(wq, WL.w13t_scale)};
+    }
+    if ((e = launch_gemm_dh(gp, gdy, gw2, h13, dh13, dwpart, hs, tm)) != hipSuccess) return MOE_ERR_LAUNCH;
+    if (f8) {
+      uint8_t* dhq = at<uint8_t>(ws, BL.dhq);
+      uint8_t* dhs = at<uint8_t>(ws, BL.dhs);
+      if ((e = launch_quant_rows(dh13, s->T * s->k, int(2 * s->I), dhq, dhs, act_block(*s), scale_rule(*s), hs,
+                                 tm, "quant_dh13")) != hipSuccess)
+        return MOE_ERR_LAUNCH;
+      gdh = GemmOperand{dhq, dhs};
+    }
+    if ((e = launch_gemm_dx(gp, gdh, gw13, dxrows, hs, tm)) != hipSuccess) return MOE_ERR_LAUNCH;
     if ((e = launch_combine(dxrows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(dx), dwpart,
                             dh_num_parts(s->I), d_topk_w, hs, tm, "combine_dx_dw")) != hipSuccess)
       return MOE_ERR_LAUNCH;

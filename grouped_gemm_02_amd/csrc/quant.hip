@@ -1,0 +1,205 @@
+// FP8 (OCP E4M3) quantization with power-of-two block scales.
+//
+// The pages name blockwise FP8 and MXFP8 as the layer's low-precision modes
+// (ic.work analysis, section on hardware constraints; MarkTechPost article,
+// "How do developers use it?"). Here every block has one scale 2^e, stored
+// as the E8M0 byte e + 127, so that the gfx950 scaled MFMA applies it:
+//   * blockwise rule: e = smallest integer with 448 * 2^e >= amax (1x128
+//     activation blocks along the reduction axis, 128x128 weight blocks);
+//   * MX rule: e = floor(log2 amax) - 8 (1x32 blocks along the reduction
+//     axis for every operand);
+//   * an all-zero block gets e = 0.
+// A value v becomes the E4M3 code nearest to v / 2^e (ties to the even code,
+// saturating at +-448; a result of zero is stored as +0).
+//
+// Scales are always stored per (row, 32-wide block along the reduction
+// axis); a 128-wide or 128x128 block writes its byte into every 32-block it
+// covers, so the GEMMs read one layout for both modes.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// E4M3 code of v (round to nearest even, saturate at 448, zero unsigned).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t s = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (!(a < 448.f)) {
+    code = 0x7Eu;                                      // also catches NaN
+  } else if (a < 0.015625f) {                          // below 2^-6: subnormal grid 2^-9
+    code = uint32_t(__builtin_rintf(a * 512.f));       // exact product, ties to even
+  } else {
+    const uint32_t ua = __float_as_uint(a);
+    const uint32_t q = (ua >> 23) & 0xFFu;             // biased fp32 exponent, 121..135
+    const uint32_t keep = (ua >> 20) & 0x7u;
+    const uint32_t rem = ua & 0xFFFFFu;
+    code = ((q - 120u) << 3) | keep;                   // E4M3 exponent bias 7
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) code += 1u;
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return code == 0u ? 0u : (code | s);
+}
+
+// floor(log2 a) for a > 0 (exact, subnormals included)
+__device__ __forceinline__ int floor_log2(float a) {
+  uint32_t u = __float_as_uint(a);
+  int bias = 127;
+  if (((u >> 23) & 0xFFu) == 0u) {  // subnormal: scale up by 2^64 first
+    u = __float_as_uint(a * 18446744073709551616.f);
+    bias += 64;
+  }
+  return int((u >> 23) & 0xFFu) - bias;
+}
+
+// block exponent e (scale 2^e) for block maximum amax >= 0
+__device__ __forceinline__ int block_exponent(float amax, int rule) {
+  if (!(amax > 0.f)) return 0;
+  const int q = floor_log2(amax);
+  if (rule == kRuleMx) return q - 8;
+  // 448 = 1.75 * 2^8: 448 * 2^(q-8) >= amax  <=>  mantissa(amax) <= 1.75
+  uint32_t u = __float_as_uint(amax);
+  if (((u >> 23) & 0xFFu) == 0u) u = __float_as_uint(amax * 18446744073709551616.f);
+  const uint32_t mant = u & 0x7FFFFFu;
+  return q - 8 + (mant > 0x600000u ? 1 : 0);
+}
+
+__device__ __forceinline__ int clamp_exp(int e) { return e < -127 ? -127 : (e > 127 ? 127 : e); }
+
+// v * 2^-e, exact for the exponents that occur (two steps keep every factor
+// a normal float)
+__device__ __forceinline__ float scale_down(float v, int e) {
+  const int h = -e / 2;
+  return v * __builtin_ldexpf(1.f, h) * __builtin_ldexpf(1.f, -e - h);
+}
+
+// ---------------------------------------------------------------- rows
+// in: bf16 [rows, K]; out codes uint8 [rows, K], scales uint8 [rows, K/32].
+// Thread g handles 8 consecutive values; the threads of one block (4 for 32,
+// 16 for 128) share its maximum through lane shuffles.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ in, int64_t rows, int K,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales, int block, int rule) {
+  const int per_row = K / 8;
+  const int64_t total = rows * per_row;
+  const int group = block / 8;  // 4 or 16 lanes, aligned within the wave
+  for (int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; g - threadIdx.x < total;
+       g += int64_t(gridDim.x) * blockDim.x) {
+    const bool live = g < total;
+    const int64_t row = live ? g / per_row : 0;
+    const int c8 = live ? int(g % per_row) : 0;
+    float v[8];
+    float amax = 0.f;
+    if (live) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(in + row * K + c8 * 8);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        v[2 * d] = bf16_lo(raw[d]);
+        v[2 * d + 1] = bf16_hi(raw[d]);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+    }
+    for (int off = 1; off < group; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (!live) continue;
+    const int e = clamp_exp(block_exponent(amax, rule));
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lo |= e4m3_code(scale_down(v[q], e)) << (8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hi |= e4m3_code(scale_down(v[4 + q], e)) << (8 * q);
+    *reinterpret_cast<u32x2*>(codes + row * K + c8 * 8) = u32x2{lo, hi};
+    if ((c8 & 3) == 0) scales[row * (K / 32) + c8 / 4] = uint8_t(e + 127);
+  }
+}
+
+hipError_t launch_quant_rows(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                             int block, int rule, hipStream_t st, KernelTimer* timer, const char* name) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t threads = rows * (K / 8);
+  int64_t grid = (threads + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  TimedLaunch tl(timer, name, st);
+  hipLaunchKernelGGL(quant_rows_kernel, dim3(unsigned(grid)), dim3(256), 0, st, in, rows, K, codes, scales,
+                     block, rule);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- weights
+// One workgroup per 128 x 128 tile (e, rb, cb) of a stack of matrices
+// W [E, R, C] (bf16). Output orientation: transpose = 0 writes codes
+// [E, R, C] with scales [E, R, C/32]; transpose = 1 writes the transposed
+// matrix codes [E, C, R] with scales [E, C, R/32]. Blockwise: one exponent
+// for the whole tile. MX: one exponent per 32 consecutive values of an
+// output row.
+__global__ __launch_bounds__(256) void quant_weight_tiles_kernel(const uint16_t* __restrict__ W, int R, int C,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales, int transpose,
+                                                                 int rule) {
+  __shared__ float tile[128][129];
+  __shared__ float red[256];
+  const int cbn = C / 128, rbn = R / 128;
+  const int cb = blockIdx.x % cbn;
+  const int rb = (blockIdx.x / cbn) % rbn;
+  const int64_t e = blockIdx.x / (int64_t(cbn) * rbn);
+  const uint16_t* src = W + (e * R + int64_t(rb) * 128) * C + int64_t(cb) * 128;
+  // load: thread t reads 8 values of row (t / 16) + 16 i
+  float amax = 0.f;
+  for (int i = 0; i < 8; ++i) {
+    const int r = (threadIdx.x >> 4) + 16 * i, c = (threadIdx.x & 15) * 8;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + int64_t(r) * C + c);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      tile[r][c + 2 * d] = bf16_lo(raw[d]);
+      tile[r][c + 2 * d + 1] = bf16_hi(raw[d]);
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[d])), fabsf(bf16_hi(raw[d]))));
+    }
+  }
+  red[threadIdx.x] = amax;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const float tile_amax = red[0];
+  // output: 128 rows of 128 codes; thread t writes 32-value segments
+  // (out row o = t / 2 (+128 / 2 per pass), segment (t % 2) * 2 + pass)
+  const int orows_total = transpose ? C : R;
+  const int olen = transpose ? R : C;
+  const int64_t orow0 = e * orows_total + (transpose ? int64_t(cb) * 128 : int64_t(rb) * 128);
+  const int ocol0 = transpose ? rb * 128 : cb * 128;
+  for (int seg = threadIdx.x; seg < 128 * 4; seg += 256) {
+    const int o = seg >> 2, part = seg & 3;
+    float v[32];
+    float smax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      v[q] = transpose ? tile[part * 32 + q][o] : tile[o][part * 32 + q];
+      smax = fmaxf(smax, fabsf(v[q]));
+    }
+    const int ex = clamp_exp(block_exponent(rule == kRuleMx ? smax : tile_amax, rule));
+    uint32_t w[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      w[d] = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[d] |= e4m3_code(scale_down(v[4 * d + q], ex)) << (8 * q);
+    }
+    uint8_t* dst = codes + (orow0 + o) * olen + ocol0 + part * 32;
+    *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
+    scales[(orow0 + o) * (olen / 32) + ocol0 / 32 + part] = uint8_t(ex + 127);
+  }
+}
+
+hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* codes, uint8_t* scales,
+                                int transpose, int rule, hipStream_t st, KernelTimer* timer) {
+  const int64_t tiles = E * (R / 128) * (C / 128);
+  if (tiles <= 0) return hipSuccess;
+  TimedLaunch tl(timer, "quant_weights", st);
+  hipLaunchKernelGGL(quant_weight_tiles_kernel, dim3(unsigned(tiles)), dim3(256), 0, st, W, R, C, codes, scales,
+                     transpose, rule);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -69,7 +69,22 @@ typedef enum moe_status {
 
 /* Precision of the expert GEMMs (ic.work analysis, hardware constraints;
  * MarkTechPost article, "How do developers use it?": bf16, mxfp8, fp8 and
- * fp8_bwd = BF16 forward with FP8 backward). */
+ * fp8_bwd = BF16 forward with FP8 backward). The pages fix no number format
+ * or scale rule; this library reads them as follows.
+ *   FP8 values are OCP E4M3 (bias 7, max 448, round to nearest even,
+ *   saturating); every block of values has one power-of-two scale 2^e,
+ *   stored as the byte e + 127.
+ *   MOE_FP8_BLOCK: activations in 1x128 blocks along the GEMM's reduction
+ *     axis, weights in 128x128 tiles; e is the smallest integer with
+ *     448 * 2^e >= the block's largest magnitude.
+ *   MOE_MXFP8: 1x32 blocks along the reduction axis for every operand;
+ *     e = floor(log2(largest magnitude)) - 8.
+ *   An all-zero block has e = 0.
+ * Quantized operands: x, w*silu(g)*u and both weight stacks in the forward;
+ * dY, [dg | du] and the weights (re-blocked for the transposed product
+ * under MXFP8) in the backward. The weight-gradient GEMMs read the bf16
+ * tensors x, dY, w*silu(g)*u and [dg | du]. MOE_FP8_BWD runs the forward of
+ * MOE_BF16 and the backward of MOE_FP8_BLOCK. */
 typedef enum moe_precision {
   MOE_BF16 = 0,
   MOE_FP8_BLOCK = 1,
@@ -111,6 +126,42 @@ typedef struct moe_saved_layout {
 } moe_saved_layout;
 moe_status moe_get_saved_layout(const moe_shape* s, moe_saved_layout* out);
 
+/* Quantized weights (E4M3 codes and scale bytes) for the FP8 precisions,
+ * made by moe_quantize_weights in one caller-owned buffer. Byte offsets:
+ *   w13, w13_scale    forward gate/up: codes [E, 2I, H], scales [E, 2I, H/32]
+ *   w2, w2_scale      forward down:    codes [E, H, I],  scales [E, H, I/32]
+ *   w2t, w2t_scale    backward dH:     W2^T  codes [E, I, H],  scales [E, I, H/32]
+ *   w13t, w13t_scale  backward dX:     W13^T codes [E, H, 2I], scales [E, H, 2I/32]
+ * Scales are stored per (row, 32 consecutive codes); a 128-wide or 128x128
+ * block repeats its byte in every 32-block it covers. Entries a precision
+ * does not use (the forward parts for MOE_FP8_BWD, everything for MOE_BF16)
+ * are SIZE_MAX; total is 0 for MOE_BF16. Pure host function. */
+typedef struct moe_wq_layout {
+  size_t w13, w13_scale, w2, w2_scale;
+  size_t w2t, w2t_scale, w13t, w13t_scale;
+  size_t total;
+} moe_wq_layout;
+moe_status moe_get_wq_layout(const moe_shape* s, moe_wq_layout* out);
+
+/* Fills `wq` (moe_get_wq_layout().total bytes, 16-byte aligned) with the
+ * quantized forms of W13 (bf16 [E, 2I, H]) and W2 (bf16 [E, H, I]) that
+ * s->precision uses. Call again whenever the weights change; moe_fwd and
+ * moe_bwd read `wq` and never the quantization of stale weights. A no-op
+ * returning MOE_OK for MOE_BF16. */
+moe_status moe_quantize_weights(const moe_shape* s, const void* W13, const void* W2, void* wq,
+                                void* stream);
+
+/* Quantizes bf16 rows in [rows, K] to E4M3 codes [rows, K] and scale bytes
+ * [rows, K/32] by the activation rule of s->precision (1x128 blocks for
+ * MOE_FP8_BLOCK and MOE_FP8_BWD, 1x32 blocks for MOE_MXFP8; see
+ * moe_precision). This is the step moe_fwd applies to x and w*silu(g)*u and
+ * moe_bwd to dY and [dg | du]; it is exposed for callers that keep
+ * activations in FP8 and for testing. Requires 0 <= rows, 128 <= K <= 65536,
+ * K % 128 == 0, rows*K < 2^31; `in` and `codes` 16-byte aligned.
+ * MOE_ERR_PRECISION for MOE_BF16. */
+moe_status moe_quantize_rows(const moe_shape* s, const void* in, int64_t rows, int64_t K, void* codes,
+                             void* scales, void* stream);
+
 /* Expert-contiguous permutation of the routed pairs (kongchang.com explainer,
  * grouped-GEMM note: routing index -> token reorder -> grouped GEMM indexed
  * by group offsets). Integer work, deterministic:
@@ -136,7 +187,9 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* cou
  *   topk_w   fp32  [T, k]       routing weight of each pair, used as given
  *   W13      bf16  [E, 2I, H]   rows [0,I) gate (W1), rows [I,2I) up (W3)
  *   W2       bf16  [E, H, I]
- *   W13_scale, W2_scale         must be NULL for MOE_BF16
+ *   wq       quantized weights (moe_quantize_weights of this W13, W2):
+ *            required for MOE_FP8_BLOCK and MOE_MXFP8, ignored for
+ *            MOE_FP8_BWD, must be NULL for MOE_BF16 (else MOE_ERR_PRECISION)
  *   y        bf16  [T, H]       output (written, not accumulated)
  *   saved    moe_workspace_size().saved_bytes, or NULL for inference only;
  *            when given it is what moe_bwd reads
@@ -144,16 +197,18 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* cou
  * Steps: permutation; gate/up grouped GEMM whose epilogue forms
  * w * silu(g) * u (SwiGLU with the routing weight folded in); down grouped
  * GEMM; gather-reduce combine (fp32 sum over ascending j, one bf16
- * rounding). */
+ * rounding). FP8 forwards quantize x before the first GEMM and
+ * w * silu(g) * u before the second. */
 moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
-                   const float* topk_w, const void* W13, const void* W2, const void* W13_scale,
-                   const void* W2_scale, void* y, void* saved, void* ws, size_t ws_bytes,
-                   void* stream);
+                   const float* topk_w, const void* W13, const void* W2, const void* wq,
+                   void* y, void* saved, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of the layer for L = <dY, y> (ic.work analysis, "From 3.11x to
  * 1.32x": the backward produces activation and weight gradients).
  *   dy       bf16 [T, H]
- *   x, topk_idx, topk_w, W13, W2, scales: as passed to moe_fwd
+ *   x, topk_idx, topk_w, W13, W2: as passed to moe_fwd
+ *   wq       quantized weights: required for every FP8 precision, must be
+ *            NULL for MOE_BF16
  *   saved    filled by moe_fwd with the same inputs
  *   dx       bf16 [T, H]        written
  *   d_topk_w fp32 [T, k]        written (0 for dropped pairs)
@@ -163,11 +218,12 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
  * Steps: dH grouped GEMM (K = H) with SwiGLU-backward and routing-weight
  * gradient partials fused in its epilogue; dX grouped GEMM (K = 2I);
  * gather-reduce of dx and d_topk_w; per-expert dW13 and dW2 GEMMs whose
- * reduction dimension is that expert's row count. */
+ * reduction dimension is that expert's row count. FP8 backwards quantize dY
+ * before the dH GEMM and [dg | du] before the dX GEMM. */
 moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int32_t* topk_idx,
-                   const float* topk_w, const void* W13, const void* W2, const void* W13_scale,
-                   const void* W2_scale, const void* saved, void* dx, float* d_topk_w,
-                   void* dW13, void* dW2, void* ws, size_t ws_bytes, void* stream);
+                   const float* topk_w, const void* W13, const void* W2, const void* wq,
+                   const void* saved, void* dx, float* d_topk_w, void* dW13, void* dW2, void* ws,
+                   size_t ws_bytes, void* stream);
 
 /* Copies the routing status word that moe_fwd left in `fwd_ws` (or that
  * moe_permute left in its scratch) to *out (MOE_OK or MOE_ERR_ROUTING).

@@ -22,6 +22,9 @@ tensors are quantized. The readings used here (listed in the design doc):
     included; e = floor(log2 amax) - 8 (the OCP MX rule; values up to just
     under 2 * 2^(e+8) saturate at 448).
   - an all-zero block gets e = 0.
+  - e is clamped to [-127, 127], the exponents an E8M0 byte can hold (the
+    byte 255 is NaN); only blocks with amax below about 2^-119 reach the
+    lower clamp, and there the larger scale leaves every value in range.
 * Quantization points: forward x (along H) and the weighted activation
   w * silu(g) * u (along I), gate/up and down weights; backward dY (along H)
   and [dg | du] (along 2I), and the weights again for the transposed use
@@ -101,7 +104,7 @@ def scale_exponent(amax, rule: str) -> np.ndarray:
         out[nz] = (ex - 1) - 8                # floor(log2 amax) - emax(E4M3)
     else:
         raise ValueError(rule)
-    return out
+    return np.clip(out, -127, 127)
 
 
 def quantize_along_last(v, block: int, rule: str):
@@ -149,24 +152,47 @@ def _weight(w, mode, reduce_axis_last: bool):
 
 # --------------------------------------------------------------- layer
 
-def forward(x, topk_idx, topk_w, W13, W2, mode: str, return_pairs: bool = False):
+_WEIGHT_USES = {
+    "W13q": ("W13", True),    # forward gate/up product reduces over H (W13's columns)
+    "W2q": ("W2", True),      # forward down product reduces over I (W2's columns)
+    "W2b": ("W2", False),     # dH product reduces over H = W2's rows
+    "W13b": ("W13", False),   # dX product reduces over 2I = W13's rows
+}
+
+
+def quantize_weights(W13, W2, mode: str, keys=("W13q", "W2q", "W2b", "W13b")) -> dict:
+    """Dequantized weight stacks for the uses in `keys`. Every block lies
+    inside one expert, so the result for a stack equals the stack of the
+    per-expert results."""
+    src = {"W13": base.as_f64(W13), "W2": base.as_f64(W2)}
+    return {k: _weight(src[_WEIGHT_USES[k][0]], mode, _WEIGHT_USES[k][1]) for k in keys}
+
+
+def _need(wq, W13, W2, mode, keys):
+    wq = dict(wq or {})
+    missing = [k for k in keys if k not in wq]
+    if missing:
+        wq.update(quantize_weights(W13, W2, mode, missing))
+    return wq
+
+
+def forward(x, topk_idx, topk_w, W13, W2, mode: str, return_pairs: bool = False, wq: dict | None = None):
     """Forward with the quantization points of `mode` ("fp8_bwd" runs the
-    forward in full precision)."""
+    forward in full precision). `wq` may carry quantize_weights() results
+    for these W13, W2."""
     if mode == "fp8_bwd":
         return base.forward(x, topk_idx, topk_w, W13, W2, return_pairs=return_pairs)
     x = base.as_f64(x)
-    W13 = base.as_f64(W13)
-    W2 = base.as_f64(W2)
     w = base.as_f64(topk_w)
     idx = base.as_i64(topk_idx)
     T, H = x.shape
-    E, I2, _ = W13.shape
+    wq = _need(wq, W13, W2, mode, ("W13q", "W2q"))
+    W13q, W2q = wq["W13q"], wq["W2q"]
+    E, I2, _ = W13q.shape
     I = I2 // 2
     k = idx.shape[1]
     wf = w.reshape(-1)
     xq = _act(x, mode)
-    W13q = _weight(W13, mode, True)
-    W2q = _weight(W2, mode, True)
     y = np.zeros((T, H))
     pairs = {"g": np.zeros((T * k, I)), "u": np.zeros((T * k, I)), "wa": np.zeros((T * k, I))} \
         if return_pairs else None
@@ -190,7 +216,7 @@ def forward(x, topk_idx, topk_w, W13, W2, mode: str, return_pairs: bool = False)
     return y
 
 
-def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str):
+def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str, wq: dict | None = None):
     """Gradients of L = <dY, y> with the backward quantization points of
     `mode`: dY and W2 quantized for the dH product, [dg | du] and W13 for the
     dX product; the weight gradients use unquantized operands. g and u come
@@ -207,12 +233,13 @@ def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str):
     k = idx.shape[1]
     wf = w.reshape(-1)
     if mode == "fp8_bwd":
+        wq = _need(wq, W13, W2, mode, ("W2b", "W13b"))
         xf, W13f = x, W13
     else:
-        xf, W13f = _act(x, mode), _weight(W13, mode, True)
+        wq = _need(wq, W13, W2, mode, ("W13q", "W2b", "W13b"))
+        xf, W13f = _act(x, mode), wq["W13q"]
     dyq = _act(dy, mode)
-    W2b = _weight(W2, mode, False)      # dH product reduces over H = W2's rows
-    W13b = _weight(W13, mode, False)    # dX product reduces over 2I = W13's rows
+    W2b, W13b = wq["W2b"], wq["W13b"]
     dx = np.zeros((T, H))
     dwf = np.zeros(T * k)
     dW13 = np.zeros((E, I2, H))
@@ -239,4 +266,4 @@ def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str):
 
 
 __all__ = ["MODES", "E4M3_MAX", "e4m3_decode_table", "e4m3_encode", "e4m3_decode", "scale_exponent",
-           "quantize_along_last", "quantize_tiles", "forward", "backward"]
+           "quantize_along_last", "quantize_tiles", "quantize_weights", "forward", "backward"]

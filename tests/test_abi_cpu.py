@@ -104,35 +104,80 @@ def _fwd_args(ptr=0x10000):
 def test_fwd_null_pointer_rejected(B):
     x, idx, w, W13, W2, y, saved, ws = _fwd_args()
     with pytest.raises(B.MoEError) as ei:
-        B.moe_fwd(_shape(B), x, idx, w, None, W2, None, None, y, saved, ws, stream=0)
+        B.moe_fwd(_shape(B), x, idx, w, None, W2, None, y, saved, ws, stream=0)
     assert ei.value.status == 1
 
 
 def test_fwd_misaligned_pointer_rejected(B):
     x, idx, w, W13, W2, y, saved, ws = _fwd_args()
     with pytest.raises(B.MoEError) as ei:
-        B.moe_fwd(_shape(B), _Fake(0x10008), idx, w, W13, W2, None, None, y, saved, ws, stream=0)
+        B.moe_fwd(_shape(B), _Fake(0x10008), idx, w, W13, W2, None, y, saved, ws, stream=0)
     assert ei.value.status == 3
 
 
 def test_fwd_small_workspace_rejected(B):
     x, idx, w, W13, W2, y, saved, _ = _fwd_args()
     with pytest.raises(B.MoEError) as ei:
-        B.moe_fwd(_shape(B), x, idx, w, W13, W2, None, None, y, saved, _Fake(0x90000, 1024), stream=0)
+        B.moe_fwd(_shape(B), x, idx, w, W13, W2, None, y, saved, _Fake(0x90000, 1024), stream=0)
     assert ei.value.status == 6
 
 
-def test_fwd_scales_with_bf16_rejected(B):
+def test_fwd_quantized_weights_with_bf16_rejected(B):
     x, idx, w, W13, W2, y, saved, ws = _fwd_args()
     with pytest.raises(B.MoEError) as ei:
-        B.moe_fwd(_shape(B), x, idx, w, W13, W2, _Fake(0x80000), None, y, saved, ws, stream=0)
+        B.moe_fwd(_shape(B), x, idx, w, W13, W2, _Fake(0x80000), y, saved, ws, stream=0)
     assert ei.value.status == 4
+
+
+@pytest.mark.parametrize("prec", ["fp8_block", "mxfp8"])
+def test_fp8_forward_requires_quantized_weights(B, prec):
+    x, idx, w, W13, W2, y, saved, ws = _fwd_args()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_fwd(_shape(B, precision=prec), x, idx, w, W13, W2, None, y, saved, ws, stream=0)
+    assert ei.value.status == 1
+
+
+@pytest.mark.parametrize("prec", ["fp8_block", "mxfp8", "fp8_bwd"])
+def test_fp8_backward_requires_quantized_weights(B, prec):
+    a = _fwd_args()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_bwd(_shape(B, precision=prec), a[0], a[1], a[2], a[3], a[4], a[5], None, a[6], a[7], a[0],
+                  a[1], a[2], _Fake(0x70000), stream=0)
+    assert ei.value.status == 1
+
+
+def test_quantized_weight_layout(B):
+    E, H, I = 128, 2048, 768
+    assert B.moe_get_wq_layout(_shape(B))["total"] == 0
+    full = B.moe_get_wq_layout(_shape(B, precision="fp8_block"))
+    bwd_only = B.moe_get_wq_layout(_shape(B, precision="fp8_bwd"))
+    codes = E * 2 * I * H + E * H * I
+    assert full["total"] >= 2 * codes * (1 + 1 / 32)
+    assert bwd_only["total"] >= codes * (1 + 1 / 32)
+    assert bwd_only["w13"] == 2 ** 64 - 1 and bwd_only["w2_scale"] == 2 ** 64 - 1
+    # regions do not overlap and are 256-byte aligned
+    sizes = {"w13": E * 2 * I * H, "w13_scale": E * 2 * I * H // 32, "w2": E * H * I, "w2_scale": E * H * I // 32,
+             "w2t": E * I * H, "w2t_scale": E * I * H // 32, "w13t": E * H * 2 * I, "w13t_scale": E * H * 2 * I // 32}
+    spans = sorted((full[n], full[n] + sz) for n, sz in sizes.items())
+    assert all(a % 256 == 0 for a, _ in spans)
+    assert all(spans[i][1] <= spans[i + 1][0] for i in range(len(spans) - 1))
+    assert spans[-1][1] <= full["total"]
+
+
+def test_fp8_workspaces_are_larger(B):
+    f0, s0, b0 = B.moe_workspace_size(_shape(B))
+    f1, s1, b1 = B.moe_workspace_size(_shape(B, precision="fp8_block"))
+    f3, s3, b3 = B.moe_workspace_size(_shape(B, precision="fp8_bwd"))
+    Tk, T, H, I = 16384 * 8, 16384, 2048, 768
+    assert s1 == s0 == s3
+    assert f1 >= f0 + T * H + Tk * I and f3 == f0
+    assert b1 >= b0 + T * H + Tk * 2 * I and b3 == b1
 
 
 def test_bwd_requires_saved(B):
     a = _fwd_args()
     with pytest.raises(B.MoEError) as ei:
-        B.moe_bwd(_shape(B), a[0], a[1], a[2], a[3], a[4], a[5], None, None, None, a[6], a[7], a[0], a[1],
+        B.moe_bwd(_shape(B), a[0], a[1], a[2], a[3], a[4], a[5], None, None, a[6], a[7], a[0], a[1],
                   _Fake(0x70000), stream=0)
     assert ei.value.status == 1
 
@@ -140,6 +185,6 @@ def test_bwd_requires_saved(B):
 def test_bwd_small_workspace_rejected(B):
     a = _fwd_args()
     with pytest.raises(B.MoEError) as ei:
-        B.moe_bwd(_shape(B), a[0], a[1], a[2], a[3], a[4], a[5], None, None, a[6], a[7], a[0], a[1], a[2],
+        B.moe_bwd(_shape(B), a[0], a[1], a[2], a[3], a[4], a[5], None, a[6], a[7], a[0], a[1], a[2],
                   _Fake(0x70000, 4096), stream=0)
     assert ei.value.status == 6

@@ -1,0 +1,301 @@
+"""GPU parity of the FP8 precisions against the oracle's FP8 emulation.
+
+Quantizers (activation rows and weight stacks) must match the oracle bit for
+bit: codes and scale bytes. Layer outputs and gradients must be within the
+FP8 max-relative-error bound (normwise by the reference maximum): small
+layers element by element, the page-sized layers on sampled tokens and
+experts that the oracle computes one by one.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from grouped_gemm_02_amd import inputs
+from oracle import moe_fp8 as f8
+from oracle import moe_oracle as orc
+from tests.helpers import TOL_FP8, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+MODES = ["fp8_block", "mxfp8", "fp8_bwd"]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from grouped_gemm_02_amd import binding
+    binding.lib()
+    return binding
+
+
+def _rule(mode):
+    return (32, "mx_floor") if mode == "mxfp8" else (128, "pow2_ceil")
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+# --------------------------------------------------------------- quantizers
+
+def _awkward_rows(rows, K, seed):
+    """bf16 rows spanning the whole exponent range plus the edge cases of
+    the encoder: zero blocks, exact ties, saturation, subnormal inputs."""
+    g = torch.Generator().manual_seed(seed)
+    mag = torch.exp(torch.empty(rows, 1).uniform_(-60, 60, generator=g))
+    x = torch.randn(rows, K, generator=g) * mag
+    x[0] = 0.0                                   # all-zero row
+    x[1, :128] = 0.0                             # one zero block
+    x[1, 5] = -0.0
+    # exact midpoints between E4M3 neighbours in a block scaled by 2^0
+    # (max 448 -> blockwise e = 0; MX e = 0 as well since 256 <= 448 < 512)
+    mids = torch.tensor([1.0625, 1.1875, 3.25, 0.01171875, 0.001953125 * 1.5, 240.0, 208.0, 448.0])
+    x[2] = mids.repeat(K // 8)
+    x[3] = -x[2]
+    x[4] = torch.randn(K, generator=g) * 1e-39   # bf16 subnormals
+    x[5] = torch.randn(K, generator=g) * 6e37    # near the top of the range
+    x[6, :] = 1.0
+    x[6, ::32] = 960.0                           # 1.875 * 2^9: saturates under the MX rule
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_quantize_rows_bit_exact(B, mode):
+    rows, K = 300, 1024
+    _say(f"case quantize_rows mode={mode} rows={rows} K={K}")
+    x = _awkward_rows(rows, K, 20)
+    shape = B.make_shape(1, 256, 128, 1, 1, mode)
+    codes = torch.empty(rows, K, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(rows, K // 32, dtype=torch.uint8, device=DEV)
+    B.moe_quantize_rows(shape, x.to(DEV), rows, K, codes, scales)
+    torch.cuda.synchronize()
+    block, rule = _rule(mode)
+    rc, re, _ = f8.quantize_along_last(orc.as_f64(x), block, rule)
+    rs = np.repeat(re + 127, block // 32, axis=-1).astype(np.uint8)
+    gc, gs = _np(codes), _np(scales)
+    bad = np.argwhere(gc != rc)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[:5].tolist()}"
+    assert np.array_equal(gs, rs)
+
+
+def _tile_bytes(e, transpose):
+    """Per-(row, 32-block) scale bytes of 128x128 tile exponents e [E, RB, CB]."""
+    if transpose:
+        e = np.swapaxes(e, -1, -2)
+    return np.repeat(np.repeat(e + 127, 128, axis=1), 4, axis=2).astype(np.uint8)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_quantize_weights_bit_exact(B, mode):
+    E, H, I = 3, 512, 384
+    _say(f"case quantize_weights mode={mode} E={E} H={H} I={I}")
+    g = torch.Generator().manual_seed(21)
+    W13 = torch.randn(E, 2 * I, H, generator=g) * torch.tensor([1e-3, 1.0, 5e3]).view(E, 1, 1)
+    W2 = torch.randn(E, H, I, generator=g) * torch.tensor([7.0, 2e-2, 1e-30]).view(E, 1, 1)
+    W13[1, :128, :128] = 0.0                   # a zero tile
+    W2[0, 128:256, 0:128] = 448.0              # a tile at exactly 448
+    W13, W2 = W13.to(torch.bfloat16), W2.to(torch.bfloat16)
+    shape = B.make_shape(1, H, I, E, 1, mode)
+    L = B.moe_get_wq_layout(shape)
+    wq = torch.zeros(L["total"], dtype=torch.uint8, device=DEV)
+    B.moe_quantize_weights(shape, W13.to(DEV), W2.to(DEV), wq)
+    torch.cuda.synchronize()
+    wq = _np(wq)
+    w13, w2 = orc.as_f64(W13), orc.as_f64(W2)
+
+    def region(name, n):
+        return wq[L[name]:L[name] + n]
+
+    def expect(w, transpose):
+        if mode == "mxfp8":
+            src = np.swapaxes(w, -1, -2) if transpose else w
+            c, e, _ = f8.quantize_along_last(src, 32, "mx_floor")
+            return c, (e + 127).astype(np.uint8)
+        c, e, _ = f8.quantize_tiles(w, 128, "pow2_ceil")
+        return (np.swapaxes(c, -1, -2) if transpose else c), _tile_bytes(e, transpose)
+
+    uses = [("w2t", w2, True), ("w13t", w13, True)]
+    if mode != "fp8_bwd":
+        uses += [("w13", w13, False), ("w2", w2, False)]
+    else:
+        assert L["w13"] == 2 ** 64 - 1 and L["w2"] == 2 ** 64 - 1
+    for name, w, tr in uses:
+        c, s = expect(w, tr)
+        got_c = region(name, c.size).reshape(c.shape)
+        got_s = region(name + "_scale", s.size).reshape(s.shape)
+        assert np.array_equal(got_c, c), (name, int(np.sum(got_c != c)))
+        assert np.array_equal(got_s, s), name
+
+
+# --------------------------------------------------------------- layer
+
+def run_layer(B, cfg, d, mode):
+    shape = B.make_shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, mode)
+    buf = B.LayerBuffers.allocate(shape)
+    buf.fwd_ws.fill_(0xFF)
+    buf.bwd_ws.fill_(0xFF)
+    buf.saved.fill_(0xFF)
+    buf.wq.fill_(0xFF)
+    B.quantize_weights(buf, d["W13"], d["W2"])
+    y = B.forward(buf, d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
+    dx, dw, dW13, dW2 = B.backward(buf, d["dy"], d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
+    torch.cuda.synchronize()
+    Tk = cfg.T * cfg.k
+    return {
+        "y": y, "dx": dx, "dw": dw, "dW13": dW13, "dW2": dW2,
+        "counts": buf.saved_view("counts", torch.int32, cfg.E).clone(),
+        "h13": buf.saved_view("h13", torch.bfloat16, Tk * 2 * cfg.I).view(Tk, 2 * cfg.I).clone(),
+        "act": buf.saved_view("act", torch.bfloat16, Tk * cfg.I).view(Tk, cfg.I).clone(),
+        "status": B.moe_read_status(buf.fwd_ws),
+    }
+
+
+SMALL = [
+    inputs.CONFIGS["tiny"],
+    inputs.LayerConfig("mid", 600, 512, 384, 7, 3, "uniform", "bf16", 10),
+    inputs.LayerConfig("skew", 333, 256, 128, 16, 4, "zipf", "bf16", 11, zipf_s=1.2, zipf_cold=5),
+    inputs.LayerConfig("top1", 257, 768, 128, 40, 1, "uniform", "bf16", 13),
+]
+CASES = [(c, m) for c in SMALL for m in MODES]
+
+
+@pytest.mark.parametrize("cfg,mode", CASES, ids=[f"{c.name}-{m}" for c, m in CASES])
+def test_fp8_layer_matches_oracle_elementwise(B, cfg, mode):
+    cfg = cfg.scaled(precision=mode)
+    _say(f"case {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    out = run_layer(B, cfg, d, mode)
+    assert out["status"] == 0
+    args = (d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
+    wq = f8.quantize_weights(d["W13"], d["W2"], mode)
+    y_ref, pairs = f8.forward(*args, mode, return_pairs=True, wq=wq)
+    dx_ref, dw_ref, dW13_ref, dW2_ref = f8.backward(d["dy"], *args, mode, wq=wq)
+    errs = {
+        "y": max_rel_err(orc.as_f64(out["y"]), y_ref),
+        "dx": max_rel_err(orc.as_f64(out["dx"]), dx_ref),
+        "d_topk_w": max_rel_err(orc.as_f64(out["dw"]), dw_ref),
+        "dW13": max_rel_err(orc.as_f64(out["dW13"]), dW13_ref),
+        "dW2": max_rel_err(orc.as_f64(out["dW2"]), dW2_ref),
+    }
+    _, _, _, src_of = orc.permute(d["topk_idx"], cfg.E)
+    M, I = src_of.size, cfg.I
+    h13 = orc.as_f64(out["h13"])[:M]
+    errs["g"] = max_rel_err(h13[:, :I], pairs["g"][src_of])
+    errs["u"] = max_rel_err(h13[:, I:], pairs["u"][src_of])
+    wf = orc.as_f64(d["topk_w"]).reshape(-1)
+    wa_ref = pairs["wa"] if "wa" in pairs else pairs["a"] * wf[:, None]
+    errs["wa"] = max_rel_err(orc.as_f64(out["act"])[:M], wa_ref[src_of])
+    _say(f"{cfg.name}/{mode}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL_FP8, (k, v)
+    counts = _np(out["counts"])
+    for e in np.nonzero(counts == 0)[0]:
+        assert not out["dW13"][e].any() and not out["dW2"][e].any()
+
+
+def test_fp8_layer_deterministic_bitwise(B):
+    cfg = SMALL[1].scaled(precision="mxfp8")
+    _say(f"case determinism {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    a = run_layer(B, cfg, d, "mxfp8")
+    b = run_layer(B, cfg, d, "mxfp8")
+    for k in ("y", "dx", "dw", "dW13", "dW2", "h13", "act"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_fp8_zero_tokens(B):
+    cfg = inputs.LayerConfig("empty", 0, 256, 128, 4, 2, "uniform", "fp8_block", 16)
+    d = inputs.make_layer_inputs(cfg, DEV)
+    out = run_layer(B, cfg, d, "fp8_block")
+    assert not out["dW13"].any() and not out["dW2"].any()
+
+
+# --------------------------------------------------------------- page-sized layers, sampled
+
+def _pick_tokens(idx, counts, n, pool=4000):
+    """n tokens whose experts overlap as much as possible (keeps the number
+    of expert weight stacks the oracle has to quantize small)."""
+    idx = idx[:pool]
+    hot = np.argsort(-np.array([counts[r].sum() for r in idx]))
+    chosen, seen = [int(hot[0])], set(idx[hot[0]].tolist())
+    while len(chosen) < n:
+        best = min((t for t in hot[:400] if t not in chosen), key=lambda t: len(set(idx[t].tolist()) - seen))
+        chosen.append(int(best))
+        seen |= set(idx[best].tolist())
+    return sorted(chosen)
+
+
+def _sampled_check(B, cfg, n_tokens, n_experts):
+    mode = cfg.precision
+    t0 = time.time()
+    _say(f"case full-size {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    out = run_layer(B, cfg, d, mode)
+    assert out["status"] == 0
+    counts = _np(out["counts"])
+    idx_h = _np(d["topk_idx"])
+    assert np.array_equal(counts, np.bincount(idx_h.reshape(-1), minlength=cfg.E))
+    _say(f"  gpu done {time.time() - t0:.1f}s")
+    toks = _pick_tokens(idx_h, counts, n_tokens)
+    experts = [int(np.argmax(counts)), int(np.argmin(counts))][:n_experts]
+    cache = {}
+    keys = ("W2b", "W13b") if mode == "fp8_bwd" else ("W13q", "W2q", "W2b", "W13b")
+
+    def wq_of(ex):
+        for e in ex:
+            if e not in cache:
+                cache[e] = f8.quantize_weights(d["W13"][e:e + 1], d["W2"][e:e + 1], mode, keys)
+        return {k: np.concatenate([cache[e][k] for e in ex]) for k in cache[ex[0]]}
+
+    ys, yr, dxs, dxr, dws, dwr = [], [], [], [], [], []
+    for t in toks:
+        ex = [int(e) for e in idx_h[t]]
+        wq = wq_of(ex)
+        sub = (d["x"][t:t + 1], np.arange(cfg.k).reshape(1, -1), d["topk_w"][t:t + 1], d["W13"][ex], d["W2"][ex])
+        yr.append(f8.forward(*sub, mode, wq=wq)[0])
+        gx, gw, _, _ = f8.backward(d["dy"][t:t + 1], *sub, mode, wq=wq)
+        dxr.append(gx[0])
+        dwr.append(gw[0])
+        ys.append(orc.as_f64(out["y"][t]))
+        dxs.append(orc.as_f64(out["dx"][t]))
+        dws.append(orc.as_f64(out["dw"][t]))
+    errs = {"y": max_rel_err(np.array(ys), np.array(yr)),
+            "dx": max_rel_err(np.array(dxs), np.array(dxr)),
+            "d_topk_w": max_rel_err(np.array(dws), np.array(dwr))}
+    _say(f"  tokens {toks} done {time.time() - t0:.1f}s ({len(cache)} experts quantized)")
+    for e in experts:
+        f, xe, ie, we, dye = orc.restrict_to_expert(d["x"], d["topk_idx"], d["topk_w"], d["dy"], e)
+        if f.size == 0:
+            assert not out["dW13"][e].any() and not out["dW2"][e].any()
+            continue
+        _, _, r13, r2 = f8.backward(dye, xe, ie, we, d["W13"][e:e + 1], d["W2"][e:e + 1], mode, wq=wq_of([e]))
+        errs[f"dW13[{e}]"] = max_rel_err(orc.as_f64(out["dW13"][e]), r13[0])
+        errs[f"dW2[{e}]"] = max_rel_err(orc.as_f64(out["dW2"][e]), r2[0])
+    _say(f"{cfg.name}/{mode}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
+         + f" ({time.time() - t0:.1f}s)")
+    for k, v in errs.items():
+        assert v <= TOL_FP8, (k, v)
+    for k in ("y", "dx", "dW13", "dW2"):
+        assert torch.isfinite(out[k].float()).all(), k
+
+
+def test_ep8_share_fp8_block_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["ep8_share"], n_tokens=16, n_experts=2)
+
+
+def test_qwen3_235b_fp8_bwd_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["qwen3_235b"], n_tokens=2, n_experts=1)
+
+
+def test_qwen3_30b_zipf_mxfp8_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["zipf"], n_tokens=3, n_experts=2)

@@ -62,6 +62,20 @@ def test_scale_exponent_rules():
     assert f8.scale_exponent(np.zeros(3), "mx_floor").tolist() == [0, 0, 0]
 
 
+def test_scale_exponent_stays_in_e8m0_range():
+    """E8M0 holds exponents -127..127; tiny blocks clamp at -127 and still
+    encode without saturating (bf16 reaches down to 2^-133)."""
+    tiny = np.array([2.0 ** -133, 2.0 ** -126, 1e-38, 2.0 ** -119 * 1.5])
+    for rule in ("pow2_ceil", "mx_floor"):
+        e = f8.scale_exponent(tiny, rule)
+        assert np.all(e >= -127) and np.all(e <= 127)
+        assert e[0] == -127 and e[1] == -127
+        codes, e2, deq = f8.quantize_along_last(tiny.reshape(1, -1).repeat(32, axis=1).reshape(4, 32), 32, rule)
+        assert np.all(np.abs(f8.e4m3_decode(codes)) < 448.0)
+    huge = np.array([3.0e38])
+    assert f8.scale_exponent(huge, "pow2_ceil")[0] == 120  # 448 * 2^120 >= 3e38 > 224 * 2^120
+
+
 @pytest.mark.parametrize("block,rule", [(128, "pow2_ceil"), (32, "mx_floor")])
 def test_quantization_error_bounds(block, rule):
     rng = np.random.default_rng(1)
@@ -232,3 +246,30 @@ def test_weight_gradients_use_unquantized_operands():
     _, _, rW13, rW2 = orc.backward(*args)
     np.testing.assert_allclose(dW2, rW2, rtol=1e-12, atol=1e-12)
     assert np.max(np.abs(dW13 - rW13)) / np.max(np.abs(rW13)) < 0.15
+
+
+@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8"])
+def test_weight_quantization_is_per_expert(mode):
+    """Blocks never straddle experts: quantizing a stack equals stacking the
+    per-expert quantizations (what the sampled full-size checks rely on)."""
+    rng = np.random.default_rng(5)
+    W13 = rng.standard_normal((3, 256, 256)) * np.array([0.01, 1.0, 100.0])[:, None, None]
+    W2 = rng.standard_normal((3, 256, 128)) * np.array([5.0, 0.02, 1.0])[:, None, None]
+    full = f8.quantize_weights(W13, W2, mode)
+    for e in range(3):
+        one = f8.quantize_weights(W13[e:e + 1], W2[e:e + 1], mode)
+        for key in full:
+            assert np.array_equal(full[key][e:e + 1], one[key]), (key, e)
+
+
+def test_prequantized_weights_give_identical_layer():
+    from grouped_gemm_02_amd import inputs
+    d = inputs.make_layer_inputs(inputs.CONFIGS["tiny"], "cpu")
+    args = (d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
+    for mode in ("fp8_block", "mxfp8", "fp8_bwd"):
+        wq = f8.quantize_weights(d["W13"], d["W2"], mode)
+        assert np.array_equal(f8.forward(*args, mode), f8.forward(*args, mode, wq=wq))
+        a = f8.backward(d["dy"], *args, mode)
+        b = f8.backward(d["dy"], *args, mode, wq=wq)
+        for u, v in zip(a, b):
+            assert np.array_equal(u, v)
