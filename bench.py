@@ -4,13 +4,16 @@ A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: permutation, gate/up grouped GEMM + SwiGLU, down
 grouped GEMM + routing-weight scale, combine, then dH GEMM + SwiGLU backward
 + routing-weight-gradient partials, dX GEMM, dx / d_topk_w reduce, dW13 and
-dW2 grouped GEMMs. Workload: the Qwen3-30B-A3B-shaped layer (T=16384, H=2048,
-I=768, E=128, top-8, uniform random routing, bf16).
+dW2 grouped GEMMs. FP8 precisions add the weight quantization (once per
+step, as after an optimizer update) and the activation quantizations.
+Default workload: the Qwen3-30B-A3B-shaped layer (T=16384, H=2048, I=768,
+E=128, top-8, uniform random routing, bf16); --config picks another layer
+shape (ep8_share: blockwise FP8, qwen3_235b: fp8_bwd, zipf: MXFP8).
 
 Prints one JSON line. `value` is TFLOP/s of algorithmic work
 (18 * T * k * H * I flops per step: 6 forward, 12 backward).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config NAME] [--precision P]
 """
 from __future__ import annotations
 
@@ -26,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer fwd+bwd ms and TFLOP/s (frac of MFMA peak), Qwen3-30B-A3B shape, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 COPY_CALIB_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 
@@ -33,12 +37,25 @@ COPY_CALIB_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 GEMM_FLOP_FACTOR = {
     "gemm1_swiglu": 4, "gemm2": 2, "gemm_dh_dswiglu": 2, "gemm_dx": 4, "gemm_dw13": 4, "gemm_dw2": 2,
 }
+GEMM_FLOP_FACTOR.update({k + "_fp8": v for k, v in list(GEMM_FLOP_FACTOR.items()) if not k.startswith("gemm_dw")})
+WORKLOADS = {
+    "tiny": "tiny MoE layer",
+    "qwen3_30b": "Qwen3-30B-A3B-shaped MoE layer fwd+bwd",
+    "ep8_share": "one EP=8 GPU's share of the Qwen3-30B-A3B layer (16 local experts) fwd+bwd",
+    "qwen3_235b": "Qwen3-235B-A22B-shaped MoE layer fwd+bwd",
+    "zipf": "Qwen3-30B-A3B-shaped MoE layer, Zipf(1.2) routing, fwd+bwd",
+}
 # timer name -> kernel function name in rocprofv3 output
 KERNEL_FN = {
     "gemm1_swiglu": "gemm1_swiglu_kernel", "gemm2": "gemm2_kernel", "gemm_dh_dswiglu": "gemm_dh_kernel",
     "gemm_dx": "gemm_dx_kernel", "gemm_dw13": "gemm_dw13_kernel", "gemm_dw2": "gemm_dw2_kernel",
 }
+
+
+def kernel_peak(name: str) -> float:
+    return PEAK_FP8_TFLOPS if name.endswith("_fp8") else PEAK_BF16_TFLOPS
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_qwen3_30b_bf16.json")
+WORKLOAD_KEY = ["qwen3_30b/bf16"]   # the workload the committed traffic summary was taken on
 
 
 def measured_traffic(kernel: str):
@@ -49,6 +66,8 @@ def measured_traffic(kernel: str):
         return None
     d = json.load(open(TRAFFIC_FILE))
     if d.get("source_sha256") != profile_summary.source_hash():
+        return None
+    if d.get("workload", "qwen3_30b/bf16") != WORKLOAD_KEY[0]:
         return None
     k = d.get("kernels", {}).get(KERNEL_FN.get(kernel, kernel))
     if not k or "fetch_size_bytes" not in k or "write_size_bytes" not in k:
@@ -61,7 +80,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="qwen3_30b")
+    ap.add_argument("--config", default="qwen3_30b", choices=sorted(WORKLOADS))
+    ap.add_argument("--precision", default=None, choices=["bf16", "fp8_block", "mxfp8", "fp8_bwd"],
+                    help="override the configuration's precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     return ap.parse_args()
@@ -89,6 +110,38 @@ def cpu_baseline(cfg, d, n_tok):
                       f"forward + backward in float64 numpy; flops counted as 18*tokens*k*H*I"}
 
 
+def cpu_baseline_fp8(cfg, d, n_experts):
+    """The CPU oracle's FP8 emulation, as it stands, on the routed pairs of
+    the first n_experts experts (other pairs dropped), weight quantization of
+    those experts included."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_fp8 as f8
+    n_experts = min(n_experts, cfg.E)
+    idx = d["topk_idx"].cpu().numpy()
+    keep = idx < n_experts
+    toks = np.nonzero(keep.any(axis=1))[0]
+    sub_idx = np.where(keep[toks], idx[toks], -1)
+    pairs = int(keep.sum())
+    x = d["x"][toks].cpu()
+    dy = d["dy"][toks].cpu()
+    w = d["topk_w"][toks].cpu()
+    W13 = d["W13"][:n_experts].cpu()
+    W2 = d["W2"][:n_experts].cpu()
+    t0 = time.perf_counter()
+    f8.forward(x, sub_idx, w, W13, W2, cfg.precision)
+    f8.backward(dy, x, sub_idx, w, W13, W2, cfg.precision)
+    dt = time.perf_counter() - t0
+    flops = 18.0 * pairs * cfg.H * cfg.I
+    threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(max(threads) if threads else 1),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the {pairs} routed pairs of experts 0..{n_experts - 1} ({len(toks)} tokens), "
+                      f"{cfg.precision} emulation (weight quantization of those experts included), "
+                      f"forward + backward in float64 numpy; flops counted as 18*pairs*H*I"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -101,8 +154,10 @@ def main():
     from grouped_gemm_02_amd import inputs
 
     cfg = inputs.CONFIGS[args.config]
-    if cfg.precision != "bf16":
-        cfg = cfg.scaled(precision="bf16")
+    if args.precision:
+        cfg = cfg.scaled(precision=args.precision)
+    WORKLOAD_KEY[0] = f"{cfg.name}/{cfg.precision}"
+    fp8 = cfg.precision != "bf16"
     torch.cuda.set_device(0)
     d = inputs.make_layer_inputs(cfg, "cuda")
     shape = B.make_shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.precision)
@@ -116,6 +171,10 @@ def main():
     def step(evs=None):
         if evs:
             evs[0].record()
+        if fp8:
+            B.quantize_weights(buf, d["W13"], d["W2"])
+        if evs:
+            evs[3].record()
         B.forward(buf, d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], y=y)
         if evs:
             evs[1].record()
@@ -139,7 +198,7 @@ def main():
     if B.moe_read_status(buf.fwd_ws) != 0:
         raise RuntimeError("routing status word set")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     B.moe_kernel_timing_collect()          # drop anything recorded before
     B.moe_set_kernel_timing(True)
     torch.cuda.synchronize()
@@ -155,7 +214,8 @@ def main():
     kt = B.moe_kernel_timing_collect()
 
     ms_step = start.elapsed_time(stop) / args.steps
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    fwd_ms = [e[3].elapsed_time(e[1]) for e in evs]
+    wq_ms = [e[0].elapsed_time(e[3]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
     flops = cfg.flops_fwd() + cfg.flops_bwd()
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -167,12 +227,15 @@ def main():
         ent = {"launches": n, "avg_ms": round(avg, 5), "ms_per_step": round(tot / args.steps, 5)}
         if name in GEMM_FLOP_FACTOR:
             ent["tflops"] = round(GEMM_FLOP_FACTOR[name] * MHI / (avg * 1e-3) / 1e12, 1)
+            ent["frac_of_peak"] = round(ent["tflops"] / kernel_peak(name), 4)
         kernels[name] = ent
     gemm_names = [n for n in kernels if n in GEMM_FLOP_FACTOR]
     dom = max(gemm_names, key=lambda n: kernels[n]["ms_per_step"])
     dom_avg = kernels[dom]["avg_ms"]
     achieved = GEMM_FLOP_FACTOR[dom] * MHI / (dom_avg * 1e-3) / 1e12
     gemm_ms = sum(kernels[n]["ms_per_step"] for n in gemm_names)
+    dtype = {"bf16": "bf16", "fp8_block": "fp8_e4m3+bf16", "mxfp8": "fp8_e4m3+bf16",
+             "fp8_bwd": "bf16+fp8_e4m3"}[cfg.precision]
 
     out = {
         "metric": METRIC,
@@ -185,22 +248,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: Qwen3-30B-A3B-shaped MoE layer fwd+bwd", "T": cfg.T, "H": cfg.H,
+        "config": {"workload": f"{cfg.name}: {WORKLOADS[cfg.name]}", "T": cfg.T, "H": cfg.H,
                    "I": cfg.I, "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "precision": cfg.precision},
         "fwd_ms": round(sum(fwd_ms) / len(fwd_ms), 4),
         "bwd_ms": round(sum(bwd_ms) / len(bwd_ms), 4),
+        "weight_quant_ms": round(sum(wq_ms) / len(wq_ms), 4),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "gemm_tflops": round((flops) / (gemm_ms * 1e-3) / 1e12, 1),
         "wall_s": round(wall, 3),
         "kernels": kernels,
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": kernel_peak(dom),
+                     "unit": "TFLOP/s", "frac": round(achieved / kernel_peak(dom), 4),
                      "traffic": measured_traffic(dom)},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample_tokens)
+        if fp8:
+            out["cpu_baseline"] = cpu_baseline_fp8(cfg, d, 8)
+        else:
+            out["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
 
 

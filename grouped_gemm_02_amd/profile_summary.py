@@ -22,7 +22,8 @@ import json
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/device_common.h", "csrc/combine.hip", "csrc/permute.hip")
+KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/device_common.h", "csrc/combine.hip", "csrc/permute.hip",
+                  "csrc/quant.hip")
 
 
 def source_hash() -> str:
@@ -69,8 +70,9 @@ def _per_dispatch(csv_path: str, counter: str):
     return vals, names
 
 
-def traffic(fetch_csv: str, write_csv: str, out_path: str, cmd: str, copy_bytes: int) -> None:
-    res = {"command": cmd, "source_sha256": source_hash(), "copy_bytes": copy_bytes, "kernels": {}}
+def traffic(fetch_csv: str, write_csv: str, out_path: str, cmd: str, copy_bytes: int, workload: str) -> None:
+    res = {"command": cmd, "workload": workload, "source_sha256": source_hash(), "copy_bytes": copy_bytes,
+           "kernels": {}}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals, names = _per_dispatch(path, counter)
         copies = [d for d, n in names.items() if "copy" in n.lower() and "moe::" not in n]
@@ -104,11 +106,12 @@ def main():
     t.add_argument("out")
     t.add_argument("--cmd", required=True)
     t.add_argument("--copy-bytes", type=int, default=1 << 30)
+    t.add_argument("--workload", default="qwen3_30b/bf16", help="<config>/<precision> the counters were taken on")
     a = ap.parse_args()
     if a.what == "stats":
         stats(a.csv, a.out, a.cmd)
     else:
-        traffic(a.fetch_csv, a.write_csv, a.out, a.cmd, a.copy_bytes)
+        traffic(a.fetch_csv, a.write_csv, a.out, a.cmd, a.copy_bytes, a.workload)
 
 
 if __name__ == "__main__":
