@@ -80,22 +80,27 @@ struct Stage {
 };
 
 // k-major operand: 256 entity rows, each with its k-values contiguous.
-// Thread t copies chunk (t % 8) of rows t/8 + 64*i. Row addresses are a
-// tile-uniform base plus a 32-bit element offset per row. Every offset must
-// address a real row: rows of the token side past the end of a ragged tile
-// are pointed at a valid row and their results are never stored, so the
-// loads need no predicate.
+// Thread t copies chunk (t % 8) of rows t/8 + 64*i. Loads go through a
+// buffer resource (tile-uniform base and extent in scalar registers, a
+// 32-bit byte offset per row in a vector register): an offset past the
+// extent reads zero instead of faulting. Every offset addresses a real row:
+// rows of the token side past the end of a ragged tile are pointed at a
+// valid row and their results are never stored, so the loads need no
+// predicate.
 struct KMajorLoader {
-  const uint16_t* base;
-  int32_t off[kPer];
+  __amdgpu_buffer_rsrc_t data;
+  uint32_t off[kPer];  // byte offset of this thread's 16 bytes of row i in slab 0
 
   __device__ __forceinline__ static int row_of_thread(int i) { return (threadIdx.x >> 3) + 64 * i; }
+  // base: element 0 of row 0; units: extent in 16-bit units
+  __device__ __forceinline__ void set_base(const uint16_t* base, int64_t units) { data = make_rsrc(base, units * 2); }
+  // row_off: offset of the row in 16-bit units
   __device__ __forceinline__ void set_row(int i, int64_t row_off) {
-    off[i] = int32_t(row_off) + (threadIdx.x & 7) * 8;
+    off[i] = uint32_t(row_off * 2) + (threadIdx.x & 7) * 16;
   }
   __device__ __forceinline__ void fetch(int kt, Stage& st) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) st.r[i] = *reinterpret_cast<const u32x4*>(base + off[i] + kt * BK);
+    for (int i = 0; i < kPer; ++i) st.r[i] = __builtin_amdgcn_raw_buffer_load_b128(data, off[i], kt * 2 * BK, 0);
     st.ok = ~0u;
   }
   __device__ __forceinline__ void store(uint16_t* lds, const Stage& st) const {
@@ -110,22 +115,27 @@ struct KMajorLoader {
 // contiguously. Thread t copies chunk (t % 32) of k-rows t/32 + 16*i.
 // RowFn::index(k) gives the memory row of absolute k, always a real row, and
 // RowFn::valid(k) whether k contributes (k-rows past the end are loaded from
-// a real row and replaced by zero when stored). Slabs are fetched in order;
-// each fetch also works out the rows of the next slab, since they may come
-// from an index array.
+// a real row and replaced by zero when stored); rows are RowFn::ld elements
+// apart. Loads go through a buffer resource over the tile's entity 0 of
+// row 0. Slabs are fetched in order; each fetch also works out the rows of
+// the next slab, since they may come from an index array.
 template <class RowFn>
 struct MNMajorLoader {
   RowFn fn;
+  __amdgpu_buffer_rsrc_t data;
   int nchunks = 32;  // 16-byte chunks of the tile that exist (partial last n-tile)
-  int32_t nxt[kPer];
-  uint32_t nxt_ok;   // bit i: k-row i of the next slab contributes
+  uint32_t nxt[kPer];  // byte offsets of the next slab's rows
+  uint32_t nxt_ok;     // bit i: k-row i of the next slab contributes
 
+  __device__ __forceinline__ void set_base(const uint16_t* base, int64_t units) {
+    data = make_rsrc(base, units > 0 ? units * 2 : 0);
+  }
   __device__ __forceinline__ void prime(int kt) {
     uint32_t ok = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int k = kt * BK + (threadIdx.x >> 5) + 16 * i;
-      nxt[i] = fn.index(k);
+      nxt[i] = uint32_t(fn.index(k)) * uint32_t(fn.ld) * 2u;
       ok |= uint32_t(fn.valid(k)) << i;
     }
     nxt_ok = ok;
@@ -133,9 +143,9 @@ struct MNMajorLoader {
   __device__ __forceinline__ void fetch(int kt, Stage& st) {
     const int c = threadIdx.x & 31;
     const bool col_ok = c < nchunks;
-    const int cc = col_ok ? c : 0;
+    const uint32_t cc = col_ok ? uint32_t(c) * 16u : 0u;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) st.r[i] = *reinterpret_cast<const u32x4*>(fn.ptr(nxt[i]) + cc * 8);
+    for (int i = 0; i < kPer; ++i) st.r[i] = __builtin_amdgcn_raw_buffer_load_b128(data, nxt[i] + cc, 0, 0);
     st.ok = col_ok ? nxt_ok : 0u;
     prime(kt + 1);
   }
@@ -290,21 +300,19 @@ struct Stage8 {
 // Of the 8 threads that share 4 rows, thread t also moves the scales of row
 // t/8 + 64 * (t % 4) (threads t and t+4 duplicate each other, which keeps
 // every load and LDS write unconditional).
-struct KMajorLoader8 {
-  __amdgpu_buffer_rsrc_t data, scale;
-  uint32_t off[kPer];  // byte offset of this thread's 16 bytes of row i in slab 0
-  uint32_t soff;       // byte offset of the scale row this thread moves
+struct KMajorLoader8 : KMajorLoader {
+  __amdgpu_buffer_rsrc_t scale;
+  uint32_t soff;  // byte offset of the scale row this thread moves
 
-  __device__ __forceinline__ static int row_of_thread(int i) { return KMajorLoader::row_of_thread(i); }
   // base: codes of row 0 (as 16-bit units), units: extent in 16-bit units;
   // sbase / sbytes: the matching scale bytes
   __device__ __forceinline__ void set_base(const uint16_t* base, int64_t units, const uint8_t* sbase,
                                            int64_t sbytes) {
-    data = make_rsrc(base, units * 2);
+    KMajorLoader::set_base(base, units);
     scale = make_rsrc(sbase, sbytes);
   }
   __device__ __forceinline__ void set_row(int i, int64_t row_off) {
-    off[i] = uint32_t(row_off * 2) + (threadIdx.x & 7) * 16;
+    KMajorLoader::set_row(i, row_off);
     if (int(threadIdx.x & 3) == i) soff = uint32_t(row_off * 2) >> 5;
   }
   __device__ __forceinline__ void fetch(int kt, Stage8& st) {
@@ -567,8 +575,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
       lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * KU, 2 * I * KU,
                   W.scales + int64_t(rt.e) * 2 * I * (H / 32), 2 * I * (H / 32));
     } else {
-      lp.base = static_cast<const uint16_t*>(X.data);
-      lq.base = static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * KU;
+      lp.set_base(static_cast<const uint16_t*>(X.data), p.T * KU);
+      lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * KU, 2 * I * KU);
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -636,8 +644,9 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
                   int64_t(BN) * KU, W.scales + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * (I / 32),
                   int64_t(BN) * (I / 32));
     } else {
-      lp.base = static_cast<const uint16_t*>(A.data) + rt.row0 * KU;
-      lq.base = static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * KU;
+      lp.set_base(static_cast<const uint16_t*>(A.data) + rt.row0 * KU, int64_t(rt.rows) * KU);
+      lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * KU,
+                  int64_t(BN) * KU);
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -659,23 +668,19 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
 // ------------------------------------------------------------------ row functions
 
 struct DirectRows {  // memory row k of a row-major tensor
-  const uint16_t* base;  // entity 0 of the tile in row 0
-  int64_t ld;
+  int32_t ld;            // elements between rows
   int32_t nrows;         // k-rows past this contribute zeros (nrows >= 1)
   __device__ __forceinline__ int32_t index(int k) const { return k < nrows ? k : nrows - 1; }
   __device__ __forceinline__ bool valid(int k) const { return k < nrows; }
-  __device__ __forceinline__ const uint16_t* ptr(int32_t row) const { return base + int64_t(row) * ld; }
 };
 
 struct TokenRows {  // k-th row of an expert segment -> its token's row
-  const uint16_t* base;  // entity 0 of the tile in token row 0
-  int64_t ld;
+  int32_t ld;            // elements between token rows
   const int32_t* src;    // src_of + segment start
   int rows;              // segment length (>= 1)
   int kk;                // experts per token
   __device__ __forceinline__ int32_t index(int k) const { return src[k < rows ? k : rows - 1] / kk; }
   __device__ __forceinline__ bool valid(int k) const { return k < rows; }
-  __device__ __forceinline__ const uint16_t* ptr(int32_t row) const { return base + int64_t(row) * ld; }
 };
 
 // ================================================================== backward dH
@@ -706,7 +711,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
     if constexpr (FP8)
       lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU, DY.scales, p.T * (H / 32));
     else
-      lp.base = static_cast<const uint16_t*>(DY.data);
+      lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
@@ -730,7 +735,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
       mainloop_fp8(lp, lq, KU / 64, lds, acc);
     } else {
       MNMajorLoader<DirectRows> lq;
-      lq.fn.base = static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN;
+      lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN,
+                  int64_t(H) * I - int64_t(rt.nt) * BN);
       lq.fn.ld = I;
       lq.fn.nrows = H;
       lq.nchunks = ncols / 8;
@@ -823,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
       lp.set_base(static_cast<const uint16_t*>(DH.data) + rt.row0 * KU, int64_t(rt.rows) * KU,
                   DH.scales + rt.row0 * (2 * I / 32), int64_t(rt.rows) * (2 * I / 32));
     else
-      lp.base = static_cast<const uint16_t*>(DH.data) + rt.row0 * KU;
+      lp.set_base(static_cast<const uint16_t*>(DH.data) + rt.row0 * KU, int64_t(rt.rows) * KU);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
@@ -841,7 +847,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
       mainloop_fp8(lp, lq, KU / 64, lds, acc);
     } else {
       MNMajorLoader<DirectRows> lq;
-      lq.fn.base = static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * H + int64_t(rt.nt) * BN;
+      lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * H + int64_t(rt.nt) * BN,
+                  int64_t(2 * I) * H - int64_t(rt.nt) * BN);
       lq.fn.ld = H;
       lq.fn.nrows = 2 * I;
       lq.prime(0);
@@ -870,11 +877,11 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     const int rows = p.counts[e];
     const int64_t off = p.offsets[e];
     MNMajorLoader<DirectRows> lp;
-    lp.fn.base = dh13 + off * 2 * I + int64_t(mt) * BM;
+    lp.set_base(dh13 + off * 2 * I + int64_t(mt) * BM, int64_t(rows) * 2 * I - int64_t(mt) * BM);
     lp.fn.ld = 2 * I;
     lp.fn.nrows = rows;
     MNMajorLoader<TokenRows> lq;
-    lq.fn.base = x + int64_t(nt) * BN;
+    lq.set_base(x + int64_t(nt) * BN, p.T * H - int64_t(nt) * BN);
     lq.fn.ld = H;
     lq.fn.src = p.src_of + off;
     lq.fn.rows = rows;
@@ -904,13 +911,13 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     const int rows = p.counts[e];
     const int64_t off = p.offsets[e];
     MNMajorLoader<TokenRows> lp;
-    lp.fn.base = dy + int64_t(mt) * BM;
+    lp.set_base(dy + int64_t(mt) * BM, p.T * H - int64_t(mt) * BM);
     lp.fn.ld = H;
     lp.fn.src = p.src_of + off;
     lp.fn.rows = rows;
     lp.fn.kk = int(p.k);
     MNMajorLoader<DirectRows> lq;
-    lq.fn.base = act + off * I + int64_t(nt) * BN;
+    lq.set_base(act + off * I + int64_t(nt) * BN, int64_t(rows) * I - int64_t(nt) * BN);
     lq.fn.ld = I;
     lq.fn.nrows = rows;
     const int ncols = min(BN, I - nt * BN);

@@ -28,6 +28,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->I < 128 || s->I > 8192 || s->I % 128 != 0) return MOE_ERR_SHAPE;
   if (s->T * s->k >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (s->T * s->H >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;  // 32-bit row offsets into x, dY
+  if (s->T * s->k * s->I >= (int64_t(1) << 30)) return MOE_ERR_SHAPE;  // 32-bit byte offsets into [g | u] rows
   if (s->num_cus < 0) return MOE_ERR_SHAPE;
   return MOE_OK;
 }

@@ -93,8 +93,9 @@ typedef enum moe_precision {
 } moe_precision;
 
 /* Problem description. Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= E,
- * T*k < 2^31, T*H < 2^31, H%256 == 0, I%128 == 0, 256 <= H <= 16384,
- * 128 <= I <= 8192.
+ * T*k < 2^31, T*H < 2^31, T*k*I < 2^30, H%256 == 0, I%128 == 0,
+ * 256 <= H <= 16384, 128 <= I <= 8192 (the kernels address rows with
+ * 32-bit byte offsets).
  * num_cus caps how many compute units the persistent GEMMs occupy
  * (0 = all), so that concurrent kernels (e.g. collectives) keep CUs. */
 typedef struct moe_shape {

@@ -55,7 +55,7 @@ def test_page_shapes_accepted_and_divisibility_enforced(B):
 
 @pytest.mark.parametrize("kw", [dict(k=0), dict(k=129), dict(E=0), dict(T=-1), dict(E=2000, k=8),
                                 dict(H=128), dict(I=64), dict(T=1 << 28, k=8), dict(num_cus=-1),
-                                dict(T=1 << 20, H=4096, k=1)])
+                                dict(T=1 << 20, H=4096, k=1), dict(T=1 << 19, H=256, I=2048, k=1)])
 def test_bad_shapes_rejected(B, kw):
     with pytest.raises(B.MoEError) as ei:
         B.moe_workspace_size(_shape(B, **kw))
