@@ -202,8 +202,11 @@ struct Acc {
 };
 
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
-__device__ __forceinline__ int wave_m() { return wave_id() % kWavesM; }
-__device__ __forceinline__ int wave_n() { return wave_id() / kWavesM; }
+// Waves w and w + 4 share a SIMD (w % 4) and own the two row halves of the
+// same column block, so a tile whose rows end in the first half leaves each
+// SIMD one wave with MFMA work instead of idling two SIMDs.
+__device__ __forceinline__ int wave_m() { return wave_id() / kWavesN; }
+__device__ __forceinline__ int wave_n() { return wave_id() % kWavesN; }
 
 // tile row held by this lane in sub-tile tm
 __device__ __forceinline__ int lane_row(int tm) { return wave_m() * WTM + tm * 32 + (lane_id() & 31); }
@@ -245,8 +248,10 @@ __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* l
 // Runs the k loop of one tile: the global loads of slab kt+1 are in flight
 // (in registers) while slab kt is multiplied out of one LDS buffer; then they
 // are written to the other buffer.
+// `active` (uniform per wave) is false for a wave whose tile rows are all
+// past the end of a ragged tile: it still moves data, but skips the MFMAs.
 template <bool P_MN, bool Q_MN, class LP, class LQ>
-__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc) {
+__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc, bool active = true) {
   if (nk <= 0) return;
   Stage sp, sq;
   lp.fetch(0, sp);
@@ -262,7 +267,7 @@ __device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, 
       lp.fetch(kt + 1, sp);
       lq.fetch(kt + 1, sq);
     }
-    mma_slab<P_MN, Q_MN>(cur, cur + kOperandLds, acc);
+    if (active) mma_slab<P_MN, Q_MN>(cur, cur + kOperandLds, acc);
     if (more) {
       lp.store(nxt, sp);
       lq.store(nxt + kOperandLds, sq);
@@ -368,7 +373,7 @@ __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_
 }
 
 __device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, uint16_t* lds,
-                                             Acc& acc) {
+                                             Acc& acc, bool active = true) {
   if (nk <= 0) return;
   Stage8 sp, sq;
   lp.fetch(0, sp);
@@ -384,7 +389,7 @@ __device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& l
       lp.fetch(kt + 1, sp);
       lq.fetch(kt + 1, sq);
     }
-    mma_slab_fp8(cur, cur + kOperandLds, acc);
+    if (active) mma_slab_fp8(cur, cur + kOperandLds, acc);
     // unconditional (after the last slab it rewrites stale data into the idle
     // buffer): a conditional block here lets the compiler sink the MFMAs
     // below it, with every fragment of the slab live at once
@@ -590,9 +595,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
     Acc acc;
     acc.zero();
     if constexpr (FP8) {
-      mainloop_fp8(lp, lq, KU / 64, lds, acc);
+      mainloop_fp8(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     } else {
-      mainloop<false, false>(lp, lq, KU / 64, lds, acc);
+      mainloop<false, false>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     }
     if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds g and u of intermediate indices nt*128 + h*64 + [0, 64):
@@ -657,9 +662,9 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
     Acc acc;
     acc.zero();
     if constexpr (FP8) {
-      mainloop_fp8(lp, lq, KU / 64, lds, acc);
+      mainloop_fp8(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     } else {
-      mainloop<false, false>(lp, lq, KU / 64, lds, acc);
+      mainloop<false, false>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     }
     store_tile(acc, lds, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
   }
@@ -732,7 +737,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
         lq.set_row(i, int64_t(min(KMajorLoader::row_of_thread(i), ncols - 1)) * KU);
-      mainloop_fp8(lp, lq, KU / 64, lds, acc);
+      mainloop_fp8(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     } else {
       MNMajorLoader<DirectRows> lq;
       lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN,
@@ -741,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
       lq.fn.nrows = H;
       lq.nchunks = ncols / 8;
       lq.prime(0);
-      mainloop<false, true>(lp, lq, KU / 64, lds, acc);
+      mainloop<false, true>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     }
     if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
@@ -844,7 +849,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
                   int64_t(BN) * (2 * I / 32));
 #pragma unroll
       for (int i = 0; i < kPer; ++i) lq.set_row(i, int64_t(KMajorLoader::row_of_thread(i)) * KU);
-      mainloop_fp8(lp, lq, KU / 64, lds, acc);
+      mainloop_fp8(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     } else {
       MNMajorLoader<DirectRows> lq;
       lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * H + int64_t(rt.nt) * BN,
@@ -852,7 +857,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
       lq.fn.ld = H;
       lq.fn.nrows = 2 * I;
       lq.prime(0);
-      mainloop<false, true>(lp, lq, KU / 64, lds, acc);
+      mainloop<false, true>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     }
     store_tile(acc, lds, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
   }
