@@ -426,25 +426,34 @@ __device__ __forceinline__ void stage_half(const Acc& acc, float* F, int half) {
 
 // Plain bf16 store of the tile into a row-major [*, ld] output starting at
 // (row0, col0); rows beyond `rows` and columns beyond `cols` are not written.
-// Each thread writes 16-byte pieces (8 columns) of rows t/16 + 32*j.
+// Every wave rounds its accumulators to bf16 (round to nearest even, as the
+// output would be) into a [256][256 + 8] LDS image (8-byte writes, two per
+// bank pair at most); then thread t copies 16-byte pieces (column chunk
+// t % 32) of rows t/32 + 16*j, so each row goes out as one 512-byte run.
+constexpr int LDT = BN + 8;
+static_assert(BM * LDT <= 2 * kStageLds, "bf16 tile image must fit in the operand LDS");
+
 __device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* lds, uint16_t* out, int64_t ld,
                                            int64_t row0, int64_t col0, int rows, int cols) {
-  float* F = reinterpret_cast<float*>(lds);
-  const int c = (threadIdx.x & 15) * 8;
-  for (int h = 0; h < 2; ++h) {
-    stage_half(acc, F, h);
-    __syncthreads();
-    if (h * 128 + c < cols) {
-      for (int m = threadIdx.x >> 4; m < rows; m += kRowPass) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(F + m * FLD + c);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(F + m * FLD + c + 4);
-        const u32x4 v = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                         pack_bf16x2(b[2], b[3])};
-        *reinterpret_cast<u32x4*>(out + (row0 + m) * ld + col0 + h * 128 + c) = v;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = lane_row(tm);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = acc.c[tm][tn];
+        const u32x2 v = {pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+        *reinterpret_cast<u32x2*>(lds + m * LDT + lane_col(tn, g)) = v;
       }
-    }
-    __syncthreads();
   }
+  __syncthreads();
+  const int c = (threadIdx.x & 31) * 8;
+  if (c < cols) {
+    for (int m = threadIdx.x >> 5; m < rows; m += kThreads / 32)
+      *reinterpret_cast<u32x4*>(out + (row0 + m) * ld + col0 + c) = *reinterpret_cast<const u32x4*>(lds + m * LDT + c);
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ scheduling
