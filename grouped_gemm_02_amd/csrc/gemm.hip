@@ -67,7 +67,9 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // ------------------------------------------------------------------ loaders
 
 // Raw buffer resource over [base, base + bytes) (bytes < 2^32; dword 3 as
-// gfx9 parts expect for untyped loads).
+// gfx9 parts expect for untyped loads). Base and extent must be uniform and
+// visibly so to the compiler (derived from scalar values), or every load
+// through the resource becomes a loop over the distinct values.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(uint32_t(bytes)), 0x00020000);
 }
@@ -877,19 +879,90 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
 // dW2[e][h][i]  = sum_{r in seg e} dY[tok(r)][h] (w a)[r][i]
 // The reduction runs over the expert's rows (K = rows_e, the ragged last
 // slab zero-filled); an expert without rows produces an exact-zero tile.
+// ------------------------------------------------------------------ dW schedule
+// A weight-gradient tile's k loop runs over its expert's rows. With balanced
+// routing the tiles cost the same and the static XCD-aware walk of the other
+// GEMMs is best (every XCD works on a contiguous run of tiles, so concurrent
+// tiles share their expert's rows in L2). Under skewed routing (largest
+// expert above twice the mean) tiles differ in cost by an order of
+// magnitude; then experts are ranked by descending row count (ties by id)
+// and workgroups take tiles from a queue (a word in device memory, zero at
+// launch), heaviest expert first, so short tiles fill in behind long ones.
+// Thread 0 takes its next ticket as soon as a tile starts, so the atomic's
+// round trip overlaps the tile's own first loads. Tile indices are 32-bit
+// and pass through readfirstlane, so the tile's buffer resources stay in
+// scalar registers.
+
+// Fills s_order (experts by descending count) and returns whether the
+// routing is skewed. Same result in every workgroup.
+__device__ bool dw_expert_order(const int32_t* counts, int E, int32_t* s_cnt, int32_t* s_order, int32_t* s_flag) {
+  for (int e = threadIdx.x; e < E; e += kThreads) s_cnt[e] = counts[e];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const int c = s_cnt[e];
+    int r = 0;
+    for (int j = 0; j < E; ++j) {
+      const int cj = s_cnt[j];
+      r += (cj > c || (cj == c && j < e)) ? 1 : 0;
+    }
+    s_order[r] = e;
+  }
+  if (threadIdx.x == 0) {
+    int64_t sum = 0;
+    int mx = 0;
+    for (int j = 0; j < E; ++j) {
+      sum += s_cnt[j];
+      mx = max(mx, s_cnt[j]);
+    }
+    *s_flag = (int64_t(mx) * E > 2 * sum) ? 1 : 0;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*s_flag) != 0;
+}
+
+// Runs body(e, local) over every tile of a weight-gradient GEMM with
+// per_expert tiles per expert. s_flag and s_next are distinct LDS words.
+template <class Body>
+__device__ __forceinline__ void dw_for_each_tile(const int32_t* counts, int E, int per_expert, int32_t* queue,
+                                                 int32_t* s_cnt, int32_t* s_order, int32_t* s_flag,
+                                                 int32_t* s_next, Body&& body) {
+  const int total = E * per_expert;
+  if (dw_expert_order(counts, E, s_cnt, s_order, s_flag)) {
+    int32_t ticket = 0;  // thread 0 only
+    if (threadIdx.x == 0) ticket = atomicAdd(queue, 1);
+    for (;;) {
+      if (threadIdx.x == 0) *s_next = ticket;
+      __syncthreads();
+      const int u = __builtin_amdgcn_readfirstlane(*s_next);
+      __syncthreads();
+      if (u >= total) break;
+      if (threadIdx.x == 0) ticket = atomicAdd(queue, 1);
+      const int e = __builtin_amdgcn_readfirstlane(s_order[u / per_expert]);
+      body(e, u % per_expert);
+    }
+  } else {
+    for (int t = int(first_tile()); t < total; t += gridDim.x) body(t / per_expert, t % per_expert);
+  }
+}
+
+#define MOE_DW_SMEM                                                            \
+  __shared__ int32_t s_cnt[1024];                                              \
+  __shared__ int32_t s_order[1024];                                            \
+  __shared__ int32_t s_flag;                                                   \
+  __shared__ int32_t s_next;
+
 __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, const uint16_t* __restrict__ dh13,
                                                              const uint16_t* __restrict__ x,
-                                                             uint16_t* __restrict__ dW13) {
+                                                             uint16_t* __restrict__ dW13, int32_t* queue) {
   MOE_GEMM_SMEM
+  MOE_DW_SMEM
   const int H = int(p.H), I = int(p.I);
   const int MT = (2 * I) / BM, NT = H / BN;
-  const int64_t total = p.E * MT * NT;
-  for (int64_t t = first_tile(); t < total; t += gridDim.x) {
-    const int nt = int(t % NT);
-    const int mt = int((t / NT) % MT);
-    const int e = int(t / (int64_t(NT) * MT));
-    const int rows = p.counts[e];
-    const int64_t off = p.offsets[e];
+  dw_for_each_tile(p.counts, int(p.E), MT * NT, queue, s_cnt, s_order, &s_flag, &s_next, [&](int e, int local) {
+    const int nt = local % NT;
+    const int mt = local / NT;
+    const int rows = __builtin_amdgcn_readfirstlane(p.counts[e]);
+    const int64_t off = __builtin_amdgcn_readfirstlane(p.offsets[e]);
     MNMajorLoader<DirectRows> lp;
     lp.set_base(dh13 + off * 2 * I + int64_t(mt) * BM, int64_t(rows) * 2 * I - int64_t(mt) * BM);
     lp.fn.ld = 2 * I;
@@ -908,22 +981,21 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     acc.zero();
     mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, lds, acc);
     store_tile(acc, lds, dW13 + int64_t(e) * 2 * I * H, H, int64_t(mt) * BM, int64_t(nt) * BN, BM, BN);
-  }
+  });
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const uint16_t* __restrict__ dy,
                                                             const uint16_t* __restrict__ act,
-                                                            uint16_t* __restrict__ dW2) {
+                                                            uint16_t* __restrict__ dW2, int32_t* queue) {
   MOE_GEMM_SMEM
+  MOE_DW_SMEM
   const int H = int(p.H), I = int(p.I);
   const int MT = H / BM, NT = (I + BN - 1) / BN;  // the last n-tile may hold 128 columns
-  const int64_t total = p.E * MT * NT;
-  for (int64_t t = first_tile(); t < total; t += gridDim.x) {
-    const int nt = int(t % NT);
-    const int mt = int((t / NT) % MT);
-    const int e = int(t / (int64_t(NT) * MT));
-    const int rows = p.counts[e];
-    const int64_t off = p.offsets[e];
+  dw_for_each_tile(p.counts, int(p.E), MT * NT, queue, s_cnt, s_order, &s_flag, &s_next, [&](int e, int local) {
+    const int nt = local % NT;
+    const int mt = local / NT;
+    const int rows = __builtin_amdgcn_readfirstlane(p.counts[e]);
+    const int64_t off = __builtin_amdgcn_readfirstlane(p.offsets[e]);
     MNMajorLoader<TokenRows> lp;
     lp.set_base(dy + int64_t(mt) * BM, p.T * H - int64_t(mt) * BM);
     lp.fn.ld = H;
@@ -944,7 +1016,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     acc.zero();
     mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, lds, acc);
     store_tile(acc, lds, dW2 + int64_t(e) * H * I, I, int64_t(mt) * BM, int64_t(nt) * BN, BM, ncols);
-  }
+  });
 }
 
 // ================================================================== launchers
@@ -1014,19 +1086,29 @@ hipError_t launch_gemm_dx(const GemmProblem& p, GemmOperand dh13, GemmOperand W1
   return hipGetLastError();
 }
 
+__global__ void zero_words_kernel(int32_t* p, int n) {
+  if (int(threadIdx.x) < n) p[threadIdx.x] = 0;
+}
+
+hipError_t launch_zero_queues(int32_t* queues, hipStream_t st, KernelTimer* timer) {
+  TimedLaunch tl(timer, "zero_queues", st);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, st, queues, kNumQueues);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x,
-                            uint16_t* dW13, hipStream_t st, KernelTimer* timer) {
+                            uint16_t* dW13, int32_t* queue, hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(p.E * (2 * p.I / BM) * (p.H / BN), p.num_cus);
   TimedLaunch tl(timer, "gemm_dw13", st);
-  hipLaunchKernelGGL(gemm_dw13_kernel, dim3(grid), dim3(kThreads), 0, st, p, dh13, x, dW13);
+  hipLaunchKernelGGL(gemm_dw13_kernel, dim3(grid), dim3(kThreads), 0, st, p, dh13, x, dW13, queue);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint16_t* act,
-                           uint16_t* dW2, hipStream_t st, KernelTimer* timer) {
+                           uint16_t* dW2, int32_t* queue, hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(p.E * (p.H / BM) * ((p.I + BN - 1) / BN), p.num_cus);
   TimedLaunch tl(timer, "gemm_dw2", st);
-  hipLaunchKernelGGL(gemm_dw2_kernel, dim3(grid), dim3(kThreads), 0, st, p, dy, act, dW2);
+  hipLaunchKernelGGL(gemm_dw2_kernel, dim3(grid), dim3(kThreads), 0, st, p, dy, act, dW2, queue);
   return hipGetLastError();
 }
 

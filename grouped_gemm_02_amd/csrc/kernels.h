@@ -70,10 +70,13 @@ hipError_t launch_gemm_dh(const GemmProblem& p, GemmOperand dy, GemmOperand W2, 
                           uint16_t* dh13, float* dwpart, hipStream_t st, KernelTimer* timer);
 hipError_t launch_gemm_dx(const GemmProblem& p, GemmOperand dh13, GemmOperand W13, uint16_t* dx_rows,
                           hipStream_t st, KernelTimer* timer);
-hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x,
-                            uint16_t* dW13, hipStream_t st, KernelTimer* timer);
-hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint16_t* act,
-                           uint16_t* dW2, hipStream_t st, KernelTimer* timer);
+// weight gradients; each takes one zeroed queue word (tile counter)
+constexpr int kNumQueues = 2;
+hipError_t launch_zero_queues(int32_t* queues, hipStream_t st, KernelTimer* timer);
+hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x, uint16_t* dW13,
+                            int32_t* queue, hipStream_t st, KernelTimer* timer);
+hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint16_t* act, uint16_t* dW2,
+                           int32_t* queue, hipStream_t st, KernelTimer* timer);
 
 // ---------------------------------------------------------------- FP8 quantization
 constexpr int kRulePow2 = 0;  // smallest 2^e with 448 * 2^e >= amax

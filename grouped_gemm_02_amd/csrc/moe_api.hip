@@ -112,6 +112,7 @@ FwdLayout fwd_layout(const moe_shape& s) {
 }
 
 struct BwdLayout {
+  size_t queues;  // int32 tile counters of the weight-gradient GEMMs
   size_t dh13, dwpart, dxrows;
   size_t dyq, dys;  // FP8 backward: dY codes [T, H], scales [T, H/32]
   size_t dhq, dhs;  // FP8 backward: [dg | du] codes [Tk, 2I], scales [Tk, 2I/32]
@@ -122,6 +123,7 @@ BwdLayout bwd_layout(const moe_shape& s) {
   const int64_t Tk = s.T * s.k;
   BwdLayout L;
   size_t o = 0;
+  L.queues = o; o = align_up(o + size_t(kNumQueues) * 4);
   L.dh13 = o;   o = align_up(o + size_t(Tk) * size_t(2 * s.I) * 2);
   L.dwpart = o; o = align_up(o + size_t(Tk) * size_t(dh_num_parts(s.I)) * 4);
   L.dxrows = o; o = align_up(o + size_t(Tk) * size_t(s.H) * 2);
@@ -432,7 +434,9 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
   std::lock_guard<std::mutex> lk(g_timer_mu);
   KernelTimer* tm = timer();
   GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w, wrow};
-  hipError_t e = hipSuccess;
+  int32_t* queues = at<int32_t>(ws, BL.queues);
+  hipError_t e = launch_zero_queues(queues, hs, tm);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
   if (s->T > 0) {
     GemmOperand gdy{dy, nullptr}, gw2{W2, nullptr}, gdh{dh13, nullptr}, gw13{W13, nullptr};
     if (f8) {
@@ -460,9 +464,9 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
                             dh_num_parts(s->I), d_topk_w, hs, tm, "combine_dx_dw")) != hipSuccess)
       return MOE_ERR_LAUNCH;
   }
-  if ((e = launch_gemm_dw13(gp, dh13, x16, static_cast<uint16_t*>(dW13), hs, tm)) != hipSuccess)
+  if ((e = launch_gemm_dw13(gp, dh13, x16, static_cast<uint16_t*>(dW13), queues, hs, tm)) != hipSuccess)
     return MOE_ERR_LAUNCH;
-  e = launch_gemm_dw2(gp, dy16, act, static_cast<uint16_t*>(dW2), hs, tm);
+  e = launch_gemm_dw2(gp, dy16, act, static_cast<uint16_t*>(dW2), queues + 1, hs, tm);
   return launch_status(e);
 }
 
