@@ -47,8 +47,11 @@ WORKLOADS = {
 }
 # timer name -> kernel function name in rocprofv3 output
 KERNEL_FN = {
-    "gemm1_swiglu": "gemm1_swiglu_kernel", "gemm2": "gemm2_kernel", "gemm_dh_dswiglu": "gemm_dh_kernel",
-    "gemm_dx": "gemm_dx_kernel", "gemm_dw13": "gemm_dw13_kernel", "gemm_dw2": "gemm_dw2_kernel",
+    "gemm1_swiglu": "gemm1_swiglu_kernel<false>", "gemm2": "gemm2_kernel<false>",
+    "gemm_dh_dswiglu": "gemm_dh_kernel<false>", "gemm_dx": "gemm_dx_kernel<false>",
+    "gemm1_swiglu_fp8": "gemm1_swiglu_kernel<true>", "gemm2_fp8": "gemm2_kernel<true>",
+    "gemm_dh_dswiglu_fp8": "gemm_dh_kernel<true>", "gemm_dx_fp8": "gemm_dx_kernel<true>",
+    "gemm_dw13": "gemm_dw13_kernel", "gemm_dw2": "gemm_dw2_kernel",
 }
 
 

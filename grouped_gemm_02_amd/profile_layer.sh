@@ -1,0 +1,30 @@
+#!/bin/bash
+# Profiles the layer with rocprofv3 on an MI355X and writes the summaries
+# that are kept under profiles/ into <out_dir>/profiles. Usage (from the
+# repository root):
+#   bash grouped_gemm_02_amd/profile_layer.sh <out_dir>
+# Kernel statistics for every workload, then FETCH_SIZE and WRITE_SIZE
+# counter passes (separate runs) for the default workload.
+set -e
+OUT=${1:-gpurun_out/prof}
+export TMPDIR=/tmp
+PROF="$OUT/profiles"
+mkdir -p "$OUT" "$PROF"
+for cp in qwen3_30b:bf16 ep8_share:fp8_block qwen3_235b:fp8_bwd zipf:mxfp8; do
+  c=${cp%%:*}; prec=${cp##*:}
+  echo "stats $c"
+  timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/stats_$c" -o run -- \
+    python3 bench.py --config $c --steps 5 --warmup 2 --no-cpu-baseline > "$OUT/stats_$c.log" 2>&1
+  python3 -m grouped_gemm_02_amd.profile_summary stats "$OUT/stats_$c/run_kernel_stats.csv" \
+    "$PROF/kernel_stats_${c}_${prec}.txt" --cmd "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/stats_$c -o run -- python3 bench.py --config $c --steps 5 --warmup 2 --no-cpu-baseline"
+done
+echo "pmc fetch"
+timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/pmc_fetch" -o pmc -- \
+  python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > "$OUT/pmc_fetch.log" 2>&1
+echo "pmc write"
+timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/pmc_write" -o pmc -- \
+  python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > "$OUT/pmc_write.log" 2>&1
+python3 -m grouped_gemm_02_amd.profile_summary traffic "$OUT/pmc_fetch/pmc_counter_collection.csv" \
+  "$OUT/pmc_write/pmc_counter_collection.csv" "$PROF/gemm_traffic_qwen3_30b_bf16.json" --workload qwen3_30b/bf16 \
+  --cmd "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline ; rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline"
+echo "profiles written"
