@@ -252,12 +252,13 @@ __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* l
 // are written to the other buffer.
 // `active` (uniform per wave) is false for a wave whose tile rows are all
 // past the end of a ragged tile: it still moves data, but skips the MFMAs.
+// mainloop_staged runs the k loop with slab 0 already fetched into sp, sq
+// (the persistent row-tile kernels fetch a tile's first slab during the
+// previous tile's epilogue); mainloop fetches it itself.
 template <bool P_MN, bool Q_MN, class LP, class LQ>
-__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc, bool active = true) {
+__device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc, bool active,
+                                                Stage& sp, Stage& sq) {
   if (nk <= 0) return;
-  Stage sp, sq;
-  lp.fetch(0, sp);
-  lq.fetch(0, sq);
   lp.store(lds, sp);
   lq.store(lds + kOperandLds, sq);
   __syncthreads();
@@ -276,6 +277,15 @@ __device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, 
     }
     __syncthreads();
   }
+}
+
+template <bool P_MN, bool Q_MN, class LP, class LQ>
+__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc, bool active = true) {
+  if (nk <= 0) return;
+  Stage sp, sq;
+  lp.fetch(0, sp);
+  lq.fetch(0, sq);
+  mainloop_staged<P_MN, Q_MN>(lp, lq, nk, lds, acc, active, sp, sq);
 }
 
 // ------------------------------------------------------------------ FP8 core
@@ -374,12 +384,9 @@ __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_
   }
 }
 
-__device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, uint16_t* lds,
-                                             Acc& acc, bool active = true) {
+__device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, uint16_t* lds,
+                                                    Acc& acc, bool active, Stage8& sp, Stage8& sq) {
   if (nk <= 0) return;
-  Stage8 sp, sq;
-  lp.fetch(0, sp);
-  lq.fetch(0, sq);
   lp.store(lds, sp);
   lq.store(lds + kOperandLds, sq);
   __syncthreads();
@@ -399,6 +406,15 @@ __device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& l
     lq.store(nxt + kOperandLds, sq);
     __syncthreads();
   }
+}
+
+__device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, uint16_t* lds, Acc& acc,
+                                             bool active = true) {
+  if (nk <= 0) return;
+  Stage8 sp, sq;
+  lp.fetch(0, sp);
+  lq.fetch(0, sq);
+  mainloop_staged_fp8(lp, lq, nk, lds, acc, active, sp, sq);
 }
 
 // ------------------------------------------------------------------ LDS-staged epilogue
@@ -543,6 +559,51 @@ __device__ __forceinline__ void store4_bf16(uint16_t* p, float a, float b, float
   __shared__ int32_t s_tmp[kThreads];                                          \
   tile_prefix(p.counts, E, s_pref, s_tmp);
 
+// Persistent walk over row tiles. With PREFETCH the next tile's loaders are
+// set up and its first k-slab fetched into registers before the current
+// tile's epilogue runs, so that fetch's latency is spent on the epilogue
+// (kernels whose epilogue needs the registers turn it off). setup(t, state)
+// configures lp and lq for tile t; epi(state, acc) must not use lp or lq.
+struct TileState {
+  RowTile rt;
+  float w;  // routing weight of tile row threadIdx.x (kernels that need it)
+};
+
+template <bool FP8, bool Q_MN, bool PREFETCH, class LP, class LQ, class Setup, class Epi>
+__device__ __forceinline__ void row_tile_walk(int64_t total, int nk, uint16_t* lds, LP& lp, LQ& lq, Setup&& setup,
+                                              Epi&& epi) {
+  typename std::conditional<FP8, Stage8, Stage>::type sp, sq;
+  TileState cur, nxt;
+  int64_t t = first_tile();
+  if (PREFETCH && t < total) {
+    setup(t, cur);
+    lp.fetch(0, sp);
+    lq.fetch(0, sq);
+  }
+  while (t < total) {
+    if (!PREFETCH) {
+      setup(t, cur);
+      lp.fetch(0, sp);
+      lq.fetch(0, sq);
+    }
+    Acc acc;
+    acc.zero();
+    const bool active = wave_m() * WTM < cur.rt.rows;
+    if constexpr (FP8)
+      mainloop_staged_fp8(lp, lq, nk, lds, acc, active, sp, sq);
+    else
+      mainloop_staged<false, Q_MN>(lp, lq, nk, lds, acc, active, sp, sq);
+    t += gridDim.x;
+    if (PREFETCH && t < total) {
+      setup(t, nxt);
+      lp.fetch(0, sp);
+      lq.fetch(0, sq);
+    }
+    epi(cur, acc);
+    if (PREFETCH) cur = nxt;
+  }
+}
+
 // ================================================================== forward GEMM1
 // C[r][q] = x[tok(r)] . W13[e][wrow(q)],  K = H. Q rows are arranged so that
 // each wave's two sub-tiles are (gate, up) of the same 32 intermediate
@@ -583,9 +644,10 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
   const int NT = (2 * I) / BN;
   const int KU = row_units<FP8>(H);
   const int64_t total = int64_t(s_pref[E]) * NT;
-  for (int64_t t = first_tile(); t < total; t += gridDim.x) {
+  KLoader<FP8> lp, lq;
+  auto setup = [&](int64_t t, TileState& st) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
-    KLoader<FP8> lp, lq;
+    st.rt = rt;
     if constexpr (FP8) {
       lp.set_base(static_cast<const uint16_t*>(X.data), p.T * KU, X.scales, p.T * (H / 32));
       lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * KU, 2 * I * KU,
@@ -602,15 +664,11 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
       lq.set_row(i, int64_t(g1::w13_row(m, rt.nt, I)) * KU);
     }
     // routing weight of tile row t: loaded now, used after the k loop
-    const float w_row = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
-    Acc acc;
-    acc.zero();
-    if constexpr (FP8) {
-      mainloop_fp8(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
-    } else {
-      mainloop<false, false>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
-    }
-    if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
+    st.w = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
+  };
+  auto epi = [&](const TileState& st, const Acc& acc) {
+    const RowTile& rt = st.rt;
+    if (threadIdx.x < BM) s_w[threadIdx.x] = st.w;
     // half h holds g and u of intermediate indices nt*128 + h*64 + [0, 64):
     // staged column (i/32)*64 + i%32 is g, +32 is u.
     float* F = reinterpret_cast<float*>(lds);
@@ -636,7 +694,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
       }
       __syncthreads();
     }
-  }
+  };
+  row_tile_walk<FP8, false, false>(total, KU / 64, lds, lp, lq, setup, epi);
 }
 
 // ================================================================== forward GEMM2
@@ -650,9 +709,10 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
   const int NT = H / BN;
   const int KU = row_units<FP8>(I);
   const int64_t total = int64_t(s_pref[E]) * NT;
-  for (int64_t t = first_tile(); t < total; t += gridDim.x) {
+  KLoader<FP8> lp, lq;
+  auto setup = [&](int64_t t, TileState& st) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
-    KLoader<FP8> lp, lq;
+    st.rt = rt;
     if constexpr (FP8) {
       lp.set_base(static_cast<const uint16_t*>(A.data) + rt.row0 * KU, int64_t(rt.rows) * KU,
                   A.scales + rt.row0 * (I / 32), int64_t(rt.rows) * (I / 32));
@@ -670,15 +730,11 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
       lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * KU);
       lq.set_row(i, int64_t(m) * KU);
     }
-    Acc acc;
-    acc.zero();
-    if constexpr (FP8) {
-      mainloop_fp8(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
-    } else {
-      mainloop<false, false>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
-    }
-    store_tile(acc, lds, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
-  }
+  };
+  auto epi = [&](const TileState& st, const Acc& acc) {
+    store_tile(acc, lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN);
+  };
+  row_tile_walk<FP8, false, true>(total, KU / 64, lds, lp, lq, setup, epi);
 }
 
 // ------------------------------------------------------------------ row functions
@@ -838,9 +894,11 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
   const int NT = H / BN;
   const int KU = row_units<FP8>(2 * I);
   const int64_t total = int64_t(s_pref[E]) * NT;
-  for (int64_t t = first_tile(); t < total; t += gridDim.x) {
+  KLoader<FP8> lp;
+  typename std::conditional<FP8, KMajorLoader8, MNMajorLoader<DirectRows>>::type lq;
+  auto setup = [&](int64_t t, TileState& st) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
-    KLoader<FP8> lp;
+    st.rt = rt;
     if constexpr (FP8)
       lp.set_base(static_cast<const uint16_t*>(DH.data) + rt.row0 * KU, int64_t(rt.rows) * KU,
                   DH.scales + rt.row0 * (2 * I / 32), int64_t(rt.rows) * (2 * I / 32));
@@ -851,27 +909,24 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
       const int m = KMajorLoader::row_of_thread(i);
       lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * KU);
     }
-    Acc acc;
-    acc.zero();
     if constexpr (FP8) {
-      KMajorLoader8 lq;
       lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * KU,
                   int64_t(BN) * KU, W.scales + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * (2 * I / 32),
                   int64_t(BN) * (2 * I / 32));
 #pragma unroll
       for (int i = 0; i < kPer; ++i) lq.set_row(i, int64_t(KMajorLoader::row_of_thread(i)) * KU);
-      mainloop_fp8(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     } else {
-      MNMajorLoader<DirectRows> lq;
       lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * H + int64_t(rt.nt) * BN,
                   int64_t(2 * I) * H - int64_t(rt.nt) * BN);
       lq.fn.ld = H;
       lq.fn.nrows = 2 * I;
       lq.prime(0);
-      mainloop<false, true>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     }
-    store_tile(acc, lds, out, H, rt.row0, int64_t(rt.nt) * BN, rt.rows, BN);
-  }
+  };
+  auto epi = [&](const TileState& st, const Acc& acc) {
+    store_tile(acc, lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN);
+  };
+  row_tile_walk<FP8, !FP8, true>(total, KU / 64, lds, lp, lq, setup, epi);
 }
 
 // ================================================================== weight gradients

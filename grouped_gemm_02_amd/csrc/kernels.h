@@ -84,9 +84,10 @@ constexpr int kRuleMx = 1;    // 2^(floor(log2 amax) - 8)
 // bf16 [rows, K] -> E4M3 codes [rows, K] + E8M0 scales [rows, K/32]; block 32 or 128
 hipError_t launch_quant_rows(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
                              int block, int rule, hipStream_t st, KernelTimer* timer, const char* name);
-// bf16 W [E, R, C] in 128x128 tiles -> codes [E, R, C] (or [E, C, R] when transpose) with scales
-// per (output row, 32-block); blockwise rule: one exponent per tile, MX rule: per 32 values
-hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* codes, uint8_t* scales,
-                                int transpose, int rule, hipStream_t st, KernelTimer* timer);
+// bf16 W [E, R, C] in 128x128 tiles -> plain codes [E, R, C] and/or transposed codes [E, C, R]
+// (either output may be null), each with scales per (output row, 32-block); blockwise rule: one
+// exponent per tile, MX rule: per 32 values of an output row
+hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* pcodes, uint8_t* pscales,
+                                uint8_t* tcodes, uint8_t* tscales, int rule, hipStream_t st, KernelTimer* timer);
 
 }  // namespace moe

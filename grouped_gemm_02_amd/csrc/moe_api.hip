@@ -298,20 +298,14 @@ moe_status moe_quantize_weights(const moe_shape* s, const void* W13, const void*
   hipStream_t hs = static_cast<hipStream_t>(stream);
   std::lock_guard<std::mutex> lk(g_timer_mu);
   KernelTimer* tm = timer();
-  hipError_t e = hipSuccess;
-  if (fp8_forward(*s)) {
-    if ((e = launch_quant_weights(w13, s->E, 2 * I, H, at<uint8_t>(wq, L.w13), at<uint8_t>(wq, L.w13_scale), 0,
-                                  rule, hs, tm)) != hipSuccess)
-      return MOE_ERR_LAUNCH;
-    if ((e = launch_quant_weights(w2, s->E, H, I, at<uint8_t>(wq, L.w2), at<uint8_t>(wq, L.w2_scale), 0, rule, hs,
-                                  tm)) != hipSuccess)
-      return MOE_ERR_LAUNCH;
-  }
-  if ((e = launch_quant_weights(w2, s->E, H, I, at<uint8_t>(wq, L.w2t), at<uint8_t>(wq, L.w2t_scale), 1, rule, hs,
-                                tm)) != hipSuccess)
-    return MOE_ERR_LAUNCH;
-  e = launch_quant_weights(w13, s->E, 2 * I, H, at<uint8_t>(wq, L.w13t), at<uint8_t>(wq, L.w13t_scale), 1, rule, hs,
-                           tm);
+  const bool fwd = fp8_forward(*s);
+  hipError_t e = launch_quant_weights(w13, s->E, 2 * I, H, fwd ? at<uint8_t>(wq, L.w13) : nullptr,
+                                      fwd ? at<uint8_t>(wq, L.w13_scale) : nullptr, at<uint8_t>(wq, L.w13t),
+                                      at<uint8_t>(wq, L.w13t_scale), rule, hs, tm);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  e = launch_quant_weights(w2, s->E, H, I, fwd ? at<uint8_t>(wq, L.w2) : nullptr,
+                           fwd ? at<uint8_t>(wq, L.w2_scale) : nullptr, at<uint8_t>(wq, L.w2t),
+                           at<uint8_t>(wq, L.w2t_scale), rule, hs, tm);
   return launch_status(e);
 }
 

@@ -126,79 +126,131 @@ hipError_t launch_quant_rows(const uint16_t* in, int64_t rows, int K, uint8_t* c
 }
 
 // ---------------------------------------------------------------- weights
-// One workgroup per 128 x 128 tile (e, rb, cb) of a stack of matrices
-// W [E, R, C] (bf16). Output orientation: transpose = 0 writes codes
-// [E, R, C] with scales [E, R, C/32]; transpose = 1 writes the transposed
-// matrix codes [E, C, R] with scales [E, C, R/32]. Blockwise: one exponent
-// for the whole tile. MX: one exponent per 32 consecutive values of an
-// output row.
+// One workgroup (256 threads) per 128 x 128 tile (e, rb, cb) of a stack of
+// matrices W [E, R, C] (bf16); it reads the tile once and writes either or
+// both of
+//   plain:      codes [E, R, C] with scales [E, R, C/32]
+//   transposed: codes [E, C, R] with scales [E, C, R/32]
+// Blockwise rule: one exponent for the whole tile. MX rule: one exponent per
+// 32 consecutive values of an output row.
+//
+// Thread t loads 16-byte pieces (8 values) of rows t/16 + 16*i, column
+// chunk t % 16; the plain output is encoded from those registers (a 32-block
+// is the 4 pieces of lanes 4j .. 4j+3). The transposed output is read back
+// from a bf16 LDS copy: thread t takes source columns 2p, 2p+1 (p = t / 4)
+// and rows 32q .. 32q+31 (q = t % 4), one 32-bit LDS word (two columns) per
+// row, and writes 32 codes to each of its two output rows; lanes 4p .. 4p+3
+// thus fill 128 contiguous bytes of an output row.
+constexpr int kQLds = 128 + 2;  // bf16 per LDS row: an odd number of words keeps column reads 2-way at most
+
+__device__ __forceinline__ uint32_t pack4_codes(const float* v, int e) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w |= e4m3_code(scale_down(v[q], e)) << (8 * q);
+  return w;
+}
+
 __global__ __launch_bounds__(256) void quant_weight_tiles_kernel(const uint16_t* __restrict__ W, int R, int C,
-                                                                 uint8_t* __restrict__ codes,
-                                                                 uint8_t* __restrict__ scales, int transpose,
-                                                                 int rule) {
-  __shared__ float tile[128][129];
-  __shared__ float red[256];
+                                                                 uint8_t* __restrict__ pcodes,
+                                                                 uint8_t* __restrict__ pscales,
+                                                                 uint8_t* __restrict__ tcodes,
+                                                                 uint8_t* __restrict__ tscales, int rule) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kQLds];
+  __shared__ float red[4];
+  const int t = threadIdx.x;
   const int cbn = C / 128, rbn = R / 128;
   const int cb = blockIdx.x % cbn;
   const int rb = (blockIdx.x / cbn) % rbn;
   const int64_t e = blockIdx.x / (int64_t(cbn) * rbn);
   const uint16_t* src = W + (e * R + int64_t(rb) * 128) * C + int64_t(cb) * 128;
-  // load: thread t reads 8 values of row (t / 16) + 16 i
+  const int c8 = (t & 15) * 8;
+  u32x4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const u32x4*>(src + int64_t((t >> 4) + 16 * i) * C + c8);
   float amax = 0.f;
+#pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = (threadIdx.x >> 4) + 16 * i, c = (threadIdx.x & 15) * 8;
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + int64_t(r) * C + c);
+    const int r = (t >> 4) + 16 * i;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      tile[r][c + 2 * d] = bf16_lo(raw[d]);
-      tile[r][c + 2 * d + 1] = bf16_hi(raw[d]);
-      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[d])), fabsf(bf16_hi(raw[d]))));
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[i][d])), fabsf(bf16_hi(raw[i][d]))));
+      *reinterpret_cast<uint32_t*>(tile + r * kQLds + c8 + 2 * d) = raw[i][d];
     }
   }
-  red[threadIdx.x] = amax;
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-    __syncthreads();
+  const float tile_amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int tile_e = clamp_exp(block_exponent(tile_amax, rule));
+
+  if (pcodes) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        v[2 * d] = bf16_lo(raw[i][d]);
+        v[2 * d + 1] = bf16_hi(raw[i][d]);
+      }
+      int ex = tile_e;
+      if (rule == kRuleMx) {
+        float m = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        ex = clamp_exp(block_exponent(m, rule));
+      }
+      const int64_t orow = e * R + int64_t(rb) * 128 + (t >> 4) + 16 * i;
+      *reinterpret_cast<u32x2*>(pcodes + orow * C + int64_t(cb) * 128 + c8) = u32x2{pack4_codes(v, ex), pack4_codes(v + 4, ex)};
+      if ((t & 3) == 0) pscales[orow * (C / 32) + cb * 4 + ((t & 15) >> 2)] = uint8_t(ex + 127);
+    }
   }
-  const float tile_amax = red[0];
-  // output: 128 rows of 128 codes; thread t writes 32-value segments
-  // (out row o = t / 2 (+128 / 2 per pass), segment (t % 2) * 2 + pass)
-  const int orows_total = transpose ? C : R;
-  const int olen = transpose ? R : C;
-  const int64_t orow0 = e * orows_total + (transpose ? int64_t(cb) * 128 : int64_t(rb) * 128);
-  const int ocol0 = transpose ? rb * 128 : cb * 128;
-  for (int seg = threadIdx.x; seg < 128 * 4; seg += 256) {
-    const int o = seg >> 2, part = seg & 3;
-    float v[32];
-    float smax = 0.f;
+  if (tcodes) {
+    const int pc = (t >> 2) * 2;  // source columns pc, pc + 1
+    const int q = t & 3;          // source rows 32q .. 32q + 31
+    float v0[32], v1[32];
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      v[q] = transpose ? tile[part * 32 + q][o] : tile[o][part * 32 + q];
-      smax = fmaxf(smax, fabsf(v[q]));
+    for (int r = 0; r < 32; ++r) {
+      const uint32_t w2 = *reinterpret_cast<const uint32_t*>(tile + (32 * q + r) * kQLds + pc);
+      v0[r] = bf16_lo(w2);
+      v1[r] = bf16_hi(w2);
     }
-    const int ex = clamp_exp(block_exponent(rule == kRuleMx ? smax : tile_amax, rule));
-    uint32_t w[8];
+    int e0 = tile_e, e1 = tile_e;
+    if (rule == kRuleMx) {
+      float m0 = 0.f, m1 = 0.f;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      w[d] = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) w[d] |= e4m3_code(scale_down(v[4 * d + q], ex)) << (8 * q);
+      for (int r = 0; r < 32; ++r) {
+        m0 = fmaxf(m0, fabsf(v0[r]));
+        m1 = fmaxf(m1, fabsf(v1[r]));
+      }
+      e0 = clamp_exp(block_exponent(m0, rule));
+      e1 = clamp_exp(block_exponent(m1, rule));
     }
-    uint8_t* dst = codes + (orow0 + o) * olen + ocol0 + part * 32;
-    *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<u32x4*>(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
-    scales[(orow0 + o) * (olen / 32) + ocol0 / 32 + part] = uint8_t(ex + 127);
+    const int64_t orow = e * C + int64_t(cb) * 128 + pc;  // output rows are source columns
+    const int64_t ocol = int64_t(rb) * 128 + 32 * q;
+    uint8_t* d0 = tcodes + orow * R + ocol;
+    uint8_t* d1 = d0 + R;
+    *reinterpret_cast<u32x4*>(d0) = u32x4{pack4_codes(v0, e0), pack4_codes(v0 + 4, e0), pack4_codes(v0 + 8, e0),
+                                          pack4_codes(v0 + 12, e0)};
+    *reinterpret_cast<u32x4*>(d0 + 16) = u32x4{pack4_codes(v0 + 16, e0), pack4_codes(v0 + 20, e0),
+                                               pack4_codes(v0 + 24, e0), pack4_codes(v0 + 28, e0)};
+    *reinterpret_cast<u32x4*>(d1) = u32x4{pack4_codes(v1, e1), pack4_codes(v1 + 4, e1), pack4_codes(v1 + 8, e1),
+                                          pack4_codes(v1 + 12, e1)};
+    *reinterpret_cast<u32x4*>(d1 + 16) = u32x4{pack4_codes(v1 + 16, e1), pack4_codes(v1 + 20, e1),
+                                               pack4_codes(v1 + 24, e1), pack4_codes(v1 + 28, e1)};
+    tscales[orow * (R / 32) + rb * 4 + q] = uint8_t(e0 + 127);
+    tscales[(orow + 1) * (R / 32) + rb * 4 + q] = uint8_t(e1 + 127);
   }
 }
 
-hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* codes, uint8_t* scales,
-                                int transpose, int rule, hipStream_t st, KernelTimer* timer) {
+hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* pcodes, uint8_t* pscales,
+                                uint8_t* tcodes, uint8_t* tscales, int rule, hipStream_t st, KernelTimer* timer) {
   const int64_t tiles = E * (R / 128) * (C / 128);
-  if (tiles <= 0) return hipSuccess;
+  if (tiles <= 0 || (!pcodes && !tcodes)) return hipSuccess;
   TimedLaunch tl(timer, "quant_weights", st);
-  hipLaunchKernelGGL(quant_weight_tiles_kernel, dim3(unsigned(tiles)), dim3(256), 0, st, W, R, C, codes, scales,
-                     transpose, rule);
+  hipLaunchKernelGGL(quant_weight_tiles_kernel, dim3(unsigned(tiles)), dim3(256), 0, st, W, R, C, pcodes, pscales,
+                     tcodes, tscales, rule);
   return hipGetLastError();
 }
 
