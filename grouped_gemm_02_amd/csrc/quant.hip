@@ -75,50 +75,60 @@ __device__ __forceinline__ float scale_down(float v, int e) {
 
 // ---------------------------------------------------------------- rows
 // in: bf16 [rows, K]; out codes uint8 [rows, K], scales uint8 [rows, K/32].
-// Thread g handles 8 consecutive values; the threads of one block (4 for 32,
-// 16 for 128) share its maximum through lane shuffles.
+// A work item is 8 consecutive values; the items of one block (4 for 32,
+// 16 for 128) sit in aligned consecutive lanes and share its maximum through
+// lane shuffles. Each thread takes kQItems items spaced one grid apart and
+// issues all their loads before encoding, so enough bytes are in flight.
+constexpr int kQItems = 4;
+
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ in, int64_t rows, int K,
                                                          uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales, int block, int rule) {
   const int per_row = K / 8;
   const int64_t total = rows * per_row;
   const int group = block / 8;  // 4 or 16 lanes, aligned within the wave
-  for (int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; g - threadIdx.x < total;
-       g += int64_t(gridDim.x) * blockDim.x) {
-    const bool live = g < total;
-    const int64_t row = live ? g / per_row : 0;
-    const int c8 = live ? int(g % per_row) : 0;
-    float v[8];
-    float amax = 0.f;
-    if (live) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(in + row * K + c8 * 8);
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t g0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; g0 - threadIdx.x < total;
+       g0 += kQItems * stride) {
+    u32x4 raw[kQItems];
+#pragma unroll
+    for (int u = 0; u < kQItems; ++u) {
+      const int64_t g = g0 + u * stride;
+      raw[u] = g < total ? *reinterpret_cast<const u32x4*>(in + g * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kQItems; ++u) {
+      const int64_t g = g0 + u * stride;
+      float v[8];
+      float amax = 0.f;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        v[2 * d] = bf16_lo(raw[d]);
-        v[2 * d + 1] = bf16_hi(raw[d]);
+        v[2 * d] = bf16_lo(raw[u][d]);
+        v[2 * d + 1] = bf16_hi(raw[u][d]);
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+      for (int off = 1; off < group; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      if (g < total) {
+        const int e = clamp_exp(block_exponent(amax, rule));
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lo |= e4m3_code(scale_down(v[q], e)) << (8 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hi |= e4m3_code(scale_down(v[4 + q], e)) << (8 * q);
+        *reinterpret_cast<u32x2*>(codes + g * 8) = u32x2{lo, hi};
+        if ((g & 3) == 0) scales[g / 4] = uint8_t(e + 127);
+      }
     }
-    for (int off = 1; off < group; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    if (!live) continue;
-    const int e = clamp_exp(block_exponent(amax, rule));
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lo |= e4m3_code(scale_down(v[q], e)) << (8 * q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hi |= e4m3_code(scale_down(v[4 + q], e)) << (8 * q);
-    *reinterpret_cast<u32x2*>(codes + row * K + c8 * 8) = u32x2{lo, hi};
-    if ((c8 & 3) == 0) scales[row * (K / 32) + c8 / 4] = uint8_t(e + 127);
   }
 }
 
 hipError_t launch_quant_rows(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
                              int block, int rule, hipStream_t st, KernelTimer* timer, const char* name) {
   if (rows <= 0) return hipSuccess;
-  const int64_t threads = rows * (K / 8);
-  int64_t grid = (threads + 255) / 256;
-  if (grid > 65536) grid = 65536;
+  const int64_t items = rows * (K / 8);
+  int64_t grid = (items + 256 * kQItems - 1) / (256 * kQItems);
+  if (grid > 16384) grid = 16384;
   TimedLaunch tl(timer, name, st);
   hipLaunchKernelGGL(quant_rows_kernel, dim3(unsigned(grid)), dim3(256), 0, st, in, rows, K, codes, scales,
                      block, rule);
