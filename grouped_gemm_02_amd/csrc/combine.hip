@@ -12,6 +12,11 @@
 // partials of each pair in a fixed order.
 //
 // HBM-bound: per token it reads k rows of H bf16 and writes one row.
+//
+// With k = 1 the down and dX GEMMs write each row straight to its token
+// (the sum has one term, so the result is the same bits); launch_combine is
+// then called with rows == nullptr and only writes the zero rows of dropped
+// tokens and the routing-weight gradients.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -58,11 +63,36 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   }
 }
 
+// k == 1, rows already in out: one thread per token zeroes the row of a
+// dropped token and sums its routing-weight-gradient partials.
+__global__ __launch_bounds__(kCombThreads) void top1_finish_kernel(const int32_t* __restrict__ row_of, int64_t T,
+                                                                   int H, uint16_t* __restrict__ out,
+                                                                   const float* __restrict__ dwpart, int nparts,
+                                                                   float* __restrict__ d_topk_w) {
+  const int64_t t = int64_t(blockIdx.x) * kCombThreads + threadIdx.x;
+  if (t >= T) return;
+  const int32_t r = row_of[t];
+  if (r < 0) {
+    for (int c0 = 0; c0 < H; c0 += 8) *reinterpret_cast<u32x4*>(out + t * H + c0) = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (dwpart != nullptr) {
+    float s = 0.f;
+    if (r >= 0)
+      for (int c = 0; c < nparts; ++c) s += dwpart[int64_t(r) * nparts + c];
+    d_topk_w[t] = s;
+  }
+}
+
 hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of, int64_t T, int k, int64_t H,
                           uint16_t* out, const float* dwpart, int nparts, float* d_topk_w,
                           hipStream_t st, KernelTimer* timer, const char* name) {
   if (T <= 0) return hipSuccess;
   TimedLaunch tl(timer, name, st);
+  if (rows == nullptr) {  // k == 1: see top1_finish_kernel
+    hipLaunchKernelGGL(top1_finish_kernel, dim3(unsigned((T + kCombThreads - 1) / kCombThreads)),
+                       dim3(kCombThreads), 0, st, row_of, T, int(H), out, dwpart, nparts, d_topk_w);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned(T)), dim3(kCombThreads), 0, st, rows, row_of, k,
                      int(H), out, dwpart, nparts, d_topk_w);
   return hipGetLastError();

@@ -444,6 +444,7 @@ __device__ __forceinline__ void stage_half(const Acc& acc, float* F, int half) {
 
 // Plain bf16 store of the tile into a row-major [*, ld] output starting at
 // (row0, col0); rows beyond `rows` and columns beyond `cols` are not written.
+// With a row map, tile row m goes to output row rowmap[row0 + m] instead.
 // Every wave rounds its accumulators to bf16 (round to nearest even, as the
 // output would be) into a [256][256 + 8] LDS image (8-byte writes, two per
 // bank pair at most); then thread t copies 16-byte pieces (column chunk
@@ -452,7 +453,11 @@ constexpr int LDT = BN + 8;
 static_assert(BM * LDT <= 2 * kStageLds, "bf16 tile image must fit in the operand LDS");
 
 __device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* lds, uint16_t* out, int64_t ld,
-                                           int64_t row0, int64_t col0, int rows, int cols) {
+                                           int64_t row0, int64_t col0, int rows, int cols,
+                                           const int32_t* rowmap = nullptr) {
+  __shared__ int32_t s_map[BM];
+  // the row map's loads overlap the image writes
+  if (rowmap && int(threadIdx.x) < rows) s_map[threadIdx.x] = rowmap[row0 + threadIdx.x];
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int m = lane_row(tm);
@@ -468,8 +473,10 @@ __device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* lds, uint16
   __syncthreads();
   const int c = (threadIdx.x & 31) * 8;
   if (c < cols) {
-    for (int m = threadIdx.x >> 5; m < rows; m += kThreads / 32)
-      *reinterpret_cast<u32x4*>(out + (row0 + m) * ld + col0 + c) = *reinterpret_cast<const u32x4*>(lds + m * LDT + c);
+    for (int m = threadIdx.x >> 5; m < rows; m += kThreads / 32) {
+      const int64_t orow = rowmap ? int64_t(s_map[m]) : row0 + m;
+      *reinterpret_cast<u32x4*>(out + orow * ld + col0 + c) = *reinterpret_cast<const u32x4*>(lds + m * LDT + c);
+    }
   }
   __syncthreads();
 }
@@ -731,8 +738,10 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
       lq.set_row(i, int64_t(m) * KU);
     }
   };
+  // k == 1: each row is its token's whole result, written to the token row
+  const int32_t* rowmap = p.k == 1 ? p.src_of : nullptr;
   auto epi = [&](const TileState& st, const Acc& acc) {
-    store_tile(acc, lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN);
+    store_tile(acc, lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap);
   };
   row_tile_walk<FP8, false, true>(total, KU / 64, lds, lp, lq, setup, epi);
 }
@@ -923,8 +932,10 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
       lq.prime(0);
     }
   };
+  // k == 1: each row is its token's whole result, written to the token row
+  const int32_t* rowmap = p.k == 1 ? p.src_of : nullptr;
   auto epi = [&](const TileState& st, const Acc& acc) {
-    store_tile(acc, lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN);
+    store_tile(acc, lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap);
   };
   row_tile_walk<FP8, !FP8, true>(total, KU / 64, lds, lp, lq, setup, epi);
 }

@@ -38,6 +38,8 @@ hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
 // ---------------------------------------------------------------- combine
 // y[t] = sum_j rows[row_of[t*k+j]]  (bf16 rows of width H, fp32 sum, ascending j)
 // and, when dwpart != nullptr, d_topk_w[f] = sum_c dwpart[row_of[f]*nparts + c].
+// rows == nullptr (k == 1 only): the rows are already in y; zero the rows of
+// dropped tokens and reduce d_topk_w.
 hipError_t launch_combine(const uint16_t* rows, const int32_t* row_of, int64_t T, int k, int64_t H,
                           uint16_t* out, const float* dwpart, int nparts, float* d_topk_w,
                           hipStream_t st, KernelTimer* timer, const char* name);

@@ -384,8 +384,12 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
       return MOE_ERR_LAUNCH;
     ga = GemmOperand{aq, as};
   }
-  if ((e = launch_gemm2(gp, ga, gw2, rows, hs, tm)) != hipSuccess) return MOE_ERR_LAUNCH;
-  e = launch_combine(rows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(y), nullptr, 0,
+  // top-1: the down GEMM writes y's rows directly; the combine only zeroes
+  // the rows of dropped tokens
+  const bool direct = s->k == 1;
+  if ((e = launch_gemm2(gp, ga, gw2, direct ? static_cast<uint16_t*>(y) : rows, hs, tm)) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  e = launch_combine(direct ? nullptr : rows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(y), nullptr, 0,
                      nullptr, hs, tm, "combine_y");
   return launch_status(e);
 }
@@ -453,8 +457,10 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
         return MOE_ERR_LAUNCH;
       gdh = GemmOperand{dhq, dhs};
     }
-    if ((e = launch_gemm_dx(gp, gdh, gw13, dxrows, hs, tm)) != hipSuccess) return MOE_ERR_LAUNCH;
-    if ((e = launch_combine(dxrows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(dx), dwpart,
+    const bool direct = s->k == 1;  // top-1: dX rows go straight to dx
+    if ((e = launch_gemm_dx(gp, gdh, gw13, direct ? static_cast<uint16_t*>(dx) : dxrows, hs, tm)) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    if ((e = launch_combine(direct ? nullptr : dxrows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(dx), dwpart,
                             dh_num_parts(s->I), d_topk_w, hs, tm, "combine_dx_dw")) != hipSuccess)
       return MOE_ERR_LAUNCH;
   }

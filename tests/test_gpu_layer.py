@@ -152,6 +152,24 @@ def test_invalid_expert_ids_are_dropped_and_reported(B):
     assert dw[3, 1] == 0 and dw[17, 0] == 0 and dw[199, 1] == 0
 
 
+def test_invalid_expert_ids_top1(B):
+    """Top-1 rows are written straight to their tokens; dropped tokens must
+    still come out as zero rows of y and dx."""
+    cfg = inputs.LayerConfig("invalid_ids_top1", 300, 256, 128, 6, 1, "uniform", "bf16", 17)
+    _say(f"case {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    idx = d["topk_idx"].clone()
+    idx[0, 0] = 6
+    idx[150, 0] = -3
+    idx[299, 0] = 1 << 30
+    d["topk_idx"] = idx
+    out = run_layer(B, cfg, d)
+    assert out["status"] == 8
+    check_full(out, cfg, d)
+    for t in (0, 150, 299):
+        assert not out["y"][t].any() and not out["dx"][t].any() and out["dw"][t, 0] == 0
+
+
 def test_zero_tokens_gives_zero_weight_grads(B):
     cfg = inputs.LayerConfig("empty", 0, 256, 128, 4, 2, "uniform", "bf16", 16)
     d = inputs.make_layer_inputs(cfg, DEV)
