@@ -452,11 +452,12 @@ __device__ __forceinline__ void stage_half(const Acc& acc, float* F, int half) {
 constexpr int LDT = BN + 8;
 static_assert(BM * LDT <= 2 * kStageLds, "bf16 tile image must fit in the operand LDS");
 
-__device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* lds, uint16_t* out, int64_t ld,
-                                           int64_t row0, int64_t col0, int rows, int cols,
-                                           const int32_t* rowmap = nullptr) {
-  __shared__ int32_t s_map[BM];
-  // the row map's loads overlap the image writes
+// store_tile in two halves: stage_image writes the bf16 image (and loads the
+// row map, so its latency overlaps the image writes) and waits; copy_image
+// writes the image out and waits. Callers may issue other loads between the
+// two, so that their waits do not include the image's stores.
+__device__ __forceinline__ void stage_image(const Acc& acc, uint16_t* lds, int64_t row0, int rows,
+                                            const int32_t* rowmap, int32_t* s_map) {
   if (rowmap && int(threadIdx.x) < rows) s_map[threadIdx.x] = rowmap[row0 + threadIdx.x];
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
@@ -471,6 +472,11 @@ __device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* lds, uint16
       }
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ void copy_image(const uint16_t* lds, uint16_t* out, int64_t ld, int64_t row0,
+                                           int64_t col0, int rows, int cols, const int32_t* rowmap,
+                                           const int32_t* s_map) {
   const int c = (threadIdx.x & 31) * 8;
   if (c < cols) {
     for (int m = threadIdx.x >> 5; m < rows; m += kThreads / 32) {
@@ -479,6 +485,12 @@ __device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* lds, uint16
     }
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* lds, uint16_t* out, int64_t ld,
+                                           int64_t row0, int64_t col0, int rows, int cols) {
+  stage_image(acc, lds, row0, rows, nullptr, nullptr);
+  copy_image(lds, out, ld, row0, col0, rows, cols, nullptr, nullptr);
 }
 
 // ------------------------------------------------------------------ scheduling
@@ -740,8 +752,13 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
   };
   // k == 1: each row is its token's whole result, written to the token row
   const int32_t* rowmap = p.k == 1 ? p.src_of : nullptr;
+  __shared__ int32_t s_map[BM];
+  auto copy = [&](const TileState& st) {
+    copy_image(lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap, s_map);
+  };
   auto epi = [&](const TileState& st, const Acc& acc) {
-    store_tile(acc, lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap);
+    stage_image(acc, lds, st.rt.row0, st.rt.rows, rowmap, s_map);
+    copy(st);
   };
   row_tile_walk<FP8, false, true>(total, KU / 64, lds, lp, lq, setup, epi);
 }
@@ -934,8 +951,13 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
   };
   // k == 1: each row is its token's whole result, written to the token row
   const int32_t* rowmap = p.k == 1 ? p.src_of : nullptr;
+  __shared__ int32_t s_map[BM];
+  auto copy = [&](const TileState& st) {
+    copy_image(lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap, s_map);
+  };
   auto epi = [&](const TileState& st, const Acc& acc) {
-    store_tile(acc, lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap);
+    stage_image(acc, lds, st.rt.row0, st.rt.rows, rowmap, s_map);
+    copy(st);
   };
   row_tile_walk<FP8, !FP8, true>(total, KU / 64, lds, lp, lq, setup, epi);
 }
