@@ -24,8 +24,8 @@
 namespace moe {
 
 constexpr int kPermThreads = 256;
-constexpr int kPermItems = 16;
-constexpr int kChunk = kPermThreads * kPermItems;  // 4096 pairs per workgroup
+constexpr int kPermItems = 4;
+constexpr int kChunk = kPermThreads * kPermItems;  // 1024 pairs per workgroup
 constexpr int kPermWaves = kPermThreads / kWave;
 
 __global__ __launch_bounds__(kPermThreads) void permute_hist(const int32_t* __restrict__ idx,
@@ -50,24 +50,35 @@ __global__ __launch_bounds__(kPermThreads) void permute_hist(const int32_t* __re
 
 // One workgroup of 1024 threads. chunk_hist [nchunk][E+1] is turned in place
 // into each chunk's first row per expert; counts/offsets written; status word
-// set when any id was out of range.
+// set when any id was out of range. The chunk axis is cut into S segments so
+// that S*(E+1) threads share the per-expert running sums: pass 1 sums each
+// segment, the segment prefixes and expert offsets follow in LDS, pass 2
+// rewrites each segment's chunks as running starts.
 __global__ __launch_bounds__(1024) void permute_scan(int32_t* __restrict__ chunk_hist, int nchunk,
                                                      int E, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ status) {
+  __shared__ int32_t seg[1025];  // [S][E+1] segment sums (S * (E+1) <= 1025)
   __shared__ int32_t tot[1025];
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
-  // per-expert running sums over chunks (column E = invalid ids)
-  for (int e = tid; e <= E; e += 1024) {
+  const int W = E + 1;                      // columns (column E = invalid ids)
+  const int S = max(1, 1024 / W);           // segments of the chunk axis
+  const int cps = (nchunk + S - 1) / S;     // chunks per segment
+  // work item w = sg * W + e: segment sg of column e (E = 1024 gives one
+  // segment and 1025 items, so thread 0 also takes item 1024)
+  for (int w = tid; w < S * W; w += 1024) {
+    const int e = w % W, sg = w / W;
+    const int c0 = min(nchunk, sg * cps), c1 = min(nchunk, c0 + cps);
+    int32_t sum = 0;
+    for (int c = c0; c < c1; ++c) sum += chunk_hist[int64_t(c) * W + e];
+    seg[w] = sum;
+  }
+  __syncthreads();
+  for (int x = tid; x < W; x += 1024) {
     int32_t run = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      int32_t* p = chunk_hist + int64_t(c) * (E + 1) + e;
-      const int32_t v = *p;
-      *p = run;
-      run += v;
-    }
-    tot[e] = run;
+    for (int q = 0; q < S; ++q) run += seg[q * W + x];
+    tot[x] = run;
   }
   __syncthreads();
   // exclusive scan of tot[0..E) (E <= 1024): Hillis-Steele on a copy
@@ -84,14 +95,23 @@ __global__ __launch_bounds__(1024) void permute_scan(int32_t* __restrict__ chunk
   if (tid < E) {
     counts[tid] = v;
     offsets[tid] = excl;
+    tot[tid] = excl;  // reused below as the expert's first row
   }
   if (tid == E - 1) offsets[E] = part[tid];
   if (tid == 0) status[0] = tot[E] > 0 ? 8 /* MOE_ERR_ROUTING */ : 0;
   __syncthreads();
-  // add each expert's offset to its per-chunk starts
-  for (int e = tid; e < E; e += 1024) {
-    const int32_t o = offsets[e];
-    for (int c = 0; c < nchunk; ++c) chunk_hist[int64_t(c) * (E + 1) + e] += o;
+  for (int w = tid; w < S * W; w += 1024) {
+    const int e = w % W, sg = w / W;
+    if (e == E) continue;
+    const int c0 = min(nchunk, sg * cps), c1 = min(nchunk, c0 + cps);
+    int32_t run = tot[e];
+    for (int q = 0; q < sg; ++q) run += seg[q * W + e];
+    for (int c = c0; c < c1; ++c) {
+      int32_t* p = chunk_hist + int64_t(c) * W + e;
+      const int32_t x = *p;
+      *p = run;
+      run += x;
+    }
   }
 }
 

@@ -41,12 +41,15 @@ CASES = [
     # (T, k, E, routing, seed)
     (1, 1, 1, "uniform", 0),
     (50, 2, 8, "uniform", 1),
-    (2048, 2, 8, "uniform", 2),      # exactly one chunk of 4096 pairs
-    (4097, 1, 3, "uniform", 3),      # one pair past a chunk
+    (512, 2, 8, "uniform", 2),       # exactly one chunk of 1024 pairs
+    (1025, 1, 3, "uniform", 3),      # one pair past a chunk
+    (4097, 1, 3, "uniform", 3),      # one pair past four chunks
+    (12800, 4, 300, "uniform", 8),   # 50 chunks over 3 scan segments
     (16384, 8, 128, "uniform", 4),   # 30B shape
     (16384, 8, 128, "zipf", 5),      # empty experts, one hot expert
     (131072, 1, 16, "uniform", 6),   # EP=8 share shape
     (3000, 4, 1024, "uniform", 7),   # the largest expert count
+    (16384, 8, 1024, "zipf", 9),     # 128 chunks, one scan segment
 ]
 
 
