@@ -38,6 +38,22 @@ GEMM_FLOP_FACTOR = {
     "gemm1_swiglu": 4, "gemm2": 2, "gemm_dh_dswiglu": 2, "gemm_dx": 4, "gemm_dw13": 4, "gemm_dw2": 2,
 }
 GEMM_FLOP_FACTOR.update({k + "_fp8": v for k, v in list(GEMM_FLOP_FACTOR.items()) if not k.startswith("gemm_dw")})
+
+
+def hbm_bytes(name: str, cfg) -> float | None:
+    """Algorithmic HBM bytes of one launch of an HBM-bound kernel (each input
+    read once, each output written once), or None."""
+    T, H, I, k, M = cfg.T, cfg.H, cfg.I, cfg.k, cfg.M
+    nparts = 2 * -(-I // 256)
+    if name == "combine_y" and k > 1:
+        return 2.0 * M * H + 4.0 * T * k + 2.0 * T * H
+    if name == "combine_dx_dw" and k > 1:
+        return 2.0 * M * H + 4.0 * T * k + 2.0 * T * H + 4.0 * M * nparts + 4.0 * T * k
+
+    def quant(rows, K):  # bf16 in, E4M3 codes + one E8M0 byte per 32 out
+        return rows * K * (2.0 + 1.0 + 1.0 / 32)
+    return {"quant_x": lambda: quant(T, H), "quant_dy": lambda: quant(T, H),
+            "quant_act": lambda: quant(M, I), "quant_dh13": lambda: quant(M, 2 * I)}.get(name, lambda: None)()
 WORKLOADS = {
     "tiny": "tiny MoE layer",
     "qwen3_30b": "Qwen3-30B-A3B-shaped MoE layer fwd+bwd",
@@ -193,6 +209,14 @@ def main():
     torch.cuda.synchronize()
     calib_out = calib.clone()
     torch.cuda.synchronize()
+    # the same copy timed (the measured HBM ceiling of a plain stream)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(3):
+        calib_out.copy_(calib)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 2.0 * COPY_CALIB_BYTES / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del calib, calib_out
 
     for _ in range(args.warmup):
@@ -231,6 +255,10 @@ def main():
         if name in GEMM_FLOP_FACTOR:
             ent["tflops"] = round(GEMM_FLOP_FACTOR[name] * MHI / (avg * 1e-3) / 1e12, 1)
             ent["frac_of_peak"] = round(ent["tflops"] / kernel_peak(name), 4)
+        nb = hbm_bytes(name, cfg)
+        if nb is not None:
+            ent["gbps"] = round(nb / (avg * 1e-3) / 1e9, 1)
+            ent["frac_of_hbm_peak"] = round(ent["gbps"] / PEAK_HBM_GBS, 4)
         kernels[name] = ent
     gemm_names = [n for n in kernels if n in GEMM_FLOP_FACTOR]
     dom = max(gemm_names, key=lambda n: kernels[n]["ms_per_step"])
@@ -263,6 +291,7 @@ def main():
         "ms_per_step_excl_weight_quant": round(ms_step - sum(wq_ms) / len(wq_ms), 4),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "gemm_tflops": round((flops) / (gemm_ms * 1e-3) / 1e12, 1),
+        "hbm_copy_gbps": round(copy_gbs, 1),
         "wall_s": round(wall, 3),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": kernel_peak(dom),

@@ -20,27 +20,6 @@
 
 namespace moe {
 
-// E4M3 code of v (round to nearest even, saturate at 448, zero unsigned).
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t s = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (!(a < 448.f)) {
-    code = 0x7Eu;                                      // also catches NaN
-  } else if (a < 0.015625f) {                          // below 2^-6: subnormal grid 2^-9
-    code = uint32_t(__builtin_rintf(a * 512.f));       // exact product, ties to even
-  } else {
-    const uint32_t ua = __float_as_uint(a);
-    const uint32_t q = (ua >> 23) & 0xFFu;             // biased fp32 exponent, 121..135
-    const uint32_t keep = (ua >> 20) & 0x7u;
-    const uint32_t rem = ua & 0xFFFFFu;
-    code = ((q - 120u) << 3) | keep;                   // E4M3 exponent bias 7
-    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) code += 1u;
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return code == 0u ? 0u : (code | s);
-}
-
 // floor(log2 a) for a > 0 (exact, subnormals included)
 __device__ __forceinline__ int floor_log2(float a) {
   uint32_t u = __float_as_uint(a);
@@ -71,6 +50,26 @@ __device__ __forceinline__ int clamp_exp(int e) { return e < -127 ? -127 : (e > 
 __device__ __forceinline__ float scale_down(float v, int e) {
   const int h = -e / 2;
   return v * __builtin_ldexpf(1.f, h) * __builtin_ldexpf(1.f, -e - h);
+}
+
+// The E4M3 codes of v[0..3] / 2^e, one byte each in order. The conversion
+// is the gfx950 instruction v_cvt_pk_fp8_f32 (OCP E4M3, round to nearest
+// even); magnitudes are clamped to 448 first, which is the saturation (a
+// NaN becomes 448 with its sign bit), and a negative zero code (0x80)
+// becomes +0.
+__device__ __forceinline__ uint32_t pack4_codes(const float* v, int e) {
+  float x[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float y = scale_down(v[q], e);
+    x[q] = __builtin_copysignf(__builtin_fminf(__builtin_fabsf(y), 448.f), y);
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+  const uint32_t u = uint32_t(w);
+  const uint32_t t = u ^ 0x80808080u;  // a 0x80 byte becomes 0x00
+  const uint32_t z = ~(((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t | 0x7F7F7F7Fu);  // 0x80 where t's byte is 0
+  return u & ~z;
 }
 
 // ---------------------------------------------------------------- rows
@@ -111,11 +110,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
       for (int off = 1; off < group; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
       if (g < total) {
         const int e = clamp_exp(block_exponent(amax, rule));
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) lo |= e4m3_code(scale_down(v[q], e)) << (8 * q);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hi |= e4m3_code(scale_down(v[4 + q], e)) << (8 * q);
+        const uint32_t lo = pack4_codes(v, e), hi = pack4_codes(v + 4, e);
         *reinterpret_cast<u32x2*>(codes + g * 8) = u32x2{lo, hi};
         if ((g & 3) == 0) scales[g / 4] = uint8_t(e + 127);
       }
@@ -153,12 +148,6 @@ hipError_t launch_quant_rows(const uint16_t* in, int64_t rows, int K, uint8_t* c
 // thus fill 128 contiguous bytes of an output row.
 constexpr int kQLds = 128 + 2;  // bf16 per LDS row: an odd number of words keeps column reads 2-way at most
 
-__device__ __forceinline__ uint32_t pack4_codes(const float* v, int e) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) w |= e4m3_code(scale_down(v[q], e)) << (8 * q);
-  return w;
-}
 
 __global__ __launch_bounds__(256) void quant_weight_tiles_kernel(const uint16_t* __restrict__ W, int R, int C,
                                                                  uint8_t* __restrict__ pcodes,
