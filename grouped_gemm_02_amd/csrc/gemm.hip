@@ -714,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
       __syncthreads();
     }
   };
-  row_tile_walk<FP8, false, false>(total, KU / 64, lds, lp, lq, setup, epi);
+  row_tile_walk<FP8, false, true>(total, KU / 64, lds, lp, lq, setup, epi);
 }
 
 // ================================================================== forward GEMM2
