@@ -255,37 +255,76 @@ __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* l
 // mainloop_staged runs the k loop with slab 0 already fetched into sp, sq
 // (the persistent row-tile kernels fetch a tile's first slab during the
 // previous tile's epilogue); mainloop fetches it itself.
-template <bool P_MN, bool Q_MN, class LP, class LQ>
+//
+// With DEFER, fragments are double buffered and the slab's last 16-deep step
+// is deferred past the slab barrier: its fragments are already in registers,
+// so its MFMAs run while the next slab's first fragments are read instead of
+// every wave starting a slab with an LDS wait. On a plain dense GEMM of this
+// core that is ~9 % more MFMA issue; inside the grouped kernels it pays only
+// in the dH GEMM (~4 %) and costs 1-2 % elsewhere, so only dH uses it.
+template <bool P_MN, bool Q_MN, bool DEFER = false, class LP, class LQ>
 __device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc, bool active,
                                                 Stage& sp, Stage& sq) {
+  static_assert(BK / 16 == 4, "the deferred step schedule is written for four 16-deep steps per slab");
   if (nk <= 0) return;
   lp.store(lds, sp);
   lq.store(lds + kOperandLds, sq);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    uint16_t* cur = lds + (kt & 1) * kStageLds;
-    uint16_t* nxt = lds + ((kt + 1) & 1) * kStageLds;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      lp.fetch(kt + 1, sp);
-      lq.fetch(kt + 1, sq);
+  if constexpr (!DEFER) {
+    for (int kt = 0; kt < nk; ++kt) {
+      uint16_t* cur = lds + (kt & 1) * kStageLds;
+      uint16_t* nxt = lds + ((kt + 1) & 1) * kStageLds;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        lp.fetch(kt + 1, sp);
+        lq.fetch(kt + 1, sq);
+      }
+      if (active) mma_slab<P_MN, Q_MN>(cur, cur + kOperandLds, acc);
+      if (more) {
+        lp.store(nxt, sp);
+        lq.store(nxt + kOperandLds, sq);
+      }
+      __syncthreads();
     }
-    if (active) mma_slab<P_MN, Q_MN>(cur, cur + kOperandLds, acc);
-    if (more) {
-      lp.store(nxt, sp);
-      lq.store(nxt + kOperandLds, sq);
+  } else {
+    bf16x8 pf0[TM], qf0[TN], pf1[TM], qf1[TN];
+    if (active) load_frags<P_MN, Q_MN>(lds, lds + kOperandLds, 0, pf0, qf0);
+    for (int kt = 0; kt < nk; ++kt) {
+      uint16_t* cur = lds + (kt & 1) * kStageLds;
+      uint16_t* nxt = lds + ((kt + 1) & 1) * kStageLds;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        lp.fetch(kt + 1, sp);
+        lq.fetch(kt + 1, sq);
+      }
+      if (active) {
+        load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 1, pf1, qf1);
+        mma_step(pf0, qf0, acc);
+        load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 2, pf0, qf0);
+        mma_step(pf1, qf1, acc);
+        load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 3, pf1, qf1);
+        mma_step(pf0, qf0, acc);
+      }
+      if (more) {
+        lp.store(nxt, sp);
+        lq.store(nxt + kOperandLds, sq);
+      }
+      __syncthreads();
+      if (active) {
+        if (more) load_frags<P_MN, Q_MN>(nxt, nxt + kOperandLds, 0, pf0, qf0);
+        mma_step(pf1, qf1, acc);
+      }
     }
-    __syncthreads();
   }
 }
 
-template <bool P_MN, bool Q_MN, class LP, class LQ>
+template <bool P_MN, bool Q_MN, bool DEFER = false, class LP, class LQ>
 __device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc, bool active = true) {
   if (nk <= 0) return;
   Stage sp, sq;
   lp.fetch(0, sp);
   lq.fetch(0, sq);
-  mainloop_staged<P_MN, Q_MN>(lp, lq, nk, lds, acc, active, sp, sq);
+  mainloop_staged<P_MN, Q_MN, DEFER>(lp, lq, nk, lds, acc, active, sp, sq);
 }
 
 // ------------------------------------------------------------------ FP8 core
@@ -839,7 +878,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
       lq.fn.nrows = H;
       lq.nchunks = ncols / 8;
       lq.prime(0);
-      mainloop<false, true>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
+      mainloop<false, true, true>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
     }
     if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
