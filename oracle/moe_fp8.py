@@ -29,8 +29,14 @@ tensors are quantized. The readings used here (listed in the design doc):
   w * silu(g) * u (along I), gate/up and down weights; backward dY (along H)
   and [dg | du] (along 2I), and the weights again for the transposed use
   (blockwise: the same 128x128 blocks; mxfp8: re-blocked along the new
-  reduction axis). The two weight-gradient GEMMs run on the unquantized
-  (bf16) operands.
+  reduction axis).
+* The two weight-gradient GEMMs (reduction over an expert's rows) have two
+  readings, chosen by `wgrad`: "bf16" runs them on the unquantized operands;
+  "fp8" quantizes all four operands (x, [dg | du], dY, w * silu(g) * u)
+  along the expert's rows, column by column, in blocks of 128 rows
+  (blockwise and fp8_bwd, pow2 rule) or 32 rows (mxfp8, MX rule) counted from
+  the expert's first row in permuted order (pairs in ascending flat index);
+  a last partial block is quantized on its own rows.
 * Quantization is applied to the exact (float64) value at each point; the
   result is dequantized (code * 2^e) and the math continues exactly.
 """
@@ -140,6 +146,19 @@ def _act(v, mode):
     return quantize_along_last(v, 128, "pow2_ceil")[2]
 
 
+def _tok(v, mode):
+    """Quantize-dequantize one expert's operand [n, C] along its rows (the
+    weight-gradient GEMM's reduction axis): each column in blocks of 128
+    (32 for mxfp8) consecutive rows from row 0; zero rows pad the last block,
+    which leaves its maximum and its other values unchanged."""
+    block, rule = (32, "mx_floor") if mode == "mxfp8" else (128, "pow2_ceil")
+    v = np.asarray(v, dtype=np.float64)
+    n, c = v.shape
+    vp = np.zeros((-(-n // block) * block, c))
+    vp[:n] = v
+    return quantize_along_last(vp.T, block, rule)[2].T[:n]
+
+
 def _weight(w, mode, reduce_axis_last: bool):
     """Quantize-dequantize a weight matrix stack [E, R, C]; the GEMM reduces
     over its last axis (reduce_axis_last) or over the middle axis."""
@@ -216,11 +235,14 @@ def forward(x, topk_idx, topk_w, W13, W2, mode: str, return_pairs: bool = False,
     return y
 
 
-def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str, wq: dict | None = None):
+def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str, wq: dict | None = None, wgrad: str = "bf16"):
     """Gradients of L = <dY, y> with the backward quantization points of
     `mode`: dY and W2 quantized for the dH product, [dg | du] and W13 for the
-    dX product; the weight gradients use unquantized operands. g and u come
+    dX product; the weight gradients use unquantized operands (wgrad="bf16")
+    or operands quantized along the expert's rows (wgrad="fp8"). g and u come
     from the forward of the same mode."""
+    if wgrad not in ("bf16", "fp8"):
+        raise ValueError(wgrad)
     dy = base.as_f64(dy)
     x = base.as_f64(x)
     W13 = base.as_f64(W13)
@@ -260,8 +282,12 @@ def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str, wq: dict | None = None
         dU = dA * G * S
         dHm = np.concatenate([dG, dU], axis=1)
         np.add.at(dx, t, _act(dHm, mode) @ W13b[e])
-        dW13[e] = dHm.T @ x[t]
-        dW2[e] = dy[t].T @ (wf[f][:, None] * A)
+        if wgrad == "fp8":
+            dW13[e] = _tok(dHm, mode).T @ _tok(x[t], mode)
+            dW2[e] = _tok(dy[t], mode).T @ _tok(wf[f][:, None] * A, mode)
+        else:
+            dW13[e] = dHm.T @ x[t]
+            dW2[e] = dy[t].T @ (wf[f][:, None] * A)
     return dx, dwf.reshape(T, k), dW13, dW2
 
 

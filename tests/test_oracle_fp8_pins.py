@@ -273,3 +273,117 @@ def test_prequantized_weights_give_identical_layer():
         b = f8.backward(d["dy"], *args, mode, wq=wq)
         for u, v in zip(a, b):
             assert np.array_equal(u, v)
+
+
+# ----------------------------------------------------- FP8 weight gradients
+
+def _wgrad_loops(x, idx, w, W13, W2, dy, mode):
+    """dW13, dW2 of the fp8 weight-gradient reading, pair by pair: each
+    expert's rows in ascending pair order, every column quantized in blocks
+    of 128 (32 for mxfp8) consecutive rows with the scalar helpers above."""
+    blk, rule = (32, "mx_floor") if mode == "mxfp8" else (128, "pow2_ceil")
+    T, H = x.shape
+    E = W13.shape[0]
+    I = W13.shape[1] // 2
+    k = idx.shape[1]
+    qa = lambda M: _q_rows(M, 32 if mode == "mxfp8" else 128, rule)  # noqa: E731
+    if mode == "fp8_bwd":
+        xq, W13q = x, W13
+    else:
+        xq, W13q = qa(x), _q_weight(W13, mode, True)
+    W2b = _q_weight(W2, mode, False)
+    dyq = qa(dy)
+    rows = {e: {"dh": [], "x": [], "dy": [], "wa": []} for e in range(E)}
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            g = W13q[e, :I] @ xq[t]
+            u = W13q[e, I:] @ xq[t]
+            sg = 1.0 / (1.0 + np.exp(-g))
+            a = g * sg * u
+            dau = W2b[e].T @ dyq[t]
+            da = w[t, j] * dau
+            rows[e]["dh"].append(np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg]))
+            rows[e]["x"].append(x[t])
+            rows[e]["dy"].append(dy[t])
+            rows[e]["wa"].append(w[t, j] * a)
+
+    def qcols(R):  # quantize each column of R [n, C] in row blocks
+        R = np.array(R)
+        out = np.zeros_like(R)
+        for c in range(R.shape[1]):
+            for s in range(0, R.shape[0], blk):
+                out[s:s + blk, c] = _q_block(list(R[s:s + blk, c]), rule)
+        return out
+    dW13 = np.zeros((E, 2 * I, H))
+    dW2 = np.zeros((E, H, I))
+    for e in range(E):
+        if not rows[e]["x"]:
+            continue
+        dW13[e] = qcols(rows[e]["dh"]).T @ qcols(rows[e]["x"])
+        dW2[e] = qcols(rows[e]["dy"]).T @ qcols(rows[e]["wa"])
+    return dW13, dW2
+
+
+@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8", "fp8_bwd"])
+def test_fp8_weight_gradients_match_pair_loops(mode):
+    """Expert segments of ~200 rows: one full and one partial 128-row block
+    (blockwise), several 32-row blocks (MX)."""
+    rng = np.random.default_rng(8)
+    T, H, I, E, k = 300, 256, 128, 3, 2
+    x = rng.standard_normal((T, H))
+    W13 = rng.standard_normal((E, 2 * I, H)) * 0.05
+    W2 = rng.standard_normal((E, H, I)) * 0.05
+    idx = np.array([rng.choice(E, k, replace=False) for _ in range(T)])
+    w = rng.uniform(0.1, 1.0, size=(T, k))
+    dy = rng.standard_normal((T, H)) * np.exp(rng.standard_normal((T, 1)))  # rows of different scale
+    _, _, dW13, dW2 = f8.backward(dy, x, idx, w, W13, W2, mode, wgrad="fp8")
+    r13, r2 = _wgrad_loops(x, idx, w, W13, W2, dy, mode)
+    np.testing.assert_allclose(dW13, r13, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(dW2, r2, rtol=1e-9, atol=1e-9)
+    # sanity scale, not a pin: quantizing along rows of mixed magnitude costs
+    # percents (more under the MX rule, which saturates the block maximum)
+    _, _, b13, b2 = f8.backward(dy, x, idx, w, W13, W2, mode, wgrad="bf16")
+    for q, b in ((dW13, b13), (dW2, b2)):
+        err = np.max(np.abs(q - b)) / np.max(np.abs(b))
+        assert 0 < err < 0.3, err
+
+
+def test_token_blocks_restart_and_stand_alone():
+    """Row blocks start at the segment's first row: the first 128 rows
+    quantize the same whatever follows, and the partial last block on its
+    own rows; values exactly representable at their block's scale come back
+    unchanged."""
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal((200, 64))
+    v[150, 3] = 1e6                       # only block 1 of column 3 sees it
+    q = f8._tok(v, "fp8_block")
+    assert np.array_equal(q[:128], f8._tok(v[:128], "fp8_block"))
+    assert np.array_equal(q[128:], f8._tok(v[128:], "fp8_block"))
+    qm = f8._tok(v, "mxfp8")
+    for s in range(0, 200, 32):
+        assert np.array_equal(qm[s:s + 32], f8._tok(v[s:s + 32], "mxfp8"))
+    exact = rng.choice([-256.0, -3.0, -0.5, 0.0, 0.25, 1.0, 7.0, 448.0], size=(160, 8))
+    exact[0] = 448.0                      # block maxima 448: scale 2^0
+    exact[128] = 448.0
+    assert np.array_equal(f8._tok(exact, "fp8_block"), exact)
+
+
+@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8"])
+def test_fp8_weight_gradients_are_per_expert(mode):
+    """An expert's weight gradients depend only on its own pairs (what the
+    sampled full-size GPU checks rely on): restricting the problem to one
+    expert's pairs, in order, gives the same bits."""
+    rng = np.random.default_rng(10)
+    T, H, I, E, k = 150, 256, 128, 4, 2
+    x = rng.standard_normal((T, H))
+    W13 = rng.standard_normal((E, 2 * I, H)) * 0.05
+    W2 = rng.standard_normal((E, H, I)) * 0.05
+    idx = np.array([rng.choice(E, k, replace=False) for _ in range(T)])
+    w = rng.uniform(0.1, 1.0, size=(T, k))
+    dy = rng.standard_normal((T, H))
+    _, _, dW13, dW2 = f8.backward(dy, x, idx, w, W13, W2, mode, wgrad="fp8")
+    for e in range(E):
+        f, xe, ie, we, dye = orc.restrict_to_expert(x, idx, w, dy, e)
+        _, _, s13, s2 = f8.backward(dye, xe, ie, we, W13[e:e + 1], W2[e:e + 1], mode, wgrad="fp8")
+        assert np.array_equal(dW13[e], s13[0]) and np.array_equal(dW2[e], s2[0]), e
