@@ -37,7 +37,7 @@ COPY_CALIB_BYTES = 1 << 30   # bytes read (and written) by the calibration copy
 GEMM_FLOP_FACTOR = {
     "gemm1_swiglu": 4, "gemm2": 2, "gemm_dh_dswiglu": 2, "gemm_dx": 4, "gemm_dw13": 4, "gemm_dw2": 2,
 }
-GEMM_FLOP_FACTOR.update({k + "_fp8": v for k, v in list(GEMM_FLOP_FACTOR.items()) if not k.startswith("gemm_dw")})
+GEMM_FLOP_FACTOR.update({k + "_fp8": v for k, v in list(GEMM_FLOP_FACTOR.items())})
 
 
 def hbm_bytes(name: str, cfg) -> float | None:
@@ -53,7 +53,10 @@ def hbm_bytes(name: str, cfg) -> float | None:
     def quant(rows, K):  # bf16 in, E4M3 codes + one E8M0 byte per 32 out
         return rows * K * (2.0 + 1.0 + 1.0 / 32)
     return {"quant_x": lambda: quant(T, H), "quant_dy": lambda: quant(T, H),
-            "quant_act": lambda: quant(M, I), "quant_dh13": lambda: quant(M, 2 * I)}.get(name, lambda: None)()
+            "quant_act": lambda: quant(M, I), "quant_dh13": lambda: quant(M, 2 * I),
+            # along tokens: every routed row read once (gathered for x, dY)
+            "quant_wg_x": lambda: quant(M, H), "quant_wg_dy": lambda: quant(M, H),
+            "quant_wg_dh13": lambda: quant(M, 2 * I), "quant_wg_act": lambda: quant(M, I)}.get(name, lambda: None)()
 WORKLOADS = {
     "tiny": "tiny MoE layer",
     "qwen3_30b": "Qwen3-30B-A3B-shaped MoE layer fwd+bwd",
@@ -102,6 +105,9 @@ def parse():
     ap.add_argument("--config", default="qwen3_30b", choices=sorted(WORKLOADS))
     ap.add_argument("--precision", default=None, choices=["bf16", "fp8_block", "mxfp8", "fp8_bwd"],
                     help="override the configuration's precision")
+    ap.add_argument("--wgrad", default="bf16", choices=["bf16", "fp8"],
+                    help="weight-gradient GEMMs on bf16 operands, or (FP8 precisions) on operands "
+                         "quantized along each expert's rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     return ap.parse_args()
@@ -129,7 +135,7 @@ def cpu_baseline(cfg, d, n_tok):
                       f"forward + backward in float64 numpy; flops counted as 18*tokens*k*H*I"}
 
 
-def cpu_baseline_fp8(cfg, d, n_experts):
+def cpu_baseline_fp8(cfg, d, n_experts, wgrad="bf16"):
     """The CPU oracle's FP8 emulation, as it stands, on the routed pairs of
     the first n_experts experts (other pairs dropped), weight quantization of
     those experts included."""
@@ -150,7 +156,7 @@ def cpu_baseline_fp8(cfg, d, n_experts):
     W2 = d["W2"][:n_experts].cpu()
     t0 = time.perf_counter()
     f8.forward(x, sub_idx, w, W13, W2, cfg.precision)
-    f8.backward(dy, x, sub_idx, w, W13, W2, cfg.precision)
+    f8.backward(dy, x, sub_idx, w, W13, W2, cfg.precision, wgrad=wgrad)
     dt = time.perf_counter() - t0
     flops = 18.0 * pairs * cfg.H * cfg.I
     threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
@@ -177,9 +183,14 @@ def main():
         cfg = cfg.scaled(precision=args.precision)
     WORKLOAD_KEY[0] = f"{cfg.name}/{cfg.precision}"
     fp8 = cfg.precision != "bf16"
+    if args.wgrad == "fp8" and not fp8:
+        print("--wgrad fp8 needs an FP8 precision", file=sys.stderr)
+        sys.exit(2)
+    if args.wgrad == "fp8":
+        WORKLOAD_KEY[0] += "/fp8_wgrad"
     torch.cuda.set_device(0)
     d = inputs.make_layer_inputs(cfg, "cuda")
-    shape = B.make_shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.precision)
+    shape = B.make_shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.precision, wgrad=args.wgrad)
     buf = B.LayerBuffers.allocate(shape)
     grads = (torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda"),
              torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda"),
@@ -282,7 +293,8 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {WORKLOADS[cfg.name]}", "T": cfg.T, "H": cfg.H,
-                   "I": cfg.I, "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "precision": cfg.precision},
+                   "I": cfg.I, "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "precision": cfg.precision,
+                   "wgrad": args.wgrad},
         "fwd_ms": round(sum(fwd_ms) / len(fwd_ms), 4),
         "bwd_ms": round(sum(bwd_ms) / len(bwd_ms), 4),
         "weight_quant_ms": round(sum(wq_ms) / len(wq_ms), 4),
@@ -303,7 +315,7 @@ def main():
             # about 24k routed pairs, at most 8 experts (the emulation also
             # quantizes the sampled experts' weights)
             n_exp = min(8, max(1, -(-cfg.E * 24576 // cfg.M)))
-            out["cpu_baseline"] = cpu_baseline_fp8(cfg, d, n_exp)
+            out["cpu_baseline"] = cpu_baseline_fp8(cfg, d, n_exp, args.wgrad)
         else:
             out["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

@@ -32,10 +32,15 @@ class MoEError(RuntimeError):
         super().__init__(f"{what}: {moe_status_string(status)}")
 
 
+MOE_FLAG_FP8_WGRAD = 1
+WGRADS = {"bf16": 0, "fp8": MOE_FLAG_FP8_WGRAD}
+
+
 class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
                 ("E", ctypes.c_int64), ("k", ctypes.c_int64),
-                ("precision", ctypes.c_int32), ("num_cus", ctypes.c_int32)]
+                ("precision", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class moe_saved_layout(ctypes.Structure):
@@ -64,6 +69,8 @@ _SIGS = {
     "moe_quantize_weights": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P]),
     "moe_quantize_rows": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                          _P]),
+    "moe_quantize_tokens": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, ctypes.c_int64, ctypes.c_int64, _P,
+                                           _P, _P, _P, _P, _P]),
     "moe_permute_scratch_bytes": (ctypes.c_size_t, [ctypes.POINTER(moe_shape)]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P]),
     "moe_fwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -118,9 +125,11 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def make_shape(T, H, I, E, k, precision="bf16", num_cus=0) -> moe_shape:
+def make_shape(T, H, I, E, k, precision="bf16", num_cus=0, wgrad="bf16") -> moe_shape:
+    """wgrad: "bf16" (default) or "fp8" (sets MOE_FLAG_FP8_WGRAD)."""
     p = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
-    return moe_shape(int(T), int(H), int(I), int(E), int(k), p, int(num_cus))
+    f = WGRADS[wgrad] if isinstance(wgrad, str) else int(wgrad)
+    return moe_shape(int(T), int(H), int(I), int(E), int(k), p, int(num_cus), f, 0)
 
 
 # ------------------------------------------------------------ C entry points
@@ -154,6 +163,17 @@ def moe_get_wq_layout(shape: moe_shape) -> dict:
 def moe_quantize_weights(shape, W13, W2, wq, stream=None) -> None:
     _check(lib().moe_quantize_weights(ctypes.byref(shape), _ptr(W13), _ptr(W2), _ptr(wq), _stream(stream)),
            "moe_quantize_weights")
+
+
+def wgrad_rows_cap(shape: moe_shape) -> int:
+    """K of moe_quantize_tokens' buffers: codes C*K bytes, scales C*K/32."""
+    return 128 * (shape.T * shape.k // 128 + shape.E)
+
+
+def moe_quantize_tokens(shape, x, ld, C, counts, offsets, src_of, codes, scales, stream=None) -> None:
+    _check(lib().moe_quantize_tokens(ctypes.byref(shape), _ptr(x), int(ld), int(C), _ptr(counts), _ptr(offsets),
+                                     _ptr(src_of), _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_tokens")
 
 
 def moe_quantize_rows(shape, x, rows, K, codes, scales, stream=None) -> None:

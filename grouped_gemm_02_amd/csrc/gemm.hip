@@ -1148,6 +1148,85 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
 
 // ================================================================== launchers
 
+// ------------------------------------------------------------------ FP8 weight gradients
+// dW[e][m][n] = sum over the expert's rows r of P'[m][r] Q'[n][r], with P'
+// and Q' the operands quantized along the expert's rows (launch_quant_tokens
+// layout: per expert, codes [C][Kp_e] with Kp_e = rows rounded up to 128 and
+// zero codes past the rows, experts packed in order, one scale byte per
+// (column, 32 rows)). Both operands are k-major there, so the tiles run the
+// FP8 k loop of the forward GEMMs over Kp_e / 128 slabs; the schedule is the
+// weight-gradient schedule above. MP % 256 == 0; NQ % 128 == 0 (a last
+// n-tile of 128 columns reuses row NQ - 1 for the rest, never stored).
+
+// s_kb[e] = sum over e' < e of ceil(counts[e'] / 128), e = 0..E (E <= 1024)
+__device__ void block_prefix128(const int32_t* counts, int E, int32_t* s_kb, int32_t* s_tmp) {
+  const int tid = threadIdx.x;
+  int32_t loc[2], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    loc[q] = e < E ? (counts[e] + 127) / 128 : 0;
+    sum += loc[q];
+  }
+  s_tmp[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int32_t add = tid >= off ? s_tmp[tid - off] : 0;
+    __syncthreads();
+    s_tmp[tid] += add;
+    __syncthreads();
+  }
+  int32_t run = s_tmp[tid] - sum;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * tid + q;
+    if (e < E) s_kb[e] = run;
+    run += loc[q];
+  }
+  if (tid == kThreads - 1) s_kb[E] = s_tmp[tid];
+  __syncthreads();
+}
+static_assert(2 * kThreads >= 1024, "block_prefix128 takes two experts per thread");
+
+__global__ __launch_bounds__(kThreads) void gemm_dw_fp8_kernel(GemmProblem p, const uint8_t* __restrict__ pcodes,
+                                                               const uint8_t* __restrict__ pscales, int MP,
+                                                               const uint8_t* __restrict__ qcodes,
+                                                               const uint8_t* __restrict__ qscales, int NQ,
+                                                               uint16_t* __restrict__ dW, int32_t* queue) {
+  MOE_GEMM_SMEM
+  MOE_DW_SMEM
+  __shared__ int32_t s_kb[1025];
+  __shared__ int32_t s_tmp[kThreads];
+  const int E = int(p.E);
+  block_prefix128(p.counts, E, s_kb, s_tmp);
+  const int MT = MP / BM, NT = (NQ + BN - 1) / BN;
+  dw_for_each_tile(p.counts, E, MT * NT, queue, s_cnt, s_order, &s_flag, &s_next, [&](int e, int local) {
+    const int nt = local % NT;
+    const int mt = local / NT;
+    const int kb = __builtin_amdgcn_readfirstlane(s_kb[e + 1] - s_kb[e]);  // 128-row blocks
+    const int64_t poff = int64_t(__builtin_amdgcn_readfirstlane(s_kb[e])) * 128;
+    const int64_t kp = int64_t(kb) * 128;
+    const int KU = int(kp / 2);  // row length in 16-bit units
+    const int ncols = min(BN, NQ - nt * BN);
+    KMajorLoader8 lp, lq;
+    lp.set_base(reinterpret_cast<const uint16_t*>(pcodes + int64_t(MP) * poff + int64_t(mt) * BM * kp),
+                int64_t(BM) * KU, pscales + (int64_t(MP) * poff + int64_t(mt) * BM * kp) / 32, int64_t(BM) * kp / 32);
+    lq.set_base(reinterpret_cast<const uint16_t*>(qcodes + int64_t(NQ) * poff + int64_t(nt) * BN * kp),
+                int64_t(ncols) * KU, qscales + (int64_t(NQ) * poff + int64_t(nt) * BN * kp) / 32,
+                int64_t(ncols) * kp / 32);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int m = KMajorLoader::row_of_thread(i);
+      lp.set_row(i, int64_t(m) * KU);
+      lq.set_row(i, int64_t(min(m, ncols - 1)) * KU);
+    }
+    Acc acc;
+    acc.zero();
+    mainloop_fp8(lp, lq, kb, lds, acc);  // an empty expert runs no slab and stores zeros
+    store_tile(acc, lds, dW + int64_t(e) * MP * NQ, NQ, int64_t(mt) * BM, int64_t(nt) * BN, BM, ncols);
+  });
+}
+
 static int grid_for(int64_t tiles, int num_cus) {
   int64_t g = int64_t(num_cus);  // one 512-thread workgroup per CU (LDS-bound)
   if (tiles < g) g = tiles;
@@ -1236,6 +1315,16 @@ hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint1
   const int grid = grid_for(p.E * (p.H / BM) * ((p.I + BN - 1) / BN), p.num_cus);
   TimedLaunch tl(timer, "gemm_dw2", st);
   hipLaunchKernelGGL(gemm_dw2_kernel, dim3(grid), dim3(kThreads), 0, st, p, dy, act, dW2, queue);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_dw_fp8(const GemmProblem& p, const uint8_t* pcodes, const uint8_t* pscales, int MP,
+                              const uint8_t* qcodes, const uint8_t* qscales, int NQ, uint16_t* dW, int32_t* queue,
+                              hipStream_t st, KernelTimer* timer, const char* name) {
+  const int grid = grid_for(p.E * (MP / BM) * ((NQ + BN - 1) / BN), p.num_cus);
+  TimedLaunch tl(timer, name, st);
+  hipLaunchKernelGGL(gemm_dw_fp8_kernel, dim3(grid), dim3(kThreads), 0, st, p, pcodes, pscales, MP, qcodes, qscales,
+                     NQ, dW, queue);
   return hipGetLastError();
 }
 

@@ -92,4 +92,17 @@ hipError_t launch_quant_rows(const uint16_t* in, int64_t rows, int K, uint8_t* c
 hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* pcodes, uint8_t* pscales,
                                 uint8_t* tcodes, uint8_t* tscales, int rule, hipStream_t st, KernelTimer* timer);
 
+// The FP8 weight-gradient operands: rows of every expert quantized along the
+// rows (codes [C][Kp_e] per expert, Kp_e = rows rounded up to 128, experts
+// packed in order; one scale byte per (column, 32 rows)). src_of == nullptr:
+// expert rows are rows offsets[e] + r of `in`; else token rows src_of[..] / kk.
+hipError_t launch_quant_tokens(const uint16_t* in, int64_t ld, int C, const int32_t* counts, const int32_t* offsets,
+                               int E, int64_t M, const int32_t* src_of, int kk, uint8_t* codes, uint8_t* scales,
+                               int rule, hipStream_t st, KernelTimer* timer, const char* name);
+// FP8 weight gradients from those operands: dW[e] (P rows x Q rows, bf16,
+// row-major [MP][NQ]) = sum over the expert's rows of P'[m][r] Q'[n][r]
+hipError_t launch_gemm_dw_fp8(const GemmProblem& p, const uint8_t* pcodes, const uint8_t* pscales, int MP,
+                              const uint8_t* qcodes, const uint8_t* qscales, int NQ, uint16_t* dW, int32_t* queue,
+                              hipStream_t st, KernelTimer* timer, const char* name);
+
 }  // namespace moe

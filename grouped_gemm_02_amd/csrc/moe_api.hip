@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/moe.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -29,7 +30,13 @@ moe_status check_shape(const moe_shape* s) {
   if (s->T * s->k >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (s->T * s->H >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;  // 32-bit row offsets into x, dY
   if (s->T * s->k * s->I >= (int64_t(1) << 30)) return MOE_ERR_SHAPE;  // 32-bit byte offsets into [g | u] rows
-  if (s->num_cus < 0) return MOE_ERR_SHAPE;
+  if (s->num_cus < 0 || s->reserved != 0) return MOE_ERR_SHAPE;
+  if ((s->flags & ~MOE_FLAG_FP8_WGRAD) != 0) return MOE_ERR_PRECISION;
+  if ((s->flags & MOE_FLAG_FP8_WGRAD) != 0) {
+    if (s->precision == MOE_BF16) return MOE_ERR_PRECISION;
+    // 32-bit offsets inside a weight-gradient tile's 256 rows of Kp codes
+    if (s->T * s->k >= (int64_t(1) << 23)) return MOE_ERR_SHAPE;
+  }
   return MOE_OK;
 }
 
@@ -40,6 +47,9 @@ bool fp8_backward(const moe_shape& s) { return s.precision != MOE_BF16; }
 // activation block (32 or 128 values along the reduction axis) and scale rule
 int act_block(const moe_shape& s) { return s.precision == MOE_MXFP8 ? 32 : 128; }
 int scale_rule(const moe_shape& s) { return s.precision == MOE_MXFP8 ? kRuleMx : kRulePow2; }
+bool fp8_wgrad(const moe_shape& s) { return (s.flags & MOE_FLAG_FP8_WGRAD) != 0; }
+// an upper bound of the sum over experts of rows rounded up to 128
+int64_t wgrad_rows_cap(const moe_shape& s) { return 128 * ((s.T * s.k) / 128 + s.E); }
 
 // bytes of E4M3 codes [rows, K] and of their scale bytes [rows, K/32]
 size_t codes_bytes(int64_t rows, int64_t K) { return align_up(size_t(rows) * size_t(K)); }
@@ -116,6 +126,8 @@ struct BwdLayout {
   size_t dh13, dwpart, dxrows;
   size_t dyq, dys;  // FP8 backward: dY codes [T, H], scales [T, H/32]
   size_t dhq, dhs;  // FP8 backward: [dg | du] codes [Tk, 2I], scales [Tk, 2I/32]
+  size_t wgp, wgps; // FP8 weight gradients: row-side operand codes / scales (along tokens)
+  size_t wgq, wgqs; // FP8 weight gradients: column-side operand codes / scales
   size_t total;
 };
 
@@ -133,6 +145,17 @@ BwdLayout bwd_layout(const moe_shape& s) {
     L.dys = o; o += scale_bytes(s.T, s.H);
     L.dhq = o; o += codes_bytes(Tk, 2 * s.I);
     L.dhs = o; o += scale_bytes(Tk, 2 * s.I);
+  }
+  L.wgp = L.wgps = L.wgq = L.wgqs = 0;
+  if (fp8_wgrad(s)) {
+    // dW13 uses [dg | du] (2I columns) and x (H); dW2 uses dY (H) and
+    // w*silu(g)*u (I), in the same two regions one after the other
+    const int64_t K = wgrad_rows_cap(s);
+    const int64_t cp = std::max<int64_t>(2 * s.I, s.H), cq = std::max<int64_t>(s.H, s.I);
+    L.wgp = o;  o += codes_bytes(cp, K);
+    L.wgps = o; o += scale_bytes(cp, K);
+    L.wgq = o;  o += codes_bytes(cq, K);
+    L.wgqs = o; o += scale_bytes(cq, K);
   }
   L.total = o;
   return L;
@@ -326,6 +349,27 @@ moe_status moe_quantize_rows(const moe_shape* s, const void* in, int64_t rows, i
                                          static_cast<hipStream_t>(stream), timer(), "quant_rows"));
 }
 
+moe_status moe_quantize_tokens(const moe_shape* s, const void* in, int64_t ld, int64_t C, const int32_t* counts,
+                               const int32_t* offsets, const int32_t* src_of, void* codes, void* scales,
+                               void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->precision == MOE_BF16) return MOE_ERR_PRECISION;
+  if (C < 128 || C > 65536 || C % 128 != 0 || ld < C || ld % 8 != 0) return MOE_ERR_SHAPE;
+  if (s->T * s->k >= (int64_t(1) << 23)) return MOE_ERR_SHAPE;
+  if (s->T == 0) return MOE_OK;
+  if (!in || !counts || !offsets || !codes || !scales) return MOE_ERR_NULL;
+  if (!aligned16(in) || !aligned16(codes)) return MOE_ERR_ALIGN;
+  int cus = 0;
+  if ((st = device_info(&cus)) != MOE_OK) return st;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  return launch_status(launch_quant_tokens(static_cast<const uint16_t*>(in), ld, int(C), counts, offsets,
+                                           int(s->E), s->T * s->k, src_of, src_of ? int(s->k) : 1,
+                                           static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                                           scale_rule(*s), static_cast<hipStream_t>(stream), timer(),
+                                           "quant_tokens"));
+}
+
 moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
                    const float* topk_w, const void* W13, const void* W2, const void* wq,
                    void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
@@ -463,6 +507,29 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
     if ((e = launch_combine(direct ? nullptr : dxrows, row_of, s->T, int(s->k), s->H, static_cast<uint16_t*>(dx), dwpart,
                             dh_num_parts(s->I), d_topk_w, hs, tm, "combine_dx_dw")) != hipSuccess)
       return MOE_ERR_LAUNCH;
+  }
+  if (fp8_wgrad(*s)) {
+    const int64_t Tk = s->T * s->k;
+    const int I = int(s->I), H = int(s->H), E = int(s->E), kk = int(s->k), rule = scale_rule(*s);
+    uint8_t* wgp = at<uint8_t>(ws, BL.wgp);
+    uint8_t* wgps = at<uint8_t>(ws, BL.wgps);
+    uint8_t* wgq = at<uint8_t>(ws, BL.wgq);
+    uint8_t* wgqs = at<uint8_t>(ws, BL.wgqs);
+    if ((e = launch_quant_tokens(dh13, 2 * I, 2 * I, counts, offsets, E, Tk, nullptr, 1, wgp, wgps, rule, hs, tm,
+                                 "quant_wg_dh13")) != hipSuccess ||
+        (e = launch_quant_tokens(x16, H, H, counts, offsets, E, Tk, src_of, kk, wgq, wgqs, rule, hs, tm,
+                                 "quant_wg_x")) != hipSuccess ||
+        (e = launch_gemm_dw_fp8(gp, wgp, wgps, 2 * I, wgq, wgqs, H, static_cast<uint16_t*>(dW13), queues, hs, tm,
+                                "gemm_dw13_fp8")) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    if ((e = launch_quant_tokens(dy16, H, H, counts, offsets, E, Tk, src_of, kk, wgp, wgps, rule, hs, tm,
+                                 "quant_wg_dy")) != hipSuccess ||
+        (e = launch_quant_tokens(act, I, I, counts, offsets, E, Tk, nullptr, 1, wgq, wgqs, rule, hs, tm,
+                                 "quant_wg_act")) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    e = launch_gemm_dw_fp8(gp, wgp, wgps, H, wgq, wgqs, I, static_cast<uint16_t*>(dW2), queues + 1, hs, tm,
+                           "gemm_dw2_fp8");
+    return launch_status(e);
   }
   if ((e = launch_gemm_dw13(gp, dh13, x16, static_cast<uint16_t*>(dW13), queues, hs, tm)) != hipSuccess)
     return MOE_ERR_LAUNCH;

@@ -243,6 +243,145 @@ __global__ __launch_bounds__(256) void quant_weight_tiles_kernel(const uint16_t*
   }
 }
 
+// ---------------------------------------------------------------- along tokens
+// Operands of the FP8 weight-gradient GEMMs, quantized along each expert's
+// rows (the reduction axis of those GEMMs). Expert e owns permuted rows
+// [offsets[e], offsets[e] + counts[e]); its r-th row is row offsets[e] + r of
+// `in` (src_of == nullptr) or the token row src_of[offsets[e] + r] / kk.
+// With Kp_e = counts[e] rounded up to 128 and poff_e = sum of Kp over the
+// experts before e, the codes of column c are the Kp_e bytes at
+//   codes + C * poff_e + c * Kp_e      (zero codes past counts[e])
+// and its scale bytes the Kp_e / 32 bytes at
+//   scales + C * poff_e / 32 + c * Kp_e / 32.
+// Blockwise rule: one exponent per column per 128-row block (its byte
+// repeated in the four 32-blocks); MX rule: one per column per 32 rows.
+// One workgroup per (128-row block of an expert, kTokCols column tiles of
+// 128): for each tile it loads the 128 x 128 bf16 values into LDS (rows past
+// the expert's end as zeros) and writes them transposed like the weight
+// quantizer: thread t takes columns 2p, 2p+1 (p = t / 4) and rows
+// 32q .. 32q+31 (q = t % 4). The block lookup and the row indices are shared
+// by the workgroup's tiles.
+constexpr int kTokCols = 4;
+__global__ __launch_bounds__(256) void quant_tokens_kernel(const uint16_t* __restrict__ in, int64_t ld, int C,
+                                                           const int32_t* __restrict__ counts,
+                                                           const int32_t* __restrict__ offsets, int E,
+                                                           const int32_t* __restrict__ src_of, int kk,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales, int rule) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kQLds];
+  __shared__ int32_t s_pref[1025];  // s_pref[e] = sum over e' < e of ceil(counts[e'] / 128)
+  __shared__ int32_t s_part[256];
+  const int t = threadIdx.x;
+  // prefix of 128-row block counts (E <= 1024: 4 experts per thread)
+  int32_t loc[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * t + q;
+    loc[q] = e < E ? (counts[e] + 127) / 128 : 0;
+    sum += loc[q];
+  }
+  s_part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int32_t add = t >= off ? s_part[t - off] : 0;
+    __syncthreads();
+    s_part[t] += add;
+    __syncthreads();
+  }
+  int32_t run = s_part[t] - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * t + q;
+    if (e < E) s_pref[e] = run;
+    run += loc[q];
+  }
+  if (t == 255) s_pref[E] = s_part[255];
+  __syncthreads();
+  const int cgn = (C / 128 + kTokCols - 1) / kTokCols;  // column groups
+  const int cg = int(blockIdx.x % unsigned(cgn));
+  const int gb = int(blockIdx.x / unsigned(cgn));
+  if (gb >= s_pref[E]) return;  // past the last block: the whole workgroup leaves
+  int lo = 0, hi = E;           // expert with s_pref[e] <= gb < s_pref[e + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= gb) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int b = gb - s_pref[e];
+  const int rows = counts[e];
+  const int64_t off = offsets[e];
+  const int64_t kp = int64_t(s_pref[e + 1] - s_pref[e]) * 128;  // Kp_e
+  const int64_t poff = int64_t(s_pref[e]) * 128;                // poff_e
+  const int c8 = (t & 15) * 8;
+  int64_t srow[8];  // source row of tile rows (t >> 4) + 16 i, or -1
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = b * 128 + (t >> 4) + 16 * i;
+    srow[i] = r < rows ? (src_of ? int64_t(src_of[off + r] / kk) : off + r) : -1;
+  }
+  const int pc = (t >> 2) * 2;  // columns pc, pc + 1 of a tile
+  const int q = t & 3;          // rows 32q .. 32q + 31 of a tile
+  const int cb_end = min(C / 128, (cg + 1) * kTokCols);
+  for (int cb = cg * kTokCols; cb < cb_end; ++cb) {
+    u32x4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      raw[i] = srow[i] >= 0 ? *reinterpret_cast<const u32x4*>(in + srow[i] * ld + int64_t(cb) * 128 + c8)
+                            : u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        *reinterpret_cast<uint32_t*>(tile + ((t >> 4) + 16 * i) * kQLds + c8 + 2 * d) = raw[i][d];
+    __syncthreads();
+    float v0[32], v1[32];
+    float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const uint32_t w2 = *reinterpret_cast<const uint32_t*>(tile + (32 * q + r) * kQLds + pc);
+      v0[r] = bf16_lo(w2);
+      v1[r] = bf16_hi(w2);
+      m0 = fmaxf(m0, fabsf(v0[r]));
+      m1 = fmaxf(m1, fabsf(v1[r]));
+    }
+    if (rule != kRuleMx) {  // 128-row blocks: the four threads of these columns share their maxima
+      m0 = fmaxf(m0, __shfl_xor(m0, 1));
+      m0 = fmaxf(m0, __shfl_xor(m0, 2));
+      m1 = fmaxf(m1, __shfl_xor(m1, 1));
+      m1 = fmaxf(m1, __shfl_xor(m1, 2));
+    }
+    const int e0 = clamp_exp(block_exponent(m0, rule));
+    const int e1 = clamp_exp(block_exponent(m1, rule));
+    const int64_t col = int64_t(cb) * 128 + pc;
+    uint8_t* d0 = codes + int64_t(C) * poff + col * kp + int64_t(b) * 128 + 32 * q;
+    uint8_t* d1 = d0 + kp;
+    *reinterpret_cast<u32x4*>(d0) = u32x4{pack4_codes(v0, e0), pack4_codes(v0 + 4, e0), pack4_codes(v0 + 8, e0),
+                                          pack4_codes(v0 + 12, e0)};
+    *reinterpret_cast<u32x4*>(d0 + 16) = u32x4{pack4_codes(v0 + 16, e0), pack4_codes(v0 + 20, e0),
+                                               pack4_codes(v0 + 24, e0), pack4_codes(v0 + 28, e0)};
+    *reinterpret_cast<u32x4*>(d1) = u32x4{pack4_codes(v1, e1), pack4_codes(v1 + 4, e1), pack4_codes(v1 + 8, e1),
+                                          pack4_codes(v1 + 12, e1)};
+    *reinterpret_cast<u32x4*>(d1 + 16) = u32x4{pack4_codes(v1 + 16, e1), pack4_codes(v1 + 20, e1),
+                                               pack4_codes(v1 + 24, e1), pack4_codes(v1 + 28, e1)};
+    uint8_t* s0 = scales + int64_t(C) * poff / 32 + col * (kp / 32) + b * 4 + q;
+    s0[0] = uint8_t(e0 + 127);
+    s0[kp / 32] = uint8_t(e1 + 127);
+  }
+}
+
+hipError_t launch_quant_tokens(const uint16_t* in, int64_t ld, int C, const int32_t* counts, const int32_t* offsets,
+                               int E, int64_t M, const int32_t* src_of, int kk, uint8_t* codes, uint8_t* scales,
+                               int rule, hipStream_t st, KernelTimer* timer, const char* name) {
+  // an upper bound of the number of 128-row blocks: M / 128 + E
+  const int64_t blocks = (M / 128 + E) * ((C / 128 + kTokCols - 1) / kTokCols);
+  if (M <= 0 || blocks <= 0) return hipSuccess;
+  TimedLaunch tl(timer, name, st);
+  hipLaunchKernelGGL(quant_tokens_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, in, ld, C, counts, offsets, E,
+                     src_of, kk, codes, scales, rule);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* pcodes, uint8_t* pscales,
                                 uint8_t* tcodes, uint8_t* tscales, int rule, hipStream_t st, KernelTimer* timer) {
   const int64_t tiles = E * (R / 128) * (C / 128);

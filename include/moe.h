@@ -82,9 +82,13 @@ typedef enum moe_status {
  *   An all-zero block has e = 0.
  * Quantized operands: x, w*silu(g)*u and both weight stacks in the forward;
  * dY, [dg | du] and the weights (re-blocked for the transposed product
- * under MXFP8) in the backward. The weight-gradient GEMMs read the bf16
- * tensors x, dY, w*silu(g)*u and [dg | du]. MOE_FP8_BWD runs the forward of
- * MOE_BF16 and the backward of MOE_FP8_BLOCK. */
+ * under MXFP8) in the backward. By default the weight-gradient GEMMs read
+ * the bf16 tensors x, dY, w*silu(g)*u and [dg | du]; with MOE_FLAG_FP8_WGRAD
+ * (see moe_shape) they read those four quantized along each expert's rows:
+ * every column in blocks of 128 rows (MOE_FP8_BLOCK, MOE_FP8_BWD; pow2 rule)
+ * or 32 rows (MOE_MXFP8; MX rule), counted from the expert's first row in
+ * permuted order. MOE_FP8_BWD runs the forward of MOE_BF16 and the backward
+ * of MOE_FP8_BLOCK. */
 typedef enum moe_precision {
   MOE_BF16 = 0,
   MOE_FP8_BLOCK = 1,
@@ -92,16 +96,25 @@ typedef enum moe_precision {
   MOE_FP8_BWD = 3
 } moe_precision;
 
+/* Flags of moe_shape.flags. MOE_FLAG_FP8_WGRAD: the weight-gradient GEMMs
+ * of an FP8 precision run in FP8 on operands quantized along each expert's
+ * rows (see moe_precision); with MOE_BF16 it is MOE_ERR_PRECISION. */
+enum { MOE_FLAG_FP8_WGRAD = 1 };
+
 /* Problem description. Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= E,
  * T*k < 2^31, T*H < 2^31, T*k*I < 2^30, H%256 == 0, I%128 == 0,
  * 256 <= H <= 16384, 128 <= I <= 8192 (the kernels address rows with
- * 32-bit byte offsets).
+ * 32-bit byte offsets); with MOE_FLAG_FP8_WGRAD also T*k < 2^23.
  * num_cus caps how many compute units the persistent GEMMs occupy
- * (0 = all), so that concurrent kernels (e.g. collectives) keep CUs. */
+ * (0 = all), so that concurrent kernels (e.g. collectives) keep CUs.
+ * flags: MOE_FLAG_* bits (unknown bits: MOE_ERR_PRECISION); reserved
+ * must be 0 (else MOE_ERR_SHAPE). */
 typedef struct moe_shape {
   int64_t T, H, I, E, k;
   int32_t precision; /* moe_precision */
   int32_t num_cus;
+  int32_t flags;
+  int32_t reserved;
 } moe_shape;
 
 /* Byte sizes of the three caller-provided buffers for `s`:
@@ -162,6 +175,27 @@ moe_status moe_quantize_weights(const moe_shape* s, const void* W13, const void*
  * MOE_ERR_PRECISION for MOE_BF16. */
 moe_status moe_quantize_rows(const moe_shape* s, const void* in, int64_t rows, int64_t K, void* codes,
                              void* scales, void* stream);
+
+/* Quantizes the rows of every expert along the rows, column by column: the
+ * step moe_bwd applies to x, [dg | du], dY and w*silu(g)*u under
+ * MOE_FLAG_FP8_WGRAD (blocks of 128 rows with the pow2 rule for
+ * MOE_FP8_BLOCK and MOE_FP8_BWD, 32 rows with the MX rule for MOE_MXFP8; see
+ * moe_precision). Exposed for testing.
+ *   in      bf16 [*, ld]; the r-th row of expert e is row offsets[e] + r of
+ *           `in` (src_of == NULL) or row src_of[offsets[e] + r] / s->k
+ *   C       columns quantized (128 <= C <= ld, C % 128 == 0, ld % 8 == 0)
+ *   counts, offsets, src_of   int32 [E], [E+1], [T*k] as moe_permute writes
+ *   codes   uint8, C * K bytes with K = 128 * (s->T * s->k / 128 + s->E):
+ *           expert e's codes [C][Kp_e] start at byte C * poff_e, where Kp_e
+ *           is counts[e] rounded up to 128 (codes past counts[e] are zero)
+ *           and poff_e the sum of Kp over the experts before e
+ *   scales  uint8, C * K / 32 bytes: expert e's bytes [C][Kp_e / 32] at
+ *           C * poff_e / 32, one per (column, 32 rows)
+ * `in` and `codes` 16-byte aligned. MOE_ERR_PRECISION for MOE_BF16;
+ * enqueued on `stream`, the caller owns every buffer. */
+moe_status moe_quantize_tokens(const moe_shape* s, const void* in, int64_t ld, int64_t C, const int32_t* counts,
+                               const int32_t* offsets, const int32_t* src_of, void* codes, void* scales,
+                               void* stream);
 
 /* Expert-contiguous permutation of the routed pairs (kongchang.com explainer,
  * grouped-GEMM note: routing index -> token reorder -> grouped GEMM indexed

@@ -174,6 +174,29 @@ def test_fp8_workspaces_are_larger(B):
     assert b1 >= b0 + T * H + Tk * 2 * I and b3 == b1
 
 
+def test_fp8_wgrad_flag_checks_and_workspace(B):
+    """MOE_FLAG_FP8_WGRAD: needs an FP8 precision, unknown flag bits and a
+    nonzero reserved word are refused, the routed-row limit is 2^23, and the
+    backward workspace gains the token-quantized operands of both weight
+    gradients (codes + scales, rows rounded up to 128 per expert)."""
+    for prec in ("fp8_block", "mxfp8", "fp8_bwd"):
+        f0, s0, b0 = B.moe_workspace_size(_shape(B, precision=prec))
+        f1, s1, b1 = B.moe_workspace_size(_shape(B, precision=prec, wgrad="fp8"))
+        Kcap = 128 * (16384 * 8 // 128 + 128)
+        assert (f1, s1) == (f0, s0)
+        assert b1 >= b0 + (2048 + 2048) * Kcap * (1 + 1 / 32)
+    for kw, status in ((dict(wgrad="fp8"), 4), (dict(precision="fp8_block", wgrad=2), 4),
+                       (dict(precision="fp8_block", wgrad="fp8", T=1 << 20, k=8), 2)):
+        with pytest.raises(B.MoEError) as ei:
+            B.moe_workspace_size(_shape(B, **kw))
+        assert ei.value.status == status, kw
+    s = _shape(B, precision="fp8_block")
+    s.reserved = 1
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_workspace_size(s)
+    assert ei.value.status == 2
+
+
 def test_bwd_requires_saved(B):
     a = _fwd_args()
     with pytest.raises(B.MoEError) as ei:

@@ -137,10 +137,70 @@ def test_quantize_weights_bit_exact(B, mode):
         assert np.array_equal(got_s, s), name
 
 
+def _token_matrix(rows, C, seed):
+    """bf16 rows whose magnitudes differ by up to 2^40, so that blocks along
+    the rows mix scales; zero, tie, saturation and subnormal columns."""
+    g = torch.Generator().manual_seed(seed)
+    mag = torch.exp(torch.empty(rows, 1).uniform_(-14, 14, generator=g))
+    x = torch.randn(rows, C, generator=g) * mag
+    x[:, 0] = 0.0                                              # an all-zero column
+    mids = torch.tensor([1.0625, 1.1875, 3.25, 0.01171875, 240.0, 208.0, 448.0, -448.0])
+    x[:, 1] = mids.repeat(rows // 8 + 1)[:rows]                # ties at scale 2^0
+    x[:, 2] = 1.0
+    x[::32, 2] = 960.0                                         # saturates under the MX rule
+    x[:, 3] = torch.randn(rows, generator=g) * 1e-39           # bf16 subnormals
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("gather", [False, True])
+def test_quantize_tokens_bit_exact(B, mode, gather):
+    """The weight-gradient quantizer: per expert (rows in permuted order,
+    from token rows when gathering), every column in 128-row (32 for MX)
+    blocks; codes and scale bytes equal the oracle's."""
+    T, k, E, C = 700, 2, 6, 384
+    _say(f"case quantize_tokens mode={mode} gather={gather} T={T} k={k} E={E} C={C}")
+    idx, _ = inputs.make_random_routing_only(T, E, k, 22, DEV, "zipf")
+    idx[idx == 4] = 5                                          # expert 4 gets no rows
+    shape = B.make_shape(T, 256, 128, E, k, mode)
+    n = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    row_of = torch.empty(n, dtype=torch.int32, device=DEV)
+    src_of = torch.empty(n, dtype=torch.int32, device=DEV)
+    scratch = torch.zeros(B.moe_permute_scratch_bytes(shape), dtype=torch.uint8, device=DEV)
+    B.moe_permute(shape, idx, counts, offsets, row_of, src_of, scratch)
+    rows_in = T if gather else n
+    x = _token_matrix(rows_in, C + 128, 23)                    # ld = C + 128: extra columns stay unread
+    K = B.wgrad_rows_cap(shape)
+    codes = torch.full((C * K,), 0xAB, dtype=torch.uint8, device=DEV)
+    scales = torch.full((C * K // 32,), 0xAB, dtype=torch.uint8, device=DEV)
+    B.moe_quantize_tokens(shape, x.to(DEV), C + 128, C, counts, offsets, src_of if gather else None, codes, scales)
+    torch.cuda.synchronize()
+    gc, gs = _np(codes), _np(scales)
+    block, rule = _rule(mode)
+    xs = orc.as_f64(x)[:, :C]
+    _, ro, _, rsrc = orc.permute(_np(idx), E)
+    poff = 0
+    for e in range(E):
+        r0, r1 = int(ro[e]), int(ro[e + 1])
+        kp = -(-(r1 - r0) // 128) * 128
+        seg = xs[rsrc[r0:r1] // k] if gather else xs[r0:r1]
+        pad = np.zeros((kp, C))
+        pad[:r1 - r0] = seg
+        rc, re, _ = f8.quantize_along_last(pad.T, block, rule)  # [C, kp], [C, kp / block]
+        rs = np.repeat(re + 127, block // 32, axis=-1).astype(np.uint8)
+        got_c = gc[C * poff:C * (poff + kp)].reshape(C, kp)
+        got_s = gs[C * poff // 32:C * (poff + kp) // 32].reshape(C, kp // 32)
+        assert np.array_equal(got_c, rc), (e, int(np.sum(got_c != rc)))
+        assert np.array_equal(got_s, rs), e
+        poff += kp
+
+
 # --------------------------------------------------------------- layer
 
-def run_layer(B, cfg, d, mode):
-    shape = B.make_shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, mode)
+def run_layer(B, cfg, d, mode, wgrad="bf16"):
+    shape = B.make_shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, mode, wgrad=wgrad)
     buf = B.LayerBuffers.allocate(shape)
     buf.fwd_ws.fill_(0xFF)
     buf.bwd_ws.fill_(0xFF)
@@ -203,6 +263,31 @@ def test_fp8_layer_matches_oracle_elementwise(B, cfg, mode):
         assert not out["dW13"][e].any() and not out["dW2"][e].any()
 
 
+@pytest.mark.parametrize("cfg,mode", CASES, ids=[f"{c.name}-{m}" for c, m in CASES])
+def test_fp8_weight_gradients_match_oracle_elementwise(B, cfg, mode):
+    """MOE_FLAG_FP8_WGRAD: dW13 and dW2 from operands quantized along each
+    expert's rows; the other outputs equal those of the default reading."""
+    cfg = cfg.scaled(precision=mode)
+    _say(f"case fp8 wgrad {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    out = run_layer(B, cfg, d, mode, wgrad="fp8")
+    base = run_layer(B, cfg, d, mode)
+    assert out["status"] == 0
+    for k in ("y", "dx", "dw"):
+        assert torch.equal(out[k], base[k]), k
+    args = (d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
+    wq = f8.quantize_weights(d["W13"], d["W2"], mode)
+    _, _, dW13_ref, dW2_ref = f8.backward(d["dy"], *args, mode, wq=wq, wgrad="fp8")
+    errs = {"dW13": max_rel_err(orc.as_f64(out["dW13"]), dW13_ref),
+            "dW2": max_rel_err(orc.as_f64(out["dW2"]), dW2_ref)}
+    _say(f"{cfg.name}/{mode}/wgrad fp8: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL_FP8, (k, v)
+    counts = _np(out["counts"])
+    for e in np.nonzero(counts == 0)[0]:
+        assert not out["dW13"][e].any() and not out["dW2"][e].any()
+
+
 def test_fp8_layer_deterministic_bitwise(B):
     cfg = SMALL[1].scaled(precision="mxfp8")
     _say(f"case determinism {inputs.describe(cfg)}")
@@ -235,12 +320,12 @@ def _pick_tokens(idx, counts, n, pool=4000):
     return sorted(chosen)
 
 
-def _sampled_check(B, cfg, n_tokens, n_experts):
+def _sampled_check(B, cfg, n_tokens, n_experts, wgrad="bf16"):
     mode = cfg.precision
     t0 = time.time()
-    _say(f"case full-size {inputs.describe(cfg)}")
+    _say(f"case full-size {inputs.describe(cfg)} wgrad={wgrad}")
     d = inputs.make_layer_inputs(cfg, DEV)
-    out = run_layer(B, cfg, d, mode)
+    out = run_layer(B, cfg, d, mode, wgrad=wgrad)
     assert out["status"] == 0
     counts = _np(out["counts"])
     idx_h = _np(d["topk_idx"])
@@ -278,7 +363,8 @@ def _sampled_check(B, cfg, n_tokens, n_experts):
         if f.size == 0:
             assert not out["dW13"][e].any() and not out["dW2"][e].any()
             continue
-        _, _, r13, r2 = f8.backward(dye, xe, ie, we, d["W13"][e:e + 1], d["W2"][e:e + 1], mode, wq=wq_of([e]))
+        _, _, r13, r2 = f8.backward(dye, xe, ie, we, d["W13"][e:e + 1], d["W2"][e:e + 1], mode, wq=wq_of([e]),
+                                    wgrad=wgrad)
         errs[f"dW13[{e}]"] = max_rel_err(orc.as_f64(out["dW13"][e]), r13[0])
         errs[f"dW2[{e}]"] = max_rel_err(orc.as_f64(out["dW2"][e]), r2[0])
     _say(f"{cfg.name}/{mode}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
@@ -299,3 +385,15 @@ def test_qwen3_235b_fp8_bwd_sampled(B):
 
 def test_qwen3_30b_zipf_mxfp8_sampled(B):
     _sampled_check(B, inputs.CONFIGS["zipf"], n_tokens=3, n_experts=2)
+
+
+def test_ep8_share_fp8_block_fp8_wgrad_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["ep8_share"], n_tokens=4, n_experts=2, wgrad="fp8")
+
+
+def test_qwen3_235b_fp8_bwd_fp8_wgrad_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["qwen3_235b"], n_tokens=1, n_experts=1, wgrad="fp8")
+
+
+def test_qwen3_30b_zipf_mxfp8_fp8_wgrad_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["zipf"], n_tokens=1, n_experts=2, wgrad="fp8")
