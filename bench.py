@@ -50,13 +50,14 @@ def hbm_bytes(name: str, cfg) -> float | None:
     if name == "combine_dx_dw" and k > 1:
         return 2.0 * M * H + 4.0 * T * k + 2.0 * T * H + 4.0 * M * nparts + 4.0 * T * k
 
-    def quant(rows, K):  # bf16 in, E4M3 codes + one E8M0 byte per 32 out
-        return rows * K * (2.0 + 1.0 + 1.0 / 32)
+    def quant(rows, K, outs=1):  # bf16 in, E4M3 codes + one E8M0 byte per 32 out (per output layout)
+        return rows * K * (2.0 + outs * (1.0 + 1.0 / 32))
     return {"quant_x": lambda: quant(T, H), "quant_dy": lambda: quant(T, H),
             "quant_act": lambda: quant(M, I), "quant_dh13": lambda: quant(M, 2 * I),
             # along tokens: every routed row read once (gathered for x, dY)
-            "quant_wg_x": lambda: quant(M, H), "quant_wg_dy": lambda: quant(M, H),
-            "quant_wg_dh13": lambda: quant(M, 2 * I), "quant_wg_act": lambda: quant(M, I)}.get(name, lambda: None)()
+            # [dg | du] (and dY under top-1) also get their row codes in the same pass
+            "quant_wg_x": lambda: quant(M, H), "quant_wg_dy": lambda: quant(M, H, 2 if k == 1 else 1),
+            "quant_wg_dh13": lambda: quant(M, 2 * I, 2), "quant_wg_act": lambda: quant(M, I)}.get(name, lambda: None)()
 WORKLOADS = {
     "tiny": "tiny MoE layer",
     "qwen3_30b": "Qwen3-30B-A3B-shaped MoE layer fwd+bwd",

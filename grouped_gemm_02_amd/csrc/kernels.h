@@ -96,9 +96,12 @@ hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint
 // rows (codes [C][Kp_e] per expert, Kp_e = rows rounded up to 128, experts
 // packed in order; one scale byte per (column, 32 rows)). src_of == nullptr:
 // expert rows are rows offsets[e] + r of `in`; else token rows src_of[..] / kk.
+// rcodes/rscales (optional): also the launch_quant_rows output of the rows
+// (each source row must occur once: a direct operand, or kk == 1).
 hipError_t launch_quant_tokens(const uint16_t* in, int64_t ld, int C, const int32_t* counts, const int32_t* offsets,
                                int E, int64_t M, const int32_t* src_of, int kk, uint8_t* codes, uint8_t* scales,
-                               int rule, hipStream_t st, KernelTimer* timer, const char* name);
+                               int rule, hipStream_t st, KernelTimer* timer, const char* name,
+                               uint8_t* rcodes = nullptr, uint8_t* rscales = nullptr);
 // FP8 weight gradients from those operands: dW[e] (P rows x Q rows, bf16,
 // row-major [MP][NQ]) = sum over the expert's rows of P'[m][r] Q'[n][r]
 hipError_t launch_gemm_dw_fp8(const GemmProblem& p, const uint8_t* pcodes, const uint8_t* pscales, int MP,

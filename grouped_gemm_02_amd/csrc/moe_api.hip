@@ -126,8 +126,9 @@ struct BwdLayout {
   size_t dh13, dwpart, dxrows;
   size_t dyq, dys;  // FP8 backward: dY codes [T, H], scales [T, H/32]
   size_t dhq, dhs;  // FP8 backward: [dg | du] codes [Tk, 2I], scales [Tk, 2I/32]
-  size_t wgp, wgps; // FP8 weight gradients: row-side operand codes / scales (along tokens)
-  size_t wgq, wgqs; // FP8 weight gradients: column-side operand codes / scales
+  // FP8 weight gradients: operands quantized along tokens (codes, scales) of
+  // [dg | du], x, dY and w*silu(g)*u
+  size_t wgd, wgds, wgx, wgxs, wgy, wgys, wga, wgas;
   size_t total;
 };
 
@@ -146,16 +147,17 @@ BwdLayout bwd_layout(const moe_shape& s) {
     L.dhq = o; o += codes_bytes(Tk, 2 * s.I);
     L.dhs = o; o += scale_bytes(Tk, 2 * s.I);
   }
-  L.wgp = L.wgps = L.wgq = L.wgqs = 0;
+  L.wgd = L.wgds = L.wgx = L.wgxs = L.wgy = L.wgys = L.wga = L.wgas = 0;
   if (fp8_wgrad(s)) {
-    // dW13 uses [dg | du] (2I columns) and x (H); dW2 uses dY (H) and
-    // w*silu(g)*u (I), in the same two regions one after the other
     const int64_t K = wgrad_rows_cap(s);
-    const int64_t cp = std::max<int64_t>(2 * s.I, s.H), cq = std::max<int64_t>(s.H, s.I);
-    L.wgp = o;  o += codes_bytes(cp, K);
-    L.wgps = o; o += scale_bytes(cp, K);
-    L.wgq = o;  o += codes_bytes(cq, K);
-    L.wgqs = o; o += scale_bytes(cq, K);
+    L.wgd = o; o += codes_bytes(2 * s.I, K);
+    L.wgds = o; o += scale_bytes(2 * s.I, K);
+    L.wgx = o; o += codes_bytes(s.H, K);
+    L.wgxs = o; o += scale_bytes(s.H, K);
+    L.wgy = o; o += codes_bytes(s.H, K);
+    L.wgys = o; o += scale_bytes(s.H, K);
+    L.wga = o; o += codes_bytes(s.I, K);
+    L.wgas = o; o += scale_bytes(s.I, K);
   }
   L.total = o;
   return L;
@@ -479,15 +481,24 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
   int32_t* queues = at<int32_t>(ws, BL.queues);
   hipError_t e = launch_zero_queues(queues, hs, tm);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  const bool wg8 = fp8_wgrad(*s);
+  const int64_t Tk = s->T * s->k;
+  const int I = int(s->I), H = int(s->H), E = int(s->E), kk = int(s->k), rule = scale_rule(*s);
   if (s->T > 0) {
     GemmOperand gdy{dy, nullptr}, gw2{W2, nullptr}, gdh{dh13, nullptr}, gw13{W13, nullptr};
     if (f8) {
       const moe_wq_layout WL = wq_layout(*s);
       uint8_t* dyq = at<uint8_t>(ws, BL.dyq);
       uint8_t* dys = at<uint8_t>(ws, BL.dys);
-      if ((e = launch_quant_rows(dy16, s->T, int(s->H), dyq, dys, act_block(*s), scale_rule(*s), hs, tm,
-                                 "quant_dy")) != hipSuccess)
-        return MOE_ERR_LAUNCH;
+      if (wg8 && kk == 1) {
+        // each token row occurs once among the expert rows: one pass gives
+        // dY's codes along H (for dH) and along the expert rows (for dW2)
+        e = launch_quant_tokens(dy16, H, H, counts, offsets, E, Tk, src_of, kk, at<uint8_t>(ws, BL.wgy),
+                                at<uint8_t>(ws, BL.wgys), rule, hs, tm, "quant_wg_dy", dyq, dys);
+      } else {
+        e = launch_quant_rows(dy16, s->T, H, dyq, dys, act_block(*s), rule, hs, tm, "quant_dy");
+      }
+      if (e != hipSuccess) return MOE_ERR_LAUNCH;
       gdy = GemmOperand{dyq, dys};
       gw2 = GemmOperand{at<uint8_t>(wq, WL.w2t), at<uint8_t>(wq, WL.w2t_scale)};
       gw13 = GemmOperand{at<uint8_t>(wq, WL.w13t), at<uint8_t>(wq, WL.w13t_scale)};
@@ -496,9 +507,12 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
     if (f8) {
       uint8_t* dhq = at<uint8_t>(ws, BL.dhq);
       uint8_t* dhs = at<uint8_t>(ws, BL.dhs);
-      if ((e = launch_quant_rows(dh13, s->T * s->k, int(2 * s->I), dhq, dhs, act_block(*s), scale_rule(*s), hs,
-                                 tm, "quant_dh13")) != hipSuccess)
-        return MOE_ERR_LAUNCH;
+      if (wg8)  // [dg | du] along 2I (for dX) and along the expert rows (for dW13) in one pass
+        e = launch_quant_tokens(dh13, 2 * I, 2 * I, counts, offsets, E, Tk, nullptr, 1, at<uint8_t>(ws, BL.wgd),
+                                at<uint8_t>(ws, BL.wgds), rule, hs, tm, "quant_wg_dh13", dhq, dhs);
+      else
+        e = launch_quant_rows(dh13, Tk, 2 * I, dhq, dhs, act_block(*s), rule, hs, tm, "quant_dh13");
+      if (e != hipSuccess) return MOE_ERR_LAUNCH;
       gdh = GemmOperand{dhq, dhs};
     }
     const bool direct = s->k == 1;  // top-1: dX rows go straight to dx
@@ -508,26 +522,29 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
                             dh_num_parts(s->I), d_topk_w, hs, tm, "combine_dx_dw")) != hipSuccess)
       return MOE_ERR_LAUNCH;
   }
-  if (fp8_wgrad(*s)) {
-    const int64_t Tk = s->T * s->k;
-    const int I = int(s->I), H = int(s->H), E = int(s->E), kk = int(s->k), rule = scale_rule(*s);
-    uint8_t* wgp = at<uint8_t>(ws, BL.wgp);
-    uint8_t* wgps = at<uint8_t>(ws, BL.wgps);
-    uint8_t* wgq = at<uint8_t>(ws, BL.wgq);
-    uint8_t* wgqs = at<uint8_t>(ws, BL.wgqs);
-    if ((e = launch_quant_tokens(dh13, 2 * I, 2 * I, counts, offsets, E, Tk, nullptr, 1, wgp, wgps, rule, hs, tm,
-                                 "quant_wg_dh13")) != hipSuccess ||
-        (e = launch_quant_tokens(x16, H, H, counts, offsets, E, Tk, src_of, kk, wgq, wgqs, rule, hs, tm,
+  if (wg8) {
+    // [dg | du] (and, for top-1, dY) were quantized along the expert rows
+    // above; with no tokens every expert is empty and no operand is read
+    uint8_t* wgd = at<uint8_t>(ws, BL.wgd);
+    uint8_t* wgds = at<uint8_t>(ws, BL.wgds);
+    uint8_t* wgx = at<uint8_t>(ws, BL.wgx);
+    uint8_t* wgxs = at<uint8_t>(ws, BL.wgxs);
+    uint8_t* wgy = at<uint8_t>(ws, BL.wgy);
+    uint8_t* wgys = at<uint8_t>(ws, BL.wgys);
+    uint8_t* wga = at<uint8_t>(ws, BL.wga);
+    uint8_t* wgas = at<uint8_t>(ws, BL.wgas);
+    if ((e = launch_quant_tokens(x16, H, H, counts, offsets, E, Tk, src_of, kk, wgx, wgxs, rule, hs, tm,
                                  "quant_wg_x")) != hipSuccess ||
-        (e = launch_gemm_dw_fp8(gp, wgp, wgps, 2 * I, wgq, wgqs, H, static_cast<uint16_t*>(dW13), queues, hs, tm,
+        (e = launch_gemm_dw_fp8(gp, wgd, wgds, 2 * I, wgx, wgxs, H, static_cast<uint16_t*>(dW13), queues, hs, tm,
                                 "gemm_dw13_fp8")) != hipSuccess)
       return MOE_ERR_LAUNCH;
-    if ((e = launch_quant_tokens(dy16, H, H, counts, offsets, E, Tk, src_of, kk, wgp, wgps, rule, hs, tm,
-                                 "quant_wg_dy")) != hipSuccess ||
-        (e = launch_quant_tokens(act, I, I, counts, offsets, E, Tk, nullptr, 1, wgq, wgqs, rule, hs, tm,
+    if (kk != 1 && (e = launch_quant_tokens(dy16, H, H, counts, offsets, E, Tk, src_of, kk, wgy, wgys, rule, hs,
+                                            tm, "quant_wg_dy")) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    if ((e = launch_quant_tokens(act, I, I, counts, offsets, E, Tk, nullptr, 1, wga, wgas, rule, hs, tm,
                                  "quant_wg_act")) != hipSuccess)
       return MOE_ERR_LAUNCH;
-    e = launch_gemm_dw_fp8(gp, wgp, wgps, H, wgq, wgqs, I, static_cast<uint16_t*>(dW2), queues + 1, hs, tm,
+    e = launch_gemm_dw_fp8(gp, wgy, wgys, H, wga, wgas, I, static_cast<uint16_t*>(dW2), queues + 1, hs, tm,
                            "gemm_dw2_fp8");
     return launch_status(e);
   }

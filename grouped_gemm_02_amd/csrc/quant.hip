@@ -261,13 +261,20 @@ __global__ __launch_bounds__(256) void quant_weight_tiles_kernel(const uint16_t*
 // quantizer: thread t takes columns 2p, 2p+1 (p = t / 4) and rows
 // 32q .. 32q+31 (q = t % 4). The block lookup and the row indices are shared
 // by the workgroup's tiles.
+// With rcodes != nullptr the kernel also writes the rows' quantization along
+// the columns (the moe_quantize_rows layout: codes [*, C] and scales
+// [*, C/32] at the source row; 128-column or 32-column blocks by the rule),
+// bit-identical to launch_quant_rows, from the same loads. Every source row
+// must then occur once (a direct operand, or token rows with kk == 1).
 constexpr int kTokCols = 4;
 __global__ __launch_bounds__(256) void quant_tokens_kernel(const uint16_t* __restrict__ in, int64_t ld, int C,
                                                            const int32_t* __restrict__ counts,
                                                            const int32_t* __restrict__ offsets, int E,
                                                            const int32_t* __restrict__ src_of, int kk,
                                                            uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales, int rule) {
+                                                           uint8_t* __restrict__ scales, int rule,
+                                                           uint8_t* __restrict__ rcodes,
+                                                           uint8_t* __restrict__ rscales) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kQLds];
   __shared__ int32_t s_pref[1025];  // s_pref[e] = sum over e' < e of ceil(counts[e'] / 128)
   __shared__ int32_t s_part[256];
@@ -328,6 +335,28 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const uint16_t* __res
     for (int i = 0; i < 8; ++i)
       raw[i] = srow[i] >= 0 ? *reinterpret_cast<const u32x4*>(in + srow[i] * ld + int64_t(cb) * 128 + c8)
                             : u32x4{0u, 0u, 0u, 0u};
+    if (rcodes) {  // along the columns: a row's 128 values sit in 16 aligned lanes
+      const int group = rule == kRuleMx ? 4 : 16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v[8];
+        float m = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          v[2 * d] = bf16_lo(raw[i][d]);
+          v[2 * d + 1] = bf16_hi(raw[i][d]);
+        }
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) m = fmaxf(m, fabsf(v[q8]));
+        for (int o = 1; o < group; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if (srow[i] >= 0) {
+          const int ex = clamp_exp(block_exponent(m, rule));
+          *reinterpret_cast<u32x2*>(rcodes + srow[i] * C + int64_t(cb) * 128 + c8) =
+              u32x2{pack4_codes(v, ex), pack4_codes(v + 4, ex)};
+          if ((t & 3) == 0) rscales[srow[i] * (C / 32) + cb * 4 + ((t & 15) >> 2)] = uint8_t(ex + 127);
+        }
+      }
+    }
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -372,13 +401,14 @@ __global__ __launch_bounds__(256) void quant_tokens_kernel(const uint16_t* __res
 
 hipError_t launch_quant_tokens(const uint16_t* in, int64_t ld, int C, const int32_t* counts, const int32_t* offsets,
                                int E, int64_t M, const int32_t* src_of, int kk, uint8_t* codes, uint8_t* scales,
-                               int rule, hipStream_t st, KernelTimer* timer, const char* name) {
+                               int rule, hipStream_t st, KernelTimer* timer, const char* name, uint8_t* rcodes,
+                               uint8_t* rscales) {
   // an upper bound of the number of 128-row blocks: M / 128 + E
   const int64_t blocks = (M / 128 + E) * ((C / 128 + kTokCols - 1) / kTokCols);
   if (M <= 0 || blocks <= 0) return hipSuccess;
   TimedLaunch tl(timer, name, st);
   hipLaunchKernelGGL(quant_tokens_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, in, ld, C, counts, offsets, E,
-                     src_of, kk, codes, scales, rule);
+                     src_of, kk, codes, scales, rule, rcodes, rscales);
   return hipGetLastError();
 }
 
