@@ -211,3 +211,41 @@ def test_bwd_small_workspace_rejected(B):
         B.moe_bwd(_shape(B), a[0], a[1], a[2], a[3], a[4], a[5], None, a[6], a[7], a[0], a[1], a[2],
                   _Fake(0x70000, 4096), stream=0)
     assert ei.value.status == 6
+
+
+def _raw_call(B, name, *args):
+    """Call an entry point with raw integers for pointers (host-side checks
+    only: every case below is refused before any device access)."""
+    return getattr(B.lib(), name)(*args)
+
+
+def test_quantize_rows_argument_checks(B):
+    import ctypes
+    P = 1 << 20  # a 16-byte-aligned stand-in address, never dereferenced
+    for kw, rows, K, ptrs, status in (
+            (dict(), 4, 256, (P, P, P), 4),                         # bf16 has no FP8 rule
+            (dict(precision="fp8_block"), 4, 100, (P, P, P), 2),     # K % 128
+            (dict(precision="fp8_block"), 1 << 24, 1 << 8, (P, P, P), 2),  # rows*K >= 2^31
+            (dict(precision="mxfp8"), 4, 256, (None, P, P), 1),
+            (dict(precision="mxfp8"), 4, 256, (P + 8, P, P), 3)):
+        s = _shape(B, **kw)
+        st = _raw_call(B, "moe_quantize_rows", ctypes.byref(s), ptrs[0], rows, K, ptrs[1], ptrs[2], None)
+        assert st == status, (kw, rows, K, ptrs, st)
+
+
+def test_quantize_tokens_argument_checks(B):
+    import ctypes
+    P = 1 << 20
+    good = (P, 2048, 2048, P, P, P, P, P)
+    for kw, args, status in (
+            (dict(), good, 4),                                           # bf16 has no FP8 rule
+            (dict(precision="fp8_block"), (P, 2048, 100, P, P, P, P, P), 2),   # C % 128
+            (dict(precision="fp8_block"), (P, 1024, 2048, P, P, P, P, P), 2),  # ld < C
+            (dict(precision="fp8_block"), (P, 2052, 2048, P, P, P, P, P), 2),  # ld % 8
+            (dict(precision="fp8_block", T=1 << 20, k=8), good, 2),      # T*k >= 2^23
+            (dict(precision="mxfp8"), (None, 2048, 2048, P, P, P, P, P), 1),
+            (dict(precision="mxfp8"), (P, 2048, 2048, None, P, P, P, P), 1),
+            (dict(precision="fp8_bwd"), (P, 2048, 2048, P, P, P, P + 4, P), 3)):
+        s = _shape(B, **kw)
+        st = _raw_call(B, "moe_quantize_tokens", ctypes.byref(s), *args, None)
+        assert st == status, (kw, args, st)
