@@ -254,7 +254,11 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
  * gradient partials fused in its epilogue; dX grouped GEMM (K = 2I);
  * gather-reduce of dx and d_topk_w; per-expert dW13 and dW2 GEMMs whose
  * reduction dimension is that expert's row count. FP8 backwards quantize dY
- * before the dH GEMM and [dg | du] before the dX GEMM. */
+ * before the dH GEMM and [dg | du] before the dX GEMM; with
+ * MOE_FLAG_FP8_WGRAD the weight-gradient GEMMs run in FP8 on x, [dg | du],
+ * dY and w*silu(g)*u quantized along each expert's rows (moe_quantize_tokens
+ * layout; [dg | du], and dY when k == 1, are quantized along both axes in
+ * one pass). */
 moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int32_t* topk_idx,
                    const float* topk_w, const void* W13, const void* W2, const void* wq,
                    const void* saved, void* dx, float* d_topk_w, void* dW13, void* dW2, void* ws,
