@@ -10,13 +10,17 @@ OUT=${1:-gpurun_out/prof}
 export TMPDIR=/tmp
 PROF="$OUT/profiles"
 mkdir -p "$OUT" "$PROF"
-for cp in qwen3_30b:bf16 ep8_share:fp8_block qwen3_235b:fp8_bwd zipf:mxfp8; do
-  c=${cp%%:*}; prec=${cp##*:}
-  echo "stats $c"
-  timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/stats_$c" -o run -- \
-    python3 bench.py --config $c --steps 5 --warmup 2 --no-cpu-baseline > "$OUT/stats_$c.log" 2>&1
-  python3 -m grouped_gemm_02_amd.profile_summary stats "$OUT/stats_$c/run_kernel_stats.csv" \
-    "$PROF/kernel_stats_${c}_${prec}.txt" --cmd "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/stats_$c -o run -- python3 bench.py --config $c --steps 5 --warmup 2 --no-cpu-baseline"
+# workload:precision:weight-gradient reading
+for cpw in qwen3_30b:bf16:bf16 ep8_share:fp8_block:bf16 qwen3_235b:fp8_bwd:bf16 zipf:mxfp8:bf16 \
+           ep8_share:fp8_block:fp8 qwen3_235b:fp8_bwd:fp8 zipf:mxfp8:fp8; do
+  c=${cpw%%:*}; rest=${cpw#*:}; prec=${rest%%:*}; wg=${rest##*:}
+  tag=${c}_${prec}; [ "$wg" = fp8 ] && tag=${tag}_fp8_wgrad
+  echo "stats $tag"
+  args="--config $c --wgrad $wg --steps 5 --warmup 2 --no-cpu-baseline"
+  timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/stats_$tag" -o run -- \
+    python3 bench.py $args > "$OUT/stats_$tag.log" 2>&1
+  python3 -m grouped_gemm_02_amd.profile_summary stats "$OUT/stats_$tag/run_kernel_stats.csv" \
+    "$PROF/kernel_stats_${tag}.txt" --cmd "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/stats_$tag -o run -- python3 bench.py $args"
 done
 echo "pmc fetch"
 timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/pmc_fetch" -o pmc -- \
