@@ -109,6 +109,9 @@ def parse():
     ap.add_argument("--wgrad", default="bf16", choices=["bf16", "fp8"],
                     help="weight-gradient GEMMs on bf16 operands, or (FP8 precisions) on operands "
                          "quantized along each expert's rows")
+    ap.add_argument("--router", default="none", choices=["none", "uniform", "skewed"],
+                    help="include the router step (moe_route before the forward, moe_route_bwd after the "
+                         "backward) on synthetic logits: N(0,1), or N(0,1) with a Zipf-like per-expert bias")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     return ap.parse_args()
@@ -189,6 +192,8 @@ def main():
         sys.exit(2)
     if args.wgrad == "fp8":
         WORKLOAD_KEY[0] += "/fp8_wgrad"
+    if args.router != "none":
+        WORKLOAD_KEY[0] += f"/router_{args.router}"
     torch.cuda.set_device(0)
     d = inputs.make_layer_inputs(cfg, "cuda")
     shape = B.make_shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.precision, wgrad=args.wgrad)
@@ -198,6 +203,13 @@ def main():
              torch.empty((cfg.E, 2 * cfg.I, cfg.H), dtype=torch.bfloat16, device="cuda"),
              torch.empty((cfg.E, cfg.H, cfg.I), dtype=torch.bfloat16, device="cuda"))
     y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    if args.router != "none":
+        # the router decides the routing each step (renormalised top-k)
+        logits = inputs.make_router_logits(cfg.T, cfg.E, cfg.seed + 100, "cuda",
+                                           skew=1.2 if args.router == "skewed" else 0.0)
+        d["topk_idx"] = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+        d["topk_w"] = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+        d_logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
 
     def step(evs=None):
         if evs:
@@ -206,10 +218,14 @@ def main():
             B.quantize_weights(buf, d["W13"], d["W2"])
         if evs:
             evs[3].record()
+        if args.router != "none":
+            B.moe_route(shape, logits, True, d["topk_idx"], d["topk_w"])
         B.forward(buf, d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], y=y)
         if evs:
             evs[1].record()
         B.backward(buf, d["dy"], d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], grads=grads)
+        if args.router != "none":
+            B.moe_route_bwd(shape, logits, d["topk_idx"], d["topk_w"], grads[1], True, d_logits)
         if evs:
             evs[2].record()
 
@@ -295,7 +311,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {WORKLOADS[cfg.name]}", "T": cfg.T, "H": cfg.H,
                    "I": cfg.I, "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "precision": cfg.precision,
-                   "wgrad": args.wgrad},
+                   "wgrad": args.wgrad, "router": args.router},
         "fwd_ms": round(sum(fwd_ms) / len(fwd_ms), 4),
         "bwd_ms": round(sum(bwd_ms) / len(bwd_ms), 4),
         "weight_quant_ms": round(sum(wq_ms) / len(wq_ms), 4),

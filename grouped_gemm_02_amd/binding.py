@@ -77,6 +77,8 @@ _SIGS = {
                                ctypes.c_size_t, _P]),
     "moe_bwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _P, ctypes.c_size_t, _P]),
+    "moe_route": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, ctypes.c_int32, _P, _P, _P]),
+    "moe_route_bwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "moe_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32), _P]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_set_kernel_timing": (ctypes.c_int, [ctypes.c_int]),
@@ -201,6 +203,16 @@ def moe_bwd(shape, dy, x, topk_idx, topk_w, W13, W2, wq, saved, dx, d_topk_w, dW
     _check(lib().moe_bwd(ctypes.byref(shape), _ptr(dy), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W13),
                          _ptr(W2), _ptr(wq), _ptr(saved), _ptr(dx), _ptr(d_topk_w), _ptr(dW13), _ptr(dW2),
                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_bwd")
+
+
+def moe_route(shape, logits, renorm, topk_idx, topk_w, stream=None) -> None:
+    _check(lib().moe_route(ctypes.byref(shape), _ptr(logits), int(bool(renorm)), _ptr(topk_idx), _ptr(topk_w),
+                           _stream(stream)), "moe_route")
+
+
+def moe_route_bwd(shape, logits, topk_idx, topk_w, d_topk_w, renorm, d_logits, stream=None) -> None:
+    _check(lib().moe_route_bwd(ctypes.byref(shape), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(d_topk_w),
+                               int(bool(renorm)), _ptr(d_logits), _stream(stream)), "moe_route_bwd")
 
 
 def moe_read_status(ws, stream=None) -> int:

@@ -108,4 +108,13 @@ hipError_t launch_gemm_dw_fp8(const GemmProblem& p, const uint8_t* pcodes, const
                               const uint8_t* qcodes, const uint8_t* qscales, int NQ, uint16_t* dW, int32_t* queue,
                               hipStream_t st, KernelTimer* timer, const char* name);
 
+// ---------------------------------------------------------------- router
+// logits fp32 [T, E] -> idx int32 [T, k] (descending logit, ties to the lower
+// id), w fp32 [T, k] (softmax probabilities, renormalised over the k if
+// renorm); the backward writes dz fp32 [T, E] = dL/dlogits from dw = dL/dw.
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int32_t* idx, float* w,
+                        hipStream_t st, KernelTimer* timer);
+hipError_t launch_route_bwd(const float* logits, int64_t T, int E, int k, int renorm, const int32_t* idx,
+                            const float* w, const float* dw, float* dz, hipStream_t st, KernelTimer* timer);
+
 }  // namespace moe

@@ -554,6 +554,32 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
   return launch_status(e);
 }
 
+moe_status moe_route(const moe_shape* s, const float* logits, int32_t renorm, int32_t* topk_idx, float* topk_w,
+                     void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  int cus = 0;
+  if ((st = device_info(&cus)) != MOE_OK) return st;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  return launch_status(launch_route(logits, s->T, int(s->E), int(s->k), renorm != 0, topk_idx, topk_w,
+                                    static_cast<hipStream_t>(stream), timer()));
+}
+
+moe_status moe_route_bwd(const moe_shape* s, const float* logits, const int32_t* topk_idx, const float* topk_w,
+                         const float* d_topk_w, int32_t renorm, float* d_logits, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w || !d_topk_w || !d_logits) return MOE_ERR_NULL;
+  int cus = 0;
+  if ((st = device_info(&cus)) != MOE_OK) return st;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  return launch_status(launch_route_bwd(logits, s->T, int(s->E), int(s->k), renorm != 0, topk_idx, topk_w, d_topk_w,
+                                        d_logits, static_cast<hipStream_t>(stream), timer()));
+}
+
 moe_status moe_read_status(const void* fwd_ws, int32_t* out, void* stream) {
   if (!fwd_ws || !out) return MOE_ERR_NULL;
   hipStream_t hs = static_cast<hipStream_t>(stream);

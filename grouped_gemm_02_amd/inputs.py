@@ -145,10 +145,26 @@ def make_random_routing_only(T: int, E: int, k: int, seed: int, device="cpu", ro
     return make_routing(T, E, k, routing, g, device)
 
 
+def make_router_logits(T: int, E: int, seed: int, device="cpu", skew: float = 0.0, ties: bool = False):
+    """fp32 router logits [T, E]: N(0, 1) per (token, expert), plus a fixed
+    per-expert bias -skew * log(1 + rank) (ranks a seeded permutation of the
+    experts), so that skew > 0 concentrates tokens on a few experts the way
+    Zipf-like popularity does. ties: logits rounded to multiples of 1/2
+    (many equal values)."""
+    g = _gen(seed, device)
+    z = torch.randn((T, E), generator=g, device=device, dtype=torch.float32)
+    if skew:
+        rank = torch.randperm(E, generator=g, device=device).to(torch.float32)
+        z = z - skew * torch.log1p(rank)[None, :]
+    if ties:
+        z = torch.round(z * 2.0) / 2.0
+    return z
+
+
 def describe(cfg: LayerConfig) -> str:
     return (f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} "
             f"routing={cfg.routing} precision={cfg.precision} seed={cfg.seed}")
 
 
 __all__ = ["LayerConfig", "CONFIGS", "make_layer_inputs", "make_routing",
-           "make_random_routing_only", "zipf_popularity", "describe"]
+           "make_random_routing_only", "make_router_logits", "zipf_popularity", "describe"]

@@ -215,6 +215,32 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* cou
                        int32_t* offsets, int32_t* row_of, int32_t* src_of, void* scratch,
                        void* stream);
 
+/* Router step before the layer. The pages leave the router outside the
+ * measured layer and name that, with uniform random routing, as their
+ * benchmark's idealisation (ic.work analysis, section on the benchmark's
+ * idealised assumptions); the router itself is not on the pages. Reading:
+ *   logits   fp32 [T, E]   a token's expert scores
+ *   topk_idx int32 [T, k]  the k experts with the largest logits, in
+ *                          descending order, ties to the lower expert id
+ *   topk_w   fp32 [T, k]   their softmax probabilities (softmax over all E);
+ *                          renorm != 0: divided by their sum (= a softmax
+ *                          over the k selected logits)
+ * Both outputs are written and can go straight to moe_fwd. Uses s->T, E, k
+ * (check as moe_workspace_size); the caller owns every buffer; enqueued on
+ * `stream`. */
+moe_status moe_route(const moe_shape* s, const float* logits, int32_t renorm, int32_t* topk_idx, float* topk_w,
+                     void* stream);
+
+/* Backward of moe_route: d_logits fp32 [T, E] (written) = dL/dlogits given
+ * d_topk_w = dL/dtopk_w (fp32 [T, k], e.g. from moe_bwd) and the topk_idx,
+ * topk_w moe_route produced from these logits with the same renorm. The
+ * selection is piecewise constant in the logits and passes no gradient:
+ * renorm: w (d_topk_w - <w, d_topk_w>) on the selected experts, 0 elsewhere;
+ * otherwise p (G - <p, G>) with p = softmax(logits) and G = d_topk_w placed
+ * on the selected experts. */
+moe_status moe_route_bwd(const moe_shape* s, const float* logits, const int32_t* topk_idx, const float* topk_w,
+                         const float* d_topk_w, int32_t renorm, float* d_logits, void* stream);
+
 /* Forward of the layer (MarkTechPost article, "How does the fused kernel
  * work?"; kongchang.com explainer, grouped-GEMM note).
  *   x        bf16  [T, H]
