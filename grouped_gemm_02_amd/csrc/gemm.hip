@@ -1047,14 +1047,92 @@ __device__ bool dw_expert_order(const int32_t* counts, int E, int32_t* s_cnt, in
   return __builtin_amdgcn_readfirstlane(*s_flag) != 0;
 }
 
-// Runs body(e, local) over every tile of a weight-gradient GEMM with
-// per_expert tiles per expert. s_flag and s_next are distinct LDS words.
+// Split-K for the hottest experts under skewed routing. A tile's k loop
+// runs over its expert's rows, so under skew the tiles of the hottest
+// experts can outlast a workgroup's share of all the work. With `avg` the
+// rows one workgroup would run if all tiles were spread over 256 of them (a
+// fixed nominal count, so that the plan, and with it the fp32 summation
+// order, does not depend on the grid), an expert with rows >= 1024 and
+// 4 * rows > 3 * avg is cut into S = min(kMaxSplit, ceil(2 * rows / avg))
+// row ranges of `chunk` rows (a multiple of 128), walking the experts in
+// the queue order above while the fp32 partial-tile budget lasts
+// (kSplitSlots tiles, at most kMaxSplitExperts experts). A split item
+// writes its fp32 partial tile to the workspace; a second kernel adds the S
+// partials of each split tile in split order and stores the tile, so the
+// result does not depend on the order the items ran in. Workgroup 0 writes
+// the plan for that kernel.
+constexpr int kMaxSplit = 4;
+constexpr int kMaxSplitExperts = 16;
+constexpr int kSplitSlots = 256;  // fp32 partial tiles of 256 x 256
+constexpr int kSplitMinRows = 1024;
+constexpr int kNominalWGs = 256;
+
+struct DwPlan {
+  int nsplit;                      // split experts: queue ranks 0 .. nsplit-1
+  int e[kMaxSplitExperts];         // their expert ids
+  int S[kMaxSplitExperts];         // their split counts
+  int chunk[kMaxSplitExperts];     // rows per split
+  int slot0[kMaxSplitExperts];     // first partial slot (tile t, split s: slot0 + t * S + s)
+  int item0[kMaxSplitExperts + 1]; // prefix of the split experts' items
+};
+static_assert(sizeof(DwPlan) <= sizeof(int32_t) * kSplitWords, "the plan fits its workspace words");
+static_assert(kSplitFloats == int64_t(kSplitSlots) * BM * BN, "the partial buffer holds kSplitSlots tiles");
+
+// One work item of a weight-gradient GEMM: tile `local` of expert e over the
+// expert's rows [k0, k0 + klen) (S == 1: all of them).
+struct DwItem {
+  int e, local;
+  int s, S;
+  int k0, klen, chunk;
+  int slot;
+};
+
+// the split plan (thread 0; every workgroup computes the same)
+__device__ void dw_plan(const int32_t* s_cnt, const int32_t* s_order, int E, int per_expert, DwPlan* plan) {
+  if (threadIdx.x != 0) return;
+  int64_t sum = 0;
+  for (int j = 0; j < E; ++j) sum += s_cnt[j];
+  const int64_t avg = max(int64_t(1), int64_t(per_expert) * sum / kNominalWGs);
+  int used = 0, n = 0;
+  plan->item0[0] = 0;
+  while (n < kMaxSplitExperts && n < E) {
+    const int e = s_order[n];
+    const int rows = s_cnt[e];
+    if (rows < kSplitMinRows || 4 * int64_t(rows) <= 3 * avg) break;
+    const int want = int(min(int64_t(kMaxSplit), (2 * int64_t(rows) + avg - 1) / avg));
+    const int chunk = ((rows + want - 1) / want + 127) / 128 * 128;
+    const int S = (rows + chunk - 1) / chunk;
+    if (S < 2 || used + per_expert * S > kSplitSlots) break;
+    plan->e[n] = e;
+    plan->S[n] = S;
+    plan->chunk[n] = chunk;
+    plan->slot0[n] = used;
+    plan->item0[n + 1] = plan->item0[n] + per_expert * S;
+    used += per_expert * S;
+    ++n;
+  }
+  plan->nsplit = n;
+}
+
+// Runs body(item) over every work item of a weight-gradient GEMM with
+// per_expert tiles per expert. Balanced routing: the static walk over
+// (expert, tile), no splits. Skewed: the queue, heaviest expert first, the
+// split experts' items first. s_flag and s_next are distinct LDS words.
+// Workgroup 0 writes the plan (no split experts when balanced) to plan_out.
 template <class Body>
-__device__ __forceinline__ void dw_for_each_tile(const int32_t* counts, int E, int per_expert, int32_t* queue,
-                                                 int32_t* s_cnt, int32_t* s_order, int32_t* s_flag,
-                                                 int32_t* s_next, Body&& body) {
-  const int total = E * per_expert;
+__device__ __forceinline__ void dw_for_each_item(const int32_t* counts, int E, int per_expert, int32_t* queue,
+                                                 int32_t* plan_out, int32_t* s_cnt, int32_t* s_order,
+                                                 int32_t* s_flag, int32_t* s_next, DwPlan* plan, Body&& body) {
   if (dw_expert_order(counts, E, s_cnt, s_order, s_flag)) {
+    dw_plan(s_cnt, s_order, E, per_expert, plan);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      const int32_t* w = reinterpret_cast<const int32_t*>(plan);
+      for (int i = threadIdx.x; i < int(sizeof(DwPlan) / sizeof(int32_t)); i += kThreads) plan_out[i] = w[i];
+    }
+    const int nsplit = __builtin_amdgcn_readfirstlane(plan->nsplit);
+    const int split_items = __builtin_amdgcn_readfirstlane(plan->item0[nsplit]);
+    const int total = split_items + (E - nsplit) * per_expert;
     int32_t ticket = 0;  // thread 0 only
     if (threadIdx.x == 0) ticket = atomicAdd(queue, 1);
     for (;;) {
@@ -1064,11 +1142,113 @@ __device__ __forceinline__ void dw_for_each_tile(const int32_t* counts, int E, i
       __syncthreads();
       if (u >= total) break;
       if (threadIdx.x == 0) ticket = atomicAdd(queue, 1);
-      const int e = __builtin_amdgcn_readfirstlane(s_order[u / per_expert]);
-      body(e, u % per_expert);
+      DwItem it;
+      if (u < split_items) {
+        int r = 0;
+        while (r + 1 < nsplit && plan->item0[r + 1] <= u) ++r;
+        r = __builtin_amdgcn_readfirstlane(r);
+        const int S = __builtin_amdgcn_readfirstlane(plan->S[r]);
+        const int within = u - __builtin_amdgcn_readfirstlane(plan->item0[r]);
+        it.e = __builtin_amdgcn_readfirstlane(plan->e[r]);
+        it.local = within / S;
+        it.s = within % S;
+        it.S = S;
+        it.chunk = __builtin_amdgcn_readfirstlane(plan->chunk[r]);
+        it.k0 = it.s * it.chunk;
+        it.klen = min(it.chunk, __builtin_amdgcn_readfirstlane(counts[it.e]) - it.k0);
+        it.slot = __builtin_amdgcn_readfirstlane(plan->slot0[r]) + it.local * S + it.s;
+      } else {
+        const int v = u - split_items;
+        it.e = __builtin_amdgcn_readfirstlane(s_order[nsplit + v / per_expert]);
+        it.local = v % per_expert;
+        it.s = 0;
+        it.S = 1;
+        it.k0 = 0;
+        it.klen = __builtin_amdgcn_readfirstlane(counts[it.e]);
+        it.chunk = it.klen;
+        it.slot = 0;
+      }
+      body(it);
     }
   } else {
-    for (int t = int(first_tile()); t < total; t += gridDim.x) body(t / per_expert, t % per_expert);
+    if (blockIdx.x == 0 && threadIdx.x == 0) plan_out[0] = 0;  // nsplit
+    for (int t = int(first_tile()); t < E * per_expert; t += gridDim.x) {
+      DwItem it;
+      it.e = t / per_expert;
+      it.local = t % per_expert;
+      it.s = 0;
+      it.S = 1;
+      it.k0 = 0;
+      it.klen = __builtin_amdgcn_readfirstlane(counts[it.e]);
+      it.chunk = it.klen;
+      it.slot = 0;
+      body(it);
+    }
+  }
+}
+
+// Stores a weight-gradient tile (rows [row0, row0 + 256), columns
+// [col0, col0 + cols) of the row-major [*, ld] output) when the item covers
+// all of the expert's rows, else writes its fp32 partial, a row-major
+// 256 x 256 tile, to its slot.
+__device__ __forceinline__ void dw_store(const Acc& acc, const DwItem& it, uint16_t* lds, uint16_t* out, int64_t ld,
+                                         int64_t row0, int64_t col0, int cols, float* partial) {
+  if (it.S == 1) {
+    store_tile(acc, lds, out, ld, row0, col0, BM, cols);
+    return;
+  }
+  float* mine = partial + int64_t(it.slot) * (BM * BN);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    float* row = mine + lane_row(tm) * BN;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = acc.c[tm][tn];
+        *reinterpret_cast<f32x4*>(row + lane_col(tn, g)) = f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+      }
+  }
+}
+
+// The split tiles of a weight-gradient GEMM: tile b (b < nsplit * per_expert)
+// is tile b % per_expert of split expert b / per_expert; each element is the
+// sum of its S partials in split order, rounded to bf16 and stored to the
+// expert's row-major [*, ld] block of `out` (expert stride `estride`; NT
+// tiles per tile row). A unit is 2048 consecutive elements of one tile, 8
+// per thread.
+constexpr int kSumThreads = 256;
+constexpr int kSumUnits = BM * BN / (8 * kSumThreads);
+constexpr int kSumGrid = 1024;
+__global__ __launch_bounds__(kSumThreads) void dw_split_sum_kernel(const int32_t* __restrict__ plan_words,
+                                                                   const float* __restrict__ partial,
+                                                                   int per_expert, int NT, uint16_t* __restrict__ out,
+                                                                   int64_t estride, int ld) {
+  const DwPlan* plan = reinterpret_cast<const DwPlan*>(plan_words);
+  const int units = plan->nsplit * per_expert * kSumUnits;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int b = u / kSumUnits, piece = u % kSumUnits;
+    const int r = b / per_expert, local = b % per_expert;
+    const int S = plan->S[r];
+    const int idx = piece * (8 * kSumThreads) + 8 * int(threadIdx.x);
+    const int m = idx / BN, c = idx % BN;
+    const int mt = local / NT, nt = local % NT;
+    if (c >= ld - nt * BN) continue;  // past the output's last column
+    const float* src = partial + int64_t(plan->slot0[r] + local * S) * (BM * BN) + idx;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < S; ++q) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src + int64_t(q) * (BM * BN));
+      const f32x4 d = *reinterpret_cast<const f32x4*>(src + int64_t(q) * (BM * BN) + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] += a[i];
+        hi[i] += d[i];
+      }
+    }
+    const u32x4 v = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                     pack_bf16x2(hi[2], hi[3])};
+    uint16_t* dst = out + int64_t(plan->e[r]) * estride + (int64_t(mt) * BM + m) * ld + int64_t(nt) * BN + c;
+    *reinterpret_cast<u32x4*>(dst) = v;
   }
 }
 
@@ -1076,20 +1256,23 @@ __device__ __forceinline__ void dw_for_each_tile(const int32_t* counts, int E, i
   __shared__ int32_t s_cnt[1024];                                              \
   __shared__ int32_t s_order[1024];                                            \
   __shared__ int32_t s_flag;                                                   \
-  __shared__ int32_t s_next;
+  __shared__ int32_t s_next;                                                   \
+  __shared__ DwPlan s_plan;
 
 __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, const uint16_t* __restrict__ dh13,
                                                              const uint16_t* __restrict__ x,
-                                                             uint16_t* __restrict__ dW13, int32_t* queue) {
+                                                             uint16_t* __restrict__ dW13, int32_t* queue,
+                                                             float* __restrict__ partial, int32_t* plan_out) {
   MOE_GEMM_SMEM
   MOE_DW_SMEM
   const int H = int(p.H), I = int(p.I);
   const int MT = (2 * I) / BM, NT = H / BN;
-  dw_for_each_tile(p.counts, int(p.E), MT * NT, queue, s_cnt, s_order, &s_flag, &s_next, [&](int e, int local) {
-    const int nt = local % NT;
-    const int mt = local / NT;
-    const int rows = __builtin_amdgcn_readfirstlane(p.counts[e]);
-    const int64_t off = __builtin_amdgcn_readfirstlane(p.offsets[e]);
+  dw_for_each_item(p.counts, int(p.E), MT * NT, queue, plan_out, s_cnt, s_order, &s_flag, &s_next, &s_plan,
+                   [&](const DwItem& it) {
+    const int nt = it.local % NT;
+    const int mt = it.local / NT;
+    const int rows = it.klen;  // this item's rows of the expert, from row it.k0
+    const int64_t off = int64_t(__builtin_amdgcn_readfirstlane(p.offsets[it.e])) + it.k0;
     MNMajorLoader<DirectRows> lp;
     lp.set_base(dh13 + off * 2 * I + int64_t(mt) * BM, int64_t(rows) * 2 * I - int64_t(mt) * BM);
     lp.fn.ld = 2 * I;
@@ -1107,22 +1290,24 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     Acc acc;
     acc.zero();
     mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, lds, acc);
-    store_tile(acc, lds, dW13 + int64_t(e) * 2 * I * H, H, int64_t(mt) * BM, int64_t(nt) * BN, BM, BN);
+    dw_store(acc, it, lds, dW13 + int64_t(it.e) * 2 * I * H, H, int64_t(mt) * BM, int64_t(nt) * BN, BN, partial);
   });
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const uint16_t* __restrict__ dy,
                                                             const uint16_t* __restrict__ act,
-                                                            uint16_t* __restrict__ dW2, int32_t* queue) {
+                                                            uint16_t* __restrict__ dW2, int32_t* queue,
+                                                            float* __restrict__ partial, int32_t* plan_out) {
   MOE_GEMM_SMEM
   MOE_DW_SMEM
   const int H = int(p.H), I = int(p.I);
   const int MT = H / BM, NT = (I + BN - 1) / BN;  // the last n-tile may hold 128 columns
-  dw_for_each_tile(p.counts, int(p.E), MT * NT, queue, s_cnt, s_order, &s_flag, &s_next, [&](int e, int local) {
-    const int nt = local % NT;
-    const int mt = local / NT;
-    const int rows = __builtin_amdgcn_readfirstlane(p.counts[e]);
-    const int64_t off = __builtin_amdgcn_readfirstlane(p.offsets[e]);
+  dw_for_each_item(p.counts, int(p.E), MT * NT, queue, plan_out, s_cnt, s_order, &s_flag, &s_next, &s_plan,
+                   [&](const DwItem& it) {
+    const int nt = it.local % NT;
+    const int mt = it.local / NT;
+    const int rows = it.klen;  // this item's rows of the expert, from row it.k0
+    const int64_t off = int64_t(__builtin_amdgcn_readfirstlane(p.offsets[it.e])) + it.k0;
     MNMajorLoader<TokenRows> lp;
     lp.set_base(dy + int64_t(mt) * BM, p.T * H - int64_t(mt) * BM);
     lp.fn.ld = H;
@@ -1142,7 +1327,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     Acc acc;
     acc.zero();
     mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, lds, acc);
-    store_tile(acc, lds, dW2 + int64_t(e) * H * I, I, int64_t(mt) * BM, int64_t(nt) * BN, BM, ncols);
+    dw_store(acc, it, lds, dW2 + int64_t(it.e) * H * I, I, int64_t(mt) * BM, int64_t(nt) * BN, ncols, partial);
   });
 }
 
@@ -1192,28 +1377,34 @@ __global__ __launch_bounds__(kThreads) void gemm_dw_fp8_kernel(GemmProblem p, co
                                                                const uint8_t* __restrict__ pscales, int MP,
                                                                const uint8_t* __restrict__ qcodes,
                                                                const uint8_t* __restrict__ qscales, int NQ,
-                                                               uint16_t* __restrict__ dW, int32_t* queue) {
+                                                               uint16_t* __restrict__ dW, int32_t* queue,
+                                                               float* __restrict__ partial, int32_t* plan_out) {
   MOE_GEMM_SMEM
   MOE_DW_SMEM
   __shared__ int32_t s_kb[1025];
-  __shared__ int32_t s_tmp[kThreads];
   const int E = int(p.E);
-  block_prefix128(p.counts, E, s_kb, s_tmp);
+  block_prefix128(p.counts, E, s_kb, s_cnt);  // s_cnt as scratch: the schedule refills it
   const int MT = MP / BM, NT = (NQ + BN - 1) / BN;
-  dw_for_each_tile(p.counts, E, MT * NT, queue, s_cnt, s_order, &s_flag, &s_next, [&](int e, int local) {
-    const int nt = local % NT;
-    const int mt = local / NT;
-    const int kb = __builtin_amdgcn_readfirstlane(s_kb[e + 1] - s_kb[e]);  // 128-row blocks
+  dw_for_each_item(p.counts, E, MT * NT, queue, plan_out, s_cnt, s_order, &s_flag, &s_next, &s_plan,
+                   [&](const DwItem& it) {
+    const int nt = it.local % NT;
+    const int mt = it.local / NT;
+    const int e = it.e;
     const int64_t poff = int64_t(__builtin_amdgcn_readfirstlane(s_kb[e])) * 128;
-    const int64_t kp = int64_t(kb) * 128;
-    const int KU = int(kp / 2);  // row length in 16-bit units
+    const int64_t kp = int64_t(__builtin_amdgcn_readfirstlane(s_kb[e + 1] - s_kb[e])) * 128;  // Kp_e
+    // this item's codes [k0, kend) of each row (k0 a multiple of 128; the
+    // last split runs to Kp_e, over the zero codes past the rows)
+    const int64_t kend = it.S == 1 ? kp : min(kp, int64_t(it.k0) + it.chunk);
+    const int kb = int((kend - it.k0) / 128);
+    const int KU = int(kp / 2);  // row stride in 16-bit units
     const int ncols = min(BN, NQ - nt * BN);
+    const int64_t pb = int64_t(MP) * poff + int64_t(mt) * BM * kp + it.k0;  // byte of P row 0, code k0
+    const int64_t qb = int64_t(NQ) * poff + int64_t(nt) * BN * kp + it.k0;
     KMajorLoader8 lp, lq;
-    lp.set_base(reinterpret_cast<const uint16_t*>(pcodes + int64_t(MP) * poff + int64_t(mt) * BM * kp),
-                int64_t(BM) * KU, pscales + (int64_t(MP) * poff + int64_t(mt) * BM * kp) / 32, int64_t(BM) * kp / 32);
-    lq.set_base(reinterpret_cast<const uint16_t*>(qcodes + int64_t(NQ) * poff + int64_t(nt) * BN * kp),
-                int64_t(ncols) * KU, qscales + (int64_t(NQ) * poff + int64_t(nt) * BN * kp) / 32,
-                int64_t(ncols) * kp / 32);
+    lp.set_base(reinterpret_cast<const uint16_t*>(pcodes + pb), int64_t(BM) * KU - it.k0 / 2, pscales + pb / 32,
+                int64_t(BM) * kp / 32 - it.k0 / 32);
+    lq.set_base(reinterpret_cast<const uint16_t*>(qcodes + qb), int64_t(ncols) * KU - it.k0 / 2, qscales + qb / 32,
+                int64_t(ncols) * kp / 32 - it.k0 / 32);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
@@ -1223,7 +1414,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw_fp8_kernel(GemmProblem p, co
     Acc acc;
     acc.zero();
     mainloop_fp8(lp, lq, kb, lds, acc);  // an empty expert runs no slab and stores zeros
-    store_tile(acc, lds, dW + int64_t(e) * MP * NQ, NQ, int64_t(mt) * BM, int64_t(nt) * BN, BM, ncols);
+    dw_store(acc, it, lds, dW + int64_t(e) * MP * NQ, NQ, int64_t(mt) * BM, int64_t(nt) * BN, ncols, partial);
   });
 }
 
@@ -1293,39 +1484,65 @@ hipError_t launch_gemm_dx(const GemmProblem& p, GemmOperand dh13, GemmOperand W1
 }
 
 __global__ void zero_words_kernel(int32_t* p, int n) {
-  if (int(threadIdx.x) < n) p[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
 hipError_t launch_zero_queues(int32_t* queues, hipStream_t st, KernelTimer* timer) {
   TimedLaunch tl(timer, "zero_queues", st);
-  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, st, queues, kNumQueues);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, st, queues, kQueueWords);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x,
-                            uint16_t* dW13, int32_t* queue, hipStream_t st, KernelTimer* timer) {
-  const int grid = grid_for(p.E * (2 * p.I / BM) * (p.H / BN), p.num_cus);
-  TimedLaunch tl(timer, "gemm_dw13", st);
-  hipLaunchKernelGGL(gemm_dw13_kernel, dim3(grid), dim3(kThreads), 0, st, p, dh13, x, dW13, queue);
+static hipError_t launch_dw_split_sum(const int32_t* plan, const float* partial, int per_expert, int NT,
+                                      uint16_t* out, int64_t estride, int ld, hipStream_t st, KernelTimer* timer,
+                                      const char* name) {
+  TimedLaunch tl(timer, name, st);
+  hipLaunchKernelGGL(dw_split_sum_kernel, dim3(kSumGrid), dim3(kSumThreads), 0, st, plan, partial, per_expert, NT,
+                     out, estride, ld);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint16_t* act,
-                           uint16_t* dW2, int32_t* queue, hipStream_t st, KernelTimer* timer) {
-  const int grid = grid_for(p.E * (p.H / BM) * ((p.I + BN - 1) / BN), p.num_cus);
-  TimedLaunch tl(timer, "gemm_dw2", st);
-  hipLaunchKernelGGL(gemm_dw2_kernel, dim3(grid), dim3(kThreads), 0, st, p, dy, act, dW2, queue);
-  return hipGetLastError();
+hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x, uint16_t* dW13,
+                            int32_t* queue, float* partial, int32_t* plan, hipStream_t st, KernelTimer* timer) {
+  const int MT = int(2 * p.I / BM), NT = int(p.H / BN);
+  const int grid = grid_for(p.E * MT * NT, p.num_cus);
+  {
+    TimedLaunch tl(timer, "gemm_dw13", st);
+    hipLaunchKernelGGL(gemm_dw13_kernel, dim3(grid), dim3(kThreads), 0, st, p, dh13, x, dW13, queue, partial, plan);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_dw_split_sum(plan, partial, MT * NT, NT, dW13, 2 * p.I * p.H, int(p.H), st, timer,
+                             "dw13_split_sum");
+}
+
+hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint16_t* act, uint16_t* dW2,
+                           int32_t* queue, float* partial, int32_t* plan, hipStream_t st, KernelTimer* timer) {
+  const int MT = int(p.H / BM), NT = int((p.I + BN - 1) / BN);
+  const int grid = grid_for(p.E * MT * NT, p.num_cus);
+  {
+    TimedLaunch tl(timer, "gemm_dw2", st);
+    hipLaunchKernelGGL(gemm_dw2_kernel, dim3(grid), dim3(kThreads), 0, st, p, dy, act, dW2, queue, partial, plan);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_dw_split_sum(plan, partial, MT * NT, NT, dW2, p.H * p.I, int(p.I), st, timer, "dw2_split_sum");
 }
 
 hipError_t launch_gemm_dw_fp8(const GemmProblem& p, const uint8_t* pcodes, const uint8_t* pscales, int MP,
                               const uint8_t* qcodes, const uint8_t* qscales, int NQ, uint16_t* dW, int32_t* queue,
-                              hipStream_t st, KernelTimer* timer, const char* name) {
-  const int grid = grid_for(p.E * (MP / BM) * ((NQ + BN - 1) / BN), p.num_cus);
-  TimedLaunch tl(timer, name, st);
-  hipLaunchKernelGGL(gemm_dw_fp8_kernel, dim3(grid), dim3(kThreads), 0, st, p, pcodes, pscales, MP, qcodes, qscales,
-                     NQ, dW, queue);
-  return hipGetLastError();
+                              float* partial, int32_t* plan, hipStream_t st, KernelTimer* timer, const char* name,
+                              const char* sum_name) {
+  const int MT = MP / BM, NT = (NQ + BN - 1) / BN;
+  const int grid = grid_for(p.E * MT * NT, p.num_cus);
+  {
+    TimedLaunch tl(timer, name, st);
+    hipLaunchKernelGGL(gemm_dw_fp8_kernel, dim3(grid), dim3(kThreads), 0, st, p, pcodes, pscales, MP, qcodes,
+                       qscales, NQ, dW, queue, partial, plan);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_dw_split_sum(plan, partial, MT * NT, NT, dW, int64_t(MP) * NQ, NQ, st, timer, sum_name);
 }
 
 }  // namespace moe

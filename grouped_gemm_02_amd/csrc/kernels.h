@@ -72,13 +72,20 @@ hipError_t launch_gemm_dh(const GemmProblem& p, GemmOperand dy, GemmOperand W2, 
                           uint16_t* dh13, float* dwpart, hipStream_t st, KernelTimer* timer);
 hipError_t launch_gemm_dx(const GemmProblem& p, GemmOperand dh13, GemmOperand W13, uint16_t* dx_rows,
                           hipStream_t st, KernelTimer* timer);
-// weight gradients; each takes one zeroed queue word (tile counter)
+// weight gradients; each takes one zeroed queue word (tile counter), the
+// fp32 partial tiles of split items (kSplitFloats floats, shared: the
+// weight-gradient GEMMs run one after the other) and kSplitWords words of its
+// own for the split plan, which the GEMM writes and its split-sum kernel
+// (launched right after it by the same call) reads
 constexpr int kNumQueues = 2;
+constexpr int kSplitWords = 256;
+constexpr int kQueueWords = kNumQueues + 2 * kSplitWords;  // queues, then the plan words of both GEMMs
+constexpr int64_t kSplitFloats = int64_t(256) * 256 * 256;
 hipError_t launch_zero_queues(int32_t* queues, hipStream_t st, KernelTimer* timer);
 hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x, uint16_t* dW13,
-                            int32_t* queue, hipStream_t st, KernelTimer* timer);
+                            int32_t* queue, float* partial, int32_t* plan, hipStream_t st, KernelTimer* timer);
 hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint16_t* act, uint16_t* dW2,
-                           int32_t* queue, hipStream_t st, KernelTimer* timer);
+                           int32_t* queue, float* partial, int32_t* plan, hipStream_t st, KernelTimer* timer);
 
 // ---------------------------------------------------------------- FP8 quantization
 constexpr int kRulePow2 = 0;  // smallest 2^e with 448 * 2^e >= amax
@@ -106,7 +113,8 @@ hipError_t launch_quant_tokens(const uint16_t* in, int64_t ld, int C, const int3
 // row-major [MP][NQ]) = sum over the expert's rows of P'[m][r] Q'[n][r]
 hipError_t launch_gemm_dw_fp8(const GemmProblem& p, const uint8_t* pcodes, const uint8_t* pscales, int MP,
                               const uint8_t* qcodes, const uint8_t* qscales, int NQ, uint16_t* dW, int32_t* queue,
-                              hipStream_t st, KernelTimer* timer, const char* name);
+                              float* partial, int32_t* plan, hipStream_t st, KernelTimer* timer, const char* name,
+                              const char* sum_name);
 
 // ---------------------------------------------------------------- router
 // logits fp32 [T, E] -> idx int32 [T, k] (descending logit, ties to the lower

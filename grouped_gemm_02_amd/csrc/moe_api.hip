@@ -122,7 +122,8 @@ FwdLayout fwd_layout(const moe_shape& s) {
 }
 
 struct BwdLayout {
-  size_t queues;  // int32 tile counters of the weight-gradient GEMMs
+  size_t queues;   // int32: tile queues, then the split plans, of the weight-gradient GEMMs
+  size_t partial;  // fp32 partial tiles of split weight-gradient items
   size_t dh13, dwpart, dxrows;
   size_t dyq, dys;  // FP8 backward: dY codes [T, H], scales [T, H/32]
   size_t dhq, dhs;  // FP8 backward: [dg | du] codes [Tk, 2I], scales [Tk, 2I/32]
@@ -136,7 +137,8 @@ BwdLayout bwd_layout(const moe_shape& s) {
   const int64_t Tk = s.T * s.k;
   BwdLayout L;
   size_t o = 0;
-  L.queues = o; o = align_up(o + size_t(kNumQueues) * 4);
+  L.queues = o; o = align_up(o + size_t(kQueueWords) * 4);
+  L.partial = o; o = align_up(o + size_t(kSplitFloats) * 4);
   L.dh13 = o;   o = align_up(o + size_t(Tk) * size_t(2 * s.I) * 2);
   L.dwpart = o; o = align_up(o + size_t(Tk) * size_t(dh_num_parts(s.I)) * 4);
   L.dxrows = o; o = align_up(o + size_t(Tk) * size_t(s.H) * 2);
@@ -479,6 +481,9 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
   KernelTimer* tm = timer();
   GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w, wrow};
   int32_t* queues = at<int32_t>(ws, BL.queues);
+  int32_t* plan13 = queues + kNumQueues;  // split plans of the two weight-gradient GEMMs
+  int32_t* plan2 = plan13 + kSplitWords;
+  float* partial = at<float>(ws, BL.partial);
   hipError_t e = launch_zero_queues(queues, hs, tm);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
   const bool wg8 = fp8_wgrad(*s);
@@ -535,8 +540,8 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
     uint8_t* wgas = at<uint8_t>(ws, BL.wgas);
     if ((e = launch_quant_tokens(x16, H, H, counts, offsets, E, Tk, src_of, kk, wgx, wgxs, rule, hs, tm,
                                  "quant_wg_x")) != hipSuccess ||
-        (e = launch_gemm_dw_fp8(gp, wgd, wgds, 2 * I, wgx, wgxs, H, static_cast<uint16_t*>(dW13), queues, hs, tm,
-                                "gemm_dw13_fp8")) != hipSuccess)
+        (e = launch_gemm_dw_fp8(gp, wgd, wgds, 2 * I, wgx, wgxs, H, static_cast<uint16_t*>(dW13), queues, partial,
+                                plan13, hs, tm, "gemm_dw13_fp8", "dw13_split_sum")) != hipSuccess)
       return MOE_ERR_LAUNCH;
     if (kk != 1 && (e = launch_quant_tokens(dy16, H, H, counts, offsets, E, Tk, src_of, kk, wgy, wgys, rule, hs,
                                             tm, "quant_wg_dy")) != hipSuccess)
@@ -544,13 +549,14 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
     if ((e = launch_quant_tokens(act, I, I, counts, offsets, E, Tk, nullptr, 1, wga, wgas, rule, hs, tm,
                                  "quant_wg_act")) != hipSuccess)
       return MOE_ERR_LAUNCH;
-    e = launch_gemm_dw_fp8(gp, wgy, wgys, H, wga, wgas, I, static_cast<uint16_t*>(dW2), queues + 1, hs, tm,
-                           "gemm_dw2_fp8");
+    e = launch_gemm_dw_fp8(gp, wgy, wgys, H, wga, wgas, I, static_cast<uint16_t*>(dW2), queues + 1, partial,
+                           plan2, hs, tm, "gemm_dw2_fp8", "dw2_split_sum");
     return launch_status(e);
   }
-  if ((e = launch_gemm_dw13(gp, dh13, x16, static_cast<uint16_t*>(dW13), queues, hs, tm)) != hipSuccess)
+  if ((e = launch_gemm_dw13(gp, dh13, x16, static_cast<uint16_t*>(dW13), queues, partial, plan13, hs, tm)) !=
+      hipSuccess)
     return MOE_ERR_LAUNCH;
-  e = launch_gemm_dw2(gp, dy16, act, static_cast<uint16_t*>(dW2), queues + 1, hs, tm);
+  e = launch_gemm_dw2(gp, dy16, act, static_cast<uint16_t*>(dW2), queues + 1, partial, plan2, hs, tm);
   return launch_status(e);
 }
 

@@ -227,6 +227,14 @@ SMALL = [
     inputs.LayerConfig("top1", 257, 768, 128, 40, 1, "uniform", "bf16", 13),
 ]
 CASES = [(c, m) for c in SMALL for m in MODES]
+# Hot experts whose weight-gradient tiles are split along the expert's rows
+# (2813 rows into 4 ranges, 1179 into 4). Blockwise only: the FP8 dW kernel's
+# split handling is the same for both scale rules, and with 32-row MX blocks
+# the kernel's bf16 operands (rounded before quantization, unlike the fp64
+# oracle's) already flip enough codes over these long reductions to reach
+# the tolerance (about 4.4e-2 from that rounding alone, on the CPU).
+HOT = inputs.LayerConfig("hot", 8192, 512, 384, 32, 1, "zipf", "bf16", 21, zipf_s=1.2, zipf_cold=8)
+WGRAD_CASES = CASES + [(HOT, "fp8_block")]
 
 
 @pytest.mark.parametrize("cfg,mode", CASES, ids=[f"{c.name}-{m}" for c, m in CASES])
@@ -263,7 +271,7 @@ def test_fp8_layer_matches_oracle_elementwise(B, cfg, mode):
         assert not out["dW13"][e].any() and not out["dW2"][e].any()
 
 
-@pytest.mark.parametrize("cfg,mode", CASES, ids=[f"{c.name}-{m}" for c, m in CASES])
+@pytest.mark.parametrize("cfg,mode", WGRAD_CASES, ids=[f"{c.name}-{m}" for c, m in WGRAD_CASES])
 def test_fp8_weight_gradients_match_oracle_elementwise(B, cfg, mode):
     """MOE_FLAG_FP8_WGRAD: dW13 and dW2 from operands quantized along each
     expert's rows; the other outputs equal those of the default reading."""

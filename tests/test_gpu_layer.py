@@ -126,6 +126,39 @@ def test_layer_matches_oracle_elementwise(B, cfg):
     check_full(out, cfg, d)
 
 
+# Skewed routing with experts hot enough that their weight-gradient tiles are
+# cut along the expert's rows (at least 1024 rows and over 3/4 of one
+# workgroup's nominal share, under a max * E > 2 * total skew): the hottest
+# expert (2813 rows) into 4 row ranges of 768, the next (1179 rows) into 4 of
+# 384, both with a ragged last range.
+HOT = inputs.LayerConfig("hot", 8192, 512, 384, 32, 1, "zipf", "bf16", 21, zipf_s=1.2, zipf_cold=8)
+
+
+def _assert_split_routing(d, cfg):
+    c = np.bincount(d["topk_idx"].cpu().numpy().ravel(), minlength=cfg.E)
+    assert int(c.max()) * cfg.E > 2 * int(c.sum()) and np.sort(c)[-2] >= 1024, np.sort(c)[-4:]
+
+
+def test_split_weight_gradients_match_oracle_elementwise(B):
+    cfg = HOT
+    _say(f"case split dW {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    _assert_split_routing(d, cfg)
+    out = run_layer(B, cfg, d)
+    assert out["status"] == 0
+    check_full(out, cfg, d)
+
+
+def test_split_weight_gradients_deterministic_bitwise(B):
+    cfg = HOT
+    _say(f"case split dW determinism {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    a = run_layer(B, cfg, d)
+    b = run_layer(B, cfg, d, num_cus=37)
+    for k in ("dW13", "dW2"):
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_layer_deterministic_bitwise(B):
     cfg = SMALL[1]
     _say(f"case determinism {inputs.describe(cfg)}")
