@@ -10,13 +10,14 @@ OUT=${1:-gpurun_out/prof}
 export TMPDIR=/tmp
 PROF="$OUT/profiles"
 mkdir -p "$OUT" "$PROF"
-# workload:precision:weight-gradient reading
-for cpw in qwen3_30b:bf16:bf16 ep8_share:fp8_block:bf16 qwen3_235b:fp8_bwd:bf16 zipf:mxfp8:bf16 \
-           ep8_share:fp8_block:fp8 qwen3_235b:fp8_bwd:fp8 zipf:mxfp8:fp8; do
-  c=${cpw%%:*}; rest=${cpw#*:}; prec=${rest%%:*}; wg=${rest##*:}
-  tag=${c}_${prec}; [ "$wg" = fp8 ] && tag=${tag}_fp8_wgrad
+# workload:precision:weight-gradient reading:router step
+for cpw in qwen3_30b:bf16:bf16:none ep8_share:fp8_block:bf16:none qwen3_235b:fp8_bwd:bf16:none \
+           zipf:mxfp8:bf16:none ep8_share:fp8_block:fp8:none qwen3_235b:fp8_bwd:fp8:none zipf:mxfp8:fp8:none \
+           qwen3_30b:bf16:bf16:skewed; do
+  IFS=: read -r c prec wg rt <<< "$cpw"
+  tag=${c}_${prec}; [ "$wg" = fp8 ] && tag=${tag}_fp8_wgrad; [ "$rt" != none ] && tag=${tag}_router_${rt}
   echo "stats $tag"
-  args="--config $c --wgrad $wg --steps 5 --warmup 2 --no-cpu-baseline"
+  args="--config $c --precision $prec --wgrad $wg --router $rt --steps 5 --warmup 2 --no-cpu-baseline"
   timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/stats_$tag" -o run -- \
     python3 bench.py $args > "$OUT/stats_$tag.log" 2>&1
   python3 -m grouped_gemm_02_amd.profile_summary stats "$OUT/stats_$tag/run_kernel_stats.csv" \
