@@ -226,7 +226,23 @@ SMALL = [
     inputs.LayerConfig("skew", 333, 256, 128, 16, 4, "zipf", "bf16", 11, zipf_s=1.2, zipf_cold=5),
     inputs.LayerConfig("top1", 257, 768, 128, 40, 1, "uniform", "bf16", 13),
 ]
-CASES = [(c, m) for c in SMALL for m in MODES]
+# the maximum expert count under skew (MX only: the oracle's weight
+# quantization of 1024 experts takes ~25 s, so it runs once per mode here)
+MAXE = inputs.LayerConfig("max_experts_zipf", 700, 256, 128, 1024, 8, "zipf", "bf16", 16, zipf_s=1.1,
+                          zipf_cold=100)
+CASES = [(c, m) for c in SMALL for m in MODES] + [(MAXE, "mxfp8")]
+
+_WQ = {}
+
+
+def _oracle_wq(cfg, mode, d):
+    """The oracle's quantized weights of a configuration's seeded weights
+    (the same values in every test that makes this configuration's inputs),
+    computed once per (configuration, mode)."""
+    key = (cfg.name, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.seed, mode)
+    if key not in _WQ:
+        _WQ[key] = f8.quantize_weights(d["W13"], d["W2"], mode)
+    return _WQ[key]
 # Hot experts whose weight-gradient tiles are split along the expert's rows
 # (2813 rows into 4 ranges, 1179 into 4). Blockwise only: the FP8 dW kernel's
 # split handling is the same for both scale rules, and with 32-row MX blocks
@@ -245,7 +261,7 @@ def test_fp8_layer_matches_oracle_elementwise(B, cfg, mode):
     out = run_layer(B, cfg, d, mode)
     assert out["status"] == 0
     args = (d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
-    wq = f8.quantize_weights(d["W13"], d["W2"], mode)
+    wq = _oracle_wq(cfg, mode, d)
     y_ref, pairs = f8.forward(*args, mode, return_pairs=True, wq=wq)
     dx_ref, dw_ref, dW13_ref, dW2_ref = f8.backward(d["dy"], *args, mode, wq=wq)
     errs = {
@@ -284,7 +300,7 @@ def test_fp8_weight_gradients_match_oracle_elementwise(B, cfg, mode):
     for k in ("y", "dx", "dw"):
         assert torch.equal(out[k], base[k]), k
     args = (d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
-    wq = f8.quantize_weights(d["W13"], d["W2"], mode)
+    wq = _oracle_wq(cfg, mode, d)
     _, _, dW13_ref, dW2_ref = f8.backward(d["dy"], *args, mode, wq=wq, wgrad="fp8")
     errs = {"dW13": max_rel_err(orc.as_f64(out["dW13"]), dW13_ref),
             "dW2": max_rel_err(orc.as_f64(out["dW2"]), dW2_ref)}

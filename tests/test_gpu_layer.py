@@ -114,6 +114,10 @@ SMALL = [
     inputs.LayerConfig("top1", 257, 768, 128, 40, 1, "uniform", "bf16", 13),
     # a single token
     inputs.LayerConfig("one_token", 1, 256, 128, 8, 8, "uniform", "bf16", 14),
+    # the maximum expert count: ~5 rows per expert, many experts empty
+    inputs.LayerConfig("max_experts", 600, 256, 128, 1024, 8, "uniform", "bf16", 15),
+    # the maximum expert count under skew (the weight gradients' queue schedule)
+    inputs.LayerConfig("max_experts_zipf", 700, 256, 384, 1024, 8, "zipf", "bf16", 16, zipf_s=1.1, zipf_cold=100),
 ]
 
 

@@ -48,6 +48,8 @@ CASES = [
     (16384, 8, 128, "uniform", 4),   # 30B shape
     (16384, 8, 128, "zipf", 5),      # empty experts, one hot expert
     (131072, 1, 16, "uniform", 6),   # EP=8 share shape
+    (3000, 8, 1024, "uniform", 9),   # the maximum expert count, most experts nearly empty
+    (3000, 8, 1024, "zipf", 10),     # the maximum expert count, skewed
     (3000, 4, 1024, "uniform", 7),   # the largest expert count
     (16384, 8, 1024, "zipf", 9),     # 128 chunks, one scan segment
 ]
