@@ -395,6 +395,52 @@ struct KMajorLoader8 : KMajorLoader {
 template <bool FP8>
 using KLoader = typename std::conditional<FP8, KMajorLoader8, KMajorLoader>::type;
 
+// k-major E2M1 operand (FP4 weights: two codes per byte, the even k in the
+// low nibble) with scales [rows, K/32]. A k-slab is 128 codes = 64 bytes per
+// row, kept in the first 64 bytes of the FP8 LDS row, its 4 scale bytes at
+// byte 128 as for FP8. Thread t moves chunk t % 4 of rows t/4 and t/4 + 128,
+// and the scale bytes of row t/4 + 128 * (t % 2) (threads t and t+2
+// duplicate each other, which keeps every load and LDS write unconditional).
+// Offsets are set in 16-bit units (K/4 units per row); the scale row of a
+// code row at byte offset o is at byte o/16 of the scales.
+struct Stage4 {
+  u32x4 r[2];
+  uint32_t s;
+};
+
+struct KMajorLoader4 {
+  __amdgpu_buffer_rsrc_t data, scale;
+  uint32_t off[2];
+  uint32_t soff;
+  static constexpr int kRows = 2;
+
+  __device__ __forceinline__ static int row_of_thread(int i) { return (threadIdx.x >> 2) + 128 * i; }
+  __device__ __forceinline__ void set_base(const uint16_t* base, int64_t units, const uint8_t* sbase,
+                                           int64_t sbytes) {
+    data = make_rsrc(base, units * 2);
+    scale = make_rsrc(sbase, sbytes);
+  }
+  __device__ __forceinline__ void set_row(int i, int64_t row_off) {
+    off[i] = uint32_t(row_off * 2) + (threadIdx.x & 3) * 16;
+    if (int(threadIdx.x & 1) == i) soff = uint32_t(row_off * 2) >> 4;
+  }
+  __device__ __forceinline__ void fetch(int kt, Stage4& st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st.r[i] = __builtin_amdgcn_raw_buffer_load_b128(data, off[i], kt * 64, 0);
+    st.s = __builtin_amdgcn_raw_buffer_load_b32(scale, soff, kt * 4, 0);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, const Stage4& st) const {
+    const int r0 = threadIdx.x >> 2, c = threadIdx.x & 3;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(lds + (r0 + 128 * i) * LDK + c * 8) = st.r[i];
+    *reinterpret_cast<uint32_t*>(lds + (r0 + 128 * (c & 1)) * LDK + BK) = st.s;
+  }
+};
+
+template <class L> struct StageOf { using type = Stage; };
+template <> struct StageOf<KMajorLoader8> { using type = Stage8; };
+template <> struct StageOf<KMajorLoader4> { using type = Stage4; };
+
 __device__ __forceinline__ i32x8 frag8(const uint16_t* lds, int ent0, int s) {
   const int lane = lane_id();
   const uint16_t* p = lds + (ent0 + (lane & 31)) * LDK + s * 32 + (lane >> 5) * 8;
@@ -409,6 +455,17 @@ __device__ __forceinline__ int scale8(const uint16_t* lds, int ent0, int s) {
   return reinterpret_cast<const uint8_t*>(lds + (ent0 + (lane & 31)) * LDK + BK)[2 * s + (lane >> 5)];
 }
 
+// An E2M1 operand of the same MFMA (measured on gfx950): a lane of half h
+// holds k = 32h .. 32h+31 of its row as 32 nibbles in registers 0-3, value
+// 2j in the low nibble of byte j, i.e. 16 consecutive bytes of the row; its
+// scale is that of k-block h, as for FP8 (the instruction reads 4 registers).
+__device__ __forceinline__ i32x8 frag4(const uint16_t* lds, int ent0, int s) {
+  const int lane = lane_id();
+  const u32x4 a = *reinterpret_cast<const u32x4*>(lds + (ent0 + (lane & 31)) * LDK + s * 16 + (lane >> 5) * 8);
+  return i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
+}
+
+template <bool W4 = false>
 __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
   const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
 #pragma unroll
@@ -417,7 +474,7 @@ __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_
     int qs[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      qf[j] = frag8(ldsQ, qn0 + 32 * j, s);
+      qf[j] = W4 ? frag4(ldsQ, qn0 + 32 * j, s) : frag8(ldsQ, qn0 + 32 * j, s);
       qs[j] = scale8(ldsQ, qn0 + 32 * j, s);
     }
 #pragma unroll
@@ -426,13 +483,16 @@ __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_
       const int ps = scale8(ldsP, pm0 + 32 * i, s);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[j], pf, acc.c[i][j], 0, 0, 0, qs[j], 0, ps);
+        acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[j], pf, acc.c[i][j], W4 ? 4 : 0, 0, 0,
+                                                                      qs[j], 0, ps);
     }
   }
 }
 
-__device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, uint16_t* lds,
-                                                    Acc& acc, bool active, Stage8& sp, Stage8& sq) {
+template <class LQ = KMajorLoader8>
+__device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc,
+                                                    bool active, Stage8& sp, typename StageOf<LQ>::type& sq) {
+  constexpr bool W4 = std::is_same<LQ, KMajorLoader4>::value;
   if (nk <= 0) return;
   lp.store(lds, sp);
   lq.store(lds + kOperandLds, sq);
@@ -445,7 +505,7 @@ __device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, KMajorLoa
       lp.fetch(kt + 1, sp);
       lq.fetch(kt + 1, sq);
     }
-    if (active) mma_slab_fp8(cur, cur + kOperandLds, acc);
+    if (active) mma_slab_fp8<W4>(cur, cur + kOperandLds, acc);
     // unconditional (after the last slab it rewrites stale data into the idle
     // buffer): a conditional block here lets the compiler sink the MFMAs
     // below it, with every fragment of the slab live at once
@@ -638,7 +698,8 @@ struct TileState {
 template <bool FP8, bool Q_MN, bool PREFETCH, class LP, class LQ, class Setup, class Epi>
 __device__ __forceinline__ void row_tile_walk(int64_t total, int nk, uint16_t* lds, LP& lp, LQ& lq, Setup&& setup,
                                               Epi&& epi) {
-  typename std::conditional<FP8, Stage8, Stage>::type sp, sq;
+  typename StageOf<LP>::type sp;
+  typename StageOf<LQ>::type sq;
   TileState cur, nxt;
   int64_t t = first_tile();
   if (PREFETCH && t < total) {
@@ -699,7 +760,7 @@ struct Operand {
 template <bool FP8>
 __device__ __forceinline__ int row_units(int K) { return FP8 ? K / 2 : K; }
 
-template <bool FP8>
+template <bool FP8, bool W4 = false>
 __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, Operand X, Operand W,
                                                                 uint16_t* __restrict__ h13,
                                                                 uint16_t* __restrict__ act) {
@@ -709,14 +770,16 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
   MOE_ROW_SCHED
   const int NT = (2 * I) / BN;
   const int KU = row_units<FP8>(H);
+  const int KW = W4 ? KU / 2 : KU;  // weight row in 16-bit units
   const int64_t total = int64_t(s_pref[E]) * NT;
-  KLoader<FP8> lp, lq;
+  KLoader<FP8> lp;
+  typename std::conditional<W4, KMajorLoader4, KLoader<FP8>>::type lq;
   auto setup = [&](int64_t t, TileState& st) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
     st.rt = rt;
     if constexpr (FP8) {
       lp.set_base(static_cast<const uint16_t*>(X.data), p.T * KU, X.scales, p.T * (H / 32));
-      lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * KU, 2 * I * KU,
+      lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * 2 * I * KW, 2 * I * KW,
                   W.scales + int64_t(rt.e) * 2 * I * (H / 32), 2 * I * (H / 32));
     } else {
       lp.set_base(static_cast<const uint16_t*>(X.data), p.T * KU);
@@ -727,7 +790,12 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
       const int m = KMajorLoader::row_of_thread(i);
       const int mc = m < rt.rows ? m : rt.rows - 1;  // past-the-end rows reuse a real row
       lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * KU);
-      lq.set_row(i, int64_t(g1::w13_row(m, rt.nt, I)) * KU);
+      if constexpr (!W4) lq.set_row(i, int64_t(g1::w13_row(m, rt.nt, I)) * KU);
+    }
+    if constexpr (W4) {
+#pragma unroll
+      for (int i = 0; i < KMajorLoader4::kRows; ++i)
+        lq.set_row(i, int64_t(g1::w13_row(KMajorLoader4::row_of_thread(i), rt.nt, I)) * KW);
     }
     // routing weight of tile row t: loaded now, used after the k loop
     st.w = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
@@ -766,7 +834,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
 
 // ================================================================== forward GEMM2
 // O[r][h] = (w a)[r] . W2[e][h],  K = I.
-template <bool FP8>
+template <bool FP8, bool W4 = false>
 __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand A, Operand W,
                                                          uint16_t* __restrict__ out) {
   MOE_GEMM_SMEM
@@ -774,16 +842,18 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
   MOE_ROW_SCHED
   const int NT = H / BN;
   const int KU = row_units<FP8>(I);
+  const int KW = W4 ? KU / 2 : KU;  // weight row in 16-bit units
   const int64_t total = int64_t(s_pref[E]) * NT;
-  KLoader<FP8> lp, lq;
+  KLoader<FP8> lp;
+  typename std::conditional<W4, KMajorLoader4, KLoader<FP8>>::type lq;
   auto setup = [&](int64_t t, TileState& st) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
     st.rt = rt;
     if constexpr (FP8) {
       lp.set_base(static_cast<const uint16_t*>(A.data) + rt.row0 * KU, int64_t(rt.rows) * KU,
                   A.scales + rt.row0 * (I / 32), int64_t(rt.rows) * (I / 32));
-      lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * KU,
-                  int64_t(BN) * KU, W.scales + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * (I / 32),
+      lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * KW,
+                  int64_t(BN) * KW, W.scales + (int64_t(rt.e) * H + int64_t(rt.nt) * BN) * (I / 32),
                   int64_t(BN) * (I / 32));
     } else {
       lp.set_base(static_cast<const uint16_t*>(A.data) + rt.row0 * KU, int64_t(rt.rows) * KU);
@@ -794,7 +864,11 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
       lp.set_row(i, int64_t(m < rt.rows ? m : rt.rows - 1) * KU);
-      lq.set_row(i, int64_t(m) * KU);
+      if constexpr (!W4) lq.set_row(i, int64_t(m) * KU);
+    }
+    if constexpr (W4) {
+#pragma unroll
+      for (int i = 0; i < KMajorLoader4::kRows; ++i) lq.set_row(i, int64_t(KMajorLoader4::row_of_thread(i)) * KW);
     }
   };
   // k == 1: each row is its token's whole result, written to the token row
@@ -1439,7 +1513,10 @@ hipError_t launch_gemm1_swiglu(const GemmProblem& p, GemmOperand x, GemmOperand 
                                uint16_t* act, hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(row_tiles_upper(p) * (2 * p.I / BN), p.num_cus);
   const Operand X{x.data, x.scales}, W{W13.data, W13.scales};
-  if (x.scales) {
+  if (W13.fp4) {
+    TimedLaunch tl(timer, "gemm1_swiglu_fp8_fp4", st);
+    hipLaunchKernelGGL((gemm1_swiglu_kernel<true, true>), dim3(grid), dim3(kThreads), 0, st, p, X, W, h13, act);
+  } else if (x.scales) {
     TimedLaunch tl(timer, "gemm1_swiglu_fp8", st);
     hipLaunchKernelGGL(gemm1_swiglu_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, X, W, h13, act);
   } else {
@@ -1453,7 +1530,10 @@ hipError_t launch_gemm2(const GemmProblem& p, GemmOperand act, GemmOperand W2, u
                         hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(row_tiles_upper(p) * (p.H / BN), p.num_cus);
   const Operand A{act.data, act.scales}, W{W2.data, W2.scales};
-  if (act.scales) {
+  if (W2.fp4) {
+    TimedLaunch tl(timer, "gemm2_fp8_fp4", st);
+    hipLaunchKernelGGL((gemm2_kernel<true, true>), dim3(grid), dim3(kThreads), 0, st, p, A, W, out_rows);
+  } else if (act.scales) {
     TimedLaunch tl(timer, "gemm2_fp8", st);
     hipLaunchKernelGGL(gemm2_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, A, W, out_rows);
   } else {

@@ -60,6 +60,7 @@ struct GemmProblem {
 struct GemmOperand {
   const void* data;
   const uint8_t* scales;
+  bool fp4 = false;  // E2M1 codes, two per byte (weights of the FP8 x FP4 forward)
 };
 // forward
 hipError_t launch_gemm1_swiglu(const GemmProblem& p, GemmOperand x, GemmOperand W13, uint16_t* h13,
@@ -98,6 +99,11 @@ hipError_t launch_quant_rows(const uint16_t* in, int64_t rows, int K, uint8_t* c
 // exponent per tile, MX rule: per 32 values of an output row
 hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* pcodes, uint8_t* pscales,
                                 uint8_t* tcodes, uint8_t* tscales, int rule, hipStream_t st, KernelTimer* timer);
+
+// bf16 [rows, C] -> E2M1 codes [rows, C/2] (two per byte, the even value in the
+// low nibble) + E8M0 scales [rows, C/32], 32-blocks along the rows, MX rule for E2M1
+hipError_t launch_quant_fp4_rows(const uint16_t* in, int64_t rows, int C, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t st, KernelTimer* timer);
 
 // The FP8 weight-gradient operands: rows of every expert quantized along the
 // rows (codes [C][Kp_e] per expert, Kp_e = rows rounded up to 128, experts

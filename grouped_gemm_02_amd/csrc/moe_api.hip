@@ -23,7 +23,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_NULL;
-  if (s->precision < MOE_BF16 || s->precision > MOE_FP8_BWD) return MOE_ERR_PRECISION;
+  if (s->precision < MOE_BF16 || s->precision > MOE_FP8_FP4) return MOE_ERR_PRECISION;
   if (s->T < 0 || s->E < 1 || s->E > 1024 || s->k < 1 || s->k > s->E) return MOE_ERR_SHAPE;
   if (s->H < 256 || s->H > 16384 || s->H % 256 != 0) return MOE_ERR_SHAPE;
   if (s->I < 128 || s->I > 8192 || s->I % 128 != 0) return MOE_ERR_SHAPE;
@@ -33,7 +33,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->num_cus < 0 || s->reserved != 0) return MOE_ERR_SHAPE;
   if ((s->flags & ~MOE_FLAG_FP8_WGRAD) != 0) return MOE_ERR_PRECISION;
   if ((s->flags & MOE_FLAG_FP8_WGRAD) != 0) {
-    if (s->precision == MOE_BF16) return MOE_ERR_PRECISION;
+    if (s->precision == MOE_BF16 || s->precision == MOE_FP8_FP4) return MOE_ERR_PRECISION;  // no FP8 backward
     // 32-bit offsets inside a weight-gradient tile's 256 rows of Kp codes
     if (s->T * s->k >= (int64_t(1) << 23)) return MOE_ERR_SHAPE;
   }
@@ -42,11 +42,17 @@ moe_status check_shape(const moe_shape* s) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool fp8_forward(const moe_shape& s) { return s.precision == MOE_FP8_BLOCK || s.precision == MOE_MXFP8; }
-bool fp8_backward(const moe_shape& s) { return s.precision != MOE_BF16; }
+bool fp8_forward(const moe_shape& s) {
+  return s.precision == MOE_FP8_BLOCK || s.precision == MOE_MXFP8 || s.precision == MOE_FP8_FP4;
+}
+bool fp8_backward(const moe_shape& s) {
+  return s.precision == MOE_FP8_BLOCK || s.precision == MOE_MXFP8 || s.precision == MOE_FP8_BWD;
+}
+bool fp4_weights(const moe_shape& s) { return s.precision == MOE_FP8_FP4; }
 // activation block (32 or 128 values along the reduction axis) and scale rule
-int act_block(const moe_shape& s) { return s.precision == MOE_MXFP8 ? 32 : 128; }
-int scale_rule(const moe_shape& s) { return s.precision == MOE_MXFP8 ? kRuleMx : kRulePow2; }
+bool mx_acts(const moe_shape& s) { return s.precision == MOE_MXFP8 || s.precision == MOE_FP8_FP4; }
+int act_block(const moe_shape& s) { return mx_acts(s) ? 32 : 128; }
+int scale_rule(const moe_shape& s) { return mx_acts(s) ? kRuleMx : kRulePow2; }
 bool fp8_wgrad(const moe_shape& s) { return (s.flags & MOE_FLAG_FP8_WGRAD) != 0; }
 // an upper bound of the sum over experts of rows rounded up to 128
 int64_t wgrad_rows_cap(const moe_shape& s) { return 128 * ((s.T * s.k) / 128 + s.E); }
@@ -73,9 +79,10 @@ moe_wq_layout wq_layout(const moe_shape& s) {
   size_t o = 0;
   const int64_t E = s.E, H = s.H, I = s.I;
   if (fp8_forward(s)) {
-    L.w13 = o;       o += codes_bytes(E * 2 * I, H);
+    const int64_t div = fp4_weights(s) ? 2 : 1;  // FP4: two codes per byte
+    L.w13 = o;       o += codes_bytes(E * 2 * I, H / div);
     L.w13_scale = o; o += scale_bytes(E * 2 * I, H);
-    L.w2 = o;        o += codes_bytes(E * H, I);
+    L.w2 = o;        o += codes_bytes(E * H, I / div);
     L.w2_scale = o;  o += scale_bytes(E * H, I);
   }
   if (fp8_backward(s)) {
@@ -325,6 +332,13 @@ moe_status moe_quantize_weights(const moe_shape* s, const void* W13, const void*
   hipStream_t hs = static_cast<hipStream_t>(stream);
   std::lock_guard<std::mutex> lk(g_timer_mu);
   KernelTimer* tm = timer();
+  if (fp4_weights(*s)) {  // forward only: W13 along H, W2 along I
+    hipError_t e = launch_quant_fp4_rows(w13, s->E * 2 * I, H, at<uint8_t>(wq, L.w13), at<uint8_t>(wq, L.w13_scale),
+                                         hs, tm);
+    if (e != hipSuccess) return MOE_ERR_LAUNCH;
+    return launch_status(launch_quant_fp4_rows(w2, s->E * H, I, at<uint8_t>(wq, L.w2), at<uint8_t>(wq, L.w2_scale),
+                                               hs, tm));
+  }
   const bool fwd = fp8_forward(*s);
   hipError_t e = launch_quant_weights(w13, s->E, 2 * I, H, fwd ? at<uint8_t>(wq, L.w13) : nullptr,
                                       fwd ? at<uint8_t>(wq, L.w13_scale) : nullptr, at<uint8_t>(wq, L.w13t),
@@ -420,8 +434,9 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
                                "quant_x")) != hipSuccess)
       return MOE_ERR_LAUNCH;
     gx = GemmOperand{xq, xs};
-    gw13 = GemmOperand{at<uint8_t>(wq, WL.w13), at<uint8_t>(wq, WL.w13_scale)};
-    gw2 = GemmOperand{at<uint8_t>(wq, WL.w2), at<uint8_t>(wq, WL.w2_scale)};
+    const bool w4 = fp4_weights(*s);
+    gw13 = GemmOperand{at<uint8_t>(wq, WL.w13), at<uint8_t>(wq, WL.w13_scale), w4};
+    gw2 = GemmOperand{at<uint8_t>(wq, WL.w2), at<uint8_t>(wq, WL.w2_scale), w4};
   }
   if ((e = launch_gemm1_swiglu(gp, gx, gw13, h13, act, hs, tm)) != hipSuccess) return MOE_ERR_LAUNCH;
   if (f8) {
@@ -449,6 +464,7 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->precision == MOE_BF16 && wq) return MOE_ERR_PRECISION;
+  if (s->precision == MOE_FP8_FP4) return MOE_ERR_PRECISION;  // an inference forward: no backward
   const bool f8 = fp8_backward(*s);
   (void)topk_idx;  // the permutation comes from `saved`
   if (!W13 || !W2 || !saved || !dW13 || !dW2 || !ws || (f8 && !wq) ||

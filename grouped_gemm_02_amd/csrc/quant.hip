@@ -412,6 +412,70 @@ hipError_t launch_quant_tokens(const uint16_t* in, int64_t ld, int C, const int3
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- FP4 weights
+// E2M1 (OCP MX FP4: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) weights for the
+// FP8 x FP4 forward, in blocks of 32 consecutive values along each row of
+// W [rows, C] (the GEMM's reduction axis), with the MX rule for E2M1:
+// e = floor(log2 amax) - 2 (0 for a zero block), so a block's values reach
+// just under 8 * 2^e and those above 6 * 2^e saturate. codes [rows, C/2]:
+// value 2j of a row in the low nibble of byte j, 2j+1 in the high nibble
+// (the order the scaled MFMA reads an FP4 operand in); scales [rows, C/32].
+// Thread = one block: 64 bytes in, 16 bytes of codes and one scale byte out.
+
+// E2M1 code of a = |v| / 2^e >= 0 (ties to the even code, saturating at 6):
+// the number of rounding boundaries a lies above, with a boundary that a
+// meets exactly counted when the code above it is even.
+__device__ __forceinline__ uint32_t e2m1_code(float v, int e) {
+  const float a = fabsf(scale_down(v, e));
+  const uint32_t c = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+                     uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.f);
+  return c | ((v < 0.f && c != 0u) ? 8u : 0u);
+}
+
+__global__ __launch_bounds__(256) void quant_fp4_rows_kernel(const uint16_t* __restrict__ in, int64_t blocks,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  for (int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; b < blocks;
+       b += int64_t(gridDim.x) * blockDim.x) {
+    u32x4 raw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) raw[q] = *reinterpret_cast<const u32x4*>(in + b * 32 + 8 * q);
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        v[8 * q + 2 * d] = bf16_lo(raw[q][d]);
+        v[8 * q + 2 * d + 1] = bf16_hi(raw[q][d]);
+      }
+#pragma unroll
+    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
+    const int e = amax > 0.f ? clamp_exp(floor_log2(amax) - 2) : 0;
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) word |= e2m1_code(v[8 * w + n], e) << (4 * n);
+      out[w] = word;
+    }
+    *reinterpret_cast<u32x4*>(codes + b * 16) = out;
+    scales[b] = uint8_t(e + 127);
+  }
+}
+
+hipError_t launch_quant_fp4_rows(const uint16_t* in, int64_t rows, int C, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t st, KernelTimer* timer) {
+  const int64_t blocks = rows * (C / 32);
+  if (blocks <= 0) return hipSuccess;
+  int64_t grid = (blocks + 255) / 256;
+  if (grid > 16384) grid = 16384;
+  TimedLaunch tl(timer, "quant_weights_fp4", st);
+  hipLaunchKernelGGL(quant_fp4_rows_kernel, dim3(unsigned(grid)), dim3(256), 0, st, in, blocks, codes, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_weights(const uint16_t* W, int64_t E, int R, int C, uint8_t* pcodes, uint8_t* pscales,
                                 uint8_t* tcodes, uint8_t* tscales, int rule, hipStream_t st, KernelTimer* timer) {
   const int64_t tiles = E * (R / 128) * (C / 128);

@@ -36,7 +36,7 @@ class LayerConfig:
     E: int          # experts
     k: int          # experts per token
     routing: str    # "uniform" | "zipf"
-    precision: str  # "bf16" | "fp8_block" | "mxfp8" | "fp8_bwd"
+    precision: str  # "bf16" | "fp8_block" | "mxfp8" | "fp8_bwd" | "fp8_fp4" (forward only)
     seed: int
     zipf_s: float = 1.2
     zipf_cold: int = 8

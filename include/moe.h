@@ -88,12 +88,20 @@ typedef enum moe_status {
  * every column in blocks of 128 rows (MOE_FP8_BLOCK, MOE_FP8_BWD; pow2 rule)
  * or 32 rows (MOE_MXFP8; MX rule), counted from the expert's first row in
  * permuted order. MOE_FP8_BWD runs the forward of MOE_BF16 and the backward
- * of MOE_FP8_BLOCK. */
+ * of MOE_FP8_BLOCK.
+ *   MOE_FP8_FP4: an inference forward with FP4 weights (the FP8 x FP4 type
+ *     of a forward-only fused MoE kernel in the MarkTechPost article's
+ *     comparison table). Activations as MOE_MXFP8; W13 and W2 in OCP MX FP4
+ *     (E2M1: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives, round to
+ *     nearest even, saturating) in 1x32 blocks along the reduction axis with
+ *     e = floor(log2(largest magnitude)) - 2. moe_bwd rejects it
+ *     (MOE_ERR_PRECISION), as does MOE_FLAG_FP8_WGRAD. */
 typedef enum moe_precision {
   MOE_BF16 = 0,
   MOE_FP8_BLOCK = 1,
   MOE_MXFP8 = 2,
-  MOE_FP8_BWD = 3
+  MOE_FP8_BWD = 3,
+  MOE_FP8_FP4 = 4
 } moe_precision;
 
 /* Flags of moe_shape.flags. MOE_FLAG_FP8_WGRAD: the weight-gradient GEMMs
@@ -147,9 +155,12 @@ moe_status moe_get_saved_layout(const moe_shape* s, moe_saved_layout* out);
  *   w2t, w2t_scale    backward dH:     W2^T  codes [E, I, H],  scales [E, I, H/32]
  *   w13t, w13t_scale  backward dX:     W13^T codes [E, H, 2I], scales [E, H, 2I/32]
  * Scales are stored per (row, 32 consecutive codes); a 128-wide or 128x128
- * block repeats its byte in every 32-block it covers. Entries a precision
- * does not use (the forward parts for MOE_FP8_BWD, everything for MOE_BF16)
- * are SIZE_MAX; total is 0 for MOE_BF16. Pure host function. */
+ * block repeats its byte in every 32-block it covers. MOE_FP8_FP4 stores
+ * only the forward parts, as E2M1 codes two per byte (w13 [E, 2I, H/2],
+ * w2 [E, H, I/2]; value 2j of a row in the low nibble of byte j). Entries a
+ * precision does not use (the forward parts for MOE_FP8_BWD, the backward
+ * parts for MOE_FP8_FP4, everything for MOE_BF16) are SIZE_MAX; total is 0
+ * for MOE_BF16. Pure host function. */
 typedef struct moe_wq_layout {
   size_t w13, w13_scale, w2, w2_scale;
   size_t w2t, w2t_scale, w13t, w13t_scale;

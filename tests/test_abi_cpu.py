@@ -164,6 +164,29 @@ def test_quantized_weight_layout(B):
     assert spans[-1][1] <= full["total"]
 
 
+def test_fp8_fp4_layout_and_forward_only(B):
+    """MOE_FP8_FP4: only the forward weight parts, E2M1 codes two per byte
+    with one scale byte per 32 values; moe_bwd and the FP8 weight-gradient
+    flag are refused with MOE_ERR_PRECISION."""
+    E, H, I = 128, 2048, 768
+    L = B.moe_get_wq_layout(_shape(B, precision="fp8_fp4"))
+    assert L["w2t"] == 2 ** 64 - 1 and L["w13t_scale"] == 2 ** 64 - 1
+    sizes = {"w13": E * 2 * I * H // 2, "w13_scale": E * 2 * I * H // 32, "w2": E * H * I // 2,
+             "w2_scale": E * H * I // 32}
+    spans = sorted((L[n], L[n] + sz) for n, sz in sizes.items())
+    assert all(a % 256 == 0 for a, _ in spans)
+    assert all(spans[i][1] <= spans[i + 1][0] for i in range(len(spans) - 1))
+    assert spans[-1][1] <= L["total"] < spans[-1][1] + 4096
+    a = _fwd_args()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_bwd(_shape(B, precision="fp8_fp4"), a[0], a[1], a[2], a[3], a[4], a[5], _Fake(0x70000), a[6], a[7],
+                  a[0], a[1], a[2], _Fake(0x70000), stream=0)
+    assert ei.value.status == 4
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_workspace_size(_shape(B, precision="fp8_fp4", wgrad="fp8"))
+    assert ei.value.status == 4
+
+
 def test_fp8_workspaces_are_larger(B):
     f0, s0, b0 = B.moe_workspace_size(_shape(B))
     f1, s1, b1 = B.moe_workspace_size(_shape(B, precision="fp8_block"))
