@@ -38,6 +38,7 @@ GEMM_FLOP_FACTOR = {
     "gemm1_swiglu": 4, "gemm2": 2, "gemm_dh_dswiglu": 2, "gemm_dx": 4, "gemm_dw13": 4, "gemm_dw2": 2,
 }
 GEMM_FLOP_FACTOR.update({k + "_fp8": v for k, v in list(GEMM_FLOP_FACTOR.items())})
+GEMM_FLOP_FACTOR.update({"gemm1_swiglu_fp8_fp4": 4, "gemm2_fp8_fp4": 2})  # FP8 activations x FP4 weights
 
 
 def hbm_bytes(name: str, cfg) -> float | None:
@@ -67,16 +68,18 @@ WORKLOADS = {
 }
 # timer name -> kernel function name in rocprofv3 output
 KERNEL_FN = {
-    "gemm1_swiglu": "gemm1_swiglu_kernel<false>", "gemm2": "gemm2_kernel<false>",
+    "gemm1_swiglu": "gemm1_swiglu_kernel<false, false>", "gemm2": "gemm2_kernel<false, false>",
     "gemm_dh_dswiglu": "gemm_dh_kernel<false>", "gemm_dx": "gemm_dx_kernel<false>",
-    "gemm1_swiglu_fp8": "gemm1_swiglu_kernel<true>", "gemm2_fp8": "gemm2_kernel<true>",
+    "gemm1_swiglu_fp8": "gemm1_swiglu_kernel<true, false>", "gemm2_fp8": "gemm2_kernel<true, false>",
+    "gemm1_swiglu_fp8_fp4": "gemm1_swiglu_kernel<true, true>", "gemm2_fp8_fp4": "gemm2_kernel<true, true>",
     "gemm_dh_dswiglu_fp8": "gemm_dh_kernel<true>", "gemm_dx_fp8": "gemm_dx_kernel<true>",
     "gemm_dw13": "gemm_dw13_kernel", "gemm_dw2": "gemm_dw2_kernel",
 }
 
 
 def kernel_peak(name: str) -> float:
-    return PEAK_FP8_TFLOPS if name.endswith("_fp8") else PEAK_BF16_TFLOPS
+    # an FP8 x FP4 product runs at the FP8 rate (the wider operand's)
+    return PEAK_FP8_TFLOPS if name.endswith("_fp8") or name.endswith("_fp8_fp4") else PEAK_BF16_TFLOPS
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_qwen3_30b_bf16.json")
 WORKLOAD_KEY = ["qwen3_30b/bf16"]   # the workload the committed traffic summary was taken on
 
@@ -104,7 +107,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_30b", choices=sorted(WORKLOADS))
-    ap.add_argument("--precision", default=None, choices=["bf16", "fp8_block", "mxfp8", "fp8_bwd"],
+    ap.add_argument("--precision", default=None, choices=["bf16", "fp8_block", "mxfp8", "fp8_bwd", "fp8_fp4"],
                     help="override the configuration's precision")
     ap.add_argument("--wgrad", default="bf16", choices=["bf16", "fp8"],
                     help="weight-gradient GEMMs on bf16 operands, or (FP8 precisions) on operands "
@@ -171,6 +174,33 @@ def cpu_baseline_fp8(cfg, d, n_experts, wgrad="bf16"):
                       f"forward + backward in float64 numpy; flops counted as 18*pairs*H*I"}
 
 
+def cpu_baseline_fp4(cfg, d, n_experts):
+    """The CPU oracle's FP8 x FP4 forward, as it stands, on the routed pairs
+    of the first n_experts experts (other pairs dropped), weight
+    quantization of those experts included."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_fp4 as f4
+    n_experts = min(n_experts, cfg.E)
+    idx = d["topk_idx"].cpu().numpy()
+    keep = idx < n_experts
+    toks = np.nonzero(keep.any(axis=1))[0]
+    sub_idx = np.where(keep[toks], idx[toks], -1)
+    pairs = int(keep.sum())
+    t0 = time.perf_counter()
+    f4.forward(d["x"][toks].cpu(), sub_idx, d["topk_w"][toks].cpu(), d["W13"][:n_experts].cpu(),
+               d["W2"][:n_experts].cpu())
+    dt = time.perf_counter() - t0
+    flops = 6.0 * pairs * cfg.H * cfg.I
+    threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(max(threads) if threads else 1),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the {pairs} routed pairs of experts 0..{n_experts - 1} ({len(toks)} tokens), "
+                      f"FP8 x FP4 forward emulation (weight quantization of those experts included) "
+                      f"in float64 numpy; flops counted as 6*pairs*H*I"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -187,8 +217,9 @@ def main():
         cfg = cfg.scaled(precision=args.precision)
     WORKLOAD_KEY[0] = f"{cfg.name}/{cfg.precision}"
     fp8 = cfg.precision != "bf16"
-    if args.wgrad == "fp8" and not fp8:
-        print("--wgrad fp8 needs an FP8 precision", file=sys.stderr)
+    fwd_only = cfg.precision == "fp8_fp4"  # an inference forward: no backward
+    if args.wgrad == "fp8" and (not fp8 or fwd_only):
+        print("--wgrad fp8 needs an FP8 precision with a backward", file=sys.stderr)
         sys.exit(2)
     if args.wgrad == "fp8":
         WORKLOAD_KEY[0] += "/fp8_wgrad"
@@ -223,9 +254,10 @@ def main():
         B.forward(buf, d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], y=y)
         if evs:
             evs[1].record()
-        B.backward(buf, d["dy"], d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], grads=grads)
-        if args.router != "none":
-            B.moe_route_bwd(shape, logits, d["topk_idx"], d["topk_w"], grads[1], True, d_logits)
+        if not fwd_only:
+            B.backward(buf, d["dy"], d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], grads=grads)
+            if args.router != "none":
+                B.moe_route_bwd(shape, logits, d["topk_idx"], d["topk_w"], grads[1], True, d_logits)
         if evs:
             evs[2].record()
 
@@ -272,7 +304,7 @@ def main():
     fwd_ms = [e[3].elapsed_time(e[1]) for e in evs]
     wq_ms = [e[0].elapsed_time(e[3]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    flops = cfg.flops_fwd() + cfg.flops_bwd()
+    flops = cfg.flops_fwd() + (0 if fwd_only else cfg.flops_bwd())
     tflops = flops / (ms_step * 1e-3) / 1e12
     MHI = float(cfg.M) * cfg.H * cfg.I
 
@@ -294,10 +326,13 @@ def main():
     achieved = GEMM_FLOP_FACTOR[dom] * MHI / (dom_avg * 1e-3) / 1e12
     gemm_ms = sum(kernels[n]["ms_per_step"] for n in gemm_names)
     dtype = {"bf16": "bf16", "fp8_block": "fp8_e4m3+bf16", "mxfp8": "fp8_e4m3+bf16",
-             "fp8_bwd": "bf16+fp8_e4m3"}[cfg.precision]
+             "fp8_bwd": "bf16+fp8_e4m3", "fp8_fp4": "fp8_e4m3+fp4_e2m1"}[cfg.precision]
+    workload = WORKLOADS[cfg.name]
+    if fwd_only:
+        workload = workload.replace("fwd+bwd", "forward only (inference)")
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if not fwd_only else METRIC.replace("fwd+bwd", "forward"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -309,7 +344,7 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {WORKLOADS[cfg.name]}", "T": cfg.T, "H": cfg.H,
+        "config": {"workload": f"{cfg.name}: {workload}", "T": cfg.T, "H": cfg.H,
                    "I": cfg.I, "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "precision": cfg.precision,
                    "wgrad": args.wgrad, "router": args.router},
         "fwd_ms": round(sum(fwd_ms) / len(fwd_ms), 4),
@@ -328,7 +363,10 @@ def main():
                      "traffic": measured_traffic(dom)},
     }
     if not args.no_cpu_baseline:
-        if fp8:
+        if fwd_only:
+            n_exp = min(8, max(1, -(-cfg.E * 24576 // cfg.M)))
+            out["cpu_baseline"] = cpu_baseline_fp4(cfg, d, n_exp)
+        elif fp8:
             # about 24k routed pairs, at most 8 experts (the emulation also
             # quantizes the sampled experts' weights)
             n_exp = min(8, max(1, -(-cfg.E * 24576 // cfg.M)))

@@ -13,7 +13,7 @@ mkdir -p "$OUT" "$PROF"
 # workload:precision:weight-gradient reading:router step
 for cpw in qwen3_30b:bf16:bf16:none ep8_share:fp8_block:bf16:none qwen3_235b:fp8_bwd:bf16:none \
            zipf:mxfp8:bf16:none ep8_share:fp8_block:fp8:none qwen3_235b:fp8_bwd:fp8:none zipf:mxfp8:fp8:none \
-           qwen3_30b:bf16:bf16:skewed; do
+           qwen3_30b:bf16:bf16:skewed qwen3_30b:fp8_fp4:bf16:none; do
   IFS=: read -r c prec wg rt <<< "$cpw"
   tag=${c}_${prec}; [ "$wg" = fp8 ] && tag=${tag}_fp8_wgrad; [ "$rt" != none ] && tag=${tag}_router_${rt}
   echo "stats $tag"
