@@ -661,12 +661,18 @@ struct RowTile {
 __device__ __forceinline__ RowTile decode_row_tile(int64_t t, int NT, const int32_t* s_pref, int E,
                                                    const int32_t* counts, const int32_t* offsets) {
   RowTile r;
-  r.nt = int(t % NT);
-  const int32_t gm = int32_t(t / NT);
   // the search reads LDS into vector registers; the result is the same in
   // every lane, and saying so keeps the tile's bases in scalar registers
-  r.e = __builtin_amdgcn_readfirstlane(find_expert(s_pref, E, gm));
-  const int mt = __builtin_amdgcn_readfirstlane(gm - s_pref[r.e]);
+  r.e = __builtin_amdgcn_readfirstlane(find_expert(s_pref, E, int32_t(t / NT)));
+  const int32_t m0 = __builtin_amdgcn_readfirstlane(s_pref[r.e]);
+  const int32_t mtiles = __builtin_amdgcn_readfirstlane(s_pref[r.e + 1]) - m0;
+  // an expert's tiles are walked n-tile by n-tile: all its m-tiles of one
+  // weight panel are neighbours in the walk (so they run together and share
+  // the panel in L2), and a cut between two rounds or two XCDs re-reads
+  // activation rows rather than weight panels
+  const int32_t l = int32_t(t - int64_t(m0) * NT);
+  r.nt = l / mtiles;
+  const int mt = l - r.nt * mtiles;
   r.row0 = int64_t(offsets[r.e]) + int64_t(mt) * BM;
   r.rows = min(BM, counts[r.e] - mt * BM);
   return r;
