@@ -19,12 +19,15 @@
 //     each lane holds one row m and 16 columns n of a sub-tile (4 runs of 4
 //     consecutive n): per-row scalars of the epilogue live in one lane.
 //   * Both operands are staged through LDS in k-slabs of BK = 64, double
-//     buffered: the global loads of slab kt+1 are in flight (in registers)
-//     while slab kt is multiplied. Every global load is a 16-byte chunk of a
-//     contiguous row:
+//     buffered: the global loads of slab kt+1 are in flight while slab kt is
+//     multiplied. Every global load is a 16-byte chunk of a contiguous row:
 //       - "k-major" operands (k contiguous in memory: activations as GEMM
 //         rows, weights in the forward) sit in LDS as [entity][64 + 8 pad]
-//         and are read with 16-byte ds_read_b128 fragments;
+//         and are read with 16-byte ds_read_b128 fragments; where both
+//         operands are k-major bf16 (the gate/up and down GEMMs) they use an
+//         unpadded, XOR-swizzled [entity][64] layout instead, which loads
+//         straight into LDS (buffer_load ... lds) can write, so those slabs
+//         never pass through registers;
 //       - "mn-major" operands (entities contiguous, one memory row per k:
 //         weights in the backward data-gradient GEMMs and both operands of
 //         the weight-gradient GEMMs, whose k is the token row) sit in LDS as
@@ -61,6 +64,15 @@ static_assert(256 * LDK == 64 * LDN, "operand layouts must have the same LDS siz
 constexpr int kStageLds = 2 * kOperandLds;  // P + Q
 constexpr int kPer = 256 * 8 / kThreads;   // 16-byte chunks per thread per operand slab
 
+// The two operand stages of the k loop are separate LDS objects, so that the
+// compiler can tell reads of one stage from loads still in flight into the
+// other (with one array it waits for every load into LDS before any LDS
+// read). After the k loop they hold the epilogue's tile images: rows
+// [0, 128) in stage 0, rows [128, 256) in stage 1.
+__shared__ __attribute__((aligned(16))) uint16_t g_stage0[kStageLds];
+__shared__ __attribute__((aligned(16))) uint16_t g_stage1[kStageLds];
+__device__ __forceinline__ uint16_t* stage_buf(int s) { return s ? g_stage1 : g_stage0; }
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -82,23 +94,46 @@ struct Stage {
 };
 
 // k-major operand: 256 entity rows, each with its k-values contiguous.
-// Thread t copies chunk (t % 8) of rows t/8 + 64*i. Loads go through a
-// buffer resource (tile-uniform base and extent in scalar registers, a
-// 32-bit byte offset per row in a vector register): an offset past the
-// extent reads zero instead of faulting. Every offset addresses a real row:
-// rows of the token side past the end of a ragged tile are pointed at a
-// valid row and their results are never stored, so the loads need no
+// Loads go through a buffer resource (tile-uniform base and extent in scalar
+// registers, a 32-bit byte offset per row in a vector register): an offset
+// past the extent reads zero instead of faulting. Every offset addresses a
+// real row: rows of the token side past the end of a ragged tile are pointed
+// at a valid row and their results are never stored, so the loads need no
 // predicate.
-struct KMajorLoader {
+//
+// Two LDS layouts of a bf16 k-major slab:
+//   * padded (SWZ = false): row r at r * LDK elements (64 k + 8 pad), chunk c
+//     at its own position; thread t moves chunk t % 8 of rows t/8 + 64*i
+//     through registers (fetch, then store after the MFMAs).
+//   * swizzled (SWZ = true): row r at r * BK elements (128 bytes, no pad),
+//     its eight 16-byte k-chunks permuted: position p holds chunk p ^ swz(r),
+//     swz(r) = (r / 2) % 8. Sixteen consecutive rows then put any one chunk
+//     in sixteen different 16-byte bank groups, so fragment reads are free of
+//     bank conflicts without padding. Thread t owns LDS slot t % 8 of rows
+//     t/8 + 64*i, i.e. a wave's 64 lanes fill 1 KB of LDS contiguously, and
+//     it loads the chunk that belongs in that slot. This is the layout a load
+//     straight into LDS (buffer_load ... lds: no registers, no LDS store
+//     instructions) can write, and slabs after a tile's first one are moved
+//     that way (dma); slab 0 still goes through registers.
+// The swizzled layout is used where both operands of a GEMM are k-major bf16
+// (the gate/up and down GEMMs); elsewhere its XOR addressing costs registers
+// and the padded layout is kept.
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
+
+template <bool SWZ>
+struct KMajorLoaderT {
+  static constexpr bool kDirect = SWZ;
   __amdgpu_buffer_rsrc_t data;
   uint32_t off[kPer];  // byte offset of this thread's 16 bytes of row i in slab 0
 
   __device__ __forceinline__ static int row_of_thread(int i) { return (threadIdx.x >> 3) + 64 * i; }
   // base: element 0 of row 0; units: extent in 16-bit units
   __device__ __forceinline__ void set_base(const uint16_t* base, int64_t units) { data = make_rsrc(base, units * 2); }
-  // row_off: offset of the row in 16-bit units
+  // row_off: offset of the row in 16-bit units. Swizzled, the chunk of slot
+  // t % 8 of row t/8 + 64*i is (t % 8) ^ swz(row), the same for every i.
   __device__ __forceinline__ void set_row(int i, int64_t row_off) {
-    off[i] = uint32_t(row_off * 2) + (threadIdx.x & 7) * 16;
+    const int c = SWZ ? int(threadIdx.x & 7) ^ kswz(int(threadIdx.x >> 3)) : int(threadIdx.x & 7);
+    off[i] = uint32_t(row_off * 2) + c * 16;
   }
   __device__ __forceinline__ void fetch(int kt, Stage& st) {
 #pragma unroll
@@ -108,10 +143,24 @@ struct KMajorLoader {
   __device__ __forceinline__ void store(uint16_t* lds, const Stage& st) const {
     const int r0 = threadIdx.x >> 3, c = threadIdx.x & 7;
 #pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      uint16_t* dst = SWZ ? lds + (int(threadIdx.x) + 512 * i) * 8 : lds + (r0 + 64 * i) * LDK + c * 8;
+      *reinterpret_cast<u32x4*>(dst) = st.r[i];
+    }
+  }
+  // swizzled only: slab kt straight into LDS; wave w's load i fills rows
+  // 8w + 64i .. +7, lane l's 16 bytes landing at byte 16 l of that 1 KB block
+  __device__ __forceinline__ void dma(int kt, uint16_t* lds) const {
+    static_assert(SWZ, "loads straight into LDS write the swizzled layout");
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+#pragma unroll
     for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<u32x4*>(lds + (r0 + 64 * i) * LDK + c * 8) = st.r[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          data, (__attribute__((address_space(3))) void*)(lds + (8 * w + 64 * i) * BK), 16, off[i], kt * 2 * BK, 0, 0);
   }
 };
+using KMajorLoader = KMajorLoaderT<false>;
+using KMajorLoaderD = KMajorLoaderT<true>;
 
 // mn-major operand: 64 k-rows per slab, each holding the tile's 256 entities
 // contiguously. Thread t copies chunk (t % 32) of k-rows t/32 + 16*i.
@@ -123,6 +172,7 @@ struct KMajorLoader {
 // the next slab, since they may come from an index array.
 template <class RowFn>
 struct MNMajorLoader {
+  static constexpr bool kDirect = false;
   RowFn fn;
   __amdgpu_buffer_rsrc_t data;
   int nchunks = 32;  // 16-byte chunks of the tile that exist (partial last n-tile)
@@ -165,10 +215,14 @@ struct MNMajorLoader {
 // ------------------------------------------------------------------ fragments
 
 // 32 entities x 16 k of a k-major tile: lane holds entity (lane % 32),
-// k = kk*16 + 8*(lane/32) + 0..7.
+// k = kk*16 + 8*(lane/32) + 0..7, i.e. chunk 2 kk + lane/32 of its row.
+template <bool SWZ>
 __device__ __forceinline__ bf16x8 frag_k(const uint16_t* lds, int ent0, int kk) {
   const int lane = lane_id();
-  return *reinterpret_cast<const bf16x8*>(lds + (ent0 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
+  const int e = ent0 + (lane & 31);
+  const int c = 2 * kk + (lane >> 5);
+  if constexpr (SWZ) return *reinterpret_cast<const bf16x8*>(lds + e * BK + ((c ^ kswz(e)) << 3));
+  return *reinterpret_cast<const bf16x8*>(lds + e * LDK + c * 8);
 }
 
 // The same fragment from an mn-major tile with two transpose reads. In each
@@ -217,14 +271,17 @@ __device__ __forceinline__ int lane_col(int tn, int g) {
   return wave_n() * WTN + tn * 32 + 8 * g + 4 * (lane_id() >> 5);
 }
 
-template <bool P_MN, bool Q_MN>
+// KSWZ: k-major operands are in the swizzled layout (see KMajorLoaderT)
+template <bool P_MN, bool Q_MN, bool KSWZ = false>
 __device__ __forceinline__ void load_frags(const uint16_t* ldsP, const uint16_t* ldsQ, int kk,
                                            bf16x8 (&pf)[TM], bf16x8 (&qf)[TN]) {
   const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) qf[j] = Q_MN ? frag_mn(ldsQ, qn0 + 32 * j, kk) : frag_k(ldsQ, qn0 + 32 * j, kk);
+  for (int j = 0; j < TN; ++j)
+    qf[j] = Q_MN ? frag_mn(ldsQ, qn0 + 32 * j, kk) : frag_k<KSWZ>(ldsQ, qn0 + 32 * j, kk);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) pf[i] = P_MN ? frag_mn(ldsP, pm0 + 32 * i, kk) : frag_k(ldsP, pm0 + 32 * i, kk);
+  for (int i = 0; i < TM; ++i)
+    pf[i] = P_MN ? frag_mn(ldsP, pm0 + 32 * i, kk) : frag_k<KSWZ>(ldsP, pm0 + 32 * i, kk);
 }
 
 __device__ __forceinline__ void mma_step(const bf16x8 (&pf)[TM], const bf16x8 (&qf)[TN], Acc& acc) {
@@ -237,7 +294,7 @@ __device__ __forceinline__ void mma_step(const bf16x8 (&pf)[TM], const bf16x8 (&
 // One k-slab (4 steps of 16) of MFMAs for this wave. With two waves per SIMD
 // the other wave's MFMAs cover this wave's fragment reads, so fragments are
 // single buffered (register budget: 128 accumulators share the 256 VGPRs).
-template <bool P_MN, bool Q_MN>
+template <bool P_MN, bool Q_MN, bool KSWZ = false>
 __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
   // The compiler's own interleave of the fragment reads with the MFMAs
   // leaves LDS latency exposed; its built-in MFMA/DS interleave strategies
@@ -250,14 +307,87 @@ __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* l
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
     bf16x8 pf[TM], qf[TN];
-    load_frags<P_MN, Q_MN>(ldsP, ldsQ, kk, pf, qf);
+    load_frags<P_MN, Q_MN, KSWZ>(ldsP, ldsQ, kk, pf, qf);
     mma_step(pf, qf, acc);
   }
 }
 
+// Slab kt of both operands into stage buffer `buf`: when both loaders can,
+// straight into LDS now; otherwise into registers (stored by store_next after
+// the MFMAs). Only both or neither: the compiler cannot tell the LDS
+// transpose reads of an mn-major operand from loads into LDS in flight, and
+// would wait for those loads before the slab's first fragment read.
+template <class LP, class LQ>
+constexpr bool kBothDirect = LP::kDirect && LQ::kDirect;
+
+template <class LP, class LQ, class SP, class SQ>
+__device__ __forceinline__ void fetch_next(LP& lp, LQ& lq, int kt, uint16_t* buf, SP& sp, SQ& sq) {
+  if constexpr (kBothDirect<LP, LQ>) {
+    lp.dma(kt, buf);
+    lq.dma(kt, buf + kOperandLds);
+  } else {
+    lp.fetch(kt, sp);
+    lq.fetch(kt, sq);
+  }
+}
+// Before the slab barrier: the straight-to-LDS loads of the wave have
+// landed (vmcnt(0); expcnt and lgkmcnt left at their maxima).
+template <class LP, class LQ>
+__device__ __forceinline__ void wait_direct() {
+  if constexpr (kBothDirect<LP, LQ>) __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+template <class LP, class LQ, class SP, class SQ>
+__device__ __forceinline__ void store_next(const LP& lp, const LQ& lq, uint16_t* buf, const SP& sp, const SQ& sq) {
+  if constexpr (!kBothDirect<LP, LQ>) {
+    lp.store(buf, sp);
+    lq.store(buf + kOperandLds, sq);
+  }
+}
+
+// One slab kt of the k loop out of stage `cur`; slab kt+1 (if any) goes to
+// stage `nxt`. Both stages are named at compile time by the caller (the loop
+// is unrolled by two), which is what lets the slab's fragment reads run while
+// straight-to-LDS loads into the other stage are in flight.
+template <bool P_MN, bool Q_MN, class LP, class LQ>
+__device__ __forceinline__ void plain_slab(LP& lp, LQ& lq, int kt, int nk, uint16_t* cur, uint16_t* nxt, Acc& acc,
+                                           bool active, Stage& sp, Stage& sq) {
+  const bool more = kt + 1 < nk;
+  if (more) fetch_next(lp, lq, kt + 1, nxt, sp, sq);
+  if (active) mma_slab<P_MN, Q_MN, kBothDirect<LP, LQ>>(cur, cur + kOperandLds, acc);
+  if (more) store_next(lp, lq, nxt, sp, sq);
+  wait_direct<LP, LQ>();
+  __syncthreads();
+}
+
+// The same with the slab's last 16-deep step deferred past the barrier
+// (fragments double buffered: pf0/qf0 hold step 0 of `cur` on entry and
+// step 0 of `nxt` on exit).
+template <bool P_MN, bool Q_MN, class LP, class LQ>
+__device__ __forceinline__ void deferred_slab(LP& lp, LQ& lq, int kt, int nk, uint16_t* cur, uint16_t* nxt,
+                                              Acc& acc, bool active, Stage& sp, Stage& sq, bf16x8 (&pf0)[TM],
+                                              bf16x8 (&qf0)[TN], bf16x8 (&pf1)[TM], bf16x8 (&qf1)[TN]) {
+  const bool more = kt + 1 < nk;
+  if (more) fetch_next(lp, lq, kt + 1, nxt, sp, sq);
+  if (active) {
+    load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 1, pf1, qf1);
+    mma_step(pf0, qf0, acc);
+    load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 2, pf0, qf0);
+    mma_step(pf1, qf1, acc);
+    load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 3, pf1, qf1);
+    mma_step(pf0, qf0, acc);
+  }
+  if (more) store_next(lp, lq, nxt, sp, sq);
+  wait_direct<LP, LQ>();
+  __syncthreads();
+  if (active) {
+    if (more) load_frags<P_MN, Q_MN>(nxt, nxt + kOperandLds, 0, pf0, qf0);
+    mma_step(pf1, qf1, acc);
+  }
+}
+
 // Runs the k loop of one tile: the global loads of slab kt+1 are in flight
-// (in registers) while slab kt is multiplied out of one LDS buffer; then they
-// are written to the other buffer.
+// while slab kt is multiplied out of one LDS stage, either straight into the
+// other stage or into registers that are written there after the MFMAs.
 // `active` (uniform per wave) is false for a wave whose tile rows are all
 // past the end of a ragged tile: it still moves data, but skips the MFMAs.
 // mainloop_staged runs the k loop with slab 0 already fetched into sp, sq
@@ -271,68 +401,45 @@ __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* l
 // core that is ~9 % more MFMA issue; inside the grouped kernels it pays only
 // in the dH GEMM (~4 %) and costs 1-2 % elsewhere, so only dH uses it.
 template <bool P_MN, bool Q_MN, bool DEFER = false, class LP, class LQ>
-__device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc, bool active,
-                                                Stage& sp, Stage& sq) {
+__device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, Acc& acc, bool active, Stage& sp,
+                                                Stage& sq) {
   static_assert(BK / 16 == 4, "the deferred step schedule is written for four 16-deep steps per slab");
   if (nk <= 0) return;
-  lp.store(lds, sp);
-  lq.store(lds + kOperandLds, sq);
+  lp.store(g_stage0, sp);
+  lq.store(g_stage0 + kOperandLds, sq);
   __syncthreads();
-  if constexpr (!DEFER) {
-    for (int kt = 0; kt < nk; ++kt) {
-      uint16_t* cur = lds + (kt & 1) * kStageLds;
-      uint16_t* nxt = lds + ((kt + 1) & 1) * kStageLds;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        lp.fetch(kt + 1, sp);
-        lq.fetch(kt + 1, sq);
-      }
-      if (active) mma_slab<P_MN, Q_MN>(cur, cur + kOperandLds, acc);
-      if (more) {
-        lp.store(nxt, sp);
-        lq.store(nxt + kOperandLds, sq);
-      }
-      __syncthreads();
+  if constexpr (!kBothDirect<LP, LQ>) {
+    // slabs through registers: one loop body (unrolled by two it would not
+    // fit the registers of the weight-gradient GEMMs)
+    if constexpr (!DEFER) {
+      for (int kt = 0; kt < nk; ++kt)
+        plain_slab<P_MN, Q_MN>(lp, lq, kt, nk, stage_buf(kt & 1), stage_buf((kt + 1) & 1), acc, active, sp, sq);
+    } else {
+      bf16x8 pf0[TM], qf0[TN], pf1[TM], qf1[TN];
+      if (active) load_frags<P_MN, Q_MN>(g_stage0, g_stage0 + kOperandLds, 0, pf0, qf0);
+      for (int kt = 0; kt < nk; ++kt)
+        deferred_slab<P_MN, Q_MN>(lp, lq, kt, nk, stage_buf(kt & 1), stage_buf((kt + 1) & 1), acc, active, sp, sq,
+                                  pf0, qf0, pf1, qf1);
     }
   } else {
-    bf16x8 pf0[TM], qf0[TN], pf1[TM], qf1[TN];
-    if (active) load_frags<P_MN, Q_MN>(lds, lds + kOperandLds, 0, pf0, qf0);
-    for (int kt = 0; kt < nk; ++kt) {
-      uint16_t* cur = lds + (kt & 1) * kStageLds;
-      uint16_t* nxt = lds + ((kt + 1) & 1) * kStageLds;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        lp.fetch(kt + 1, sp);
-        lq.fetch(kt + 1, sq);
-      }
-      if (active) {
-        load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 1, pf1, qf1);
-        mma_step(pf0, qf0, acc);
-        load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 2, pf0, qf0);
-        mma_step(pf1, qf1, acc);
-        load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 3, pf1, qf1);
-        mma_step(pf0, qf0, acc);
-      }
-      if (more) {
-        lp.store(nxt, sp);
-        lq.store(nxt + kOperandLds, sq);
-      }
-      __syncthreads();
-      if (active) {
-        if (more) load_frags<P_MN, Q_MN>(nxt, nxt + kOperandLds, 0, pf0, qf0);
-        mma_step(pf1, qf1, acc);
-      }
+    // straight-to-LDS slabs: unrolled by two, so that each slab's stages are
+    // known at compile time
+    static_assert(!DEFER, "the deferred schedule is not combined with straight-to-LDS loads");
+    for (int kt = 0; kt < nk; kt += 2) {
+      plain_slab<P_MN, Q_MN>(lp, lq, kt, nk, g_stage0, g_stage1, acc, active, sp, sq);
+      if (kt + 1 >= nk) break;
+      plain_slab<P_MN, Q_MN>(lp, lq, kt + 1, nk, g_stage1, g_stage0, acc, active, sp, sq);
     }
   }
 }
 
 template <bool P_MN, bool Q_MN, bool DEFER = false, class LP, class LQ>
-__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc, bool active = true) {
+__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, Acc& acc, bool active = true) {
   if (nk <= 0) return;
   Stage sp, sq;
   lp.fetch(0, sp);
   lq.fetch(0, sq);
-  mainloop_staged<P_MN, Q_MN, DEFER>(lp, lq, nk, lds, acc, active, sp, sq);
+  mainloop_staged<P_MN, Q_MN, DEFER>(lp, lq, nk, acc, active, sp, sq);
 }
 
 // ------------------------------------------------------------------ FP8 core
@@ -365,6 +472,7 @@ struct Stage8 {
 // t/8 + 64 * (t % 4) (threads t and t+4 duplicate each other, which keeps
 // every load and LDS write unconditional).
 struct KMajorLoader8 : KMajorLoader {
+  static constexpr bool kDirect = false;
   __amdgpu_buffer_rsrc_t scale;
   uint32_t soff;  // byte offset of the scale row this thread moves
 
@@ -375,8 +483,9 @@ struct KMajorLoader8 : KMajorLoader {
     KMajorLoader::set_base(base, units);
     scale = make_rsrc(sbase, sbytes);
   }
+  // (the FP8 layout keeps chunk t % 8 in slot t % 8, rows padded to LDK)
   __device__ __forceinline__ void set_row(int i, int64_t row_off) {
-    KMajorLoader::set_row(i, row_off);
+    off[i] = uint32_t(row_off * 2) + (threadIdx.x & 7) * 16;
     if (int(threadIdx.x & 3) == i) soff = uint32_t(row_off * 2) >> 5;
   }
   __device__ __forceinline__ void fetch(int kt, Stage8& st) {
@@ -394,6 +503,10 @@ struct KMajorLoader8 : KMajorLoader {
 
 template <bool FP8>
 using KLoader = typename std::conditional<FP8, KMajorLoader8, KMajorLoader>::type;
+// the same, with bf16 in the swizzled layout moved straight into LDS (for
+// GEMMs whose two operands are both k-major)
+template <bool FP8>
+using KLoaderD = typename std::conditional<FP8, KMajorLoader8, KMajorLoaderD>::type;
 
 // k-major E2M1 operand (FP4 weights: two codes per byte, the even k in the
 // low nibble) with scales [rows, K/32]. A k-slab is 128 codes = 64 bytes per
@@ -409,6 +522,7 @@ struct Stage4 {
 };
 
 struct KMajorLoader4 {
+  static constexpr bool kDirect = false;
   __amdgpu_buffer_rsrc_t data, scale;
   uint32_t off[2];
   uint32_t soff;
@@ -490,16 +604,16 @@ __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_
 }
 
 template <class LQ = KMajorLoader8>
-__device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, LQ& lq, int nk, uint16_t* lds, Acc& acc,
-                                                    bool active, Stage8& sp, typename StageOf<LQ>::type& sq) {
+__device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, LQ& lq, int nk, Acc& acc, bool active,
+                                                    Stage8& sp, typename StageOf<LQ>::type& sq) {
   constexpr bool W4 = std::is_same<LQ, KMajorLoader4>::value;
   if (nk <= 0) return;
-  lp.store(lds, sp);
-  lq.store(lds + kOperandLds, sq);
+  lp.store(g_stage0, sp);
+  lq.store(g_stage0 + kOperandLds, sq);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    uint16_t* cur = lds + (kt & 1) * kStageLds;
-    uint16_t* nxt = lds + ((kt + 1) & 1) * kStageLds;
+    uint16_t* cur = stage_buf(kt & 1);
+    uint16_t* nxt = stage_buf((kt + 1) & 1);
     const bool more = kt + 1 < nk;
     if (more) {
       lp.fetch(kt + 1, sp);
@@ -515,13 +629,13 @@ __device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, LQ& lq, i
   }
 }
 
-__device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, uint16_t* lds, Acc& acc,
+__device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, Acc& acc,
                                              bool active = true) {
   if (nk <= 0) return;
   Stage8 sp, sq;
   lp.fetch(0, sp);
   lq.fetch(0, sq);
-  mainloop_staged_fp8(lp, lq, nk, lds, acc, active, sp, sq);
+  mainloop_staged_fp8(lp, lq, nk, acc, active, sp, sq);
 }
 
 // ------------------------------------------------------------------ LDS-staged epilogue
@@ -529,10 +643,14 @@ __device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& l
 // waves of one column half (wave_n() in {2h, 2h+1}) are written there as fp32
 // F[m][c], m < 256, c < 128 (this half's columns, in tile order).
 constexpr int FLD = 128 + 4;  // fp32 row stride (the pad spreads rows over banks)
-static_assert(256 * FLD * 4 <= 2 * kStageLds * 2, "fp32 staging must fit the operand buffers");
+static_assert(128 * FLD * 4 <= kStageLds * 2, "fp32 staging of 128 rows must fit one operand stage");
+// row m of the fp32 staging (rows [0, 128) in stage 0, [128, 256) in stage 1)
+__device__ __forceinline__ float* frow(int m) {
+  return reinterpret_cast<float*>(m < BM / 2 ? g_stage0 : g_stage1) + (m & (BM / 2 - 1)) * FLD;
+}
 constexpr int kRowPass = kThreads / 16;  // rows per pass when 16 threads share a row
 
-__device__ __forceinline__ void stage_half(const Acc& acc, float* F, int half) {
+__device__ __forceinline__ void stage_half(const Acc& acc, int half) {
   if ((wave_n() >> 1) != half) return;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
@@ -544,7 +662,7 @@ __device__ __forceinline__ void stage_half(const Acc& acc, float* F, int half) {
         const int c = lane_col(tn, g) - half * 128;
         const f32x16& a = acc.c[tm][tn];
         const f32x4 v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-        *reinterpret_cast<f32x4*>(F + m * FLD + c) = v;
+        *reinterpret_cast<f32x4*>(frow(m) + c) = v;
       }
   }
 }
@@ -557,13 +675,17 @@ __device__ __forceinline__ void stage_half(const Acc& acc, float* F, int half) {
 // bank pair at most); then thread t copies 16-byte pieces (column chunk
 // t % 32) of rows t/32 + 16*j, so each row goes out as one 512-byte run.
 constexpr int LDT = BN + 8;
-static_assert(BM * LDT <= 2 * kStageLds, "bf16 tile image must fit in the operand LDS");
+static_assert((BM / 2) * LDT <= kStageLds, "half of the bf16 tile image must fit one operand stage");
+// row m of the bf16 tile image (rows [0, 128) in stage 0, [128, 256) in stage 1)
+__device__ __forceinline__ uint16_t* img_row(int m) {
+  return (m < BM / 2 ? g_stage0 : g_stage1) + (m & (BM / 2 - 1)) * LDT;
+}
 
 // store_tile in two halves: stage_image writes the bf16 image (and loads the
 // row map, so its latency overlaps the image writes) and waits; copy_image
 // writes the image out and waits. Callers may issue other loads between the
 // two, so that their waits do not include the image's stores.
-__device__ __forceinline__ void stage_image(const Acc& acc, uint16_t* lds, int64_t row0, int rows,
+__device__ __forceinline__ void stage_image(const Acc& acc, int64_t row0, int rows,
                                             const int32_t* rowmap, int32_t* s_map) {
   if (rowmap && int(threadIdx.x) < rows) s_map[threadIdx.x] = rowmap[row0 + threadIdx.x];
 #pragma unroll
@@ -575,29 +697,29 @@ __device__ __forceinline__ void stage_image(const Acc& acc, uint16_t* lds, int64
       for (int g = 0; g < 4; ++g) {
         const f32x16& a = acc.c[tm][tn];
         const u32x2 v = {pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
-        *reinterpret_cast<u32x2*>(lds + m * LDT + lane_col(tn, g)) = v;
+        *reinterpret_cast<u32x2*>(img_row(m) + lane_col(tn, g)) = v;
       }
   }
   __syncthreads();
 }
 
-__device__ __forceinline__ void copy_image(const uint16_t* lds, uint16_t* out, int64_t ld, int64_t row0,
+__device__ __forceinline__ void copy_image(uint16_t* out, int64_t ld, int64_t row0,
                                            int64_t col0, int rows, int cols, const int32_t* rowmap,
                                            const int32_t* s_map) {
   const int c = (threadIdx.x & 31) * 8;
   if (c < cols) {
     for (int m = threadIdx.x >> 5; m < rows; m += kThreads / 32) {
       const int64_t orow = rowmap ? int64_t(s_map[m]) : row0 + m;
-      *reinterpret_cast<u32x4*>(out + orow * ld + col0 + c) = *reinterpret_cast<const u32x4*>(lds + m * LDT + c);
+      *reinterpret_cast<u32x4*>(out + orow * ld + col0 + c) = *reinterpret_cast<const u32x4*>(img_row(m) + c);
     }
   }
   __syncthreads();
 }
 
-__device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* lds, uint16_t* out, int64_t ld,
+__device__ __forceinline__ void store_tile(const Acc& acc, uint16_t* out, int64_t ld,
                                            int64_t row0, int64_t col0, int rows, int cols) {
-  stage_image(acc, lds, row0, rows, nullptr, nullptr);
-  copy_image(lds, out, ld, row0, col0, rows, cols, nullptr, nullptr);
+  stage_image(acc, row0, rows, nullptr, nullptr);
+  copy_image(out, ld, row0, col0, rows, cols, nullptr, nullptr);
 }
 
 // ------------------------------------------------------------------ scheduling
@@ -683,8 +805,6 @@ __device__ __forceinline__ void store4_bf16(uint16_t* p, float a, float b, float
   *reinterpret_cast<u32x2*>(p) = v;
 }
 
-#define MOE_GEMM_SMEM                                                          \
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStageLds];
 
 #define MOE_ROW_SCHED                                                          \
   __shared__ int32_t s_pref[1025];                                             \
@@ -702,7 +822,7 @@ struct TileState {
 };
 
 template <bool FP8, bool Q_MN, bool PREFETCH, class LP, class LQ, class Setup, class Epi>
-__device__ __forceinline__ void row_tile_walk(int64_t total, int nk, uint16_t* lds, LP& lp, LQ& lq, Setup&& setup,
+__device__ __forceinline__ void row_tile_walk(int64_t total, int nk, LP& lp, LQ& lq, Setup&& setup,
                                               Epi&& epi) {
   typename StageOf<LP>::type sp;
   typename StageOf<LQ>::type sq;
@@ -723,9 +843,9 @@ __device__ __forceinline__ void row_tile_walk(int64_t total, int nk, uint16_t* l
     acc.zero();
     const bool active = wave_m() * WTM < cur.rt.rows;
     if constexpr (FP8)
-      mainloop_staged_fp8(lp, lq, nk, lds, acc, active, sp, sq);
+      mainloop_staged_fp8(lp, lq, nk, acc, active, sp, sq);
     else
-      mainloop_staged<false, Q_MN>(lp, lq, nk, lds, acc, active, sp, sq);
+      mainloop_staged<false, Q_MN>(lp, lq, nk, acc, active, sp, sq);
     t += gridDim.x;
     if (PREFETCH && t < total) {
       setup(t, nxt);
@@ -770,7 +890,6 @@ template <bool FP8, bool W4 = false>
 __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, Operand X, Operand W,
                                                                 uint16_t* __restrict__ h13,
                                                                 uint16_t* __restrict__ act) {
-  MOE_GEMM_SMEM
   __shared__ float s_w[BM];
   const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
   MOE_ROW_SCHED
@@ -778,8 +897,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
   const int KU = row_units<FP8>(H);
   const int KW = W4 ? KU / 2 : KU;  // weight row in 16-bit units
   const int64_t total = int64_t(s_pref[E]) * NT;
-  KLoader<FP8> lp;
-  typename std::conditional<W4, KMajorLoader4, KLoader<FP8>>::type lq;
+  KLoaderD<FP8> lp;
+  typename std::conditional<W4, KMajorLoader4, KLoaderD<FP8>>::type lq;
   auto setup = [&](int64_t t, TileState& st) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
     st.rt = rt;
@@ -811,18 +930,17 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
     if (threadIdx.x < BM) s_w[threadIdx.x] = st.w;
     // half h holds g and u of intermediate indices nt*128 + h*64 + [0, 64):
     // staged column (i/32)*64 + i%32 is g, +32 is u.
-    float* F = reinterpret_cast<float*>(lds);
     const int io = (threadIdx.x & 15) * 4;  // 4 intermediate indices per thread
     const int gc = (io >> 5) * 64 + (io & 31);
     for (int h = 0; h < 2; ++h) {
-      stage_half(acc, F, h);
+      stage_half(acc, h);
       __syncthreads();
       const int i = rt.nt * g1::IPT + h * 64 + io;
       for (int m = threadIdx.x >> 4; m < rt.rows; m += kRowPass) {
         const int64_t r = rt.row0 + m;
         const float w = s_w[m];
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(F + m * FLD + gc);
-        const f32x4 uv = *reinterpret_cast<const f32x4*>(F + m * FLD + gc + 32);
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(frow(m) + gc);
+        const f32x4 uv = *reinterpret_cast<const f32x4*>(frow(m) + gc + 32);
         float av[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) av[q] = w * (gv[q] * sigmoidf_fast(gv[q]) * uv[q]);
@@ -835,7 +953,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
       __syncthreads();
     }
   };
-  row_tile_walk<FP8, false, true>(total, KU / 64, lds, lp, lq, setup, epi);
+  row_tile_walk<FP8, false, true>(total, KU / 64, lp, lq, setup, epi);
 }
 
 // ================================================================== forward GEMM2
@@ -843,15 +961,14 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
 template <bool FP8, bool W4 = false>
 __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand A, Operand W,
                                                          uint16_t* __restrict__ out) {
-  MOE_GEMM_SMEM
   const int E = int(p.E), H = int(p.H), I = int(p.I);
   MOE_ROW_SCHED
   const int NT = H / BN;
   const int KU = row_units<FP8>(I);
   const int KW = W4 ? KU / 2 : KU;  // weight row in 16-bit units
   const int64_t total = int64_t(s_pref[E]) * NT;
-  KLoader<FP8> lp;
-  typename std::conditional<W4, KMajorLoader4, KLoader<FP8>>::type lq;
+  KLoaderD<FP8> lp;
+  typename std::conditional<W4, KMajorLoader4, KLoaderD<FP8>>::type lq;
   auto setup = [&](int64_t t, TileState& st) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
     st.rt = rt;
@@ -881,13 +998,13 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
   const int32_t* rowmap = p.k == 1 ? p.src_of : nullptr;
   __shared__ int32_t s_map[BM];
   auto copy = [&](const TileState& st) {
-    copy_image(lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap, s_map);
+    copy_image(out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap, s_map);
   };
   auto epi = [&](const TileState& st, const Acc& acc) {
-    stage_image(acc, lds, st.rt.row0, st.rt.rows, rowmap, s_map);
+    stage_image(acc, st.rt.row0, st.rt.rows, rowmap, s_map);
     copy(st);
   };
-  row_tile_walk<FP8, false, true>(total, KU / 64, lds, lp, lq, setup, epi);
+  row_tile_walk<FP8, false, true>(total, KU / 64, lp, lq, setup, epi);
 }
 
 // ------------------------------------------------------------------ row functions
@@ -922,7 +1039,6 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
                                                            const uint16_t* __restrict__ h13,
                                                            uint16_t* __restrict__ dh13,
                                                            float* __restrict__ dwpart) {
-  MOE_GEMM_SMEM
   __shared__ float s_w[BM];
   const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
   MOE_ROW_SCHED
@@ -957,7 +1073,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
         lq.set_row(i, int64_t(min(KMajorLoader::row_of_thread(i), ncols - 1)) * KU);
-      mainloop_fp8(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
+      mainloop_fp8(lp, lq, KU / 64, acc, wave_m() * WTM < rt.rows);
     } else {
       MNMajorLoader<DirectRows> lq;
       lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN,
@@ -966,19 +1082,18 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
       lq.fn.nrows = H;
       lq.nchunks = ncols / 8;
       lq.prime(0);
-      mainloop<false, true, true>(lp, lq, KU / 64, lds, acc, wave_m() * WTM < rt.rows);
+      mainloop<false, true, true>(lp, lq, KU / 64, acc, wave_m() * WTM < rt.rows);
     }
     if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
     // Thread t works on 8 of them (c) for tile rows t/16 + 32*j, j < 8, in
     // two batches of four rows; each batch's [g | u] pieces are requested
     // together (the first batch's before the staging barrier).
-    float* F = reinterpret_cast<float*>(lds);
     const int c = (threadIdx.x & 15) * 8;
     for (int h = 0; h < 2; ++h) {
       const bool col_ok = h * 128 + c < ncols;
       const int i = rt.nt * BN + h * 128 + (col_ok ? c : 0);
-      stage_half(acc, F, h);
+      stage_half(acc, h);
       for (int bt = 0; bt < 2; ++bt) {
         u32x4 gq[4], uq[4];
 #pragma unroll
@@ -997,8 +1112,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
           if (row_ok && col_ok) {
             const int64_t r = rt.row0 + m;
             const float w = s_w[m];
-            const f32x4 d0 = *reinterpret_cast<const f32x4*>(F + m * FLD + c);
-            const f32x4 d1 = *reinterpret_cast<const f32x4*>(F + m * FLD + c + 4);
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(frow(m) + c);
+            const f32x4 d1 = *reinterpret_cast<const f32x4*>(frow(m) + c + 4);
             u32x4 dgq, duq;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1041,7 +1156,6 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operand DH, Operand W,
                                                            uint16_t* __restrict__ out) {
-  MOE_GEMM_SMEM
   const int E = int(p.E), H = int(p.H), I = int(p.I);
   MOE_ROW_SCHED
   const int NT = H / BN;
@@ -1080,13 +1194,13 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
   const int32_t* rowmap = p.k == 1 ? p.src_of : nullptr;
   __shared__ int32_t s_map[BM];
   auto copy = [&](const TileState& st) {
-    copy_image(lds, out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap, s_map);
+    copy_image(out, H, st.rt.row0, int64_t(st.rt.nt) * BN, st.rt.rows, BN, rowmap, s_map);
   };
   auto epi = [&](const TileState& st, const Acc& acc) {
-    stage_image(acc, lds, st.rt.row0, st.rt.rows, rowmap, s_map);
+    stage_image(acc, st.rt.row0, st.rt.rows, rowmap, s_map);
     copy(st);
   };
-  row_tile_walk<FP8, !FP8, true>(total, KU / 64, lds, lp, lq, setup, epi);
+  row_tile_walk<FP8, !FP8, true>(total, KU / 64, lp, lq, setup, epi);
 }
 
 // ================================================================== weight gradients
@@ -1279,10 +1393,10 @@ __device__ __forceinline__ void dw_for_each_item(const int32_t* counts, int E, i
 // [col0, col0 + cols) of the row-major [*, ld] output) when the item covers
 // all of the expert's rows, else writes its fp32 partial, a row-major
 // 256 x 256 tile, to its slot.
-__device__ __forceinline__ void dw_store(const Acc& acc, const DwItem& it, uint16_t* lds, uint16_t* out, int64_t ld,
+__device__ __forceinline__ void dw_store(const Acc& acc, const DwItem& it, uint16_t* out, int64_t ld,
                                          int64_t row0, int64_t col0, int cols, float* partial) {
   if (it.S == 1) {
-    store_tile(acc, lds, out, ld, row0, col0, BM, cols);
+    store_tile(acc, out, ld, row0, col0, BM, cols);
     return;
   }
   float* mine = partial + int64_t(it.slot) * (BM * BN);
@@ -1351,7 +1465,6 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
                                                              const uint16_t* __restrict__ x,
                                                              uint16_t* __restrict__ dW13, int32_t* queue,
                                                              float* __restrict__ partial, int32_t* plan_out) {
-  MOE_GEMM_SMEM
   MOE_DW_SMEM
   const int H = int(p.H), I = int(p.I);
   const int MT = (2 * I) / BM, NT = H / BN;
@@ -1377,8 +1490,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     }
     Acc acc;
     acc.zero();
-    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, lds, acc);
-    dw_store(acc, it, lds, dW13 + int64_t(it.e) * 2 * I * H, H, int64_t(mt) * BM, int64_t(nt) * BN, BN, partial);
+    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, acc);
+    dw_store(acc, it, dW13 + int64_t(it.e) * 2 * I * H, H, int64_t(mt) * BM, int64_t(nt) * BN, BN, partial);
   });
 }
 
@@ -1386,7 +1499,6 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
                                                             const uint16_t* __restrict__ act,
                                                             uint16_t* __restrict__ dW2, int32_t* queue,
                                                             float* __restrict__ partial, int32_t* plan_out) {
-  MOE_GEMM_SMEM
   MOE_DW_SMEM
   const int H = int(p.H), I = int(p.I);
   const int MT = H / BM, NT = (I + BN - 1) / BN;  // the last n-tile may hold 128 columns
@@ -1414,8 +1526,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     }
     Acc acc;
     acc.zero();
-    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, lds, acc);
-    dw_store(acc, it, lds, dW2 + int64_t(it.e) * H * I, I, int64_t(mt) * BM, int64_t(nt) * BN, ncols, partial);
+    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, acc);
+    dw_store(acc, it, dW2 + int64_t(it.e) * H * I, I, int64_t(mt) * BM, int64_t(nt) * BN, ncols, partial);
   });
 }
 
@@ -1467,7 +1579,6 @@ __global__ __launch_bounds__(kThreads) void gemm_dw_fp8_kernel(GemmProblem p, co
                                                                const uint8_t* __restrict__ qscales, int NQ,
                                                                uint16_t* __restrict__ dW, int32_t* queue,
                                                                float* __restrict__ partial, int32_t* plan_out) {
-  MOE_GEMM_SMEM
   MOE_DW_SMEM
   __shared__ int32_t s_kb[1025];
   const int E = int(p.E);
@@ -1501,8 +1612,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dw_fp8_kernel(GemmProblem p, co
     }
     Acc acc;
     acc.zero();
-    mainloop_fp8(lp, lq, kb, lds, acc);  // an empty expert runs no slab and stores zeros
-    dw_store(acc, it, lds, dW + int64_t(e) * MP * NQ, NQ, int64_t(mt) * BM, int64_t(nt) * BN, ncols, partial);
+    mainloop_fp8(lp, lq, kb, acc);  // an empty expert runs no slab and stores zeros
+    dw_store(acc, it, dW + int64_t(e) * MP * NQ, NQ, int64_t(mt) * BM, int64_t(nt) * BN, ncols, partial);
   });
 }
 
