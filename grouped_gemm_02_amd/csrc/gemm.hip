@@ -359,32 +359,6 @@ __device__ __forceinline__ void plain_slab(LP& lp, LQ& lq, int kt, int nk, uint1
   __syncthreads();
 }
 
-// The same with the slab's last 16-deep step deferred past the barrier
-// (fragments double buffered: pf0/qf0 hold step 0 of `cur` on entry and
-// step 0 of `nxt` on exit).
-template <bool P_MN, bool Q_MN, class LP, class LQ>
-__device__ __forceinline__ void deferred_slab(LP& lp, LQ& lq, int kt, int nk, uint16_t* cur, uint16_t* nxt,
-                                              Acc& acc, bool active, Stage& sp, Stage& sq, bf16x8 (&pf0)[TM],
-                                              bf16x8 (&qf0)[TN], bf16x8 (&pf1)[TM], bf16x8 (&qf1)[TN]) {
-  const bool more = kt + 1 < nk;
-  if (more) fetch_next(lp, lq, kt + 1, nxt, sp, sq);
-  if (active) {
-    load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 1, pf1, qf1);
-    mma_step(pf0, qf0, acc);
-    load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 2, pf0, qf0);
-    mma_step(pf1, qf1, acc);
-    load_frags<P_MN, Q_MN>(cur, cur + kOperandLds, 3, pf1, qf1);
-    mma_step(pf0, qf0, acc);
-  }
-  if (more) store_next(lp, lq, nxt, sp, sq);
-  wait_direct<LP, LQ>();
-  __syncthreads();
-  if (active) {
-    if (more) load_frags<P_MN, Q_MN>(nxt, nxt + kOperandLds, 0, pf0, qf0);
-    mma_step(pf1, qf1, acc);
-  }
-}
-
 // Runs the k loop of one tile: the global loads of slab kt+1 are in flight
 // while slab kt is multiplied out of one LDS stage, either straight into the
 // other stage or into registers that are written there after the MFMAs.
@@ -393,17 +367,9 @@ __device__ __forceinline__ void deferred_slab(LP& lp, LQ& lq, int kt, int nk, ui
 // mainloop_staged runs the k loop with slab 0 already fetched into sp, sq
 // (the persistent row-tile kernels fetch a tile's first slab during the
 // previous tile's epilogue); mainloop fetches it itself.
-//
-// With DEFER, fragments are double buffered and the slab's last 16-deep step
-// is deferred past the slab barrier: its fragments are already in registers,
-// so its MFMAs run while the next slab's first fragments are read instead of
-// every wave starting a slab with an LDS wait. On a plain dense GEMM of this
-// core that is ~9 % more MFMA issue; inside the grouped kernels it pays only
-// in the dH GEMM (~4 %) and costs 1-2 % elsewhere, so only dH uses it.
-template <bool P_MN, bool Q_MN, bool DEFER = false, class LP, class LQ>
+template <bool P_MN, bool Q_MN, class LP, class LQ>
 __device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, Acc& acc, bool active, Stage& sp,
                                                 Stage& sq) {
-  static_assert(BK / 16 == 4, "the deferred step schedule is written for four 16-deep steps per slab");
   if (nk <= 0) return;
   lp.store(g_stage0, sp);
   lq.store(g_stage0 + kOperandLds, sq);
@@ -411,20 +377,11 @@ __device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, Acc& acc
   if constexpr (!kBothDirect<LP, LQ>) {
     // slabs through registers: one loop body (unrolled by two it would not
     // fit the registers of the weight-gradient GEMMs)
-    if constexpr (!DEFER) {
-      for (int kt = 0; kt < nk; ++kt)
-        plain_slab<P_MN, Q_MN>(lp, lq, kt, nk, stage_buf(kt & 1), stage_buf((kt + 1) & 1), acc, active, sp, sq);
-    } else {
-      bf16x8 pf0[TM], qf0[TN], pf1[TM], qf1[TN];
-      if (active) load_frags<P_MN, Q_MN>(g_stage0, g_stage0 + kOperandLds, 0, pf0, qf0);
-      for (int kt = 0; kt < nk; ++kt)
-        deferred_slab<P_MN, Q_MN>(lp, lq, kt, nk, stage_buf(kt & 1), stage_buf((kt + 1) & 1), acc, active, sp, sq,
-                                  pf0, qf0, pf1, qf1);
-    }
+    for (int kt = 0; kt < nk; ++kt)
+      plain_slab<P_MN, Q_MN>(lp, lq, kt, nk, stage_buf(kt & 1), stage_buf((kt + 1) & 1), acc, active, sp, sq);
   } else {
     // straight-to-LDS slabs: unrolled by two, so that each slab's stages are
     // known at compile time
-    static_assert(!DEFER, "the deferred schedule is not combined with straight-to-LDS loads");
     for (int kt = 0; kt < nk; kt += 2) {
       plain_slab<P_MN, Q_MN>(lp, lq, kt, nk, g_stage0, g_stage1, acc, active, sp, sq);
       if (kt + 1 >= nk) break;
@@ -433,13 +390,13 @@ __device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, Acc& acc
   }
 }
 
-template <bool P_MN, bool Q_MN, bool DEFER = false, class LP, class LQ>
+template <bool P_MN, bool Q_MN, class LP, class LQ>
 __device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, Acc& acc, bool active = true) {
   if (nk <= 0) return;
   Stage sp, sq;
   lp.fetch(0, sp);
   lq.fetch(0, sq);
-  mainloop_staged<P_MN, Q_MN, DEFER>(lp, lq, nk, acc, active, sp, sq);
+  mainloop_staged<P_MN, Q_MN>(lp, lq, nk, acc, active, sp, sq);
 }
 
 // ------------------------------------------------------------------ FP8 core
@@ -1082,7 +1039,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
       lq.fn.nrows = H;
       lq.nchunks = ncols / 8;
       lq.prime(0);
-      mainloop<false, true, true>(lp, lq, KU / 64, acc, wave_m() * WTM < rt.rows);
+      mainloop<false, true>(lp, lq, KU / 64, acc, wave_m() * WTM < rt.rows);
     }
     if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).

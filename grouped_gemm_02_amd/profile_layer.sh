@@ -3,8 +3,10 @@
 # that are kept under profiles/ into <out_dir>/profiles. Usage (from the
 # repository root):
 #   bash grouped_gemm_02_amd/profile_layer.sh <out_dir>
-# Kernel statistics for every workload, then FETCH_SIZE and WRITE_SIZE
-# counter passes (separate runs) for the default workload.
+# Kernel statistics for every workload (the bench defaults: 20 timed steps
+# after 5 warm-up steps, so the averages compare with its event timings),
+# then FETCH_SIZE and WRITE_SIZE counter passes (separate runs) for the
+# default workload.
 set -e
 OUT=${1:-gpurun_out/prof}
 export TMPDIR=/tmp
@@ -17,7 +19,7 @@ for cpw in qwen3_30b:bf16:bf16:none ep8_share:fp8_block:bf16:none qwen3_235b:fp8
   IFS=: read -r c prec wg rt <<< "$cpw"
   tag=${c}_${prec}; [ "$wg" = fp8 ] && tag=${tag}_fp8_wgrad; [ "$rt" != none ] && tag=${tag}_router_${rt}
   echo "stats $tag"
-  args="--config $c --precision $prec --wgrad $wg --router $rt --steps 5 --warmup 2 --no-cpu-baseline"
+  args="--config $c --precision $prec --wgrad $wg --router $rt --steps 20 --warmup 5 --no-cpu-baseline"
   timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/stats_$tag" -o run -- \
     python3 bench.py $args > "$OUT/stats_$tag.log" 2>&1
   python3 -m grouped_gemm_02_amd.profile_summary stats "$OUT/stats_$tag/run_kernel_stats.csv" \
