@@ -344,6 +344,42 @@ __device__ __forceinline__ void store_next(const LP& lp, const LQ& lq, uint16_t*
   }
 }
 
+// A slab whose k-major operand P is loaded straight into LDS while the
+// mn-major operand Q goes through registers (the dX and dH GEMMs). The
+// compiler cannot tell Q's transpose reads from loads into LDS in flight and
+// would wait for P's loads before any of them that follows; so Q's fragments
+// of the whole slab (32 registers) are read first, then slab kt+1 is
+// requested, then P's fragments are read step by step between the MFMAs.
+template <class LP, class LQ>
+__device__ __forceinline__ void mixed_slab(LP& lp, LQ& lq, int kt, int nk, uint16_t* cur, uint16_t* nxt, Acc& acc,
+                                           bool active, Stage& sq) {
+  const bool more = kt + 1 < nk;
+  bf16x8 qf[BK / 16][TN];
+  const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
+  if (active) {
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) qf[kk][j] = frag_mn(cur + kOperandLds, qn0 + 32 * j, kk);
+  }
+  if (more) {
+    lp.dma(kt + 1, nxt);
+    lq.fetch(kt + 1, sq);
+  }
+  if (active) {
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 pf[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) pf[i] = frag_k<true>(cur, pm0 + 32 * i, kk);
+      mma_step(pf, qf[kk], acc);
+    }
+  }
+  if (more) lq.store(nxt + kOperandLds, sq);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // P's loads into LDS have landed (vmcnt(0))
+  __syncthreads();
+}
+
 // One slab kt of the k loop out of stage `cur`; slab kt+1 (if any) goes to
 // stage `nxt`. Both stages are named at compile time by the caller (the loop
 // is unrolled by two), which is what lets the slab's fragment reads run while
@@ -374,7 +410,11 @@ __device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, Acc& acc
   lp.store(g_stage0, sp);
   lq.store(g_stage0 + kOperandLds, sq);
   __syncthreads();
-  if constexpr (!kBothDirect<LP, LQ>) {
+  if constexpr (LP::kDirect && !LQ::kDirect) {
+    static_assert(!P_MN && Q_MN, "mixed slabs: P k-major and loaded straight into LDS, Q mn-major");
+    for (int kt = 0; kt < nk; ++kt)
+      mixed_slab(lp, lq, kt, nk, stage_buf(kt & 1), stage_buf((kt + 1) & 1), acc, active, sq);
+  } else if constexpr (!kBothDirect<LP, LQ>) {
     // slabs through registers: one loop body (unrolled by two it would not
     // fit the registers of the weight-gradient GEMMs)
     for (int kt = 0; kt < nk; ++kt)
@@ -1118,7 +1158,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
   const int NT = H / BN;
   const int KU = row_units<FP8>(2 * I);
   const int64_t total = int64_t(s_pref[E]) * NT;
-  KLoader<FP8> lp;
+  KLoaderD<FP8> lp;
   typename std::conditional<FP8, KMajorLoader8, MNMajorLoader<DirectRows>>::type lq;
   auto setup = [&](int64_t t, TileState& st) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
