@@ -115,9 +115,10 @@ struct Stage {
 //     straight into LDS (buffer_load ... lds: no registers, no LDS store
 //     instructions) can write, and slabs after a tile's first one are moved
 //     that way (dma); slab 0 still goes through registers.
-// The swizzled layout is used where both operands of a GEMM are k-major bf16
-// (the gate/up and down GEMMs); elsewhere its XOR addressing costs registers
-// and the padded layout is kept.
+// The swizzled layout is used for the bf16 k-major operands that are loaded
+// straight into LDS: both operands of the gate/up and down GEMMs and the
+// k-major operand of the dX GEMM. The dH GEMM keeps the padded layout (there
+// the XOR addressing costs registers and the straight loads did not pay).
 __device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 
 template <bool SWZ>
@@ -314,9 +315,11 @@ __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* l
 
 // Slab kt of both operands into stage buffer `buf`: when both loaders can,
 // straight into LDS now; otherwise into registers (stored by store_next after
-// the MFMAs). Only both or neither: the compiler cannot tell the LDS
+// the MFMAs). Only both or neither here: the compiler cannot tell the LDS
 // transpose reads of an mn-major operand from loads into LDS in flight, and
-// would wait for those loads before the slab's first fragment read.
+// would wait for those loads before the slab's first fragment read (the
+// mixed case, a straight k-major operand with an mn-major one, has its own
+// slab order: mixed_slab).
 template <class LP, class LQ>
 constexpr bool kBothDirect = LP::kDirect && LQ::kDirect;
 
