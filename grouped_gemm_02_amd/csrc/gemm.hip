@@ -298,13 +298,11 @@ __device__ __forceinline__ void mma_step(const bf16x8 (&pf)[TM], const bf16x8 (&
 template <bool P_MN, bool Q_MN, bool KSWZ = false>
 __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
   // The compiler's own interleave of the fragment reads with the MFMAs
-  // leaves LDS latency exposed; its built-in MFMA/DS interleave strategies
-  // measured 2-5 % faster: strategy 1 where both operands are k-major,
-  // strategy 0 where one is read transposed.
-  if constexpr (!P_MN && !Q_MN)
-    __builtin_amdgcn_iglp_opt(1);
-  else
-    __builtin_amdgcn_iglp_opt(0);
+  // leaves LDS latency exposed; its built-in MFMA/DS interleave strategy 0
+  // measured 2-5 % faster. (Strategy 1 was better for two k-major operands
+  // while their slabs went through registers; with the slabs loaded straight
+  // into LDS, strategy 0 is 1-2 % faster there too.)
+  __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
     bf16x8 pf[TM], qf[TN];
