@@ -205,7 +205,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the layer is one GPU's share; see DESIGN.md on sharding)", file=sys.stderr)
+              f"(the layer is one GPU's share: a sharded step adds an all-to-all of the token rows "
+              f"before and after it)", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -7,7 +7,7 @@ path.
 The pages list FP8 x FP4 among the data types of DeepGEMM's Mega MoE, a
 forward-only fused MoE kernel (MarkTechPost article, comparison table of
 fused MoE options: data-type and backward-pass rows), and give no recipe for
-it. The reading used here (listed in the design doc), an inference forward of the
+it. The reading used here, an inference forward of the
 layer:
 
 * expert weights in FP4 E2M1 (OCP MX: sign, 2 exponent bits with bias 1, one

@@ -8,7 +8,7 @@ The pages name the precisions (ic.work analysis, section on hardware
 constraints: BF16, MXFP8 and blockwise FP8; MarkTechPost article, "How do
 developers use it?": bf16, mxfp8, fp8 and fp8_bwd = BF16 forward with FP8
 backward) but not the number format, block shapes, scale rule or which
-tensors are quantized. The readings used here (listed in the design doc):
+tensors are quantized. The readings used here:
 
 * FP8 is OCP E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7,
   3 mantissa bits, subnormals, no infinities, largest finite value 448.

@@ -21,7 +21,7 @@ is exact), with no intermediate rounding:
   (ic.work analysis, section "From 3.11x to 1.32x": backward adds weight
   gradients on top of activation gradients).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * W13 is [E, 2I, H]: rows [0, I) are the gate projection W1, rows [I, 2I) the
   up projection W3. W2 is [E, H, I]. Both are nn.Linear-style (h = W x).

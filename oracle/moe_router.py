@@ -8,7 +8,7 @@ The pages leave the router outside the measured layer and criticise exactly
 that, together with uniform random routing (ic.work analysis, section on the
 benchmark's idealised assumptions: the router's cost is excluded and real
 token distributions are skewed). What a router computes is not on the pages;
-the plain reading used here (listed in the design doc):
+the plain reading used here:
 
 * probabilities p = softmax(z) over the E logits of a token;
 * the k experts with the largest logits (equivalently probabilities), in
