@@ -264,7 +264,7 @@ const char* moe_status_string(moe_status st) {
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than required";
     case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: HIP launch or runtime call failed";
     case MOE_ERR_ROUTING: return "MOE_ERR_ROUTING: an expert id was outside [0, E)";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: not implemented in this build";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: not implemented by this library";
   }
   return "unknown moe_status";
 }

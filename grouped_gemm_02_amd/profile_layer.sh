@@ -8,7 +8,7 @@
 # then FETCH_SIZE and WRITE_SIZE counter passes (separate runs) for the
 # default workload.
 set -e
-OUT=${1:-gpurun_out/prof}
+OUT=${1:-rocprof_out}
 export TMPDIR=/tmp
 PROF="$OUT/profiles"
 mkdir -p "$OUT" "$PROF"

@@ -64,7 +64,7 @@ typedef enum moe_status {
   MOE_ERR_WORKSPACE = 6,   /* workspace or saved buffer smaller than required  */
   MOE_ERR_LAUNCH = 7,      /* a HIP launch or runtime call failed              */
   MOE_ERR_ROUTING = 8,     /* device: some expert id was outside [0, E)        */
-  MOE_ERR_UNSUPPORTED = 9  /* valid request this build does not implement      */
+  MOE_ERR_UNSUPPORTED = 9  /* valid request this library does not implement    */
 } moe_status;
 
 /* Precision of the expert GEMMs (ic.work analysis, hardware constraints;
