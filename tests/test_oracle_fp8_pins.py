@@ -387,3 +387,71 @@ def test_fp8_weight_gradients_are_per_expert(mode):
         f, xe, ie, we, dye = orc.restrict_to_expert(x, idx, w, dy, e)
         _, _, s13, s2 = f8.backward(dye, xe, ie, we, W13[e:e + 1], W2[e:e + 1], mode, wgrad="fp8")
         assert np.array_equal(dW13[e], s13[0]) and np.array_equal(dW2[e], s2[0]), e
+
+
+# ----------------------------------------------------- default (bf16) weight gradients of the FP8 modes
+
+def _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip=None):
+    """dW13, dW2 under the default reading (weight-gradient GEMMs on the
+    unquantized operands) of an FP8 mode, accumulated pair by pair as outer
+    products: dW13[e] += [dg | du] x[t]^T and dW2[e] += dY[t] (w a)^T, where
+    g, u and a come from that mode's forward (quantized x and W13 in
+    fp8_block and mxfp8, exact in fp8_bwd) and [dg | du] from its quantized
+    dH product. `slip` plants a mistake on purpose: "xq" multiplies the
+    quantized x in dW13, "exact_a" takes a from the unquantized forward."""
+    blk, rule = (32, "mx_floor") if mode == "mxfp8" else (128, "pow2_ceil")
+    T, H = x.shape
+    E = W13.shape[0]
+    I = W13.shape[1] // 2
+    k = idx.shape[1]
+    qa = lambda M: _q_rows(M, blk, rule)  # noqa: E731
+    if mode == "fp8_bwd":
+        xq, W13q = x, W13
+    else:
+        xq, W13q = qa(x), _q_weight(W13, mode, True)
+    W2b = _q_weight(W2, mode, False)
+    dyq = qa(dy)
+    dW13 = np.zeros((E, 2 * I, H))
+    dW2 = np.zeros((E, H, I))
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            g = W13q[e, :I] @ xq[t]
+            u = W13q[e, I:] @ xq[t]
+            sg = 1.0 / (1.0 + np.exp(-g))
+            a = g * sg * u
+            dau = W2b[e].T @ dyq[t]
+            da = w[t, j] * dau
+            dh = np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg])
+            if slip == "exact_a":
+                ge, ue = W13[e, :I] @ x[t], W13[e, I:] @ x[t]
+                a = ge / (1.0 + np.exp(-ge)) * ue
+            dW13[e] += np.outer(dh, xq[t] if slip == "xq" else x[t])
+            dW2[e] += np.outer(dy[t], w[t, j] * a)
+    return dW13, dW2
+
+
+@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8", "fp8_bwd"])
+def test_default_weight_gradients_match_pair_loops(mode):
+    """The default weight-gradient reading of every FP8 mode against outer
+    products summed pair by pair, with the scalar rounding helpers above for
+    every quantization point of the forward and the dH product. The planted
+    slips (the quantized x in dW13; a from the unquantized forward in dW2)
+    are far outside the pin's tolerance, so the pin would catch them."""
+    rng = np.random.default_rng(11)
+    T, H, I, E, k = 7, 256, 128, 3, 2
+    x = rng.standard_normal((T, H)) * np.exp(rng.standard_normal((T, 1)))
+    W13 = rng.standard_normal((E, 2 * I, H)) * 0.05
+    W2 = rng.standard_normal((E, H, I)) * 0.05
+    idx = np.array([rng.choice(E, k, replace=False) for _ in range(T)])
+    w = rng.uniform(0.1, 1.0, size=(T, k))
+    dy = rng.standard_normal((T, H))
+    _, _, dW13, dW2 = f8.backward(dy, x, idx, w, W13, W2, mode)
+    r13, r2 = _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode)
+    np.testing.assert_allclose(dW13, r13, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(dW2, r2, rtol=1e-9, atol=1e-9)
+    if mode != "fp8_bwd":  # (fp8_bwd's forward is exact: both slips are no-ops there)
+        s13, _ = _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip="xq")
+        _, s2 = _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip="exact_a")
+        assert np.max(np.abs(s13 - dW13)) / np.max(np.abs(dW13)) > 1e-4
+        assert np.max(np.abs(s2 - dW2)) / np.max(np.abs(dW2)) > 1e-4
