@@ -119,6 +119,30 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+MOE_ERR_SHAPE = 2
+
+
+def _want(t, name: str, dtype, numel: int | None = None, optional: bool = False) -> None:
+    """Checks a tensor argument before its pointer crosses the C ABI, which
+    cannot see dtypes, strides or sizes: it must be a contiguous GPU tensor of
+    `dtype` with at least `numel` elements. Raises MoEError(MOE_ERR_SHAPE)
+    otherwise. Anything that is not a torch tensor (None, a raw address) is
+    passed through for the library's own checks (NULL, alignment)."""
+    if not isinstance(t, torch.Tensor):
+        return
+    if t.dtype != dtype:
+        raise MoEError(MOE_ERR_SHAPE, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise MoEError(MOE_ERR_SHAPE, f"{name} is not contiguous")
+    if numel is not None and t.numel() < numel:
+        raise MoEError(MOE_ERR_SHAPE, f"{name} holds {t.numel()} elements, needs {numel}")
+    if t.device.type != "cuda":
+        raise MoEError(MOE_ERR_SHAPE, f"{name} is on {t.device}, expected a GPU tensor")
+
+
+_BF16, _I32, _F32, _U8 = torch.bfloat16, torch.int32, torch.float32, torch.uint8
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         if torch.cuda.is_available():
@@ -163,6 +187,11 @@ def moe_get_wq_layout(shape: moe_shape) -> dict:
 
 
 def moe_quantize_weights(shape, W13, W2, wq, stream=None) -> None:
+    if shape.precision != PRECISIONS["bf16"]:
+        E, H, I = shape.E, shape.H, shape.I
+        _want(W13, "W13", _BF16, E * 2 * I * H)
+        _want(W2, "W2", _BF16, E * H * I)
+        _want(wq, "wq", _U8, moe_get_wq_layout(shape)["total"])
     _check(lib().moe_quantize_weights(ctypes.byref(shape), _ptr(W13), _ptr(W2), _ptr(wq), _stream(stream)),
            "moe_quantize_weights")
 
@@ -173,12 +202,24 @@ def wgrad_rows_cap(shape: moe_shape) -> int:
 
 
 def moe_quantize_tokens(shape, x, ld, C, counts, offsets, src_of, codes, scales, stream=None) -> None:
+    if shape.T > 0:
+        K = wgrad_rows_cap(shape)
+        _want(x, "in", _BF16)
+        _want(counts, "counts", _I32, shape.E)
+        _want(offsets, "offsets", _I32, shape.E + 1)
+        _want(src_of, "src_of", _I32, shape.T * shape.k, optional=True)
+        _want(codes, "codes", _U8, int(C) * K)
+        _want(scales, "scales", _U8, int(C) * K // 32)
     _check(lib().moe_quantize_tokens(ctypes.byref(shape), _ptr(x), int(ld), int(C), _ptr(counts), _ptr(offsets),
                                      _ptr(src_of), _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_quantize_tokens")
 
 
 def moe_quantize_rows(shape, x, rows, K, codes, scales, stream=None) -> None:
+    if rows > 0:
+        _want(x, "in", _BF16, int(rows) * int(K))
+        _want(codes, "codes", _U8, int(rows) * int(K))
+        _want(scales, "scales", _U8, int(rows) * int(K) // 32)
     _check(lib().moe_quantize_rows(ctypes.byref(shape), _ptr(x), int(rows), int(K), _ptr(codes), _ptr(scales),
                                    _stream(stream)), "moe_quantize_rows")
 
@@ -188,11 +229,29 @@ def moe_permute_scratch_bytes(shape: moe_shape) -> int:
 
 
 def moe_permute(shape, topk_idx, counts, offsets, row_of, src_of, scratch, stream=None) -> None:
+    Tk = shape.T * shape.k
+    _want(topk_idx, "topk_idx", _I32, Tk, optional=Tk == 0)
+    _want(counts, "counts", _I32, shape.E)
+    _want(offsets, "offsets", _I32, shape.E + 1)
+    _want(row_of, "row_of", _I32, Tk, optional=Tk == 0)
+    _want(src_of, "src_of", _I32, Tk, optional=Tk == 0)
+    _want(scratch, "scratch", _U8, moe_permute_scratch_bytes(shape))
     _check(lib().moe_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(row_of),
                              _ptr(src_of), _ptr(scratch), _stream(stream)), "moe_permute")
 
 
 def moe_fwd(shape, x, topk_idx, topk_w, W13, W2, wq, y, saved, ws, stream=None) -> None:
+    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    f, s, _ = moe_workspace_size(shape)
+    _want(x, "x", _BF16, T * H, optional=T == 0)
+    _want(topk_idx, "topk_idx", _I32, T * k, optional=T == 0)
+    _want(topk_w, "topk_w", _F32, T * k, optional=T == 0)
+    _want(W13, "W13", _BF16, E * 2 * I * H)
+    _want(W2, "W2", _BF16, E * H * I)
+    _want(wq, "wq", _U8, moe_get_wq_layout(shape)["total"], optional=True)
+    _want(y, "y", _BF16, T * H, optional=T == 0)
+    _want(saved, "saved", _U8, s, optional=True)
+    _want(ws, "ws", _U8, f)
     _check(lib().moe_fwd(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W13), _ptr(W2),
                          _ptr(wq), _ptr(y), _ptr(saved), _ptr(ws), ws.numel() * ws.element_size(),
                          _stream(stream)), "moe_fwd")
@@ -200,17 +259,41 @@ def moe_fwd(shape, x, topk_idx, topk_w, W13, W2, wq, y, saved, ws, stream=None) 
 
 def moe_bwd(shape, dy, x, topk_idx, topk_w, W13, W2, wq, saved, dx, d_topk_w, dW13, dW2, ws,
             stream=None) -> None:
+    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    _, s, b = moe_workspace_size(shape)
+    for t, n, dt, cnt in ((dy, "dy", _BF16, T * H), (x, "x", _BF16, T * H), (topk_idx, "topk_idx", _I32, T * k),
+                          (topk_w, "topk_w", _F32, T * k), (dx, "dx", _BF16, T * H),
+                          (d_topk_w, "d_topk_w", _F32, T * k)):
+        _want(t, n, dt, cnt, optional=T == 0)
+    _want(W13, "W13", _BF16, E * 2 * I * H)
+    _want(W2, "W2", _BF16, E * H * I)
+    _want(wq, "wq", _U8, moe_get_wq_layout(shape)["total"], optional=True)
+    _want(saved, "saved", _U8, s)
+    _want(dW13, "dW13", _BF16, E * 2 * I * H)
+    _want(dW2, "dW2", _BF16, E * H * I)
+    _want(ws, "ws", _U8, b)
     _check(lib().moe_bwd(ctypes.byref(shape), _ptr(dy), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(W13),
                          _ptr(W2), _ptr(wq), _ptr(saved), _ptr(dx), _ptr(d_topk_w), _ptr(dW13), _ptr(dW2),
                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_bwd")
 
 
 def moe_route(shape, logits, renorm, topk_idx, topk_w, stream=None) -> None:
+    if shape.T > 0:
+        _want(logits, "logits", _F32, shape.T * shape.E)
+        _want(topk_idx, "topk_idx", _I32, shape.T * shape.k)
+        _want(topk_w, "topk_w", _F32, shape.T * shape.k)
     _check(lib().moe_route(ctypes.byref(shape), _ptr(logits), int(bool(renorm)), _ptr(topk_idx), _ptr(topk_w),
                            _stream(stream)), "moe_route")
 
 
 def moe_route_bwd(shape, logits, topk_idx, topk_w, d_topk_w, renorm, d_logits, stream=None) -> None:
+    if shape.T > 0:
+        for t, n, dt, cnt in ((logits, "logits", _F32, shape.T * shape.E),
+                              (topk_idx, "topk_idx", _I32, shape.T * shape.k),
+                              (topk_w, "topk_w", _F32, shape.T * shape.k),
+                              (d_topk_w, "d_topk_w", _F32, shape.T * shape.k),
+                              (d_logits, "d_logits", _F32, shape.T * shape.E)):
+            _want(t, n, dt, cnt)
     _check(lib().moe_route_bwd(ctypes.byref(shape), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(d_topk_w),
                                int(bool(renorm)), _ptr(d_logits), _stream(stream)), "moe_route_bwd")
 

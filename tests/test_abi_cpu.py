@@ -272,3 +272,30 @@ def test_quantize_tokens_argument_checks(B):
         s = _shape(B, **kw)
         st = _raw_call(B, "moe_quantize_tokens", ctypes.byref(s), *args, None)
         assert st == status, (kw, args, st)
+
+
+def test_binding_checks_tensor_arguments(B):
+    """The binding refuses tensors the C ABI cannot check (wrong dtype,
+    non-contiguous, too small, not on the GPU) with MOE_ERR_SHAPE before any
+    pointer crosses the boundary."""
+    import torch
+    T, H, I, E, k = 64, 256, 128, 8, 2
+    s = B.make_shape(T, H, I, E, k)
+    f, sv, _ = B.moe_workspace_size(s)
+    ok = dict(x=torch.zeros(T, H, dtype=torch.bfloat16), idx=torch.zeros(T, k, dtype=torch.int32),
+              w=torch.zeros(T, k), W13=torch.zeros(E, 2 * I, H, dtype=torch.bfloat16),
+              W2=torch.zeros(E, H, I, dtype=torch.bfloat16), y=torch.zeros(T, H, dtype=torch.bfloat16),
+              saved=torch.zeros(sv, dtype=torch.uint8), ws=torch.zeros(f, dtype=torch.uint8))
+    bad = {"x": ok["x"].float(), "idx": ok["idx"].long(), "w": ok["w"].double(),
+           "W13": ok["W13"].transpose(1, 2), "W2": ok["W2"][:, :, :64], "y": ok["y"][:1],
+           "ws": ok["ws"][:16]}
+    for name, t in bad.items():
+        a = dict(ok, **{name: t})
+        with pytest.raises(B.MoEError) as ei:
+            B.moe_fwd(s, a["x"], a["idx"], a["w"], a["W13"], a["W2"], None, a["y"], a["saved"], a["ws"], stream=0)
+        assert ei.value.status == 2, name
+    # every argument well formed but on the CPU: refused as well
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_fwd(s, ok["x"], ok["idx"], ok["w"], ok["W13"], ok["W2"], None, ok["y"], ok["saved"], ok["ws"],
+                  stream=0)
+    assert ei.value.status == 2 and "GPU" in str(ei.value)
