@@ -13,7 +13,7 @@ shape (ep8_share: blockwise FP8, qwen3_235b: fp8_bwd, zipf: MXFP8).
 Prints one JSON line. `value` is TFLOP/s of algorithmic work
 (18 * T * k * H * I flops per step: 6 forward, 12 backward).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config NAME] [--precision P]
+    python bench.py [--gpus 1] [--steps 15] [--warmup 5] [--config NAME] [--precision P]
 """
 from __future__ import annotations
 
@@ -46,6 +46,8 @@ def hbm_bytes(name: str, cfg) -> float | None:
     read once, each output written once), or None."""
     T, H, I, k, M = cfg.T, cfg.H, cfg.I, cfg.k, cfg.M
     nparts = 2 * -(-I // 256)
+    if name == "permute":  # histogram + scan + scatter: ids and weights in; counts, offsets, maps, row weights out
+        return 4.0 * T * k + 4.0 * T * k + 8.0 * cfg.E + 4.0 * (3 * T * k)
     if name == "combine_y" and k > 1:
         return 2.0 * M * H + 4.0 * T * k + 2.0 * T * H
     if name == "combine_dx_dw" and k > 1:
@@ -104,7 +106,7 @@ def measured_traffic(kernel: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=15)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_30b", choices=sorted(WORKLOADS))
     ap.add_argument("--precision", default=None, choices=["bf16", "fp8_block", "mxfp8", "fp8_bwd", "fp8_fp4"],
@@ -120,26 +122,61 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(cfg, d, n_tok):
-    """The CPU oracle, as it stands, on the first n_tok tokens of the workload."""
-    import numpy as np
+def host_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, CPUs this process may
+    use, the CPU model and the thread settings."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"nproc": usable, "logical_cpus": os.cpu_count(), "cpu_model": model,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def _blas_threads() -> int:
     from threadpoolctl import threadpool_info
+    threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return int(max(threads) if threads else 1)
+
+
+def cpu_baseline(cfg, d, n_tok, n_tok_1core=1024):
+    """The CPU oracle, as it stands, on the first n_tok tokens of the workload
+    with every BLAS thread, and on the first n_tok_1core tokens with one."""
+    from threadpoolctl import threadpool_limits
 
     from oracle import moe_oracle as orc
-    n_tok = min(n_tok, cfg.T)
-    sub = {k: d[k][:n_tok].cpu() for k in ("x", "topk_idx", "topk_w", "dy")}
     W13 = d["W13"].cpu()
     W2 = d["W2"].cpu()
-    t0 = time.perf_counter()
-    orc.forward(sub["x"], sub["topk_idx"], sub["topk_w"], W13, W2)
-    orc.backward(sub["dy"], sub["x"], sub["topk_idx"], sub["topk_w"], W13, W2)
-    dt = time.perf_counter() - t0
-    flops = 18.0 * n_tok * cfg.k * cfg.H * cfg.I
-    threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(max(threads) if threads else 1),
+
+    def run(n):
+        sub = {k: d[k][:n].cpu() for k in ("x", "topk_idx", "topk_w", "dy")}
+        t0 = time.perf_counter()
+        orc.forward(sub["x"], sub["topk_idx"], sub["topk_w"], W13, W2)
+        orc.backward(sub["dy"], sub["x"], sub["topk_idx"], sub["topk_w"], W13, W2)
+        return time.perf_counter() - t0
+    n_tok = min(n_tok, cfg.T)
+    dt = run(n_tok)
+    threads = _blas_threads()
+    n1 = min(n_tok_1core, cfg.T)
+    with threadpool_limits(limits=1, user_api="blas"):
+        dt1 = run(n1)
+    per_tok = 18.0 * cfg.k * cfg.H * cfg.I
+    return {"value": per_tok * n_tok / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
+            "one_core": {"value": per_tok * n1 / dt1 / 1e12, "unit": "TFLOP/s", "seconds": round(dt1, 3),
+                         "sample": f"first {n1} tokens, BLAS limited to 1 thread"},
+            "host": host_info(),
             "sample": f"first {n_tok} tokens of the workload (all {cfg.E} experts, full weights), "
-                      f"forward + backward in float64 numpy; flops counted as 18*tokens*k*H*I"}
+                      f"forward + backward in float64 numpy with {threads} BLAS threads; "
+                      f"flops counted as 18*tokens*k*H*I"}
 
 
 def cpu_baseline_fp8(cfg, d, n_experts, wgrad="bf16"):
@@ -169,6 +206,7 @@ def cpu_baseline_fp8(cfg, d, n_experts, wgrad="bf16"):
     threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(max(threads) if threads else 1),
             "kind": "oracle", "seconds": round(dt, 3),
+            "host": host_info(),
             "sample": f"the {pairs} routed pairs of experts 0..{n_experts - 1} ({len(toks)} tokens), "
                       f"{cfg.precision} emulation (weight quantization of those experts included), "
                       f"forward + backward in float64 numpy; flops counted as 18*pairs*H*I"}
@@ -196,6 +234,7 @@ def cpu_baseline_fp4(cfg, d, n_experts):
     threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(max(threads) if threads else 1),
             "kind": "oracle", "seconds": round(dt, 3),
+            "host": host_info(),
             "sample": f"the {pairs} routed pairs of experts 0..{n_experts - 1} ({len(toks)} tokens), "
                       f"FP8 x FP4 forward emulation (weight quantization of those experts included) "
                       f"in float64 numpy; flops counted as 6*pairs*H*I"}
@@ -305,6 +344,8 @@ def main():
     fwd_ms = [e[3].elapsed_time(e[1]) for e in evs]
     wq_ms = [e[0].elapsed_time(e[3]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    med = lambda v: (sorted(v)[(len(v) - 1) // 2] + sorted(v)[len(v) // 2]) / 2  # noqa: E731
     flops = cfg.flops_fwd() + (0 if fwd_only else cfg.flops_bwd())
     tflops = flops / (ms_step * 1e-3) / 1e12
     MHI = float(cfg.M) * cfg.H * cfg.I
@@ -321,6 +362,16 @@ def main():
             ent["gbps"] = round(nb / (avg * 1e-3) / 1e9, 1)
             ent["frac_of_hbm_peak"] = round(ent["gbps"] / PEAK_HBM_GBS, 4)
         kernels[name] = ent
+    perm = [kt[n] for n in ("permute_hist", "permute_scan", "permute_scatter") if n in kt]
+    if perm:
+        n_launch = perm[0][0]
+        tot = sum(t for _, t in perm)
+        avg = tot / max(n_launch, 1)
+        nb = hbm_bytes("permute", cfg)
+        kernels["permute"] = {"launches": n_launch, "avg_ms": round(avg, 5), "ms_per_step": round(tot / args.steps, 5),
+                              "avg_us": round(avg * 1e3, 1), "gbps": round(nb / (avg * 1e-3) / 1e9, 1),
+                              "frac_of_hbm_peak": round(nb / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "note": "histogram + scan + scatter together (latency-bound)"}
     gemm_names = [n for n in kernels if n in GEMM_FLOP_FACTOR]
     dom = max(gemm_names, key=lambda n: kernels[n]["ms_per_step"])
     dom_avg = kernels[dom]["avg_ms"]
@@ -348,8 +399,18 @@ def main():
         "config": {"workload": f"{cfg.name}: {workload}", "T": cfg.T, "H": cfg.H,
                    "I": cfg.I, "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "precision": cfg.precision,
                    "wgrad": args.wgrad, "router": args.router},
+        # per-step event times over the timed steps (after the warm-up: with
+        # the default 5 + 15 these are the mean, median and min of steps 6-20)
+        "step_ms": {"mean": round(sum(step_ms) / len(step_ms), 4), "median": round(med(step_ms), 4),
+                    "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4)},
         "fwd_ms": round(sum(fwd_ms) / len(fwd_ms), 4),
+        "fwd_ms_median": round(med(fwd_ms), 4),
+        "fwd_ms_min": round(min(fwd_ms), 4),
         "bwd_ms": round(sum(bwd_ms) / len(bwd_ms), 4),
+        "bwd_ms_median": round(med(bwd_ms), 4),
+        "bwd_ms_min": round(min(bwd_ms), 4),
+        # a training step with activation checkpointing runs the forward twice
+        "two_fwd_plus_bwd_ms": None if fwd_only else round(2 * sum(fwd_ms) / len(fwd_ms) + sum(bwd_ms) / len(bwd_ms), 4),
         "weight_quant_ms": round(sum(wq_ms) / len(wq_ms), 4),
         # the weights are quantized once per optimizer step; a step that reuses
         # them (e.g. gradient accumulation) costs this much
