@@ -20,7 +20,8 @@ layer:
 * a value v becomes the E2M1 magnitude nearest to |v| / 2^e, ties to the
   even code, with the sign of v (a zero result is +0);
 * activations (x along H, w * silu(g) * u along I) in MXFP8 exactly as the
-  mxfp8 mode of moe_fp8 (E4M3, 1x32 blocks, MX rule);
+  mxfp8 mode of moe_fp8 (E4M3, 1x32 blocks, MX rule), the activation taken,
+  as there, at its stored bf16 value;
 * everything after quantization is exact (float64), as in moe_fp8.
 """
 from __future__ import annotations
@@ -118,7 +119,7 @@ def forward(x, topk_idx, topk_w, W13, W2, return_pairs: bool = False, wq: dict |
         G = X @ W13q[e, :I].T
         U = X @ W13q[e, I:].T
         WA = wf[f][:, None] * (base.silu(G) * U)
-        O = _act(WA) @ W2q[e].T
+        O = _act(f8.bf16_round(WA)) @ W2q[e].T   # quantized as stored: in bf16
         np.add.at(y, t, O)
         if return_pairs:
             pairs["g"][f] = G

@@ -37,8 +37,16 @@ tensors are quantized. The readings used here:
   (blockwise and fp8_bwd, pow2 rule) or 32 rows (mxfp8, MX rule) counted from
   the expert's first row in permuted order (pairs in ascending flat index);
   a last partial block is quantized on its own rows.
-* Quantization is applied to the exact (float64) value at each point; the
-  result is dequantized (code * 2^e) and the math continues exactly.
+* The layer keeps what it passes between its GEMMs in bf16 (round to
+  nearest even): g and u and the weighted activation w * silu(g) * u, which
+  the forward saves for the backward, and [dg | du], which the dH product
+  hands to the dX and dW13 products. A quantized code is an integer decided
+  by a floating-point value, so it is taken on that stored bf16 value: the
+  activation and [dg | du] are rounded to bf16, then quantized. The
+  backward reads the saved bf16 g, u and w * silu(g) * u. Inputs (x, dY and
+  the weights) are bf16 already; every other step stays exact.
+* Quantization is applied to the (float64) value at each point; the result
+  is dequantized (code * 2^e) and the math continues exactly.
 """
 from __future__ import annotations
 
@@ -90,6 +98,19 @@ def e4m3_encode(v) -> np.ndarray:
 
 def e4m3_decode(codes) -> np.ndarray:
     return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+# --------------------------------------------------------------- bf16 storage
+
+def bf16_round(v) -> np.ndarray:
+    """Round to the nearest bf16 value (8 significant bits, the float32
+    exponent range), ties to the even value: v = m * 2^ex with m in [0.5, 1)
+    keeps round(m * 2^8) / 2^8, and below the smallest normal (2^-126) the
+    spacing stays 2^-133. Used where the layer stores a value in bf16."""
+    v = np.asarray(v, dtype=np.float64)
+    _, ex = np.frexp(v)
+    ex = np.maximum(ex, -125)            # the subnormal range keeps the spacing of 2^-126's binade
+    return np.ldexp(np.rint(np.ldexp(v, 8 - ex)), ex - 8)
 
 
 # --------------------------------------------------------------- block scales
@@ -224,7 +245,7 @@ def forward(x, topk_idx, topk_w, W13, W2, mode: str, return_pairs: bool = False,
         G = X @ W13q[e, :I].T
         U = X @ W13q[e, I:].T
         WA = wf[f][:, None] * (base.silu(G) * U)
-        O = _act(WA, mode) @ W2q[e].T
+        O = _act(bf16_round(WA), mode) @ W2q[e].T
         np.add.at(y, t, O)
         if return_pairs:
             pairs["g"][f] = G
@@ -271,8 +292,11 @@ def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str, wq: dict | None = None
         if f.size == 0:
             continue
         t = f // k
-        G = xf[t] @ W13f[e, :I].T
-        U = xf[t] @ W13f[e, I:].T
+        # what the forward saved, in bf16: g, u and w * silu(g) * u
+        G0 = xf[t] @ W13f[e, :I].T
+        U0 = xf[t] @ W13f[e, I:].T
+        WA = bf16_round(wf[f][:, None] * (base.silu(G0) * U0))
+        G, U = bf16_round(G0), bf16_round(U0)
         S = base.sigmoid(G)
         A = G * S * U
         dAu = dyq[t] @ W2b[e]
@@ -281,15 +305,16 @@ def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str, wq: dict | None = None
         dG = dA * U * S * (1.0 + G * (1.0 - S))
         dU = dA * G * S
         dHm = np.concatenate([dG, dU], axis=1)
-        np.add.at(dx, t, _act(dHm, mode) @ W13b[e])
+        dHs = bf16_round(dHm)                 # [dg | du] as handed to the next products
+        np.add.at(dx, t, _act(dHs, mode) @ W13b[e])
         if wgrad == "fp8":
-            dW13[e] = _tok(dHm, mode).T @ _tok(x[t], mode)
-            dW2[e] = _tok(dy[t], mode).T @ _tok(wf[f][:, None] * A, mode)
+            dW13[e] = _tok(dHs, mode).T @ _tok(x[t], mode)
+            dW2[e] = _tok(dy[t], mode).T @ _tok(WA, mode)
         else:
             dW13[e] = dHm.T @ x[t]
-            dW2[e] = dy[t].T @ (wf[f][:, None] * A)
+            dW2[e] = dy[t].T @ WA
     return dx, dwf.reshape(T, k), dW13, dW2
 
 
-__all__ = ["MODES", "E4M3_MAX", "e4m3_decode_table", "e4m3_encode", "e4m3_decode", "scale_exponent",
+__all__ = ["MODES", "E4M3_MAX", "bf16_round", "e4m3_decode_table", "e4m3_encode", "e4m3_decode", "scale_exponent",
            "quantize_along_last", "quantize_tiles", "quantize_weights", "forward", "backward"]

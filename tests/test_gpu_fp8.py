@@ -6,6 +6,7 @@ FP8 max-relative-error bound (normwise by the reference maximum): small
 layers element by element, the page-sized layers on sampled tokens and
 experts that the oracle computes one by one.
 """
+import os
 import sys
 import time
 
@@ -257,7 +258,27 @@ WGRAD_CASES = CASES + [(HOT, "fp8_block")]
 def test_fp8_layer_matches_oracle_elementwise(B, cfg, mode):
     cfg = cfg.scaled(precision=mode)
     _say(f"case {inputs.describe(cfg)}")
+    _fp8_elementwise(B, cfg, mode, inputs.make_layer_inputs(cfg, DEV))
+
+
+DUP = inputs.LayerConfig("dup", 500, 512, 384, 6, 3, "uniform", "bf16", 31)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_duplicate_expert_in_one_token_elementwise(B, mode):
+    """Every third token names one expert in two of its slots (two rows,
+    summed)."""
+    cfg = DUP.scaled(precision=mode)
+    _say(f"case duplicate experts {inputs.describe(cfg)}")
     d = inputs.make_layer_inputs(cfg, DEV)
+    idx = d["topk_idx"].clone()
+    idx[::3, 1] = idx[::3, 0]
+    d["topk_idx"] = idx
+    _WQ.pop((cfg.name, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.seed, mode), None)
+    _fp8_elementwise(B, cfg, mode, d)
+
+
+def _fp8_elementwise(B, cfg, mode, d):
     out = run_layer(B, cfg, d, mode)
     assert out["status"] == 0
     args = (d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
@@ -331,23 +352,51 @@ def test_fp8_zero_tokens(B):
 
 # --------------------------------------------------------------- page-sized layers, sampled
 
-def _pick_tokens(idx, counts, n, pool=4000):
-    """n tokens whose experts overlap as much as possible (keeps the number
-    of expert weight stacks the oracle has to quantize small)."""
-    idx = idx[:pool]
-    hot = np.argsort(-np.array([counts[r].sum() for r in idx]))
-    chosen, seen = [int(hot[0])], set(idx[hot[0]].tolist())
-    while len(chosen) < n:
-        best = min((t for t in hot[:400] if t not in chosen), key=lambda t: len(set(idx[t].tolist()) - seen))
-        chosen.append(int(best))
-        seen |= set(idx[best].tolist())
-    return sorted(chosen)
+_WQ_EXPERT = {}
 
 
-def _sampled_check(B, cfg, n_tokens, n_experts, wgrad="bf16"):
+def _expert_wq(cfg, mode, d, experts, keys):
+    """The oracle's quantized weights of the given experts of a configuration
+    (cached per configuration, mode and expert; the oracle's weight blocks
+    never straddle experts, so an expert's quantization is its own). Experts
+    not yet cached are quantized on a pool of threads: numpy releases the
+    interpreter lock in the quantizer's array operations."""
+    from concurrent.futures import ThreadPoolExecutor
+    key = (cfg.name, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.seed, mode)
+    for other in [k for k in _WQ_EXPERT if k != key]:  # one configuration's weights at a time
+        del _WQ_EXPERT[other]
+    cache = _WQ_EXPERT.setdefault(key, {})
+    todo = sorted({int(e) for e in experts} - set(cache))
+    if todo:
+        W13, W2 = d["W13"].cpu(), d["W2"].cpu()
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            res = ex.map(lambda e: f8.quantize_weights(W13[e:e + 1], W2[e:e + 1], mode, keys), todo)
+            for e, r in zip(todo, res):
+                cache[e] = r
+    return cache
+
+
+def _check_experts(counts):
+    """The hottest expert (the one split along its rows, under skew), the
+    coldest non-empty one and two of median row count."""
+    nz = np.nonzero(counts > 0)[0]
+    order = nz[np.argsort(counts[nz], kind="stable")]
+    picks = [int(order[-1]), int(order[0]), int(order[len(order) // 2]), int(order[(len(order) - 1) // 2 - 1])]
+    out = []
+    for e in picks:
+        if e not in out:
+            out.append(e)
+    return out
+
+
+def _sampled_check(B, cfg, n_tokens=64, wgrad="bf16"):
+    """The page-sized FP8 layer on `n_tokens` tokens drawn uniformly over
+    [0, T) (seeded) and on four experts (hottest, coldest non-empty, two
+    median), each computed by the oracle on its own: a token needs only its k
+    experts' weights and an expert's weight gradients only its own rows."""
     mode = cfg.precision
     t0 = time.time()
-    _say(f"case full-size {inputs.describe(cfg)} wgrad={wgrad}")
+    _say(f"case full-size {inputs.describe(cfg)} wgrad={wgrad} tokens={n_tokens}")
     d = inputs.make_layer_inputs(cfg, DEV)
     out = run_layer(B, cfg, d, mode, wgrad=wgrad)
     assert out["status"] == 0
@@ -355,15 +404,13 @@ def _sampled_check(B, cfg, n_tokens, n_experts, wgrad="bf16"):
     idx_h = _np(d["topk_idx"])
     assert np.array_equal(counts, np.bincount(idx_h.reshape(-1), minlength=cfg.E))
     _say(f"  gpu done {time.time() - t0:.1f}s")
-    toks = _pick_tokens(idx_h, counts, n_tokens)
-    experts = [int(np.argmax(counts)), int(np.argmin(counts))][:n_experts]
-    cache = {}
+    toks = np.sort(np.random.default_rng(1000 + cfg.seed).choice(cfg.T, n_tokens, replace=False))
+    experts = _check_experts(counts)
     keys = ("W2b", "W13b") if mode == "fp8_bwd" else ("W13q", "W2q", "W2b", "W13b")
+    cache = _expert_wq(cfg, mode, d, set(idx_h[toks].reshape(-1).tolist()) | set(experts), keys)
+    _say(f"  {len(cache)} experts' weights quantized by the oracle ({time.time() - t0:.1f}s)")
 
     def wq_of(ex):
-        for e in ex:
-            if e not in cache:
-                cache[e] = f8.quantize_weights(d["W13"][e:e + 1], d["W2"][e:e + 1], mode, keys)
         return {k: np.concatenate([cache[e][k] for e in ex]) for k in cache[ex[0]]}
 
     ys, yr, dxs, dxr, dws, dwr = [], [], [], [], [], []
@@ -381,16 +428,18 @@ def _sampled_check(B, cfg, n_tokens, n_experts, wgrad="bf16"):
     errs = {"y": max_rel_err(np.array(ys), np.array(yr)),
             "dx": max_rel_err(np.array(dxs), np.array(dxr)),
             "d_topk_w": max_rel_err(np.array(dws), np.array(dwr))}
-    _say(f"  tokens {toks} done {time.time() - t0:.1f}s ({len(cache)} experts quantized)")
+    # and per token row
+    errs["y_row"] = max(max_rel_err(a, b) for a, b in zip(ys, yr))
+    errs["dx_row"] = max(max_rel_err(a, b) for a, b in zip(dxs, dxr))
+    _say(f"  {n_tokens} tokens (first {toks[:4].tolist()}, last {toks[-1]}) done {time.time() - t0:.1f}s")
     for e in experts:
         f, xe, ie, we, dye = orc.restrict_to_expert(d["x"], d["topk_idx"], d["topk_w"], d["dy"], e)
-        if f.size == 0:
-            assert not out["dW13"][e].any() and not out["dW2"][e].any()
-            continue
         _, _, r13, r2 = f8.backward(dye, xe, ie, we, d["W13"][e:e + 1], d["W2"][e:e + 1], mode, wq=wq_of([e]),
                                     wgrad=wgrad)
-        errs[f"dW13[{e}]"] = max_rel_err(orc.as_f64(out["dW13"][e]), r13[0])
-        errs[f"dW2[{e}]"] = max_rel_err(orc.as_f64(out["dW2"][e]), r2[0])
+        errs[f"dW13[{e}:{counts[e]}]"] = max_rel_err(orc.as_f64(out["dW13"][e]), r13[0])
+        errs[f"dW2[{e}:{counts[e]}]"] = max_rel_err(orc.as_f64(out["dW2"][e]), r2[0])
+    for e in np.nonzero(counts == 0)[0]:
+        assert not out["dW13"][e].any() and not out["dW2"][e].any(), e
     _say(f"{cfg.name}/{mode}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
          + f" ({time.time() - t0:.1f}s)")
     for k, v in errs.items():
@@ -400,24 +449,24 @@ def _sampled_check(B, cfg, n_tokens, n_experts, wgrad="bf16"):
 
 
 def test_ep8_share_fp8_block_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["ep8_share"], n_tokens=16, n_experts=2)
-
-
-def test_qwen3_235b_fp8_bwd_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["qwen3_235b"], n_tokens=2, n_experts=1)
-
-
-def test_qwen3_30b_zipf_mxfp8_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["zipf"], n_tokens=3, n_experts=2)
+    _sampled_check(B, inputs.CONFIGS["ep8_share"])
 
 
 def test_ep8_share_fp8_block_fp8_wgrad_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["ep8_share"], n_tokens=4, n_experts=2, wgrad="fp8")
+    _sampled_check(B, inputs.CONFIGS["ep8_share"], wgrad="fp8")
+
+
+def test_qwen3_235b_fp8_bwd_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["qwen3_235b"])
 
 
 def test_qwen3_235b_fp8_bwd_fp8_wgrad_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["qwen3_235b"], n_tokens=1, n_experts=1, wgrad="fp8")
+    _sampled_check(B, inputs.CONFIGS["qwen3_235b"], wgrad="fp8")
+
+
+def test_qwen3_30b_zipf_mxfp8_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["zipf"])
 
 
 def test_qwen3_30b_zipf_mxfp8_fp8_wgrad_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["zipf"], n_tokens=1, n_experts=2, wgrad="fp8")
+    _sampled_check(B, inputs.CONFIGS["zipf"], wgrad="fp8")

@@ -3,8 +3,9 @@
 Indices (counts, offsets, row_of, src_of) must match bit-exactly; floating
 outputs and gradients must be within the bf16 max-relative-error bound
 (normwise by the reference maximum). Small layers are compared element by
-element; the Qwen3-30B-A3B-shaped layer is compared on sampled tokens and
-experts that the oracle computes one by one.
+element, and so is the Qwen3-30B-A3B-shaped layer (uniform and Zipf
+routing), whose every token row and every expert is also held to the bound
+on its own.
 """
 import os
 import sys
@@ -100,6 +101,7 @@ def check_full(out, cfg, d, tol=TOL_BF16):
     for e in np.nonzero(counts == 0)[0]:
         assert not out["dW13"][e].any() and not out["dW2"][e].any()
     assert np.all(np.isfinite(orc.as_f64(out["dx"])))
+    return {"y": y_ref, "dx": dx_ref, "dW13": dW13_ref, "dW2": dW2_ref}
 
 
 SMALL = [
@@ -226,52 +228,85 @@ def test_num_cus_cap_gives_identical_results(B):
 
 # --------------------------------------------------------------- full size
 
-def _sampled_check(B, cfg, n_tokens=24, experts=None):
-    _say(f"case full-size {inputs.describe(cfg)}")
+def _row_errs(got, ref):
+    """Per-row max-relative error (max |diff| over the row / max |ref| over
+    the row); rows whose reference is all zero must come out all zero."""
+    got = orc.as_f64(got)
+    diff = np.max(np.abs(got - ref), axis=1)
+    scale = np.max(np.abs(ref), axis=1)
+    z = scale == 0
+    assert not np.any(diff[z]), "rows with an all-zero reference must be zero"
+    return diff[~z] / scale[~z]
+
+
+def _full_size_check(B, cfg):
+    """The page-sized layer compared element by element with the full oracle
+    (every token, every pair, every expert): the stated per-tensor bound, and
+    the same bound per token row of y and dx and per expert of dW13 and dW2,
+    so that an error confined to some tiles (the XCD remap, the n-tile-major
+    walk, the split plan under skew) cannot hide behind the largest values."""
+    import time
+    t0 = time.time()
+    _say(f"case full-size elementwise {inputs.describe(cfg)}")
     d = inputs.make_layer_inputs(cfg, DEV)
     out = run_layer(B, cfg, d)
     assert out["status"] == 0
-    check_permutation(out, d["topk_idx"], cfg.E)
-    g = np.random.default_rng(cfg.seed)
-    toks = np.sort(g.choice(cfg.T, n_tokens, replace=False))
-    idx_h = d["topk_idx"].cpu()
-    ys, yr, dxs, dxr, dws, dwr = [], [], [], [], [], []
-    for t in toks:
-        ex = idx_h[t].long()
-        sub = dict(x=d["x"][t:t + 1], idx=torch.arange(cfg.k).view(1, -1), w=d["topk_w"][t:t + 1],
-                   W13=d["W13"][ex], W2=d["W2"][ex], dy=d["dy"][t:t + 1])
-        yr.append(orc.forward(sub["x"], sub["idx"], sub["w"], sub["W13"], sub["W2"])[0])
-        gx, gw, _, _ = orc.backward(sub["dy"], sub["x"], sub["idx"], sub["w"], sub["W13"], sub["W2"])
-        dxr.append(gx[0])
-        dwr.append(gw[0])
-        ys.append(orc.as_f64(out["y"][t]))
-        dxs.append(orc.as_f64(out["dx"][t]))
-        dws.append(orc.as_f64(out["dw"][t]))
-    errs = {"y": max_rel_err(np.array(ys), np.array(yr)),
-            "dx": max_rel_err(np.array(dxs), np.array(dxr)),
-            "d_topk_w": max_rel_err(np.array(dws), np.array(dwr))}
+    _say(f"  gpu done {time.time() - t0:.1f}s")
+    ref = check_full(out, cfg, d)
+    _say(f"  oracle + per-tensor check done {time.time() - t0:.1f}s")
+    y_ref, dx_ref, dW13_ref, dW2_ref = ref["y"], ref["dx"], ref["dW13"], ref["dW2"]
+    del ref
+    worst = {"y_row": float(np.max(_row_errs(out["y"], y_ref))),
+             "dx_row": float(np.max(_row_errs(out["dx"], dx_ref)))}
+    del y_ref, dx_ref
     counts = out["counts"].cpu().numpy()
-    if experts is None:
-        experts = [int(np.argmax(counts)), int(np.argmin(counts)), cfg.E // 2]
-    for e in experts:
-        f, xe, ie, we, dye = orc.restrict_to_expert(d["x"], d["topk_idx"], d["topk_w"], d["dy"], e)
-        if f.size == 0:
-            assert not out["dW13"][e].any() and not out["dW2"][e].any()
+    e13, e2 = [], []
+    for e in range(cfg.E):
+        if counts[e] == 0:
             continue
-        _, _, r13, r2 = orc.backward(dye, xe, ie, we, d["W13"][e:e + 1], d["W2"][e:e + 1])
-        errs[f"dW13[{e}]"] = max_rel_err(orc.as_f64(out["dW13"][e]), r13[0])
-        errs[f"dW2[{e}]"] = max_rel_err(orc.as_f64(out["dW2"][e]), r2[0])
-    _say(f"{cfg.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    for k, v in errs.items():
+        e13.append(max_rel_err(orc.as_f64(out["dW13"][e]), dW13_ref[e]))
+        e2.append(max_rel_err(orc.as_f64(out["dW2"][e]), dW2_ref[e]))
+    worst["dW13_expert"] = max(e13)
+    worst["dW2_expert"] = max(e2)
+    _say(f"{cfg.name}: worst " + " ".join(f"{k}={v:.2e}" for k, v in worst.items())
+         + f" over {cfg.T} tokens, {len(e13)} non-empty experts ({time.time() - t0:.1f}s)")
+    for k, v in worst.items():
         assert v <= TOL_BF16, (k, v)
-    for k in ("y", "dx", "dW13", "dW2"):
-        assert torch.isfinite(out[k].float()).all(), k
 
 
-def test_qwen3_30b_shape_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["qwen3_30b"])
+def test_qwen3_30b_shape_elementwise(B):
+    _full_size_check(B, inputs.CONFIGS["qwen3_30b"])
 
 
-def test_qwen3_30b_shape_zipf_routing_bf16_sampled(B):
+def test_qwen3_30b_shape_zipf_routing_bf16_elementwise(B):
     cfg = inputs.CONFIGS["zipf"].scaled(name="zipf_bf16", precision="bf16")
-    _sampled_check(B, cfg)
+    _full_size_check(B, cfg)
+
+
+# --------------------------------------------------------------- duplicate experts
+
+def _with_duplicates(d, every=3):
+    """Every `every`-th token sends two of its slots to the same expert
+    (slot 1 repeats slot 0): two rows of that expert, summed in y."""
+    idx = d["topk_idx"].clone()
+    idx[::every, 1] = idx[::every, 0]
+    d["topk_idx"] = idx
+    return d
+
+
+DUPS = [inputs.LayerConfig("dup", 500, 512, 384, 6, 3, "uniform", "bf16", 31),
+        inputs.LayerConfig("dup_top2", 300, 256, 128, 4, 2, "uniform", "bf16", 32)]
+
+
+@pytest.mark.parametrize("cfg", DUPS, ids=[c.name for c in DUPS])
+def test_duplicate_expert_in_one_token_elementwise(B, cfg):
+    """A token may name one expert twice (the reading: two rows, summed):
+    the permutation keeps both pairs in flat order and every output matches
+    the oracle element by element."""
+    _say(f"case duplicate experts {inputs.describe(cfg)}")
+    d = _with_duplicates(inputs.make_layer_inputs(cfg, DEV))
+    idx = d["topk_idx"].cpu().numpy()
+    assert np.any(idx[:, 0] == idx[:, 1])
+    out = run_layer(B, cfg, d)
+    assert out["status"] == 0
+    check_full(out, cfg, d)

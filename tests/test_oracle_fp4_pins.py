@@ -132,6 +132,17 @@ def _mx8_block(vals):
     return [_e4m3_scalar(v, e) for v in vals]
 
 
+def _bf(v):
+    """bf16 rounding of each element (8 significant bits, halves to even via
+    Python's round), written with math.frexp."""
+    def one(x):
+        if x == 0.0:
+            return 0.0
+        m, ex = math.frexp(x)
+        return math.ldexp(round(m * 256.0), ex - 8)
+    return np.vectorize(one, otypes=[np.float64])(np.asarray(v, dtype=np.float64))
+
+
 def _rows(M, fn):
     return np.array([[q for s in range(0, len(row), 32) for q in fn(list(row[s:s + 32]))] for row in M])
 
@@ -155,7 +166,8 @@ def test_forward_matches_per_token_loops():
             g = W13q[e, :I] @ xq[t]
             u = W13q[e, I:] @ xq[t]
             a = g / (1.0 + np.exp(-g)) * u
-            ry[t] += W2q[e] @ _rows((w[t, j] * a)[None, :], _mx8_block)[0]
+            # the activation is quantized at its stored bf16 value
+            ry[t] += W2q[e] @ _rows(_bf(w[t, j] * a)[None, :], _mx8_block)[0]
     np.testing.assert_allclose(y, ry, rtol=1e-9, atol=1e-9)
 
 

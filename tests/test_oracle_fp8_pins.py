@@ -126,6 +126,19 @@ def _q_scalar(v, e):
     return s * min(r * lsb, 448.0) * 2.0 ** e
 
 
+def _bf(v):
+    """Round a float to bf16 (8 significant bits, ties to even) with
+    math.frexp and Python's round (which rounds halves to even); applied
+    element by element to arrays. Magnitudes here stay far from the bf16
+    subnormal range."""
+    def one(x):
+        if x == 0.0:
+            return 0.0
+        m, ex = math.frexp(x)            # x = m * 2^ex, |m| in [0.5, 1)
+        return math.ldexp(round(m * 256.0), ex - 8)
+    return np.vectorize(one, otypes=[np.float64])(np.asarray(v, dtype=np.float64))
+
+
 def _q_block(vals, rule):
     amax = max(abs(v) for v in vals)
     if amax == 0.0:
@@ -196,13 +209,18 @@ def _layer_loops(x, idx, w, W13, W2, dy, mode):
             u = W13q[e, I:] @ xq[t]
             sg = 1.0 / (1.0 + np.exp(-g))
             a = g * sg * u
-            wa = fwd_q((w[t, j] * a)[None, :])[0]
+            # the stored (bf16) activation is what gets quantized
+            wa = w[t, j] * a if mode == "fp8_bwd" else fwd_q(_bf(w[t, j] * a)[None, :])[0]
             y[t] += W2q[e] @ wa
+            # the backward reads the saved bf16 g and u
+            g, u = _bf(g), _bf(u)
+            sg = 1.0 / (1.0 + np.exp(-g))
+            a = g * sg * u
             dau = W2b[e].T @ dyq[t]
             dw[t, j] = float(dau @ a)
             da = w[t, j] * dau
             dh = np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg])
-            dx[t] += W13b[e].T @ qa(dh[None, :])[0]
+            dx[t] += W13b[e].T @ qa(_bf(dh)[None, :])[0]
     return y, dx, dw
 
 
@@ -237,14 +255,15 @@ def test_quantized_layer_close_to_exact_layer(mode):
 
 def test_weight_gradients_use_unquantized_operands():
     """With a full-precision forward, dW2 = dY^T (w a) involves no quantized
-    operand and equals the exact gradient; dW13 inherits the quantized dH
-    product through [dg | du] only."""
+    operand: it equals the exact gradient up to the bf16 storage of w a
+    (relative 2^-9 per element); dW13 inherits the quantized dH product
+    through [dg | du] only."""
     from grouped_gemm_02_amd import inputs
     d = inputs.make_layer_inputs(inputs.CONFIGS["tiny"], "cpu")
     args = (d["dy"], d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"])
     _, _, dW13, dW2 = f8.backward(*args, mode="fp8_bwd")
     _, _, rW13, rW2 = orc.backward(*args)
-    np.testing.assert_allclose(dW2, rW2, rtol=1e-12, atol=1e-12)
+    assert 0 < np.max(np.abs(dW2 - rW2)) / np.max(np.abs(rW2)) < 2.0 ** -8
     assert np.max(np.abs(dW13 - rW13)) / np.max(np.abs(rW13)) < 0.15
 
 
@@ -299,14 +318,15 @@ def _wgrad_loops(x, idx, w, W13, W2, dy, mode):
             e = idx[t, j]
             g = W13q[e, :I] @ xq[t]
             u = W13q[e, I:] @ xq[t]
+            wa = _bf(w[t, j] * g / (1.0 + np.exp(-g)) * u)   # the saved activation
+            g, u = _bf(g), _bf(u)                             # the saved g, u
             sg = 1.0 / (1.0 + np.exp(-g))
-            a = g * sg * u
             dau = W2b[e].T @ dyq[t]
             da = w[t, j] * dau
-            rows[e]["dh"].append(np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg]))
+            rows[e]["dh"].append(_bf(np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg])))
             rows[e]["x"].append(x[t])
             rows[e]["dy"].append(dy[t])
-            rows[e]["wa"].append(w[t, j] * a)
+            rows[e]["wa"].append(wa)
 
     def qcols(R):  # quantize each column of R [n, C] in row blocks
         R = np.array(R)
@@ -395,9 +415,9 @@ def _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip=None):
     """dW13, dW2 under the default reading (weight-gradient GEMMs on the
     unquantized operands) of an FP8 mode, accumulated pair by pair as outer
     products: dW13[e] += [dg | du] x[t]^T and dW2[e] += dY[t] (w a)^T, where
-    g, u and a come from that mode's forward (quantized x and W13 in
-    fp8_block and mxfp8, exact in fp8_bwd) and [dg | du] from its quantized
-    dH product. `slip` plants a mistake on purpose: "xq" multiplies the
+    g, u and w a are the forward's saved bf16 values (quantized x and W13 in
+    fp8_block and mxfp8, exact in fp8_bwd) and [dg | du] comes from the
+    quantized dH product. `slip` plants a mistake on purpose: "xq" multiplies the
     quantized x in dW13, "exact_a" takes a from the unquantized forward."""
     blk, rule = (32, "mx_floor") if mode == "mxfp8" else (128, "pow2_ceil")
     T, H = x.shape
@@ -418,16 +438,17 @@ def _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip=None):
             e = idx[t, j]
             g = W13q[e, :I] @ xq[t]
             u = W13q[e, I:] @ xq[t]
+            wa = _bf(w[t, j] * g / (1.0 + np.exp(-g)) * u)   # the saved activation
+            if slip == "exact_a":
+                ge, ue = W13[e, :I] @ x[t], W13[e, I:] @ x[t]
+                wa = _bf(w[t, j] * ge / (1.0 + np.exp(-ge)) * ue)
+            g, u = _bf(g), _bf(u)                             # the saved g, u
             sg = 1.0 / (1.0 + np.exp(-g))
-            a = g * sg * u
             dau = W2b[e].T @ dyq[t]
             da = w[t, j] * dau
             dh = np.concatenate([da * u * sg * (1 + g * (1 - sg)), da * g * sg])
-            if slip == "exact_a":
-                ge, ue = W13[e, :I] @ x[t], W13[e, I:] @ x[t]
-                a = ge / (1.0 + np.exp(-ge)) * ue
             dW13[e] += np.outer(dh, xq[t] if slip == "xq" else x[t])
-            dW2[e] += np.outer(dy[t], w[t, j] * a)
+            dW2[e] += np.outer(dy[t], wa)
     return dW13, dW2
 
 
@@ -455,3 +476,23 @@ def test_default_weight_gradients_match_pair_loops(mode):
         _, s2 = _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip="exact_a")
         assert np.max(np.abs(s13 - dW13)) / np.max(np.abs(dW13)) > 1e-4
         assert np.max(np.abs(s2 - dW2)) / np.max(np.abs(dW2)) > 1e-4
+
+
+def test_bf16_round_matches_library_and_scalar_rounding():
+    """The oracle's bf16 rounding against torch's float32 -> bfloat16
+    conversion (on float32 values, where that conversion rounds once),
+    against the scalar math.frexp rounding above on float64 values, and on
+    hand-made ties (halfway values go to the even neighbour)."""
+    import torch
+    rng = np.random.default_rng(12)
+    v32 = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    lib = torch.from_numpy(v32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(f8.bf16_round(v32.astype(np.float64)), lib)
+    v64 = rng.standard_normal(5000) * np.exp(rng.uniform(-20, 20, 5000))
+    assert np.array_equal(f8.bf16_round(v64), _bf(v64))
+    one = 1.0 + 2.0 ** -8                      # halfway between 1 and 1 + 2^-7: to 1 (even)
+    three = 1.0 + 3 * 2.0 ** -8                # halfway between 1 + 2^-7 and 1 + 2^-6: to 1 + 2^-6
+    assert f8.bf16_round(np.array([one, -one, three, np.nextafter(one, 2.0), 0.0])).tolist() == \
+        [1.0, -1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, 0.0]
+    assert f8.bf16_round(np.array([2.0 ** -133, 2.0 ** -134 * 3, 2.0 ** -135])).tolist() == \
+        [2.0 ** -133, 2.0 ** -132, 0.0]         # subnormals: spacing 2^-133, ties to even
