@@ -77,6 +77,7 @@ _SIGS = {
                                ctypes.c_size_t, _P]),
     "moe_bwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _P, ctypes.c_size_t, _P]),
+    "moe_permute_noalloc": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, ctypes.c_int32, _P, _P, _P]),
     "moe_route_bwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "moe_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32), _P]),
@@ -238,6 +239,18 @@ def moe_permute(shape, topk_idx, counts, offsets, row_of, src_of, scratch, strea
     _want(scratch, "scratch", _U8, moe_permute_scratch_bytes(shape))
     _check(lib().moe_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(row_of),
                              _ptr(src_of), _ptr(scratch), _stream(stream)), "moe_permute")
+
+
+def moe_permute_noalloc(shape, topk_idx, counts, offsets, row_of, src_of, status, stream=None) -> None:
+    Tk = shape.T * shape.k
+    _want(topk_idx, "topk_idx", _I32, Tk, optional=Tk == 0)
+    _want(counts, "counts", _I32, shape.E)
+    _want(offsets, "offsets", _I32, shape.E + 1)
+    _want(row_of, "row_of", _I32, Tk, optional=Tk == 0)
+    _want(src_of, "src_of", _I32, Tk, optional=Tk == 0)
+    _want(status, "status", _I32, 1)
+    _check(lib().moe_permute_noalloc(ctypes.byref(shape), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(row_of),
+                                     _ptr(src_of), _ptr(status), _stream(stream)), "moe_permute_noalloc")
 
 
 def moe_fwd(shape, x, topk_idx, topk_w, W13, W2, wq, y, saved, ws, stream=None) -> None:

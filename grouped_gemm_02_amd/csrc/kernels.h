@@ -35,6 +35,18 @@ hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
                           hipStream_t st, KernelTimer* timer, const float* topk_w = nullptr,
                           float* wrow = nullptr);
 
+// The same with the status word and the chunk table given apart.
+hipError_t launch_permute_split(const int32_t* idx, int64_t n, int E, int32_t* counts, int32_t* offsets,
+                                int32_t* row_of, int32_t* src_of, int32_t* status, int32_t* chunk_tab,
+                                hipStream_t st, KernelTimer* timer, const float* topk_w = nullptr,
+                                float* wrow = nullptr);
+// A fixed chunk table in device memory the library owns (no allocation):
+// kStaticPermuteWords int32 per device, found once per device with
+// hipGetSymbolAddress; *out is its address on the current device.
+constexpr int64_t kStaticPermuteWords = int64_t(1) << 20;  // 4 MiB
+constexpr int kMaxDevices = 64;
+hipError_t permute_static_scratch(int32_t** out);
+
 // ---------------------------------------------------------------- combine
 // y[t] = sum_j rows[row_of[t*k+j]]  (bf16 rows of width H, fp32 sum, ascending j)
 // and, when dwpart != nullptr, d_topk_w[f] = sum_c dwpart[row_of[f]*nparts + c].

@@ -308,6 +308,24 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* cou
                                       scratch, static_cast<hipStream_t>(stream), timer()));
 }
 
+moe_status moe_permute_noalloc(const moe_shape* s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                               int32_t* row_of, int32_t* src_of, int32_t* status, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  const int64_t Tk = s->T * s->k;
+  if (!counts || !offsets || !status || (Tk > 0 && (!topk_idx || !row_of || !src_of))) return MOE_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return MOE_ERR_ALIGN;
+  // the chunk table must fit the library's fixed array
+  if (int64_t(permute_num_chunks(Tk)) * (s->E + 1) > kStaticPermuteWords) return MOE_ERR_WORKSPACE;
+  int cus = 0;
+  if ((st = device_info(&cus)) != MOE_OK) return st;
+  int32_t* table = nullptr;
+  if (permute_static_scratch(&table) != hipSuccess) return MOE_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  return launch_status(launch_permute_split(topk_idx, Tk, int(s->E), counts, offsets, row_of, src_of, status,
+                                            table, static_cast<hipStream_t>(stream), timer()));
+}
+
 moe_status moe_get_wq_layout(const moe_shape* s, moe_wq_layout* out) {
   const moe_status st = check_shape(s);
   if (st != MOE_OK) return st;

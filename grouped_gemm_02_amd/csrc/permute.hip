@@ -18,6 +18,8 @@
 //                   in LDS and a running per-chunk count, then
 //                   row_of[f] = start + rank and src_of[row] = f (and, for
 //                   the layer, the pair's routing weight at its row).
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -182,8 +184,14 @@ size_t permute_scratch_bytes(int64_t n, int E) {
 hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
                           int32_t* offsets, int32_t* row_of, int32_t* src_of, void* scratch,
                           hipStream_t st, KernelTimer* timer, const float* topk_w, float* wrow) {
-  int32_t* status = static_cast<int32_t*>(scratch);
-  int32_t* chunk_tab = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + 256);
+  return launch_permute_split(idx, n, E, counts, offsets, row_of, src_of, static_cast<int32_t*>(scratch),
+                              reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + 256), st, timer, topk_w,
+                              wrow);
+}
+
+hipError_t launch_permute_split(const int32_t* idx, int64_t n, int E, int32_t* counts, int32_t* offsets,
+                                int32_t* row_of, int32_t* src_of, int32_t* status, int32_t* chunk_tab,
+                                hipStream_t st, KernelTimer* timer, const float* topk_w, float* wrow) {
   const int nchunk = permute_num_chunks(n);
   int id_bits = 0;
   while ((1 << id_bits) <= E) ++id_bits;  // ids 0..E (E marks invalid) fit
@@ -204,6 +212,38 @@ hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
                        src_of, topk_w, wrow);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fixed scratch
+// The chunk table of launch_permute in a file-scope device array, for
+// callers that cannot allocate (see permute_static_scratch). Each device the
+// library runs on holds its own copy until the process ends; every call on a
+// device uses the same copy, so calls that overlap on one device race.
+// Nothing in it needs to start at zero: permute_hist writes every entry of
+// the table before permute_scan or permute_scatter reads it.
+static __device__ __align__(256) int32_t scratch[kStaticPermuteWords];
+
+namespace {
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t permute_static_scratch(int32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // the array's device address on the current device (the host-side name
+    // is only a stand-in and must never reach a kernel)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace moe

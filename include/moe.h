@@ -226,6 +226,22 @@ moe_status moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* cou
                        int32_t* offsets, int32_t* row_of, int32_t* src_of, void* scratch,
                        void* stream);
 
+/* moe_permute without a caller-provided scratch buffer, for callers that
+ * cannot allocate device memory or hand the library a workspace (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same permutation and outputs as moe_permute (counts, offsets, row_of,
+ * src_of); the status word (MOE_OK or MOE_ERR_ROUTING) goes to `status`, one
+ * int32 in device memory (4-byte aligned), written. The chunk table lives in
+ * a fixed device array of the library (4 MiB per device, held until the
+ * process ends); it never allocates or frees. Limit: ceil(T*k / 1024) *
+ * (E + 1) <= 2^20 table entries (e.g. T*k <= 8,323,072 pairs at E = 128,
+ * <= 1,047,552 at E = 1024), else MOE_ERR_WORKSPACE and nothing is enqueued.
+ * Every call on one device shares that array: calls that overlap on one
+ * device (other streams, other threads) race and must not be issued. */
+moe_status moe_permute_noalloc(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
+                               int32_t* offsets, int32_t* row_of, int32_t* src_of, int32_t* status,
+                               void* stream);
+
 /* Router step before the layer. The pages leave the router outside the
  * measured layer and name that, with uniform random routing, as their
  * benchmark's idealisation (ic.work analysis, section on the benchmark's
