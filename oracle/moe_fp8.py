@@ -22,6 +22,15 @@ tensors are quantized. The readings used here:
     included; e = floor(log2 amax) - 8 (the OCP MX rule; values up to just
     under 2 * 2^(e+8) saturate at 448).
   - an all-zero block gets e = 0.
+* "fp8_block_f32" and "fp8_bwd_f32" (blockwise with fp32 scales): the same
+  blocks as "fp8_block" (1x128 activations, 128x128 weights), each with an
+  fp32 scale s = amax / 448 rounded to fp32; a value v becomes
+  code(v * inv), with inv = 448 / amax rounded to fp32 and the product
+  rounded to fp32, so the block maximum lands on +-448 (the product is within
+  an fp32 rounding of 448, and the E4M3 grid there is 32 apart). An all-zero
+  block, or one so small that 448 / amax overflows fp32 (amax below about
+  1.3e-36), gets s = 1 and zero codes. The value stored is code * s.
+  "fp8_bwd_f32" runs the bf16 forward and the "fp8_block_f32" backward.
   - e is clamped to [-127, 127], the exponents an E8M0 byte can hold (the
     byte 255 is NaN); only blocks with amax below about 2^-119 reach the
     lower clamp, and there the larger scale leaves every value in range.
@@ -55,7 +64,9 @@ import numpy as np
 from oracle import moe_oracle as base
 
 E4M3_MAX = 448.0
-MODES = ("fp8_block", "mxfp8", "fp8_bwd")
+MODES = ("fp8_block", "mxfp8", "fp8_bwd", "fp8_block_f32", "fp8_bwd_f32")
+F32_MODES = ("fp8_block_f32", "fp8_bwd_f32")
+BF16_FORWARD_MODES = ("fp8_bwd", "fp8_bwd_f32")
 
 
 # --------------------------------------------------------------- E4M3 codes
@@ -147,6 +158,52 @@ def quantize_along_last(v, block: int, rule: str):
     return codes.reshape(v.shape), e, deq.reshape(v.shape)
 
 
+def f32_block_scale(amax):
+    """(inv, s) of the fp32-scale rule for block maxima `amax`: inv = 448 /
+    amax and s = amax / 448, each one float32 division (correctly rounded);
+    zero blocks and blocks whose inv overflows get inv = 0 and s = 1."""
+    a = np.asarray(amax, dtype=np.float64).astype(np.float32)   # block maxima of bf16 values: exact
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = np.float32(E4M3_MAX) / a
+        s = a / np.float32(E4M3_MAX)
+    flat = ~np.isfinite(inv) | (a == 0)
+    inv = np.where(flat, np.float32(0.0), inv).astype(np.float32)
+    s = np.where(flat, np.float32(1.0), s).astype(np.float32)
+    return inv, s
+
+
+def _f32_codes(vb, inv):
+    """E4M3 codes of fl32(v * inv) for float32-exact values vb."""
+    y = vb.astype(np.float32) * inv              # one float32 rounding
+    return e4m3_encode(y.astype(np.float64))
+
+
+def quantize_along_last_f32(v, block: int = 128):
+    """fp32-scale blocks of `block` along the last axis. Returns (codes,
+    float32 scales per block, dequantized float64)."""
+    v = np.asarray(v, dtype=np.float64)
+    *lead, n = v.shape
+    assert n % block == 0
+    vb = v.reshape(*lead, n // block, block)
+    inv, s = f32_block_scale(np.max(np.abs(vb), axis=-1))
+    codes = _f32_codes(vb, inv[..., None])
+    deq = e4m3_decode(codes) * s.astype(np.float64)[..., None]
+    return codes.reshape(v.shape), s, deq.reshape(v.shape)
+
+
+def quantize_tiles_f32(w, tile: int = 128):
+    """fp32-scale tile x tile blocks over the last two axes. Returns (codes,
+    float32 scales per tile, dequantized float64)."""
+    w = np.asarray(w, dtype=np.float64)
+    *lead, r, c = w.shape
+    assert r % tile == 0 and c % tile == 0
+    wb = w.reshape(*lead, r // tile, tile, c // tile, tile)
+    inv, s = f32_block_scale(np.max(np.abs(wb), axis=(-3, -1)))
+    codes = _f32_codes(wb, inv[..., :, None, :, None])
+    deq = e4m3_decode(codes) * s.astype(np.float64)[..., :, None, :, None]
+    return codes.reshape(w.shape), s, deq.reshape(w.shape)
+
+
 def quantize_tiles(w, tile: int, rule: str):
     """tile x tile blocks over the last two axes. Returns (codes, e, deq)."""
     w = np.asarray(w, dtype=np.float64)
@@ -164,6 +221,8 @@ def _act(v, mode):
     """Quantize-dequantize an activation along its last (reduction) axis."""
     if mode == "mxfp8":
         return quantize_along_last(v, 32, "mx_floor")[2]
+    if mode in F32_MODES:
+        return quantize_along_last_f32(v, 128)[2]
     return quantize_along_last(v, 128, "pow2_ceil")[2]
 
 
@@ -172,6 +231,8 @@ def _tok(v, mode):
     weight-gradient GEMM's reduction axis): each column in blocks of 128
     (32 for mxfp8) consecutive rows from row 0; zero rows pad the last block,
     which leaves its maximum and its other values unchanged."""
+    if mode in F32_MODES:
+        raise ValueError("the fp32-scale modes have no FP8 weight-gradient reading")
     block, rule = (32, "mx_floor") if mode == "mxfp8" else (128, "pow2_ceil")
     v = np.asarray(v, dtype=np.float64)
     n, c = v.shape
@@ -187,6 +248,8 @@ def _weight(w, mode, reduce_axis_last: bool):
         if reduce_axis_last:
             return quantize_along_last(w, 32, "mx_floor")[2]
         return np.swapaxes(quantize_along_last(np.swapaxes(w, -1, -2), 32, "mx_floor")[2], -1, -2)
+    if mode in F32_MODES:
+        return quantize_tiles_f32(w, 128)[2]
     return quantize_tiles(w, 128, "pow2_ceil")[2]
 
 
@@ -220,7 +283,7 @@ def forward(x, topk_idx, topk_w, W13, W2, mode: str, return_pairs: bool = False,
     """Forward with the quantization points of `mode` ("fp8_bwd" runs the
     forward in full precision). `wq` may carry quantize_weights() results
     for these W13, W2."""
-    if mode == "fp8_bwd":
+    if mode in BF16_FORWARD_MODES:
         return base.forward(x, topk_idx, topk_w, W13, W2, return_pairs=return_pairs)
     x = base.as_f64(x)
     w = base.as_f64(topk_w)
@@ -275,7 +338,7 @@ def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str, wq: dict | None = None
     I = I2 // 2
     k = idx.shape[1]
     wf = w.reshape(-1)
-    if mode == "fp8_bwd":
+    if mode in BF16_FORWARD_MODES:
         wq = _need(wq, W13, W2, mode, ("W2b", "W13b"))
         xf, W13f = x, W13
     else:
@@ -316,5 +379,6 @@ def backward(dy, x, topk_idx, topk_w, W13, W2, mode: str, wq: dict | None = None
     return dx, dwf.reshape(T, k), dW13, dW2
 
 
-__all__ = ["MODES", "E4M3_MAX", "bf16_round", "e4m3_decode_table", "e4m3_encode", "e4m3_decode", "scale_exponent",
+__all__ = ["MODES", "F32_MODES", "BF16_FORWARD_MODES", "E4M3_MAX", "bf16_round", "f32_block_scale",
+           "quantize_along_last_f32", "quantize_tiles_f32", "e4m3_decode_table", "e4m3_encode", "e4m3_decode", "scale_exponent",
            "quantize_along_last", "quantize_tiles", "quantize_weights", "forward", "backward"]

@@ -7,6 +7,7 @@ round-to-nearest-even, and a per-token loop implementation of the quantized
 layer with its own scalar rounding (math.frexp based) on tiny inputs.
 """
 import math
+import struct
 
 import numpy as np
 import pytest
@@ -139,7 +140,29 @@ def _bf(v):
     return np.vectorize(one, otypes=[np.float64])(np.asarray(v, dtype=np.float64))
 
 
+def _fl32(x):
+    """Round a Python float to float32 (the C conversion: nearest, ties to
+    even) through struct."""
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def _q_block_f32(vals):
+    """The fp32-scale rule, scalar: inv = 448 / amax and the products v * inv
+    each rounded once to float32 (a quotient or product of float32 values is
+    exact or correctly rounded in double first, so rounding that double to
+    float32 is the float32 operation), then the nearest E4M3 value with the
+    scalar rounding above; the stored value is code * fl32(amax / 448)."""
+    amax = max(abs(v) for v in vals)
+    if amax == 0.0 or 448.0 / amax > 3.4028234663852886e38:
+        return [0.0 for _ in vals]
+    inv = _fl32(448.0 / amax)
+    s = _fl32(amax / 448.0)
+    return [_q_scalar(_fl32(v * inv), 0) * s for v in vals]
+
+
 def _q_block(vals, rule):
+    if rule == "f32":
+        return _q_block_f32(vals)
     amax = max(abs(v) for v in vals)
     if amax == 0.0:
         e = 0
@@ -168,6 +191,13 @@ def _q_rows(M, block, rule):
     return np.array(out)
 
 
+def _mode_rule(mode):
+    """(activation block, scale rule) of an FP8 mode."""
+    if mode == "mxfp8":
+        return 32, "mx_floor"
+    return 128, ("f32" if mode.endswith("_f32") else "pow2_ceil")
+
+
 def _q_weight(W, mode, reduce_last):
     if mode == "mxfp8":
         if reduce_last:
@@ -178,19 +208,20 @@ def _q_weight(W, mode, reduce_last):
         for r in range(0, W.shape[1], 128):
             for c in range(0, W.shape[2], 128):
                 blk = W[e, r:r + 128, c:c + 128]
-                out[e, r:r + 128, c:c + 128] = np.array(_q_block(list(blk.reshape(-1)), "pow2_ceil")).reshape(
+                out[e, r:r + 128, c:c + 128] = np.array(_q_block(list(blk.reshape(-1)), _mode_rule(mode)[1])).reshape(
                     blk.shape)
     return out
 
 
 def _layer_loops(x, idx, w, W13, W2, dy, mode):
     """Forward and dx/d_topk_w of the quantized layer, token by token."""
-    blk, rule = (32, "mx_floor") if mode == "mxfp8" else (128, "pow2_ceil")
+    blk, rule = _mode_rule(mode)
     T, H = x.shape
     I = W13.shape[1] // 2
     k = idx.shape[1]
     qa = lambda M: _q_rows(M, blk, rule)  # noqa: E731
-    if mode == "fp8_bwd":
+    bf16_fwd = mode in ("fp8_bwd", "fp8_bwd_f32")
+    if bf16_fwd:
         xq, W13q, W2q = x, W13, W2
         fwd_q = lambda M: M  # noqa: E731
     else:
@@ -210,7 +241,7 @@ def _layer_loops(x, idx, w, W13, W2, dy, mode):
             sg = 1.0 / (1.0 + np.exp(-g))
             a = g * sg * u
             # the stored (bf16) activation is what gets quantized
-            wa = w[t, j] * a if mode == "fp8_bwd" else fwd_q(_bf(w[t, j] * a)[None, :])[0]
+            wa = w[t, j] * a if bf16_fwd else fwd_q(_bf(w[t, j] * a)[None, :])[0]
             y[t] += W2q[e] @ wa
             # the backward reads the saved bf16 g and u
             g, u = _bf(g), _bf(u)
@@ -224,16 +255,18 @@ def _layer_loops(x, idx, w, W13, W2, dy, mode):
     return y, dx, dw
 
 
-@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8", "fp8_bwd"])
+@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8", "fp8_bwd", "fp8_block_f32", "fp8_bwd_f32"])
 def test_quantized_layer_matches_per_token_loops(mode):
     rng = np.random.default_rng(3)
     T, H, I, E, k = 6, 256, 128, 3, 2
-    x = rng.standard_normal((T, H))
-    W13 = rng.standard_normal((E, 2 * I, H)) * 0.05
-    W2 = rng.standard_normal((E, H, I)) * 0.05
+    # bf16-valued inputs, as the layer's are (the fp32-scale rule reads its
+    # block maxima as float32 values)
+    x = torch_bf16(rng.standard_normal((T, H)))
+    W13 = torch_bf16(rng.standard_normal((E, 2 * I, H)) * 0.05)
+    W2 = torch_bf16(rng.standard_normal((E, H, I)) * 0.05)
     idx = np.array([rng.choice(E, k, replace=False) for _ in range(T)])
     w = rng.uniform(0.1, 1.0, size=(T, k))
-    dy = rng.standard_normal((T, H))
+    dy = torch_bf16(rng.standard_normal((T, H)))
     y = f8.forward(x, idx, w, W13, W2, mode)
     dx, dw, _, _ = f8.backward(dy, x, idx, w, W13, W2, mode)
     ry, rdx, rdw = _layer_loops(x, idx, w, W13, W2, dy, mode)
@@ -419,13 +452,13 @@ def _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip=None):
     fp8_block and mxfp8, exact in fp8_bwd) and [dg | du] comes from the
     quantized dH product. `slip` plants a mistake on purpose: "xq" multiplies the
     quantized x in dW13, "exact_a" takes a from the unquantized forward."""
-    blk, rule = (32, "mx_floor") if mode == "mxfp8" else (128, "pow2_ceil")
+    blk, rule = _mode_rule(mode)
     T, H = x.shape
     E = W13.shape[0]
     I = W13.shape[1] // 2
     k = idx.shape[1]
     qa = lambda M: _q_rows(M, blk, rule)  # noqa: E731
-    if mode == "fp8_bwd":
+    if mode in ("fp8_bwd", "fp8_bwd_f32"):
         xq, W13q = x, W13
     else:
         xq, W13q = qa(x), _q_weight(W13, mode, True)
@@ -452,7 +485,7 @@ def _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip=None):
     return dW13, dW2
 
 
-@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8", "fp8_bwd"])
+@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8", "fp8_bwd", "fp8_block_f32", "fp8_bwd_f32"])
 def test_default_weight_gradients_match_pair_loops(mode):
     """The default weight-gradient reading of every FP8 mode against outer
     products summed pair by pair, with the scalar rounding helpers above for
@@ -461,17 +494,17 @@ def test_default_weight_gradients_match_pair_loops(mode):
     are far outside the pin's tolerance, so the pin would catch them."""
     rng = np.random.default_rng(11)
     T, H, I, E, k = 7, 256, 128, 3, 2
-    x = rng.standard_normal((T, H)) * np.exp(rng.standard_normal((T, 1)))
-    W13 = rng.standard_normal((E, 2 * I, H)) * 0.05
-    W2 = rng.standard_normal((E, H, I)) * 0.05
+    x = torch_bf16(rng.standard_normal((T, H)) * np.exp(rng.standard_normal((T, 1))))
+    W13 = torch_bf16(rng.standard_normal((E, 2 * I, H)) * 0.05)
+    W2 = torch_bf16(rng.standard_normal((E, H, I)) * 0.05)
     idx = np.array([rng.choice(E, k, replace=False) for _ in range(T)])
     w = rng.uniform(0.1, 1.0, size=(T, k))
-    dy = rng.standard_normal((T, H))
+    dy = torch_bf16(rng.standard_normal((T, H)))
     _, _, dW13, dW2 = f8.backward(dy, x, idx, w, W13, W2, mode)
     r13, r2 = _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode)
     np.testing.assert_allclose(dW13, r13, rtol=1e-9, atol=1e-9)
     np.testing.assert_allclose(dW2, r2, rtol=1e-9, atol=1e-9)
-    if mode != "fp8_bwd":  # (fp8_bwd's forward is exact: both slips are no-ops there)
+    if mode not in ("fp8_bwd", "fp8_bwd_f32"):  # (a bf16 forward is exact: both slips are no-ops there)
         s13, _ = _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip="xq")
         _, s2 = _bf16_wgrad_loops(x, idx, w, W13, W2, dy, mode, slip="exact_a")
         assert np.max(np.abs(s13 - dW13)) / np.max(np.abs(dW13)) > 1e-4
@@ -496,3 +529,62 @@ def test_bf16_round_matches_library_and_scalar_rounding():
         [1.0, -1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, 0.0]
     assert f8.bf16_round(np.array([2.0 ** -133, 2.0 ** -134 * 3, 2.0 ** -135])).tolist() == \
         [2.0 ** -133, 2.0 ** -132, 0.0]         # subnormals: spacing 2^-133, ties to even
+
+
+# ----------------------------------------------------- fp32-scale blockwise rule
+
+def test_f32_rule_block_maximum_maps_to_448_and_scale_is_amax_over_448():
+    """Every block's largest magnitude gets the code of +-448, the stored
+    scale is amax / 448 in float32, and so the dequantized maximum is amax
+    to within a float32 rounding; blocks of every magnitude, both signs."""
+    rng = np.random.default_rng(13)
+    v = rng.standard_normal((400, 256)) * np.exp(rng.uniform(-60, 60, size=(400, 1)))
+    v = torch_bf16(v)
+    codes, s, deq = f8.quantize_along_last_f32(v, 128)
+    vb = v.reshape(400, 2, 128)
+    cb = codes.reshape(400, 2, 128)
+    arg = np.argmax(np.abs(vb), axis=-1)
+    top = np.take_along_axis(cb, arg[..., None], axis=-1)[..., 0]
+    sign = np.take_along_axis(vb, arg[..., None], axis=-1)[..., 0] < 0
+    assert np.array_equal(top, np.where(sign, 0xFE, 0x7E))
+    amax = np.max(np.abs(vb), axis=-1)
+    assert np.array_equal(s, (amax.astype(np.float32) / np.float32(448.0)).astype(np.float32))
+    dmax = np.max(np.abs(deq.reshape(400, 2, 128)), axis=-1)
+    assert np.all(np.abs(dmax - amax) <= amax * 2.0 ** -22)
+    # zero and overflowing blocks: scale 1, zero codes
+    z = np.zeros((2, 128))
+    z[1, 5] = 1e-38                       # 448 / 1e-38 overflows float32
+    c, sz, dz = f8.quantize_along_last_f32(z, 128)
+    assert not c.any() and not dz.any() and sz.reshape(-1).tolist() == [1.0, 1.0]
+
+
+def torch_bf16(v):
+    import torch
+    return torch.from_numpy(np.asarray(v, dtype=np.float64)).float().bfloat16().double().numpy()
+
+
+def test_f32_rule_matches_scalar_rounding():
+    """Rows and 128 x 128 tiles against the scalar rule written with Python
+    floats and struct's float32 rounding."""
+    rng = np.random.default_rng(14)
+    v = torch_bf16(rng.standard_normal((12, 384)) * np.exp(rng.uniform(-8, 8, size=(12, 1))))
+    v[3, :128] = 0.0
+    v[4, 130] = 448.0 * 3                  # a block whose maximum is an exact multiple of 448
+    _, _, deq = f8.quantize_along_last_f32(v, 128)
+    assert np.array_equal(deq, _q_rows(v, 128, "f32"))
+    w = torch_bf16(rng.standard_normal((1, 256, 128)) * 0.02)
+    _, s, dw = f8.quantize_tiles_f32(w, 128)
+    assert s.shape == (1, 2, 1)
+    assert np.array_equal(dw, _q_weight(w, "fp8_block_f32", True))
+
+
+def test_f32_rule_error_bound():
+    """Within a block the error is at most half an E4M3 step of the value
+    (relative 2^-4 for normal codes) plus half the subnormal step times the
+    scale, and the rule never saturates a value other than the maximum."""
+    rng = np.random.default_rng(15)
+    v = rng.standard_normal((64, 512)) * np.exp(rng.uniform(-6, 6, size=(64, 1)))
+    codes, s, deq = f8.quantize_along_last_f32(v, 128)
+    sc = np.repeat(s.astype(np.float64), 128, axis=-1)
+    bound = np.abs(v) * 2.0 ** -4 + sc * 2.0 ** -10 + np.abs(v) * 2.0 ** -22
+    assert np.all(np.abs(deq - v) <= bound)
