@@ -8,7 +8,8 @@ dW2 grouped GEMMs. FP8 precisions add the weight quantization (once per
 step, as after an optimizer update) and the activation quantizations.
 Default workload: the Qwen3-30B-A3B-shaped layer (T=16384, H=2048, I=768,
 E=128, top-8, uniform random routing, bf16); --config picks another layer
-shape (ep8_share: blockwise FP8, qwen3_235b: fp8_bwd, zipf: MXFP8).
+shape (ep8_share: blockwise FP8 with fp32 block scales, qwen3_235b: bf16
+forward with that FP8 backward, zipf: MXFP8).
 
 Prints one JSON line. `value` is TFLOP/s of algorithmic work
 (18 * T * k * H * I flops per step: 6 forward, 12 backward).
@@ -38,6 +39,8 @@ GEMM_FLOP_FACTOR = {
     "gemm1_swiglu": 4, "gemm2": 2, "gemm_dh_dswiglu": 2, "gemm_dx": 4, "gemm_dw13": 4, "gemm_dw2": 2,
 }
 GEMM_FLOP_FACTOR.update({k + "_fp8": v for k, v in list(GEMM_FLOP_FACTOR.items())})
+# fp32 block scales (fp8_block_f32, fp8_bwd_f32)
+GEMM_FLOP_FACTOR.update({k + "f32": v for k, v in list(GEMM_FLOP_FACTOR.items()) if k.endswith("_fp8")})
 GEMM_FLOP_FACTOR.update({"gemm1_swiglu_fp8_fp4": 4, "gemm2_fp8_fp4": 2})  # FP8 activations x FP4 weights
 
 
@@ -76,12 +79,14 @@ KERNEL_FN = {
     "gemm1_swiglu_fp8_fp4": "gemm1_swiglu_kernel<true, true>", "gemm2_fp8_fp4": "gemm2_kernel<true, true>",
     "gemm_dh_dswiglu_fp8": "gemm_dh_kernel<true>", "gemm_dx_fp8": "gemm_dx_kernel<true>",
     "gemm_dw13": "gemm_dw13_kernel", "gemm_dw2": "gemm_dw2_kernel",
+    "gemm1_swiglu_fp8f32": "gemm1_swiglu_kernel<true, false, true>", "gemm2_fp8f32": "gemm2_kernel<true, false, true>",
+    "gemm_dh_dswiglu_fp8f32": "gemm_dh_kernel<true, true>", "gemm_dx_fp8f32": "gemm_dx_kernel<true, true>",
 }
 
 
 def kernel_peak(name: str) -> float:
     # an FP8 x FP4 product runs at the FP8 rate (the wider operand's)
-    return PEAK_FP8_TFLOPS if name.endswith("_fp8") or name.endswith("_fp8_fp4") else PEAK_BF16_TFLOPS
+    return PEAK_FP8_TFLOPS if name.endswith(("_fp8", "_fp8_fp4", "_fp8f32")) else PEAK_BF16_TFLOPS
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_qwen3_30b_bf16.json")
 WORKLOAD_KEY = ["qwen3_30b/bf16"]   # the workload the committed traffic summary was taken on
 
@@ -109,7 +114,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=15)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_30b", choices=sorted(WORKLOADS))
-    ap.add_argument("--precision", default=None, choices=["bf16", "fp8_block", "mxfp8", "fp8_bwd", "fp8_fp4"],
+    ap.add_argument("--precision", default=None, choices=["bf16", "fp8_block", "mxfp8", "fp8_bwd", "fp8_fp4",
+                                                          "fp8_block_f32", "fp8_bwd_f32"],
                     help="override the configuration's precision")
     ap.add_argument("--wgrad", default="bf16", choices=["bf16", "fp8"],
                     help="weight-gradient GEMMs on bf16 operands, or (FP8 precisions) on operands "
@@ -378,7 +384,8 @@ def main():
     achieved = GEMM_FLOP_FACTOR[dom] * MHI / (dom_avg * 1e-3) / 1e12
     gemm_ms = sum(kernels[n]["ms_per_step"] for n in gemm_names)
     dtype = {"bf16": "bf16", "fp8_block": "fp8_e4m3+bf16", "mxfp8": "fp8_e4m3+bf16",
-             "fp8_bwd": "bf16+fp8_e4m3", "fp8_fp4": "fp8_e4m3+fp4_e2m1"}[cfg.precision]
+             "fp8_bwd": "bf16+fp8_e4m3", "fp8_fp4": "fp8_e4m3+fp4_e2m1", "fp8_block_f32": "fp8_e4m3+bf16",
+             "fp8_bwd_f32": "bf16+fp8_e4m3"}[cfg.precision]
     workload = WORKLOADS[cfg.name]
     if fwd_only:
         workload = workload.replace("fwd+bwd", "forward only (inference)")

@@ -17,7 +17,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-PRECISIONS = {"bf16": 0, "fp8_block": 1, "mxfp8": 2, "fp8_bwd": 3, "fp8_fp4": 4}
+PRECISIONS = {"bf16": 0, "fp8_block": 1, "mxfp8": 2, "fp8_bwd": 3, "fp8_fp4": 4, "fp8_block_f32": 5,
+              "fp8_bwd_f32": 6}
 
 STATUS_NAMES = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",

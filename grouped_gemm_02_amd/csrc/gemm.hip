@@ -248,6 +248,9 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t* lds, int ent0, int kk)
 
 struct Acc {
   f32x16 c[TM][TN];
+  // fp32 block scales only: the scale mantissas the accumulators are in
+  // units of (see mma_slab_fp8_f32s)
+  float mP[TM], mQ[TN];
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -255,6 +258,10 @@ struct Acc {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) c[i][j][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) mP[i] = 1.f;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) mQ[j] = 1.f;
   }
 };
 
@@ -577,8 +584,91 @@ __device__ __forceinline__ i32x8 frag4(const uint16_t* lds, int ent0, int s) {
   return i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
 }
 
-template <bool W4 = false>
+// fp32 scale of this lane's row for the slab: with fp32 block scales
+// (kRuleF32) the slab's 4 scale bytes of a row are one float, the scale of
+// its 128-code block
+__device__ __forceinline__ float fscale8(const uint16_t* lds, int ent0) {
+  return *reinterpret_cast<const float*>(lds + (ent0 + (lane_id() & 31)) * LDK + BK);
+}
+
+// s = m * 2^e with m in [1, 2) and e in E8M0's range [-127, 127]; a
+// subnormal s (amax / 448 below 2^-126) takes e = -127 and m < 1
+__device__ __forceinline__ void split_scale(float s, int& e, float& m) {
+  const uint32_t u = __float_as_uint(s);
+  const int be = int((u >> 23) & 0xFFu);
+  if (be == 0) {
+    e = -127;
+    m = s * 1.7014118346046923e38f;  // * 2^127, exact
+  } else {
+    e = be - 127;
+    m = __uint_as_float((u & 0x007FFFFFu) | 0x3F800000u);
+  }
+}
+
+// One slab with fp32 block scales. The slab is one 128-deep block of both
+// operands. A lane's accumulators are one P row and 16 Q columns of one
+// 32-row group, which never straddles a 128-row weight block, so the
+// block's scale product s_P[m] * s_Q[n-block] is one float per lane and
+// sub-tile. Write it m_P m_Q 2^(e_P + e_Q): the MFMA applies 2^(e_P + e_Q)
+// through its E8M0 scale operands, and the accumulators are kept in units of
+// the current block's m_P m_Q (bounded, [1, 4)): each slab first rescales
+// them by the previous block's m_P m_Q over this one's, and after the last
+// slab mainloop_staged_fp8 multiplies by the last m_P m_Q.
+__device__ __forceinline__ void mma_slab_fp8_f32s(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
+  const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
+  int pe[TM], qe[TN];
+  float pmant[TM], qmant[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) split_scale(fscale8(ldsP, pm0 + 32 * i), pe[i], pmant[i]);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) split_scale(fscale8(ldsQ, qn0 + 32 * j), qe[j], qmant[j]);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float r = (acc.mP[i] * acc.mQ[j]) * __builtin_amdgcn_rcpf(pmant[i] * qmant[j]);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc.c[i][j][q] *= r;
+    }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc.mP[i] = pmant[i];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) acc.mQ[j] = qmant[j];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    i32x8 qf[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) qf[j] = frag8(ldsQ, qn0 + 32 * j, s);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const i32x8 pf = frag8(ldsP, pm0 + 32 * i, s);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[j], pf, acc.c[i][j], 0, 0, 0, qe[j] + 127,
+                                                                      0, pe[i] + 127);
+    }
+  }
+}
+
+// the accumulators back from units of the last block's m_P m_Q
+__device__ __forceinline__ void finish_f32s(Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float f = acc.mP[i] * acc.mQ[j];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc.c[i][j][q] *= f;
+    }
+}
+
+template <bool W4 = false, bool F32S = false>
 __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
+  if constexpr (F32S) {
+    static_assert(!W4, "fp32 block scales are for E4M3 operands");
+    mma_slab_fp8_f32s(ldsP, ldsQ, acc);
+    return;
+  }
   const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -601,7 +691,7 @@ __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_
   }
 }
 
-template <class LQ = KMajorLoader8>
+template <bool F32S = false, class LQ = KMajorLoader8>
 __device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, LQ& lq, int nk, Acc& acc, bool active,
                                                     Stage8& sp, typename StageOf<LQ>::type& sq) {
   constexpr bool W4 = std::is_same<LQ, KMajorLoader4>::value;
@@ -617,7 +707,7 @@ __device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, LQ& lq, i
       lp.fetch(kt + 1, sp);
       lq.fetch(kt + 1, sq);
     }
-    if (active) mma_slab_fp8<W4>(cur, cur + kOperandLds, acc);
+    if (active) mma_slab_fp8<W4, F32S>(cur, cur + kOperandLds, acc);
     // unconditional (after the last slab it rewrites stale data into the idle
     // buffer): a conditional block here lets the compiler sink the MFMAs
     // below it, with every fragment of the slab live at once
@@ -625,15 +715,17 @@ __device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, LQ& lq, i
     lq.store(nxt + kOperandLds, sq);
     __syncthreads();
   }
+  if constexpr (F32S) finish_f32s(acc);
 }
 
+template <bool F32S = false>
 __device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, Acc& acc,
                                              bool active = true) {
   if (nk <= 0) return;
   Stage8 sp, sq;
   lp.fetch(0, sp);
   lq.fetch(0, sq);
-  mainloop_staged_fp8(lp, lq, nk, acc, active, sp, sq);
+  mainloop_staged_fp8<F32S>(lp, lq, nk, acc, active, sp, sq);
 }
 
 // ------------------------------------------------------------------ LDS-staged epilogue
@@ -819,7 +911,7 @@ struct TileState {
   float w;  // routing weight of tile row threadIdx.x (kernels that need it)
 };
 
-template <bool FP8, bool Q_MN, bool PREFETCH, class LP, class LQ, class Setup, class Epi>
+template <bool FP8, bool Q_MN, bool PREFETCH, bool F32S = false, class LP, class LQ, class Setup, class Epi>
 __device__ __forceinline__ void row_tile_walk(int64_t total, int nk, LP& lp, LQ& lq, Setup&& setup,
                                               Epi&& epi) {
   typename StageOf<LP>::type sp;
@@ -841,7 +933,7 @@ __device__ __forceinline__ void row_tile_walk(int64_t total, int nk, LP& lp, LQ&
     acc.zero();
     const bool active = wave_m() * WTM < cur.rt.rows;
     if constexpr (FP8)
-      mainloop_staged_fp8(lp, lq, nk, acc, active, sp, sq);
+      mainloop_staged_fp8<F32S>(lp, lq, nk, acc, active, sp, sq);
     else
       mainloop_staged<false, Q_MN>(lp, lq, nk, acc, active, sp, sq);
     t += gridDim.x;
@@ -884,7 +976,7 @@ struct Operand {
 template <bool FP8>
 __device__ __forceinline__ int row_units(int K) { return FP8 ? K / 2 : K; }
 
-template <bool FP8, bool W4 = false>
+template <bool FP8, bool W4 = false, bool F32S = false>
 __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, Operand X, Operand W,
                                                                 uint16_t* __restrict__ h13,
                                                                 uint16_t* __restrict__ act) {
@@ -951,12 +1043,12 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
       __syncthreads();
     }
   };
-  row_tile_walk<FP8, false, true>(total, KU / 64, lp, lq, setup, epi);
+  row_tile_walk<FP8, false, true, F32S>(total, KU / 64, lp, lq, setup, epi);
 }
 
 // ================================================================== forward GEMM2
 // O[r][h] = (w a)[r] . W2[e][h],  K = I.
-template <bool FP8, bool W4 = false>
+template <bool FP8, bool W4 = false, bool F32S = false>
 __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand A, Operand W,
                                                          uint16_t* __restrict__ out) {
   const int E = int(p.E), H = int(p.H), I = int(p.I);
@@ -1002,7 +1094,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
     stage_image(acc, st.rt.row0, st.rt.rows, rowmap, s_map);
     copy(st);
   };
-  row_tile_walk<FP8, false, true>(total, KU / 64, lp, lq, setup, epi);
+  row_tile_walk<FP8, false, true, F32S>(total, KU / 64, lp, lq, setup, epi);
 }
 
 // ------------------------------------------------------------------ row functions
@@ -1032,7 +1124,7 @@ struct TokenRows {  // k-th row of an expert segment -> its token's row
 int dh_num_parts(int64_t I) { return int((I + BN - 1) / BN) * 2; }
 
 // In the FP8 variant W2 arrives transposed, [E, I, H] (k-major rows i).
-template <bool FP8>
+template <bool FP8, bool F32S = false>
 __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operand DY, Operand W,
                                                            const uint16_t* __restrict__ h13,
                                                            uint16_t* __restrict__ dh13,
@@ -1071,7 +1163,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
         lq.set_row(i, int64_t(min(KMajorLoader::row_of_thread(i), ncols - 1)) * KU);
-      mainloop_fp8(lp, lq, KU / 64, acc, wave_m() * WTM < rt.rows);
+      mainloop_fp8<F32S>(lp, lq, KU / 64, acc, wave_m() * WTM < rt.rows);
     } else {
       MNMajorLoader<DirectRows> lq;
       lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN,
@@ -1151,7 +1243,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
 // ================================================================== backward dX
 // dXr[r][h] = [dg | du][r] . W13[e][:, h]  (K = 2I; W13 read mn-major).
 // In the FP8 variant W13 arrives transposed, [E, H, 2I] (k-major rows h).
-template <bool FP8>
+template <bool FP8, bool F32S = false>
 __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operand DH, Operand W,
                                                            uint16_t* __restrict__ out) {
   const int E = int(p.E), H = int(p.H), I = int(p.I);
@@ -1198,7 +1290,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
     stage_image(acc, st.rt.row0, st.rt.rows, rowmap, s_map);
     copy(st);
   };
-  row_tile_walk<FP8, !FP8, true>(total, KU / 64, lp, lq, setup, epi);
+  row_tile_walk<FP8, !FP8, true, F32S>(total, KU / 64, lp, lq, setup, epi);
 }
 
 // ================================================================== weight gradients
@@ -1631,6 +1723,10 @@ hipError_t launch_gemm1_swiglu(const GemmProblem& p, GemmOperand x, GemmOperand 
   if (W13.fp4) {
     TimedLaunch tl(timer, "gemm1_swiglu_fp8_fp4", st);
     hipLaunchKernelGGL((gemm1_swiglu_kernel<true, true>), dim3(grid), dim3(kThreads), 0, st, p, X, W, h13, act);
+  } else if (x.f32s) {
+    TimedLaunch tl(timer, "gemm1_swiglu_fp8f32", st);
+    hipLaunchKernelGGL((gemm1_swiglu_kernel<true, false, true>), dim3(grid), dim3(kThreads), 0, st, p, X, W, h13,
+                       act);
   } else if (x.scales) {
     TimedLaunch tl(timer, "gemm1_swiglu_fp8", st);
     hipLaunchKernelGGL(gemm1_swiglu_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, X, W, h13, act);
@@ -1648,6 +1744,9 @@ hipError_t launch_gemm2(const GemmProblem& p, GemmOperand act, GemmOperand W2, u
   if (W2.fp4) {
     TimedLaunch tl(timer, "gemm2_fp8_fp4", st);
     hipLaunchKernelGGL((gemm2_kernel<true, true>), dim3(grid), dim3(kThreads), 0, st, p, A, W, out_rows);
+  } else if (act.f32s) {
+    TimedLaunch tl(timer, "gemm2_fp8f32", st);
+    hipLaunchKernelGGL((gemm2_kernel<true, false, true>), dim3(grid), dim3(kThreads), 0, st, p, A, W, out_rows);
   } else if (act.scales) {
     TimedLaunch tl(timer, "gemm2_fp8", st);
     hipLaunchKernelGGL(gemm2_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, A, W, out_rows);
@@ -1662,7 +1761,10 @@ hipError_t launch_gemm_dh(const GemmProblem& p, GemmOperand dy, GemmOperand W2, 
                           uint16_t* dh13, float* dwpart, hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(row_tiles_upper(p) * ((p.I + BN - 1) / BN), p.num_cus);
   const Operand D{dy.data, dy.scales}, W{W2.data, W2.scales};
-  if (dy.scales) {
+  if (dy.f32s) {
+    TimedLaunch tl(timer, "gemm_dh_dswiglu_fp8f32", st);
+    hipLaunchKernelGGL((gemm_dh_kernel<true, true>), dim3(grid), dim3(kThreads), 0, st, p, D, W, h13, dh13, dwpart);
+  } else if (dy.scales) {
     TimedLaunch tl(timer, "gemm_dh_dswiglu_fp8", st);
     hipLaunchKernelGGL(gemm_dh_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, D, W, h13, dh13, dwpart);
   } else {
@@ -1676,7 +1778,10 @@ hipError_t launch_gemm_dx(const GemmProblem& p, GemmOperand dh13, GemmOperand W1
                           hipStream_t st, KernelTimer* timer) {
   const int grid = grid_for(row_tiles_upper(p) * (p.H / BN), p.num_cus);
   const Operand D{dh13.data, dh13.scales}, W{W13.data, W13.scales};
-  if (dh13.scales) {
+  if (dh13.f32s) {
+    TimedLaunch tl(timer, "gemm_dx_fp8f32", st);
+    hipLaunchKernelGGL((gemm_dx_kernel<true, true>), dim3(grid), dim3(kThreads), 0, st, p, D, W, dx_rows);
+  } else if (dh13.scales) {
     TimedLaunch tl(timer, "gemm_dx_fp8", st);
     hipLaunchKernelGGL(gemm_dx_kernel<true>, dim3(grid), dim3(kThreads), 0, st, p, D, W, dx_rows);
   } else {

@@ -73,6 +73,7 @@ struct GemmOperand {
   const void* data;
   const uint8_t* scales;
   bool fp4 = false;  // E2M1 codes, two per byte (weights of the FP8 x FP4 forward)
+  bool f32s = false;  // scales are fp32 per (row, 128-block) (kRuleF32), not E8M0 bytes
 };
 // forward
 hipError_t launch_gemm1_swiglu(const GemmProblem& p, GemmOperand x, GemmOperand W13, uint16_t* h13,
@@ -103,6 +104,10 @@ hipError_t launch_gemm_dw2(const GemmProblem& p, const uint16_t* dy, const uint1
 // ---------------------------------------------------------------- FP8 quantization
 constexpr int kRulePow2 = 0;  // smallest 2^e with 448 * 2^e >= amax
 constexpr int kRuleMx = 1;    // 2^(floor(log2 amax) - 8)
+// fp32 scale s = amax / 448, codes of fl32(v * fl32(448 / amax)) (128 or
+// 128x128 blocks); the scale array holds one float per (row, 128 values):
+// the bytes the E8M0 layout gives that row's four 32-blocks
+constexpr int kRuleF32 = 2;
 // bf16 [rows, K] -> E4M3 codes [rows, K] + E8M0 scales [rows, K/32]; block 32 or 128
 hipError_t launch_quant_rows(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
                              int block, int rule, hipStream_t st, KernelTimer* timer, const char* name);

@@ -23,7 +23,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_NULL;
-  if (s->precision < MOE_BF16 || s->precision > MOE_FP8_FP4) return MOE_ERR_PRECISION;
+  if (s->precision < MOE_BF16 || s->precision > MOE_FP8_BWD_F32) return MOE_ERR_PRECISION;
   if (s->T < 0 || s->E < 1 || s->E > 1024 || s->k < 1 || s->k > s->E) return MOE_ERR_SHAPE;
   if (s->H < 256 || s->H > 16384 || s->H % 256 != 0) return MOE_ERR_SHAPE;
   if (s->I < 128 || s->I > 8192 || s->I % 128 != 0) return MOE_ERR_SHAPE;
@@ -34,6 +34,8 @@ moe_status check_shape(const moe_shape* s) {
   if ((s->flags & ~MOE_FLAG_FP8_WGRAD) != 0) return MOE_ERR_PRECISION;
   if ((s->flags & MOE_FLAG_FP8_WGRAD) != 0) {
     if (s->precision == MOE_BF16 || s->precision == MOE_FP8_FP4) return MOE_ERR_PRECISION;  // no FP8 backward
+    // the row-axis quantizer has the power-of-two and MX rules only
+    if (s->precision == MOE_FP8_BLOCK_F32 || s->precision == MOE_FP8_BWD_F32) return MOE_ERR_UNSUPPORTED;
     // 32-bit offsets inside a weight-gradient tile's 256 rows of Kp codes
     if (s->T * s->k >= (int64_t(1) << 23)) return MOE_ERR_SHAPE;
   }
@@ -43,16 +45,20 @@ moe_status check_shape(const moe_shape* s) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool fp8_forward(const moe_shape& s) {
-  return s.precision == MOE_FP8_BLOCK || s.precision == MOE_MXFP8 || s.precision == MOE_FP8_FP4;
+  return s.precision == MOE_FP8_BLOCK || s.precision == MOE_MXFP8 || s.precision == MOE_FP8_FP4 ||
+         s.precision == MOE_FP8_BLOCK_F32;
 }
 bool fp8_backward(const moe_shape& s) {
-  return s.precision == MOE_FP8_BLOCK || s.precision == MOE_MXFP8 || s.precision == MOE_FP8_BWD;
+  return s.precision == MOE_FP8_BLOCK || s.precision == MOE_MXFP8 || s.precision == MOE_FP8_BWD ||
+         s.precision == MOE_FP8_BLOCK_F32 || s.precision == MOE_FP8_BWD_F32;
 }
 bool fp4_weights(const moe_shape& s) { return s.precision == MOE_FP8_FP4; }
+// blockwise with fp32 block scales
+bool f32_scales(const moe_shape& s) { return s.precision == MOE_FP8_BLOCK_F32 || s.precision == MOE_FP8_BWD_F32; }
 // activation block (32 or 128 values along the reduction axis) and scale rule
 bool mx_acts(const moe_shape& s) { return s.precision == MOE_MXFP8 || s.precision == MOE_FP8_FP4; }
 int act_block(const moe_shape& s) { return mx_acts(s) ? 32 : 128; }
-int scale_rule(const moe_shape& s) { return mx_acts(s) ? kRuleMx : kRulePow2; }
+int scale_rule(const moe_shape& s) { return mx_acts(s) ? kRuleMx : (f32_scales(s) ? kRuleF32 : kRulePow2); }
 bool fp8_wgrad(const moe_shape& s) { return (s.flags & MOE_FLAG_FP8_WGRAD) != 0; }
 // an upper bound of the sum over experts of rows rounded up to 128
 int64_t wgrad_rows_cap(const moe_shape& s) { return 128 * ((s.T * s.k) / 128 + s.E); }
@@ -377,6 +383,7 @@ moe_status moe_quantize_rows(const moe_shape* s, const void* in, int64_t rows, i
   if (rows == 0) return MOE_OK;
   if (!in || !codes || !scales) return MOE_ERR_NULL;
   if (!aligned16(in) || !aligned16(codes)) return MOE_ERR_ALIGN;
+  if (f32_scales(*s) && (reinterpret_cast<uintptr_t>(scales) & 3u) != 0) return MOE_ERR_ALIGN;
   int cus = 0;
   if ((st = device_info(&cus)) != MOE_OK) return st;
   std::lock_guard<std::mutex> lk(g_timer_mu);
@@ -391,6 +398,7 @@ moe_status moe_quantize_tokens(const moe_shape* s, const void* in, int64_t ld, i
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->precision == MOE_BF16) return MOE_ERR_PRECISION;
+  if (f32_scales(*s)) return MOE_ERR_UNSUPPORTED;  // the row-axis reading has pow2 and MX scales only
   if (C < 128 || C > 65536 || C % 128 != 0 || ld < C || ld % 8 != 0) return MOE_ERR_SHAPE;
   if (s->T * s->k >= (int64_t(1) << 23)) return MOE_ERR_SHAPE;
   if (s->T == 0) return MOE_OK;
@@ -451,10 +459,10 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
     if ((e = launch_quant_rows(static_cast<const uint16_t*>(x), s->T, int(s->H), xq, xs, blk, rule, hs, tm,
                                "quant_x")) != hipSuccess)
       return MOE_ERR_LAUNCH;
-    gx = GemmOperand{xq, xs};
-    const bool w4 = fp4_weights(*s);
-    gw13 = GemmOperand{at<uint8_t>(wq, WL.w13), at<uint8_t>(wq, WL.w13_scale), w4};
-    gw2 = GemmOperand{at<uint8_t>(wq, WL.w2), at<uint8_t>(wq, WL.w2_scale), w4};
+    const bool w4 = fp4_weights(*s), f32 = f32_scales(*s);
+    gx = GemmOperand{xq, xs, false, f32};
+    gw13 = GemmOperand{at<uint8_t>(wq, WL.w13), at<uint8_t>(wq, WL.w13_scale), w4, f32};
+    gw2 = GemmOperand{at<uint8_t>(wq, WL.w2), at<uint8_t>(wq, WL.w2_scale), w4, f32};
   }
   if ((e = launch_gemm1_swiglu(gp, gx, gw13, h13, act, hs, tm)) != hipSuccess) return MOE_ERR_LAUNCH;
   if (f8) {
@@ -463,7 +471,7 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
     if ((e = launch_quant_rows(act, Tk, int(s->I), aq, as, act_block(*s), scale_rule(*s), hs, tm,
                                "quant_act")) != hipSuccess)
       return MOE_ERR_LAUNCH;
-    ga = GemmOperand{aq, as};
+    ga = GemmOperand{aq, as, false, f32_scales(*s)};
   }
   // top-1: the down GEMM writes y's rows directly; the combine only zeroes
   // the rows of dropped tokens
@@ -538,9 +546,10 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
         e = launch_quant_rows(dy16, s->T, H, dyq, dys, act_block(*s), rule, hs, tm, "quant_dy");
       }
       if (e != hipSuccess) return MOE_ERR_LAUNCH;
-      gdy = GemmOperand{dyq, dys};
-      gw2 = GemmOperand{at<uint8_t>(wq, WL.w2t), at<uint8_t>(wq, WL.w2t_scale)};
-      gw13 = GemmOperand{at<uint8_t>(wq, WL.w13t), at<uint8_t>(wq, WL.w13t_scale)};
+      const bool f32 = f32_scales(*s);
+      gdy = GemmOperand{dyq, dys, false, f32};
+      gw2 = GemmOperand{at<uint8_t>(wq, WL.w2t), at<uint8_t>(wq, WL.w2t_scale), false, f32};
+      gw13 = GemmOperand{at<uint8_t>(wq, WL.w13t), at<uint8_t>(wq, WL.w13t_scale), false, f32};
     }
     if ((e = launch_gemm_dh(gp, gdy, gw2, h13, dh13, dwpart, hs, tm)) != hipSuccess) return MOE_ERR_LAUNCH;
     if (f8) {
@@ -552,7 +561,7 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
       else
         e = launch_quant_rows(dh13, Tk, 2 * I, dhq, dhs, act_block(*s), rule, hs, tm, "quant_dh13");
       if (e != hipSuccess) return MOE_ERR_LAUNCH;
-      gdh = GemmOperand{dhq, dhs};
+      gdh = GemmOperand{dhq, dhs, false, f32_scales(*s)};
     }
     const bool direct = s->k == 1;  // top-1: dX rows go straight to dx
     if ((e = launch_gemm_dx(gp, gdh, gw13, direct ? static_cast<uint16_t*>(dx) : dxrows, hs, tm)) != hipSuccess)

@@ -15,6 +15,14 @@
 // Scales are always stored per (row, 32-wide block along the reduction
 // axis); a 128-wide or 128x128 block writes its byte into every 32-block it
 // covers, so the GEMMs read one layout for both modes.
+//
+// The blockwise rule with fp32 scales (kRuleF32: the EP=8-share workload's
+// "fp32 scales") keeps the same blocks with s = amax / 448 in fp32: a value
+// becomes the code of fl32(v * inv), inv = fl32(448 / amax), so the block
+// maximum lands on +-448; an all-zero block, or one whose 448 / amax
+// overflows fp32, gets s = 1 and zero codes. Its float takes the four bytes
+// that the E8M0 layout gives the 128 values' four 32-blocks, so the arrays
+// keep their size and every loader its offsets.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -72,6 +80,33 @@ __device__ __forceinline__ uint32_t pack4_codes(const float* v, int e) {
   return u & ~z;
 }
 
+// fp32-scale rule: inv = 448 / amax and s = amax / 448 (correctly rounded
+// divisions); inv = 0, s = 1 for a zero block or where 448 / amax overflows
+__device__ __forceinline__ void f32_block_rule(float amax, float& inv, float& s) {
+  inv = 448.f / amax;
+  s = amax / 448.f;
+  if (!(amax > 0.f) || !(inv <= 3.40282347e38f)) {
+    inv = 0.f;
+    s = 1.f;
+  }
+}
+
+// The E4M3 codes of fl32(v[0..3] * inv), saturating, +0 for zero results
+__device__ __forceinline__ uint32_t pack4_codes_inv(const float* v, float inv) {
+  float x[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float y = v[q] * inv;
+    x[q] = __builtin_copysignf(__builtin_fminf(__builtin_fabsf(y), 448.f), y);
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+  const uint32_t u = uint32_t(w);
+  const uint32_t t = u ^ 0x80808080u;
+  const uint32_t z = ~(((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t | 0x7F7F7F7Fu);
+  return u & ~z;
+}
+
 // ---------------------------------------------------------------- rows
 // in: bf16 [rows, K]; out codes uint8 [rows, K], scales uint8 [rows, K/32].
 // A work item is 8 consecutive values; the items of one block (4 for 32,
@@ -109,10 +144,17 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
       for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
       for (int off = 1; off < group; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
       if (g < total) {
-        const int e = clamp_exp(block_exponent(amax, rule));
-        const uint32_t lo = pack4_codes(v, e), hi = pack4_codes(v + 4, e);
-        *reinterpret_cast<u32x2*>(codes + g * 8) = u32x2{lo, hi};
-        if ((g & 3) == 0) scales[g / 4] = uint8_t(e + 127);
+        if (rule == kRuleF32) {  // 128-blocks: one float per 16 items
+          float inv, sc;
+          f32_block_rule(amax, inv, sc);
+          *reinterpret_cast<u32x2*>(codes + g * 8) = u32x2{pack4_codes_inv(v, inv), pack4_codes_inv(v + 4, inv)};
+          if ((g & 15) == 0) reinterpret_cast<float*>(scales)[g / 16] = sc;
+        } else {
+          const int e = clamp_exp(block_exponent(amax, rule));
+          const uint32_t lo = pack4_codes(v, e), hi = pack4_codes(v + 4, e);
+          *reinterpret_cast<u32x2*>(codes + g * 8) = u32x2{lo, hi};
+          if ((g & 3) == 0) scales[g / 4] = uint8_t(e + 127);
+        }
       }
     }
   }
@@ -180,7 +222,9 @@ __global__ __launch_bounds__(256) void quant_weight_tiles_kernel(const uint16_t*
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   const float tile_amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const int tile_e = clamp_exp(block_exponent(tile_amax, rule));
+  const int tile_e = rule == kRuleF32 ? 0 : clamp_exp(block_exponent(tile_amax, rule));
+  float tile_inv = 0.f, tile_s = 1.f;
+  if (rule == kRuleF32) f32_block_rule(tile_amax, tile_inv, tile_s);
 
   if (pcodes) {
 #pragma unroll
@@ -201,6 +245,12 @@ __global__ __launch_bounds__(256) void quant_weight_tiles_kernel(const uint16_t*
         ex = clamp_exp(block_exponent(m, rule));
       }
       const int64_t orow = e * R + int64_t(rb) * 128 + (t >> 4) + 16 * i;
+      if (rule == kRuleF32) {
+        *reinterpret_cast<u32x2*>(pcodes + orow * C + int64_t(cb) * 128 + c8) =
+            u32x2{pack4_codes_inv(v, tile_inv), pack4_codes_inv(v + 4, tile_inv)};
+        if ((t & 15) == 0) reinterpret_cast<float*>(pscales)[orow * (C / 128) + cb] = tile_s;
+        continue;
+      }
       *reinterpret_cast<u32x2*>(pcodes + orow * C + int64_t(cb) * 128 + c8) = u32x2{pack4_codes(v, ex), pack4_codes(v + 4, ex)};
       if ((t & 3) == 0) pscales[orow * (C / 32) + cb * 4 + ((t & 15) >> 2)] = uint8_t(ex + 127);
     }
@@ -230,6 +280,22 @@ __global__ __launch_bounds__(256) void quant_weight_tiles_kernel(const uint16_t*
     const int64_t ocol = int64_t(rb) * 128 + 32 * q;
     uint8_t* d0 = tcodes + orow * R + ocol;
     uint8_t* d1 = d0 + R;
+    if (rule == kRuleF32) {
+      const float iv = tile_inv;
+      *reinterpret_cast<u32x4*>(d0) = u32x4{pack4_codes_inv(v0, iv), pack4_codes_inv(v0 + 4, iv),
+                                            pack4_codes_inv(v0 + 8, iv), pack4_codes_inv(v0 + 12, iv)};
+      *reinterpret_cast<u32x4*>(d0 + 16) = u32x4{pack4_codes_inv(v0 + 16, iv), pack4_codes_inv(v0 + 20, iv),
+                                                 pack4_codes_inv(v0 + 24, iv), pack4_codes_inv(v0 + 28, iv)};
+      *reinterpret_cast<u32x4*>(d1) = u32x4{pack4_codes_inv(v1, iv), pack4_codes_inv(v1 + 4, iv),
+                                            pack4_codes_inv(v1 + 8, iv), pack4_codes_inv(v1 + 12, iv)};
+      *reinterpret_cast<u32x4*>(d1 + 16) = u32x4{pack4_codes_inv(v1 + 16, iv), pack4_codes_inv(v1 + 20, iv),
+                                                 pack4_codes_inv(v1 + 24, iv), pack4_codes_inv(v1 + 28, iv)};
+      if (q == 0) {
+        reinterpret_cast<float*>(tscales)[orow * (R / 128) + rb] = tile_s;
+        reinterpret_cast<float*>(tscales)[(orow + 1) * (R / 128) + rb] = tile_s;
+      }
+      return;
+    }
     *reinterpret_cast<u32x4*>(d0) = u32x4{pack4_codes(v0, e0), pack4_codes(v0 + 4, e0), pack4_codes(v0 + 8, e0),
                                           pack4_codes(v0 + 12, e0)};
     *reinterpret_cast<u32x4*>(d0 + 16) = u32x4{pack4_codes(v0 + 16, e0), pack4_codes(v0 + 20, e0),

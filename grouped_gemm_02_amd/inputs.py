@@ -61,9 +61,9 @@ CONFIGS = {
     # Qwen3-30B-A3B-shaped layer, all 128 experts local
     "qwen3_30b": LayerConfig("qwen3_30b", 16384, 2048, 768, 128, 8, "uniform", "bf16", 1),
     # one EP=8 rank's share of the 30B layer: 16 local experts, 131072 rows
-    "ep8_share": LayerConfig("ep8_share", 131072, 2048, 768, 16, 1, "uniform", "fp8_block", 2),
+    "ep8_share": LayerConfig("ep8_share", 131072, 2048, 768, 16, 1, "uniform", "fp8_block_f32", 2),
     # Qwen3-235B-A22B-shaped layer
-    "qwen3_235b": LayerConfig("qwen3_235b", 16384, 4096, 1536, 128, 8, "uniform", "fp8_bwd", 3),
+    "qwen3_235b": LayerConfig("qwen3_235b", 16384, 4096, 1536, 128, 8, "uniform", "fp8_bwd_f32", 3),
     # skewed routing on the 30B shape
     "zipf": LayerConfig("zipf", 16384, 2048, 768, 128, 8, "zipf", "mxfp8", 4),
 }

@@ -96,12 +96,28 @@ typedef enum moe_status {
  *     nearest even, saturating) in 1x32 blocks along the reduction axis with
  *     e = floor(log2(largest magnitude)) - 2. moe_bwd rejects it
  *     (MOE_ERR_PRECISION), as does MOE_FLAG_FP8_WGRAD. */
+/*   MOE_FP8_BLOCK_F32, MOE_FP8_BWD_F32: blockwise FP8 with fp32 block
+ *     scales (the blocks of MOE_FP8_BLOCK: 1x128 activations, 128x128
+ *     weights). A block with largest magnitude amax > 0 has the scale
+ *     s = amax / 448 and inv = 448 / amax (each an fp32 division, correctly
+ *     rounded); a value v is stored as the E4M3 code of fl32(v * inv), so
+ *     the block maximum becomes +-448; an all-zero block, or one whose
+ *     448 / amax overflows fp32 (amax below about 1.3e-36), has s = 1 and
+ *     zero codes. The GEMMs run each 128-deep block at unit hardware scale
+ *     and add it to the fp32 accumulators times s_x * s_w. A scale array
+ *     holds one float per (row, 128 values), in the bytes the E8M0 layout
+ *     gives those 128 values' four 32-blocks (the layouts below keep their
+ *     sizes). MOE_FP8_BWD_F32 runs the forward of MOE_BF16 and the backward
+ *     of MOE_FP8_BLOCK_F32. Both reject MOE_FLAG_FP8_WGRAD
+ *     (MOE_ERR_UNSUPPORTED). */
 typedef enum moe_precision {
   MOE_BF16 = 0,
   MOE_FP8_BLOCK = 1,
   MOE_MXFP8 = 2,
   MOE_FP8_BWD = 3,
-  MOE_FP8_FP4 = 4
+  MOE_FP8_FP4 = 4,
+  MOE_FP8_BLOCK_F32 = 5,
+  MOE_FP8_BWD_F32 = 6
 } moe_precision;
 
 /* Flags of moe_shape.flags. MOE_FLAG_FP8_WGRAD: the weight-gradient GEMMs
@@ -155,10 +171,13 @@ moe_status moe_get_saved_layout(const moe_shape* s, moe_saved_layout* out);
  *   w2t, w2t_scale    backward dH:     W2^T  codes [E, I, H],  scales [E, I, H/32]
  *   w13t, w13t_scale  backward dX:     W13^T codes [E, H, 2I], scales [E, H, 2I/32]
  * Scales are stored per (row, 32 consecutive codes); a 128-wide or 128x128
- * block repeats its byte in every 32-block it covers. MOE_FP8_FP4 stores
+ * block repeats its byte in every 32-block it covers. Under the fp32-scale
+ * precisions the same bytes hold one float per (row, 128 codes): the
+ * 128x128 tile's scale, repeated on each of its rows. MOE_FP8_FP4 stores
  * only the forward parts, as E2M1 codes two per byte (w13 [E, 2I, H/2],
  * w2 [E, H, I/2]; value 2j of a row in the low nibble of byte j). Entries a
- * precision does not use (the forward parts for MOE_FP8_BWD, the backward
+ * precision does not use (the forward parts for MOE_FP8_BWD and
+ * MOE_FP8_BWD_F32, the backward
  * parts for MOE_FP8_FP4, everything for MOE_BF16) are SIZE_MAX; total is 0
  * for MOE_BF16. Pure host function. */
 typedef struct moe_wq_layout {
@@ -182,8 +201,10 @@ moe_status moe_quantize_weights(const moe_shape* s, const void* W13, const void*
  * moe_precision). This is the step moe_fwd applies to x and w*silu(g)*u and
  * moe_bwd to dY and [dg | du]; it is exposed for callers that keep
  * activations in FP8 and for testing. Requires 0 <= rows, 128 <= K <= 65536,
- * K % 128 == 0, rows*K < 2^31; `in` and `codes` 16-byte aligned.
- * MOE_ERR_PRECISION for MOE_BF16. */
+ * K % 128 == 0, rows*K < 2^31; `in` and `codes` 16-byte aligned. Under
+ * MOE_FP8_BLOCK_F32 and MOE_FP8_BWD_F32 `scales` holds fp32 scales
+ * [rows, K/128] (the same bytes; 4-byte aligned). MOE_ERR_PRECISION for
+ * MOE_BF16. */
 moe_status moe_quantize_rows(const moe_shape* s, const void* in, int64_t rows, int64_t K, void* codes,
                              void* scales, void* stream);
 
@@ -202,7 +223,8 @@ moe_status moe_quantize_rows(const moe_shape* s, const void* in, int64_t rows, i
  *           and poff_e the sum of Kp over the experts before e
  *   scales  uint8, C * K / 32 bytes: expert e's bytes [C][Kp_e / 32] at
  *           C * poff_e / 32, one per (column, 32 rows)
- * `in` and `codes` 16-byte aligned. MOE_ERR_PRECISION for MOE_BF16;
+ * `in` and `codes` 16-byte aligned. MOE_ERR_PRECISION for MOE_BF16,
+ * MOE_ERR_UNSUPPORTED for MOE_FP8_BLOCK_F32 and MOE_FP8_BWD_F32;
  * enqueued on `stream`, the caller owns every buffer. */
 moe_status moe_quantize_tokens(const moe_shape* s, const void* in, int64_t ld, int64_t C, const int32_t* counts,
                                const int32_t* offsets, const int32_t* src_of, void* codes, void* scales,

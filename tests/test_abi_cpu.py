@@ -299,3 +299,22 @@ def test_binding_checks_tensor_arguments(B):
         B.moe_fwd(s, ok["x"], ok["idx"], ok["w"], ok["W13"], ok["W2"], None, ok["y"], ok["saved"], ok["ws"],
                   stream=0)
     assert ei.value.status == 2 and "GPU" in str(ei.value)
+
+
+def test_fp32_scale_precisions(B):
+    """fp8_block_f32 / fp8_bwd_f32: the quantized-weight layout and workspaces
+    of the power-of-two precisions (the fp32 scales take the same bytes); the
+    FP8 weight-gradient reading and the row-axis quantizer are refused as
+    unsupported."""
+    import ctypes
+    for f32, p2 in (("fp8_block_f32", "fp8_block"), ("fp8_bwd_f32", "fp8_bwd")):
+        assert B.moe_get_wq_layout(_shape(B, precision=f32)) == B.moe_get_wq_layout(_shape(B, precision=p2))
+        assert B.moe_workspace_size(_shape(B, precision=f32)) == B.moe_workspace_size(_shape(B, precision=p2))
+        with pytest.raises(B.MoEError) as ei:
+            B.moe_workspace_size(_shape(B, precision=f32, wgrad="fp8"))
+        assert ei.value.status == 9
+        P = 1 << 20
+        s = _shape(B, precision=f32)
+        assert _raw_call(B, "moe_quantize_tokens", ctypes.byref(s), P, 2048, 2048, P, P, P, P, P, None) == 9
+        # fp32 scales need 4-byte alignment
+        assert _raw_call(B, "moe_quantize_rows", ctypes.byref(s), P, 4, 256, P, P + 2, None) == 3

@@ -22,7 +22,9 @@ from tests.helpers import TOL_FP8, max_rel_err
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-MODES = ["fp8_block", "mxfp8", "fp8_bwd"]
+MODES = ["fp8_block", "mxfp8", "fp8_bwd"]            # E8M0 (power-of-two) scales
+F32_MODES = ["fp8_block_f32", "fp8_bwd_f32"]         # fp32 block scales
+ALL_MODES = MODES + F32_MODES
 
 
 def _say(msg):
@@ -70,7 +72,7 @@ def _awkward_rows(rows, K, seed):
     return x.to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("mode", ALL_MODES)
 def test_quantize_rows_bit_exact(B, mode):
     rows, K = 300, 1024
     _say(f"case quantize_rows mode={mode} rows={rows} K={K}")
@@ -80,6 +82,13 @@ def test_quantize_rows_bit_exact(B, mode):
     scales = torch.empty(rows, K // 32, dtype=torch.uint8, device=DEV)
     B.moe_quantize_rows(shape, x.to(DEV), rows, K, codes, scales)
     torch.cuda.synchronize()
+    if mode in F32_MODES:  # codes and the float scales [rows, K/128] bit for bit
+        rc, rs, _ = f8.quantize_along_last_f32(orc.as_f64(x), 128)
+        gc, gs = _np(codes), _np(scales).view(np.float32)
+        bad = np.argwhere(gc != rc)
+        assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[:5].tolist()}"
+        assert np.array_equal(gs.view(np.uint32), rs.astype(np.float32).view(np.uint32))
+        return
     block, rule = _rule(mode)
     rc, re, _ = f8.quantize_along_last(orc.as_f64(x), block, rule)
     rs = np.repeat(re + 127, block // 32, axis=-1).astype(np.uint8)
@@ -96,7 +105,7 @@ def _tile_bytes(e, transpose):
     return np.repeat(np.repeat(e + 127, 128, axis=1), 4, axis=2).astype(np.uint8)
 
 
-@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("mode", ALL_MODES)
 def test_quantize_weights_bit_exact(B, mode):
     E, H, I = 3, 512, 384
     _say(f"case quantize_weights mode={mode} E={E} H={H} I={I}")
@@ -122,11 +131,16 @@ def test_quantize_weights_bit_exact(B, mode):
             src = np.swapaxes(w, -1, -2) if transpose else w
             c, e, _ = f8.quantize_along_last(src, 32, "mx_floor")
             return c, (e + 127).astype(np.uint8)
+        if mode in F32_MODES:  # one float per (row, 128 codes): the tile's scale on each of its rows
+            c, sc, _ = f8.quantize_tiles_f32(w, 128)
+            sc = np.swapaxes(sc, -1, -2) if transpose else sc
+            return (np.swapaxes(c, -1, -2) if transpose else c), \
+                np.repeat(sc.astype(np.float32), 128, axis=1).view(np.uint8)
         c, e, _ = f8.quantize_tiles(w, 128, "pow2_ceil")
         return (np.swapaxes(c, -1, -2) if transpose else c), _tile_bytes(e, transpose)
 
     uses = [("w2t", w2, True), ("w13t", w13, True)]
-    if mode != "fp8_bwd":
+    if mode not in ("fp8_bwd", "fp8_bwd_f32"):
         uses += [("w13", w13, False), ("w2", w2, False)]
     else:
         assert L["w13"] == 2 ** 64 - 1 and L["w2"] == 2 ** 64 - 1
@@ -231,7 +245,7 @@ SMALL = [
 # quantization of 1024 experts takes ~25 s, so it runs once per mode here)
 MAXE = inputs.LayerConfig("max_experts_zipf", 700, 256, 128, 1024, 8, "zipf", "bf16", 16, zipf_s=1.1,
                           zipf_cold=100)
-CASES = [(c, m) for c in SMALL for m in MODES] + [(MAXE, "mxfp8")]
+CASES = [(c, m) for c in SMALL for m in ALL_MODES] + [(MAXE, "mxfp8")]
 
 _WQ = {}
 
@@ -245,13 +259,10 @@ def _oracle_wq(cfg, mode, d):
         _WQ[key] = f8.quantize_weights(d["W13"], d["W2"], mode)
     return _WQ[key]
 # Hot experts whose weight-gradient tiles are split along the expert's rows
-# (2813 rows into 4 ranges, 1179 into 4). Blockwise only: the FP8 dW kernel's
-# split handling is the same for both scale rules, and with 32-row MX blocks
-# the kernel's bf16 operands (rounded before quantization, unlike the fp64
-# oracle's) already flip enough codes over these long reductions to reach
-# the tolerance (about 4.4e-2 from that rounding alone, on the CPU).
+# (2813 rows into 4 ranges, 1179 into 4), under both row-block rules (128
+# rows, power-of-two; 32 rows, MX).
 HOT = inputs.LayerConfig("hot", 8192, 512, 384, 32, 1, "zipf", "bf16", 21, zipf_s=1.2, zipf_cold=8)
-WGRAD_CASES = CASES + [(HOT, "fp8_block")]
+WGRAD_CASES = [(c, m) for c, m in CASES if m in MODES] + [(HOT, "fp8_block"), (HOT, "mxfp8")]
 
 
 @pytest.mark.parametrize("cfg,mode", CASES, ids=[f"{c.name}-{m}" for c, m in CASES])
@@ -264,7 +275,7 @@ def test_fp8_layer_matches_oracle_elementwise(B, cfg, mode):
 DUP = inputs.LayerConfig("dup", 500, 512, 384, 6, 3, "uniform", "bf16", 31)
 
 
-@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("mode", ALL_MODES)
 def test_fp8_duplicate_expert_in_one_token_elementwise(B, mode):
     """Every third token names one expert in two of its slots (two rows,
     summed)."""
@@ -406,7 +417,7 @@ def _sampled_check(B, cfg, n_tokens=64, wgrad="bf16"):
     _say(f"  gpu done {time.time() - t0:.1f}s")
     toks = np.sort(np.random.default_rng(1000 + cfg.seed).choice(cfg.T, n_tokens, replace=False))
     experts = _check_experts(counts)
-    keys = ("W2b", "W13b") if mode == "fp8_bwd" else ("W13q", "W2q", "W2b", "W13b")
+    keys = ("W2b", "W13b") if mode in f8.BF16_FORWARD_MODES else ("W13q", "W2q", "W2b", "W13b")
     cache = _expert_wq(cfg, mode, d, set(idx_h[toks].reshape(-1).tolist()) | set(experts), keys)
     _say(f"  {len(cache)} experts' weights quantized by the oracle ({time.time() - t0:.1f}s)")
 
@@ -448,20 +459,32 @@ def _sampled_check(B, cfg, n_tokens=64, wgrad="bf16"):
         assert torch.isfinite(out[k].float()).all(), k
 
 
-def test_ep8_share_fp8_block_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["ep8_share"])
+def test_ep8_share_fp8_block_f32_sampled(B):
+    cfg = inputs.CONFIGS["ep8_share"]
+    assert cfg.precision == "fp8_block_f32"      # the workload's stated fp32 block scales
+    _sampled_check(B, cfg)
 
 
-def test_ep8_share_fp8_block_fp8_wgrad_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["ep8_share"], wgrad="fp8")
+def test_ep8_share_fp8_block_pow2_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["ep8_share"].scaled(precision="fp8_block"))
 
 
-def test_qwen3_235b_fp8_bwd_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["qwen3_235b"])
+def test_ep8_share_fp8_block_pow2_fp8_wgrad_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["ep8_share"].scaled(precision="fp8_block"), wgrad="fp8")
 
 
-def test_qwen3_235b_fp8_bwd_fp8_wgrad_sampled(B):
-    _sampled_check(B, inputs.CONFIGS["qwen3_235b"], wgrad="fp8")
+def test_qwen3_235b_fp8_bwd_f32_sampled(B):
+    cfg = inputs.CONFIGS["qwen3_235b"]
+    assert cfg.precision == "fp8_bwd_f32"
+    _sampled_check(B, cfg)
+
+
+def test_qwen3_235b_fp8_bwd_pow2_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["qwen3_235b"].scaled(precision="fp8_bwd"))
+
+
+def test_qwen3_235b_fp8_bwd_pow2_fp8_wgrad_sampled(B):
+    _sampled_check(B, inputs.CONFIGS["qwen3_235b"].scaled(precision="fp8_bwd"), wgrad="fp8")
 
 
 def test_qwen3_30b_zipf_mxfp8_sampled(B):
