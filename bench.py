@@ -121,8 +121,9 @@ def parse():
                     help="weight-gradient GEMMs on bf16 operands, or (FP8 precisions) on operands "
                          "quantized along each expert's rows")
     ap.add_argument("--router", default="none", choices=["none", "uniform", "skewed"],
-                    help="include the router step (moe_route before the forward, moe_route_bwd after the "
-                         "backward) on synthetic logits: N(0,1), or N(0,1) with a Zipf-like per-expert bias")
+                    help="include the router step (moe_fwd_logits: the router fused with the permutation's "
+                         "first pass; moe_route_bwd after the backward) on synthetic logits: N(0,1), or N(0,1) "
+                         "with a Zipf-like per-expert bias")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     return ap.parse_args()
@@ -295,9 +296,10 @@ def main():
             B.quantize_weights(buf, d["W13"], d["W2"])
         if evs:
             evs[3].record()
-        if args.router != "none":
-            B.moe_route(shape, logits, True, d["topk_idx"], d["topk_w"])
-        B.forward(buf, d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], y=y)
+        if args.router != "none":  # the router fused with the permutation's first pass
+            B.forward_logits(buf, d["x"], logits, True, d["topk_idx"], d["topk_w"], d["W13"], d["W2"], y=y)
+        else:
+            B.forward(buf, d["x"], d["topk_idx"], d["topk_w"], d["W13"], d["W2"], y=y)
         if evs:
             evs[1].record()
         if not fwd_only:

@@ -76,6 +76,8 @@ _SIGS = {
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P]),
     "moe_fwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                ctypes.c_size_t, _P]),
+    "moe_fwd_logits": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                                      _P, _P, ctypes.c_size_t, _P]),
     "moe_bwd": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _P, ctypes.c_size_t, _P]),
     "moe_permute_noalloc": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P]),
@@ -271,6 +273,24 @@ def moe_fwd(shape, x, topk_idx, topk_w, W13, W2, wq, y, saved, ws, stream=None) 
                          _stream(stream)), "moe_fwd")
 
 
+def moe_fwd_logits(shape, x, logits, renorm, topk_idx, topk_w, W13, W2, wq, y, saved, ws, stream=None) -> None:
+    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    f, s, _ = moe_workspace_size(shape)
+    _want(x, "x", _BF16, T * H, optional=T == 0)
+    _want(logits, "logits", _F32, T * E, optional=T == 0)
+    _want(topk_idx, "topk_idx", _I32, T * k, optional=T == 0)
+    _want(topk_w, "topk_w", _F32, T * k, optional=T == 0)
+    _want(W13, "W13", _BF16, E * 2 * I * H)
+    _want(W2, "W2", _BF16, E * H * I)
+    _want(wq, "wq", _U8, moe_get_wq_layout(shape)["total"], optional=True)
+    _want(y, "y", _BF16, T * H, optional=T == 0)
+    _want(saved, "saved", _U8, s, optional=True)
+    _want(ws, "ws", _U8, f)
+    _check(lib().moe_fwd_logits(ctypes.byref(shape), _ptr(x), _ptr(logits), int(bool(renorm)), _ptr(topk_idx),
+                                _ptr(topk_w), _ptr(W13), _ptr(W2), _ptr(wq), _ptr(y), _ptr(saved), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)), "moe_fwd_logits")
+
+
 def moe_bwd(shape, dy, x, topk_idx, topk_w, W13, W2, wq, saved, dx, d_topk_w, dW13, dW2, ws,
             stream=None) -> None:
     T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
@@ -369,6 +389,17 @@ def forward(buf: LayerBuffers, x, topk_idx, topk_w, W13, W2, y=None, training=Tr
     if y is None:
         y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=x.device)
     moe_fwd(s, x, topk_idx, topk_w, W13, W2, buf.wq, y, buf.saved if training else None, buf.fwd_ws, stream)
+    return y
+
+
+def forward_logits(buf: LayerBuffers, x, logits, renorm, topk_idx, topk_w, W13, W2, y=None, training=True,
+                   stream=None):
+    """Forward with the router fused in: writes topk_idx and topk_w."""
+    s = buf.shape
+    if y is None:
+        y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=x.device)
+    moe_fwd_logits(s, x, logits, renorm, topk_idx, topk_w, W13, W2, buf.wq, y, buf.saved if training else None,
+                   buf.fwd_ws, stream)
     return y
 
 

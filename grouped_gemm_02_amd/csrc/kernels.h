@@ -27,6 +27,7 @@ struct TimedLaunch {
 };
 
 // ---------------------------------------------------------------- permute
+constexpr int kPermChunk = 1024;  // pairs per chunk of the permutation's passes
 int permute_num_chunks(int64_t n);
 size_t permute_scratch_bytes(int64_t n, int E);
 // When wrow != nullptr also wrow[row_of[f]] = topk_w[f].
@@ -35,11 +36,13 @@ hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
                           hipStream_t st, KernelTimer* timer, const float* topk_w = nullptr,
                           float* wrow = nullptr);
 
-// The same with the status word and the chunk table given apart.
+// The same with the status word and the chunk table given apart. With
+// hist_done the table already holds the chunks' per-expert counts (the
+// router's fused pass wrote them) and the histogram launch is skipped.
 hipError_t launch_permute_split(const int32_t* idx, int64_t n, int E, int32_t* counts, int32_t* offsets,
                                 int32_t* row_of, int32_t* src_of, int32_t* status, int32_t* chunk_tab,
                                 hipStream_t st, KernelTimer* timer, const float* topk_w = nullptr,
-                                float* wrow = nullptr);
+                                float* wrow = nullptr, bool hist_done = false);
 // A fixed chunk table in device memory the library owns (no allocation):
 // kStaticPermuteWords int32 per device, found once per device with
 // hipGetSymbolAddress; *out is its address on the current device.
@@ -145,6 +148,10 @@ hipError_t launch_gemm_dw_fp8(const GemmProblem& p, const uint8_t* pcodes, const
 // renorm); the backward writes dz fp32 [T, E] = dL/dlogits from dw = dL/dw.
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int32_t* idx, float* w,
                         hipStream_t st, KernelTimer* timer);
+// the router and the permutation's histogram pass in one launch: writes idx,
+// w and the chunk table [nchunk][E+1] of launch_permute_split (hist_done)
+hipError_t launch_route_hist(const float* logits, int64_t T, int E, int k, int renorm, int32_t* idx, float* w,
+                             int32_t* chunk_hist, hipStream_t st, KernelTimer* timer);
 hipError_t launch_route_bwd(const float* logits, int64_t T, int E, int k, int renorm, const int32_t* idx,
                             const float* w, const float* dw, float* dz, hipStream_t st, KernelTimer* timer);
 

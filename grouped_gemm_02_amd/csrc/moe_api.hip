@@ -414,17 +414,25 @@ moe_status moe_quantize_tokens(const moe_shape* s, const void* in, int64_t ld, i
                                            "quant_tokens"));
 }
 
-moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
-                   const float* topk_w, const void* W13, const void* W2, const void* wq,
-                   void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward; with logits != nullptr the router runs first, fused with the
+// permutation's histogram pass, and writes topk_idx and topk_w.
+moe_status fwd_impl(const moe_shape* s, const void* x, const float* logits, int32_t renorm, int32_t* topk_idx,
+                    float* topk_w, const void* W13, const void* W2, const void* wq, void* y, void* saved, void* ws,
+                    size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->precision == MOE_BF16 && wq) return MOE_ERR_PRECISION;
   const bool f8 = fp8_forward(*s);
   const int64_t Tk = s->T * s->k;
-  if (!W13 || !W2 || !ws || (f8 && !wq) || (s->T > 0 && (!x || !topk_idx || !topk_w || !y)))
+  // the FP8 forwards read only the quantized weights
+  if ((!f8 && (!W13 || !W2)) || !ws || (f8 && !wq) ||
+      (s->T > 0 && (!x || !topk_idx || !topk_w || !y)))
     return MOE_ERR_NULL;
-  const void* ptrs[] = {x, topk_idx, topk_w, W13, W2, y, saved, ws, wq};
+  const void* ptrs[] = {x, topk_idx, topk_w, W13, W2, y, saved, ws, wq, logits};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_ALIGN;
   const FwdLayout FL = fwd_layout(*s);
@@ -446,8 +454,15 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
 
   std::lock_guard<std::mutex> lk(g_timer_mu);
   KernelTimer* tm = timer();
-  hipError_t e = launch_permute(topk_idx, Tk, int(s->E), counts, offsets, row_of, src_of,
-                                at<char>(ws, FL.perm), hs, tm, topk_w, wrow);
+  int32_t* perm_status = at<int32_t>(ws, FL.perm);
+  int32_t* chunk_tab = at<int32_t>(ws, FL.perm + 256);
+  hipError_t e = hipSuccess;
+  if (logits) {
+    e = launch_route_hist(logits, s->T, int(s->E), int(s->k), renorm, topk_idx, topk_w, chunk_tab, hs, tm);
+    if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  }
+  e = launch_permute_split(topk_idx, Tk, int(s->E), counts, offsets, row_of, src_of, perm_status, chunk_tab, hs, tm,
+                           topk_w, wrow, logits != nullptr);
   if (e != hipSuccess || s->T == 0) return launch_status(e);
   GemmProblem gp{s->T, s->H, s->I, s->E, s->k, effective_cus(*s, cus), counts, offsets, src_of, topk_w, wrow};
   GemmOperand gx{x, nullptr}, gw13{W13, nullptr}, ga{act, nullptr}, gw2{W2, nullptr};
@@ -483,6 +498,26 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
   return launch_status(e);
 }
 
+}  // namespace
+
+extern "C" {
+
+moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                   const float* topk_w, const void* W13, const void* W2, const void* wq,
+                   void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  // read only: without logits fwd_impl writes neither routing buffer
+  return fwd_impl(s, x, nullptr, 0, const_cast<int32_t*>(topk_idx), const_cast<float*>(topk_w), W13, W2, wq, y,
+                  saved, ws, ws_bytes, stream);
+}
+
+moe_status moe_fwd_logits(const moe_shape* s, const void* x, const float* logits, int32_t renorm,
+                          int32_t* topk_idx, float* topk_w, const void* W13, const void* W2, const void* wq,
+                          void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  if (s && s->T > 0 && !logits) return MOE_ERR_NULL;
+  return fwd_impl(s, x, s && s->T > 0 ? logits : nullptr, renorm, topk_idx, topk_w, W13, W2, wq, y, saved, ws,
+                  ws_bytes, stream);
+}
+
 moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int32_t* topk_idx,
                    const float* topk_w, const void* W13, const void* W2, const void* wq,
                    const void* saved, void* dx, float* d_topk_w, void* dW13, void* dW2, void* ws,
@@ -493,7 +528,8 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
   if (s->precision == MOE_FP8_FP4) return MOE_ERR_PRECISION;  // an inference forward: no backward
   const bool f8 = fp8_backward(*s);
   (void)topk_idx;  // the permutation comes from `saved`
-  if (!W13 || !W2 || !saved || !dW13 || !dW2 || !ws || (f8 && !wq) ||
+  // the FP8 backwards read only the quantized weights
+  if ((!f8 && (!W13 || !W2)) || !saved || !dW13 || !dW2 || !ws || (f8 && !wq) ||
       (s->T > 0 && (!dy || !x || !topk_w || !dx || !d_topk_w)))
     return MOE_ERR_NULL;
   const void* ptrs[] = {dy, x, topk_idx, topk_w, W13, W2, saved, dx, d_topk_w, dW13, dW2, ws, wq};

@@ -28,6 +28,7 @@ namespace moe {
 constexpr int kPermThreads = 256;
 constexpr int kPermItems = 4;
 constexpr int kChunk = kPermThreads * kPermItems;  // 1024 pairs per workgroup
+static_assert(kChunk == kPermChunk, "the router's fused histogram uses the same chunks");
 constexpr int kPermWaves = kPermThreads / kWave;
 
 __global__ __launch_bounds__(kPermThreads) void permute_hist(const int32_t* __restrict__ idx,
@@ -191,11 +192,12 @@ hipError_t launch_permute(const int32_t* idx, int64_t n, int E, int32_t* counts,
 
 hipError_t launch_permute_split(const int32_t* idx, int64_t n, int E, int32_t* counts, int32_t* offsets,
                                 int32_t* row_of, int32_t* src_of, int32_t* status, int32_t* chunk_tab,
-                                hipStream_t st, KernelTimer* timer, const float* topk_w, float* wrow) {
+                                hipStream_t st, KernelTimer* timer, const float* topk_w, float* wrow,
+                                bool hist_done) {
   const int nchunk = permute_num_chunks(n);
   int id_bits = 0;
   while ((1 << id_bits) <= E) ++id_bits;  // ids 0..E (E marks invalid) fit
-  if (nchunk > 0) {
+  if (nchunk > 0 && !hist_done) {
     TimedLaunch t(timer, "permute_hist", st);
     hipLaunchKernelGGL(permute_hist, dim3(nchunk), dim3(kPermThreads), (E + 1) * 4, st, idx, n,
                        E, chunk_tab);

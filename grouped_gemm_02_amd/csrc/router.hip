@@ -40,16 +40,15 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
   }
 }
 
-// PER logits per lane: E <= 64 * PER (instantiated for 2, 4 and 16)
+// Routes token t (one wave): the k experts with the largest logits in
+// descending order (ties to the lower id) and their weights. Slot j ends in
+// lane j % 64, register j / 64: sel_i[i] (expert) and sel_w[i] (weight) for
+// j = lane + 64 i < k. PER logits per lane: E <= 64 * PER.
 template <int PER>
-__global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(const float* __restrict__ logits, int64_t T, int E,
-                                                                 int k, int renorm, int32_t* __restrict__ idx,
-                                                                 float* __restrict__ w) {
+__device__ __forceinline__ void route_token(const float* __restrict__ z, int E, int k, int renorm, int (&sel_i)[PER],
+                                            float (&sel_w)[PER]) {
   constexpr int kRouteMaxPer = PER;
-  const int64_t t = int64_t(blockIdx.x) * kRouteWaves + (threadIdx.x >> 6);
-  if (t >= T) return;  // the whole wave
   const int lane = lane_id();
-  const float* z = logits + t * E;
   float v[kRouteMaxPer];
 #pragma unroll
   for (int i = 0; i < kRouteMaxPer; ++i) v[i] = lane + 64 * i < E ? z[lane + 64 * i] : -INFINITY;
@@ -64,7 +63,6 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(const float* __
   // selection: slot j is kept by lane j % 64 in its register j / 64
   uint32_t taken = 0;
   float sel_v[kRouteMaxPer];
-  int sel_i[kRouteMaxPer];
   float first = 0.f;  // the largest selected logit
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
@@ -97,11 +95,61 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(const float* __
     ref = first;
   }
 #pragma unroll
-  for (int i = 0; i < kRouteMaxPer; ++i) {
+  for (int i = 0; i < kRouteMaxPer; ++i)
+    if (lane + 64 * i < k) sel_w[i] = expf(sel_v[i] - ref) / den;
+}
+
+template <int PER>
+__global__ __launch_bounds__(64 * kRouteWaves) void route_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                                 int k, int renorm, int32_t* __restrict__ idx,
+                                                                 float* __restrict__ w) {
+  const int64_t t = int64_t(blockIdx.x) * kRouteWaves + (threadIdx.x >> 6);
+  if (t >= T) return;  // the whole wave
+  int sel_i[PER];
+  float sel_w[PER];
+  route_token<PER>(logits + t * E, E, k, renorm, sel_i, sel_w);
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
     const int j = lane + 64 * i;
     if (j < k) {
       idx[t * k + j] = sel_i[i];
-      w[t * k + j] = expf(sel_v[i] - ref) / den;
+      w[t * k + j] = sel_w[i];
+    }
+  }
+}
+
+// The router fused with the permutation's first pass: one wave per token
+// as route_kernel, and each selected pair f is also counted in its chunk's
+// row of the chunk table (chunks of kPermChunk pairs: the counts
+// permute_scan reads). The table starts at zero (zero_table_kernel); the
+// counts are integer atomics, so the table does not depend on their order.
+// Column E (ids outside [0, E)) stays 0: the router names experts in [0, E).
+__global__ void zero_table_kernel(int32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
+template <int PER>
+__global__ __launch_bounds__(64 * kRouteWaves) void route_hist_kernel(const float* __restrict__ logits, int64_t T,
+                                                                      int E, int k, int renorm,
+                                                                      int32_t* __restrict__ idx,
+                                                                      float* __restrict__ w,
+                                                                      int32_t* __restrict__ chunk_hist) {
+  const int64_t t = int64_t(blockIdx.x) * kRouteWaves + (threadIdx.x >> 6);
+  if (t >= T) return;  // the whole wave
+  int sel_i[PER];
+  float sel_w[PER];
+  route_token<PER>(logits + t * E, E, k, renorm, sel_i, sel_w);
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = lane + 64 * i;
+    if (j < k) {
+      const int64_t f = t * k + j;
+      idx[f] = sel_i[i];
+      w[f] = sel_w[i];
+      atomicAdd(chunk_hist + (f / kPermChunk) * (E + 1) + sel_i[i], 1);
     }
   }
 }
@@ -187,6 +235,27 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm
     hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, st, logits, T, E, k, renorm, idx, w);
   else
     hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, st, logits, T, E, k, renorm, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_hist(const float* logits, int64_t T, int E, int k, int renorm, int32_t* idx, float* w,
+                             int32_t* chunk_hist, hipStream_t st, KernelTimer* timer) {
+  if (T <= 0) return hipSuccess;
+  const int64_t words = (T * k + kPermChunk - 1) / kPermChunk * (E + 1);
+  {
+    TimedLaunch tl(timer, "route_table_zero", st);
+    const int64_t g = (words + 255) / 256;
+    hipLaunchKernelGGL(zero_table_kernel, dim3(static_cast<unsigned>(g < 1024 ? g : 1024)), dim3(256), 0, st,
+                       chunk_hist, words);
+  }
+  TimedLaunch tl(timer, "route_hist", st);
+  const dim3 grid(static_cast<unsigned>((T + kRouteWaves - 1) / kRouteWaves)), block(64 * kRouteWaves);
+  if (E <= 128)
+    hipLaunchKernelGGL(route_hist_kernel<2>, grid, block, 0, st, logits, T, E, k, renorm, idx, w, chunk_hist);
+  else if (E <= 256)
+    hipLaunchKernelGGL(route_hist_kernel<4>, grid, block, 0, st, logits, T, E, k, renorm, idx, w, chunk_hist);
+  else
+    hipLaunchKernelGGL(route_hist_kernel<16>, grid, block, 0, st, logits, T, E, k, renorm, idx, w, chunk_hist);
   return hipGetLastError();
 }
 

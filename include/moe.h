@@ -296,7 +296,9 @@ moe_status moe_route_bwd(const moe_shape* s, const float* logits, const int32_t*
  *   topk_idx int32 [T, k]       expert of each pair
  *   topk_w   fp32  [T, k]       routing weight of each pair, used as given
  *   W13      bf16  [E, 2I, H]   rows [0,I) gate (W1), rows [I,2I) up (W3)
- *   W2       bf16  [E, H, I]
+ *   W2       bf16  [E, H, I]    (W13 and W2 may be NULL where the forward
+ *                               reads only wq: MOE_FP8_BLOCK, MOE_MXFP8,
+ *                               MOE_FP8_FP4, MOE_FP8_BLOCK_F32)
  *   wq       quantized weights (moe_quantize_weights of this W13, W2):
  *            required for MOE_FP8_BLOCK and MOE_MXFP8, ignored for
  *            MOE_FP8_BWD, must be NULL for MOE_BF16 (else MOE_ERR_PRECISION)
@@ -313,10 +315,25 @@ moe_status moe_fwd(const moe_shape* s, const void* x, const int32_t* topk_idx,
                    const float* topk_w, const void* W13, const void* W2, const void* wq,
                    void* y, void* saved, void* ws, size_t ws_bytes, void* stream);
 
+/* The forward with the router step in front of it, fused with the
+ * permutation: one pass routes each token's fp32 logits [T, E] exactly as
+ * moe_route with the same renorm (the routing is the step the pages keep out
+ * of their measured layer: ic.work analysis, section on the benchmark's
+ * idealised assumptions) and counts, per chunk of 1024 pairs, the rows each
+ * expert receives, which is the permutation's first pass; the rest is
+ * moe_fwd. topk_idx int32 [T, k] and topk_w fp32 [T, k] are outputs here,
+ * bit-identical to moe_route's, for moe_bwd and moe_route_bwd. Everything
+ * else (buffers, errors, precisions) as moe_fwd; logits may be NULL only
+ * when T == 0. */
+moe_status moe_fwd_logits(const moe_shape* s, const void* x, const float* logits, int32_t renorm,
+                          int32_t* topk_idx, float* topk_w, const void* W13, const void* W2, const void* wq,
+                          void* y, void* saved, void* ws, size_t ws_bytes, void* stream);
+
 /* Backward of the layer for L = <dY, y> (ic.work analysis, "From 3.11x to
  * 1.32x": the backward produces activation and weight gradients).
  *   dy       bf16 [T, H]
- *   x, topk_idx, topk_w, W13, W2: as passed to moe_fwd
+ *   x, topk_idx, topk_w, W13, W2: as passed to moe_fwd (W13 and W2 may be
+ *            NULL for every FP8 precision: its backward reads only wq)
  *   wq       quantized weights: required for every FP8 precision, must be
  *            NULL for MOE_BF16
  *   saved    filled by moe_fwd with the same inputs

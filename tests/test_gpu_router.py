@@ -78,3 +78,41 @@ def test_skew_concentrates_tokens(B):
     counts = np.bincount(idx.reshape(-1), minlength=E)
     assert counts.max() > 4 * T * k / E
     assert (idx[:, :, None] != idx[:, None, :]).sum() == T * k * (k - 1)  # distinct per token
+
+
+FUSED = [
+    # (T, E, k, renorm, skew, precision)
+    (2000, 128, 8, True, 1.2, "bf16"),    # skewed, chunks of 128 tokens
+    (1333, 64, 3, False, 0.0, "bf16"),    # 1024 % k != 0: tokens straddle chunks
+    (700, 1024, 8, True, 0.0, "mxfp8"),   # the largest expert count, FP8 forward
+    (257, 40, 1, True, 0.5, "bf16"),      # top-1: rows go straight to their tokens
+]
+
+
+@pytest.mark.parametrize("T,E,k,renorm,skew,prec", FUSED)
+def test_forward_with_fused_router_matches_route_then_forward(B, T, E, k, renorm, skew, prec):
+    """moe_fwd_logits (the router fused with the permutation's histogram pass)
+    against moe_route followed by moe_fwd: routing, permutation, saved
+    buffers and y bit for bit; the backward from either is then the same."""
+    print(f"case fused router T={T} E={E} k={k} renorm={renorm} skew={skew} precision={prec}", flush=True)
+    H, I = 256, 128
+    z = inputs.make_router_logits(T, E, 70 + T, DEV, skew)
+    cfg = inputs.LayerConfig("fused", T, H, I, E, k, "uniform", prec, 71)
+    d = inputs.make_layer_inputs(cfg, DEV)
+    shape = B.make_shape(T, H, I, E, k, prec)
+    ref_buf, got_buf = B.LayerBuffers.allocate(shape), B.LayerBuffers.allocate(shape)
+    for b in (ref_buf, got_buf):
+        b.saved.fill_(0xEE)
+        B.quantize_weights(b, d["W13"], d["W2"])
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, k), -7.0, dtype=torch.float32, device=DEV)
+    B.moe_route(shape, z, renorm, idx, w)
+    y_ref = B.forward(ref_buf, d["x"], idx, w, d["W13"], d["W2"])
+    idx2 = torch.full((T, k), -9, dtype=torch.int32, device=DEV)
+    w2 = torch.full((T, k), -9.0, dtype=torch.float32, device=DEV)
+    y = B.forward_logits(got_buf, d["x"], z, renorm, idx2, w2, d["W13"], d["W2"])
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(w, w2)
+    assert torch.equal(y, y_ref)
+    assert torch.equal(ref_buf.saved, got_buf.saved)
+    assert B.moe_read_status(got_buf.fwd_ws) == 0
