@@ -662,6 +662,15 @@ __device__ __forceinline__ void finish_f32s(Acc& acc) {
     }
 }
 
+// The slab's 4 scale bytes of this lane's row, one LDS word (byte 2s + h is
+// the scale of k-block h of step s)
+__device__ __forceinline__ uint32_t scale_word8(const uint16_t* lds, int ent0) {
+  return *reinterpret_cast<const uint32_t*>(lds + (ent0 + (lane_id() & 31)) * LDK + BK);
+}
+__device__ __forceinline__ int scale_byte8(uint32_t w, int s) {
+  return int((w >> (8 * (2 * s + (lane_id() >> 5)))) & 0xFFu);
+}
+
 template <bool W4 = false, bool F32S = false>
 __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
   if constexpr (F32S) {
@@ -670,23 +679,32 @@ __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_
     return;
   }
   const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
+  // scale words of the slab: one LDS read per row block
+  uint32_t qsw[TN], psw[TM];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) qsw[j] = scale_word8(ldsQ, qn0 + 32 * j);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) psw[i] = scale_word8(ldsP, pm0 + 32 * i);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     i32x8 qf[TN];
-    int qs[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      qf[j] = W4 ? frag4(ldsQ, qn0 + 32 * j, s) : frag8(ldsQ, qn0 + 32 * j, s);
-      qs[j] = scale8(ldsQ, qn0 + 32 * j, s);
-    }
+    for (int j = 0; j < TN; ++j) qf[j] = W4 ? frag4(ldsQ, qn0 + 32 * j, s) : frag8(ldsQ, qn0 + 32 * j, s);
+    // the P fragments are software-pipelined: row block i+1's read is issued
+    // before row block i's MFMAs, so its LDS latency hides behind them
+    i32x8 pf = frag8(ldsP, pm0, s);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const i32x8 pf = frag8(ldsP, pm0 + 32 * i, s);
-      const int ps = scale8(ldsP, pm0 + 32 * i, s);
+      i32x8 pn;
+      if (i + 1 < TM) pn = frag8(ldsP, pm0 + 32 * (i + 1), s);
+      __builtin_amdgcn_sched_barrier(0);
+      const int ps = scale_byte8(psw[i], s);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[j], pf, acc.c[i][j], W4 ? 4 : 0, 0, 0,
-                                                                      qs[j], 0, ps);
+                                                                      scale_byte8(qsw[j], s), 0, ps);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < TM) pf = pn;
     }
   }
 }
