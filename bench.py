@@ -87,17 +87,18 @@ KERNEL_FN = {
 def kernel_peak(name: str) -> float:
     # an FP8 x FP4 product runs at the FP8 rate (the wider operand's)
     return PEAK_FP8_TFLOPS if name.endswith(("_fp8", "_fp8_fp4", "_fp8f32")) else PEAK_BF16_TFLOPS
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_qwen3_30b_bf16.json")
-WORKLOAD_KEY = ["qwen3_30b/bf16"]   # the workload the committed traffic summary was taken on
+WORKLOAD_KEY = ["qwen3_30b/bf16"]   # <config>/<precision>[/...] of this run
 
 
 def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None when there is none or the kernels changed since it was taken."""
+    """HBM bytes per launch of `kernel` from the committed counter summary of
+    this workload (profiles/gemm_traffic_<config>_<precision>.json), or None
+    when there is none or the kernels changed since it was taken."""
     from grouped_gemm_02_amd import profile_summary
-    if not os.path.exists(TRAFFIC_FILE):
+    path = os.path.join(ROOT, "profiles", "gemm_traffic_" + "_".join(WORKLOAD_KEY[0].split("/")[:2]) + ".json")
+    if not os.path.exists(path):
         return None
-    d = json.load(open(TRAFFIC_FILE))
+    d = json.load(open(path))
     if d.get("source_sha256") != profile_summary.source_hash():
         return None
     if d.get("workload", "qwen3_30b/bf16") != WORKLOAD_KEY[0]:

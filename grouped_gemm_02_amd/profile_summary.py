@@ -3,6 +3,8 @@
     python -m grouped_gemm_02_amd.profile_summary stats <kernel_stats.csv> <out.txt> --cmd "<command>"
     python -m grouped_gemm_02_amd.profile_summary traffic <fetch_counter_collection.csv> \
         <write_counter_collection.csv> <out.json> --cmd "<command>"
+    python -m grouped_gemm_02_amd.profile_summary mfma <counter_collection.csv> <out.txt> --cmd "<command>" \
+        --title "<workload>"
 
 `stats` turns the --kernel-trace --stats table into a short text table.
 `traffic` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE, both in KiB per
@@ -93,6 +95,36 @@ def traffic(fetch_csv: str, write_csv: str, out_path: str, cmd: str, copy_bytes:
         json.dump(res, f, indent=1)
 
 
+def mfma(csv_path: str, out_path: str, cmd: str, title: str, simds: int = 1024, xcds: int = 8) -> None:
+    """MFMA utilisation per layer kernel from one --pmc pass of
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over every SIMD) and GRBM_GUI_ACTIVE
+    (summed over the XCDs): busy = mfma / (gui_active / xcds * simds)."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = r["Dispatch_Id"]
+        vals[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    agg = collections.defaultdict(list)
+    for d, v in vals.items():
+        if "moe::" in names[d] and v.get("GRBM_GUI_ACTIVE", 0) > 0:
+            agg[short_name(names[d])].append((v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), v["GRBM_GUI_ACTIVE"]))
+    lines = [f"# rocprofv3 MFMA-busy counters, {title} (one pass)", f"# command: {cmd}",
+             "# values: average per dispatch. GRBM_GUI_ACTIVE is summed over the "
+             f"{xcds} XCDs (the kernel's cycles are gui_active / {xcds});",
+             f"# SQ_VALU_MFMA_BUSY_CYCLES is summed over all {simds} SIMDs; busy = mfma_busy / "
+             f"(gui_active / {xcds} * {simds}).", "#",
+             f"{'kernel':36s} {'mfma_busy_cycles':>17s} {'gui_active':>11s} {'busy':>6s}"]
+    for k in sorted(agg):
+        mb = sum(a for a, _ in agg[k]) / len(agg[k])
+        ga = sum(b for _, b in agg[k]) / len(agg[k])
+        if mb <= 0:
+            continue
+        lines.append(f"{k:36s} {mb:17.0f} {ga:11.0f} {mb / (ga / xcds * simds):6.3f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -107,9 +139,16 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--copy-bytes", type=int, default=1 << 30)
     t.add_argument("--workload", default="qwen3_30b/bf16", help="<config>/<precision> the counters were taken on")
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("out")
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--title", required=True)
     a = ap.parse_args()
     if a.what == "stats":
         stats(a.csv, a.out, a.cmd)
+    elif a.what == "mfma":
+        mfma(a.csv, a.out, a.cmd, a.title)
     else:
         traffic(a.fetch_csv, a.write_csv, a.out, a.cmd, a.copy_bytes, a.workload)
 

@@ -493,3 +493,24 @@ def test_qwen3_30b_zipf_mxfp8_sampled(B):
 
 def test_qwen3_30b_zipf_mxfp8_fp8_wgrad_sampled(B):
     _sampled_check(B, inputs.CONFIGS["zipf"], wgrad="fp8")
+
+
+@pytest.mark.parametrize("mode", ["fp8_block", "mxfp8", "fp8_block_f32", "fp8_bwd_f32"])
+def test_fp8_steps_run_without_bf16_weights(B, mode):
+    """Where a step reads only the quantized weights (every FP8 backward; the
+    FP8 forwards except fp8_bwd's bf16 one), W13 and W2 may be NULL: the
+    results equal those of a call that passes them."""
+    cfg = SMALL[1].scaled(precision=mode)
+    _say(f"case no bf16 weights {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    ref = run_layer(B, cfg, d, mode)
+    shape = B.make_shape(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, mode)
+    buf = B.LayerBuffers.allocate(shape)
+    B.quantize_weights(buf, d["W13"], d["W2"])
+    fwd_w = (d["W13"], d["W2"]) if mode in f8.BF16_FORWARD_MODES else (None, None)
+    y = B.forward(buf, d["x"], d["topk_idx"], d["topk_w"], *fwd_w)
+    got = B.backward(buf, d["dy"], d["x"], d["topk_idx"], d["topk_w"], None, None)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref["y"])
+    for k, g in zip(("dx", "dw", "dW13", "dW2"), got):
+        assert torch.equal(g, ref[k]), k
