@@ -44,6 +44,15 @@ python3 -m grouped_gemm_02_amd.profile_summary traffic "$OUT/pmc_${T8}_fetch/pmc
 python3 -m grouped_gemm_02_amd.profile_summary mfma "$OUT/pmc_${T8}_mfma/pmc_counter_collection.csv" \
   "$PROF/mfma_busy_$T8.txt" --title "EP=8 share of the 30B layer, blockwise FP8 with fp32 scales" \
   --cmd "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $OUT/pmc_${T8}_mfma -o pmc -- python3 bench.py --config ep8_share --steps 2 --warmup 1 --no-cpu-baseline"
+# the other FP8 workloads: MFMA busy
+for t in zipf_mxfp8:zipf:"Qwen3-30B-A3B shape, Zipf(1.2) routing, MXFP8" \
+         qwen3_235b_fp8_bwd_f32:qwen3_235b:"Qwen3-235B-A22B shape, bf16 forward, blockwise FP8 backward with fp32 scales"; do
+  IFS=: read -r tag cfg title <<< "$t"
+  pmc $tag mfma "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE" --config $cfg
+  python3 -m grouped_gemm_02_amd.profile_summary mfma "$OUT/pmc_${tag}_mfma/pmc_counter_collection.csv" \
+    "$PROF/mfma_busy_$tag.txt" --title "$title" \
+    --cmd "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $OUT/pmc_${tag}_mfma -o pmc -- python3 bench.py --config $cfg --steps 2 --warmup 1 --no-cpu-baseline"
+done
 # bf16 (the 30B layer): MFMA busy
 pmc qwen3_30b_bf16 mfma "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE" --config qwen3_30b
 python3 -m grouped_gemm_02_amd.profile_summary mfma "$OUT/pmc_qwen3_30b_bf16_mfma/pmc_counter_collection.csv" \
