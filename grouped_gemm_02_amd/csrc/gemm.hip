@@ -149,6 +149,8 @@ struct KMajorLoaderT {
       *reinterpret_cast<u32x4*>(dst) = st.r[i];
     }
   }
+  // offsets of a k-major slab follow from kt alone (scalar offset)
+  __device__ __forceinline__ void advance(int) {}
   // swizzled only: slab kt straight into LDS; wave w's load i fills rows
   // 8w + 64i .. +7, lane l's 16 bytes landing at byte 16 l of that 1 KB block
   __device__ __forceinline__ void dma(int kt, uint16_t* lds) const {
@@ -213,6 +215,84 @@ struct MNMajorLoader {
   }
 };
 
+// mn-major operand in an unpadded, swizzled layout that loads straight into
+// LDS can write: k-row k of the slab at k * 256 elements (512 bytes, the
+// tile's 256 entities), its 16-byte chunk c (entities 8c .. 8c+7) at slot
+// c ^ 4 (k % 4). The transpose read of a fragment has each 16-lane group
+// read 4 consecutive k-rows at 4 chunks; with the XOR those 16 (row, chunk)
+// pairs fall in 16 different slots of a 256-byte bank window, so the reads
+// are free of bank conflicts without padding. Load i of wave w fills k-rows
+// 2 (8 i + w) and 2 (8 i + w) + 1: lane l writes slot l % 32 of k-row
+// 2 (8 i + w) + l / 32, loading the chunk that belongs there. k-rows past
+// the end (RowFn::valid false) and chunks past the tile's columns get an
+// offset beyond the buffer resource's extent, which the buffer unit reads
+// as zero (into LDS too): the zero-fill costs no instruction.
+//
+// The rows may come from an index array (a gathered operand), and the
+// vector-memory counter retires loads in order, so a wait for an index load
+// issued after a slab's loads would also wait for that slab. Hence the
+// offsets of a slab are built in two steps: dma(kt) issues slab kt and then
+// the index loads of slab kt + 1 (request); advance(kt + 1), called after
+// the slab barrier's vmcnt(0), turns them into offsets. prime(kt) does both
+// at once (a tile's first slab). Slab 0 of a row tile may also go through
+// registers (fetch, store) when the persistent walk prefetches it during the
+// previous tile's epilogue.
+constexpr uint32_t kPastExtent = 0x80000000u;  // beyond any operand's extent (< 2 GiB)
+
+template <class RowFn>
+struct MNMajorLoaderD {
+  static constexpr bool kDirect = true;
+  RowFn fn;
+  __amdgpu_buffer_rsrc_t data;
+  int nchunks = 32;           // 16-byte chunks of the tile that exist (partial last n-tile)
+  uint32_t nxt[kPer];         // byte offsets of this lane's 16 bytes in the next slab
+  typename RowFn::Raw raw[kPer];  // the next slab's row indices as loaded
+
+  __device__ __forceinline__ void set_base(const uint16_t* base, int64_t units) {
+    data = make_rsrc(base, units > 0 ? units * 2 : 0);
+  }
+  __device__ __forceinline__ static int krow(int i) { return 2 * (8 * i + int(threadIdx.x >> 6)) + (lane_id() >> 5); }
+  __device__ __forceinline__ void request(int kt) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) raw[i] = fn.load(kt * BK + krow(i));
+  }
+  __device__ __forceinline__ void advance(int kt) {
+    const int p = lane_id() & 31;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int kr = krow(i);
+      const int c = p ^ (4 * (kr & 3));
+      const int k = kt * BK + kr;
+      nxt[i] = (fn.valid(k) && c < nchunks) ? uint32_t(fn.row(raw[i])) * uint32_t(fn.ld) * 2u + uint32_t(c) * 16u
+                                            : kPastExtent;
+    }
+  }
+  __device__ __forceinline__ void prime(int kt) {
+    request(kt);
+    advance(kt);
+  }
+  // slab kt (advanced) straight into LDS, then the index loads of slab kt + 1
+  __device__ __forceinline__ void dma(int kt, uint16_t* lds) {
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          data, (__attribute__((address_space(3))) void*)(lds + (8 * i + w) * 512), 16, nxt[i], 0, 0, 0);
+    request(kt + 1);
+  }
+  __device__ __forceinline__ void fetch(int kt, Stage& st) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) st.r[i] = __builtin_amdgcn_raw_buffer_load_b128(data, nxt[i], 0, 0);
+    st.ok = ~0u;
+    request(kt + 1);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, const Stage& st) const {
+    const int w = int(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4*>(lds + (8 * i + w) * 512 + lane_id() * 8) = st.r[i];
+  }
+};
+
 // ------------------------------------------------------------------ fragments
 
 // 32 entities x 16 k of a k-major tile: lane holds entity (lane % 32),
@@ -239,6 +319,28 @@ __device__ __forceinline__ bf16x8 frag_mn(const uint16_t* lds, int ent0, int kk)
   const uint16_t* a = lds + k * LDN + n;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a));
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 4 * LDN));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// The same fragment from the swizzled unpadded mn-major layout of
+// MNMajorLoaderD. Rows k and k + 4, and k + 16 kk, have the same k % 4, so
+// all of a sub-tile's reads share one lane offset and differ by constants.
+// That offset is passed through an empty asm operand: otherwise the
+// optimizer splits the address into a chain of pointer steps too long for
+// the compiler to see which LDS variable the read touches, and it then
+// waits for every load into LDS in flight (other stage included) first.
+__device__ __forceinline__ bf16x8 frag_ms(const uint16_t* lds, int ent0, int kk) {
+  const int lane = lane_id();
+  const int g = lane >> 4, p = lane & 15;
+  const int n = ent0 + 16 * (g & 1) + 4 * (p & 3);
+  const int k0 = 8 * (g >> 1) + (p >> 2);
+  int off = k0 * 256 + (((n >> 3) ^ (4 * (k0 & 3))) << 3) + (n & 7);
+  asm("" : "+v"(off));
+  const uint16_t* a = lds + off + kk * 16 * 256;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 4 * 256));
   typedef short v8i16 __attribute__((ext_vector_type(8)));
   const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
@@ -279,17 +381,23 @@ __device__ __forceinline__ int lane_col(int tn, int g) {
   return wave_n() * WTN + tn * 32 + 8 * g + 4 * (lane_id() >> 5);
 }
 
-// KSWZ: k-major operands are in the swizzled layout (see KMajorLoaderT)
-template <bool P_MN, bool Q_MN, bool KSWZ = false>
+// SWZ: both operands are in the layouts loads straight into LDS write (the
+// swizzled k-major layout of KMajorLoaderT, the swizzled mn-major layout of
+// MNMajorLoaderD); otherwise the padded layouts.
+template <bool MN, bool SWZ>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* lds, int ent0, int kk) {
+  if constexpr (MN) return SWZ ? frag_ms(lds, ent0, kk) : frag_mn(lds, ent0, kk);
+  return frag_k<SWZ>(lds, ent0, kk);
+}
+
+template <bool P_MN, bool Q_MN, bool SWZ = false>
 __device__ __forceinline__ void load_frags(const uint16_t* ldsP, const uint16_t* ldsQ, int kk,
                                            bf16x8 (&pf)[TM], bf16x8 (&qf)[TN]) {
   const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
-    qf[j] = Q_MN ? frag_mn(ldsQ, qn0 + 32 * j, kk) : frag_k<KSWZ>(ldsQ, qn0 + 32 * j, kk);
+  for (int j = 0; j < TN; ++j) qf[j] = frag<Q_MN, SWZ>(ldsQ, qn0 + 32 * j, kk);
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-    pf[i] = P_MN ? frag_mn(ldsP, pm0 + 32 * i, kk) : frag_k<KSWZ>(ldsP, pm0 + 32 * i, kk);
+  for (int i = 0; i < TM; ++i) pf[i] = frag<P_MN, SWZ>(ldsP, pm0 + 32 * i, kk);
 }
 
 __device__ __forceinline__ void mma_step(const bf16x8 (&pf)[TM], const bf16x8 (&qf)[TN], Acc& acc) {
@@ -302,7 +410,7 @@ __device__ __forceinline__ void mma_step(const bf16x8 (&pf)[TM], const bf16x8 (&
 // One k-slab (4 steps of 16) of MFMAs for this wave. With two waves per SIMD
 // the other wave's MFMAs cover this wave's fragment reads, so fragments are
 // single buffered (register budget: 128 accumulators share the 256 VGPRs).
-template <bool P_MN, bool Q_MN, bool KSWZ = false>
+template <bool P_MN, bool Q_MN, bool SWZ = false>
 __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
   // The compiler's own interleave of the fragment reads with the MFMAs
   // leaves LDS latency exposed; its built-in MFMA/DS interleave strategy 0
@@ -313,7 +421,7 @@ __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* l
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
     bf16x8 pf[TM], qf[TN];
-    load_frags<P_MN, Q_MN, KSWZ>(ldsP, ldsQ, kk, pf, qf);
+    load_frags<P_MN, Q_MN, SWZ>(ldsP, ldsQ, kk, pf, qf);
     mma_step(pf, qf, acc);
   }
 }
@@ -401,6 +509,30 @@ __device__ __forceinline__ void plain_slab(LP& lp, LQ& lq, int kt, int nk, uint1
   if (more) store_next(lp, lq, nxt, sp, sq);
   wait_direct<LP, LQ>();
   __syncthreads();
+  if constexpr (kBothDirect<LP, LQ>) {
+    // slab kt + 2's offsets from the indices requested with slab kt + 1's
+    // loads, which the vmcnt(0) above has seen land
+    if (kt + 2 < nk) {
+      lp.advance(kt + 2);
+      lq.advance(kt + 2);
+    }
+  }
+}
+
+// Straight-to-LDS slabs 0 .. nk-1, slab 0 already in stage 0: unrolled by
+// two so that each slab's stages are known at compile time (the compiler
+// can then tell a slab's fragment reads, transpose reads included, from the
+// loads in flight into the other stage), in whole pairs and a last odd slab:
+// a loop with an exit between the two halves made the compiler keep extra
+// copies of values live across it (spills).
+template <bool P_MN, bool Q_MN, class LP, class LQ>
+__device__ __forceinline__ void direct_pairs(LP& lp, LQ& lq, int nk, Acc& acc, bool active, Stage& sp, Stage& sq) {
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    plain_slab<P_MN, Q_MN>(lp, lq, kt, nk, g_stage0, g_stage1, acc, active, sp, sq);
+    plain_slab<P_MN, Q_MN>(lp, lq, kt + 1, nk, g_stage1, g_stage0, acc, active, sp, sq);
+  }
+  if (kt < nk) plain_slab<P_MN, Q_MN>(lp, lq, kt, nk, g_stage0, g_stage1, acc, active, sp, sq);
 }
 
 // Runs the k loop of one tile: the global loads of slab kt+1 are in flight
@@ -418,6 +550,12 @@ __device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, Acc& acc
   lp.store(g_stage0, sp);
   lq.store(g_stage0 + kOperandLds, sq);
   __syncthreads();
+  if constexpr (kBothDirect<LP, LQ>) {
+    if (nk > 1) {
+      lp.advance(1);
+      lq.advance(1);
+    }
+  }
   if constexpr (LP::kDirect && !LQ::kDirect) {
     static_assert(!P_MN && Q_MN, "mixed slabs: P k-major and loaded straight into LDS, Q mn-major");
     for (int kt = 0; kt < nk; ++kt)
@@ -428,13 +566,7 @@ __device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, Acc& acc
     for (int kt = 0; kt < nk; ++kt)
       plain_slab<P_MN, Q_MN>(lp, lq, kt, nk, stage_buf(kt & 1), stage_buf((kt + 1) & 1), acc, active, sp, sq);
   } else {
-    // straight-to-LDS slabs: unrolled by two, so that each slab's stages are
-    // known at compile time
-    for (int kt = 0; kt < nk; kt += 2) {
-      plain_slab<P_MN, Q_MN>(lp, lq, kt, nk, g_stage0, g_stage1, acc, active, sp, sq);
-      if (kt + 1 >= nk) break;
-      plain_slab<P_MN, Q_MN>(lp, lq, kt + 1, nk, g_stage1, g_stage0, acc, active, sp, sq);
-    }
+    direct_pairs<P_MN, Q_MN>(lp, lq, nk, acc, active, sp, sq);
   }
 }
 
@@ -445,6 +577,25 @@ __device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nk, Acc& acc, bool 
   lp.fetch(0, sp);
   lq.fetch(0, sq);
   mainloop_staged<P_MN, Q_MN>(lp, lq, nk, acc, active, sp, sq);
+}
+
+// The k loop of a tile whose operands both load straight into LDS, with
+// slab 0 loaded the same way (no register stage): the weight-gradient
+// GEMMs, which do not prefetch across tiles.
+template <bool P_MN, bool Q_MN, class LP, class LQ>
+__device__ __forceinline__ void mainloop_direct(LP& lp, LQ& lq, int nk, Acc& acc, bool active = true) {
+  static_assert(kBothDirect<LP, LQ>, "both operands load straight into LDS");
+  if (nk <= 0) return;
+  lp.dma(0, g_stage0);
+  lq.dma(0, g_stage0 + kOperandLds);
+  wait_direct<LP, LQ>();
+  __syncthreads();
+  if (nk > 1) {
+    lp.advance(1);
+    lq.advance(1);
+  }
+  Stage sp, sq;  // unused: straight-to-LDS slabs pass no registers
+  direct_pairs<P_MN, Q_MN>(lp, lq, nk, acc, active, sp, sq);
 }
 
 // ------------------------------------------------------------------ FP8 core
@@ -1117,20 +1268,30 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(GemmProblem p, Operand 
 
 // ------------------------------------------------------------------ row functions
 
+// A row function maps k (a row of an expert segment) to a memory row:
+// index(k) directly, or in two steps, load(k) (which may read an index
+// array) and row(raw), so that a loader can issue the loads early and use
+// them later.
 struct DirectRows {  // memory row k of a row-major tensor
+  using Raw = int32_t;
   int32_t ld;            // elements between rows
   int32_t nrows;         // k-rows past this contribute zeros (nrows >= 1)
   __device__ __forceinline__ int32_t index(int k) const { return k < nrows ? k : nrows - 1; }
   __device__ __forceinline__ bool valid(int k) const { return k < nrows; }
+  __device__ __forceinline__ Raw load(int k) const { return index(k); }
+  __device__ __forceinline__ int32_t row(Raw r) const { return r; }
 };
 
 struct TokenRows {  // k-th row of an expert segment -> its token's row
+  using Raw = int32_t;
   int32_t ld;            // elements between token rows
   const int32_t* src;    // src_of + segment start
   int rows;              // segment length (>= 1)
   int kk;                // experts per token
   __device__ __forceinline__ int32_t index(int k) const { return src[k < rows ? k : rows - 1] / kk; }
   __device__ __forceinline__ bool valid(int k) const { return k < rows; }
+  __device__ __forceinline__ Raw load(int k) const { return src[k < rows ? k : rows - 1]; }
+  __device__ __forceinline__ int32_t row(Raw r) const { return r / kk; }
 };
 
 // ================================================================== backward dH
@@ -1270,7 +1431,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
   const int KU = row_units<FP8>(2 * I);
   const int64_t total = int64_t(s_pref[E]) * NT;
   KLoaderD<FP8> lp;
-  typename std::conditional<FP8, KMajorLoader8, MNMajorLoader<DirectRows>>::type lq;
+  typename std::conditional<FP8, KMajorLoader8, MNMajorLoaderD<DirectRows>>::type lq;
   auto setup = [&](int64_t t, TileState& st) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
     st.rt = rt;
@@ -1582,11 +1743,11 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     const int mt = it.local / NT;
     const int rows = it.klen;  // this item's rows of the expert, from row it.k0
     const int64_t off = int64_t(__builtin_amdgcn_readfirstlane(p.offsets[it.e])) + it.k0;
-    MNMajorLoader<DirectRows> lp;
+    MNMajorLoaderD<DirectRows> lp;
     lp.set_base(dh13 + off * 2 * I + int64_t(mt) * BM, int64_t(rows) * 2 * I - int64_t(mt) * BM);
     lp.fn.ld = 2 * I;
     lp.fn.nrows = rows;
-    MNMajorLoader<TokenRows> lq;
+    MNMajorLoaderD<TokenRows> lq;
     lq.set_base(x + int64_t(nt) * BN, p.T * H - int64_t(nt) * BN);
     lq.fn.ld = H;
     lq.fn.src = p.src_of + off;
@@ -1598,7 +1759,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     }
     Acc acc;
     acc.zero();
-    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, acc);
+    mainloop_direct<true, true>(lp, lq, (rows + BK - 1) / BK, acc);
     dw_store(acc, it, dW13 + int64_t(it.e) * 2 * I * H, H, int64_t(mt) * BM, int64_t(nt) * BN, BN, partial);
   });
 }
@@ -1616,13 +1777,13 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     const int mt = it.local / NT;
     const int rows = it.klen;  // this item's rows of the expert, from row it.k0
     const int64_t off = int64_t(__builtin_amdgcn_readfirstlane(p.offsets[it.e])) + it.k0;
-    MNMajorLoader<TokenRows> lp;
+    MNMajorLoaderD<TokenRows> lp;
     lp.set_base(dy + int64_t(mt) * BM, p.T * H - int64_t(mt) * BM);
     lp.fn.ld = H;
     lp.fn.src = p.src_of + off;
     lp.fn.rows = rows;
     lp.fn.kk = int(p.k);
-    MNMajorLoader<DirectRows> lq;
+    MNMajorLoaderD<DirectRows> lq;
     lq.set_base(act + off * I + int64_t(nt) * BN, int64_t(rows) * I - int64_t(nt) * BN);
     lq.fn.ld = I;
     lq.fn.nrows = rows;
@@ -1634,7 +1795,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     }
     Acc acc;
     acc.zero();
-    mainloop<true, true>(lp, lq, (rows + BK - 1) / BK, acc);
+    mainloop_direct<true, true>(lp, lq, (rows + BK - 1) / BK, acc);
     dw_store(acc, it, dW2 + int64_t(it.e) * H * I, I, int64_t(mt) * BM, int64_t(nt) * BN, ncols, partial);
   });
 }
