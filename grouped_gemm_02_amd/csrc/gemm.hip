@@ -1303,11 +1303,88 @@ struct TokenRows {  // k-th row of an expert segment -> its token's row
 int dh_num_parts(int64_t I) { return int((I + BN - 1) / BN) * 2; }
 
 // In the FP8 variant W2 arrives transposed, [E, I, H] (k-major rows i).
-template <bool FP8, bool F32S = false>
-__global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operand DY, Operand W,
-                                                           const uint16_t* __restrict__ h13,
-                                                           uint16_t* __restrict__ dh13,
-                                                           float* __restrict__ dwpart) {
+// The dH epilogue of one row tile: dA_u (the accumulators) with the saved
+// [g | u] rows gives dh13 = [dg | du] and the routing-weight partials.
+// Rows per batch of the dH epilogue (8 rows a thread in all): fewer rows
+// leave registers for the k loop.
+constexpr int kDhRows = 1;
+constexpr int kDhBatches = 8 / kDhRows;
+
+__device__ __forceinline__ void dh_epilogue(const TileState& st, const Acc& acc, int I, int nparts, float* s_w,
+                                            const uint16_t* __restrict__ h13, uint16_t* __restrict__ dh13,
+                                            float* __restrict__ dwpart) {
+    const RowTile& rt = st.rt;
+    const int ncols = min(BN, I - rt.nt * BN);
+    if (threadIdx.x < BM) s_w[threadIdx.x] = st.w;
+    // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
+    // Thread t works on 8 of them (c) for tile rows t/16 + 32*j, j < 8, in
+    // batches of kDhRows rows; each batch's [g | u] pieces are requested
+    // together (the first batch's before the staging barrier).
+    const int c = (threadIdx.x & 15) * 8;
+    for (int h = 0; h < 2; ++h) {
+      const bool col_ok = h * 128 + c < ncols;
+      const int i = rt.nt * BN + h * 128 + (col_ok ? c : 0);
+      stage_half(acc, h);
+      for (int bt = 0; bt < kDhBatches; ++bt) {
+        u32x4 gq[kDhRows], uq[kDhRows];
+#pragma unroll
+        for (int j = 0; j < kDhRows; ++j) {
+          const int m = min((int(threadIdx.x) >> 4) + kRowPass * (kDhRows * bt + j), rt.rows - 1);
+          const uint16_t* src = h13 + (rt.row0 + m) * 2 * I + i;
+          gq[j] = *reinterpret_cast<const u32x4*>(src);
+          uq[j] = *reinterpret_cast<const u32x4*>(src + I);
+        }
+        if (bt == 0) __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kDhRows; ++j) {
+          const int m = (threadIdx.x >> 4) + kRowPass * (kDhRows * bt + j);
+          const bool row_ok = m < rt.rows;
+          float dws = 0.f;
+          if (row_ok && col_ok) {
+            const int64_t r = rt.row0 + m;
+            const float w = s_w[m];
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(frow(m) + c);
+            const f32x4 d1 = *reinterpret_cast<const f32x4*>(frow(m) + c + 4);
+            u32x4 dgq, duq;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float dgp[2], dup[2];
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const float gv = hh ? bf16_hi(gq[j][q]) : bf16_lo(gq[j][q]);
+                const float uv = hh ? bf16_hi(uq[j][q]) : bf16_lo(uq[j][q]);
+                const int e8 = 2 * q + hh;
+                const float dau = e8 < 4 ? d0[e8] : d1[e8 - 4];
+                const float sg_ = sigmoidf_fast(gv);
+                const float sl = gv * sg_;  // silu(g)
+                dws += dau * sl * uv;
+                const float da = w * dau;
+                dgp[hh] = da * uv * sg_ * (1.f + gv * (1.f - sg_));
+                dup[hh] = da * sl;
+              }
+              dgq[q] = pack_bf16x2(dgp[0], dgp[1]);
+              duq[q] = pack_bf16x2(dup[0], dup[1]);
+            }
+            *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i) = dgq;
+            *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i) = duq;
+          }
+          // sum over the 16 threads of this row (lanes 16g .. 16g+15)
+          dws += __shfl_xor(dws, 8);
+          dws += __shfl_xor(dws, 4);
+          dws += __shfl_xor(dws, 2);
+          dws += __shfl_xor(dws, 1);
+          if (row_ok && (threadIdx.x & 15) == 0) dwpart[(rt.row0 + m) * nparts + 2 * rt.nt + h] = dws;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+// The FP8 dH (W2 arrives as transposed codes): k loop through registers.
+template <bool F32S, bool FP8 = true>
+__device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand& DY, const Operand& W,
+                                             const uint16_t* __restrict__ h13, uint16_t* __restrict__ dh13,
+                                             float* __restrict__ dwpart) {
   __shared__ float s_w[BM];
   const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
   MOE_ROW_SCHED
@@ -1416,6 +1493,73 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
       }
       __syncthreads();
     }
+  }
+}
+
+
+template <bool FP8, bool F32S = false>
+__global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operand DY, Operand W,
+                                                           const uint16_t* __restrict__ h13,
+                                                           uint16_t* __restrict__ dh13,
+                                                           float* __restrict__ dwpart) {
+  if constexpr (FP8) {
+    dh_fp8_tiles<F32S>(p, DY, W, h13, dh13, dwpart);
+    return;
+  }
+  __shared__ float s_w[BM];
+  const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
+  MOE_ROW_SCHED
+  const int NT = (I + BN - 1) / BN;  // the last n-tile may hold 128 columns
+  const int nparts = 2 * NT;
+  const int64_t total = int64_t(s_pref[E]) * NT;
+  const int KU = row_units<FP8>(H);
+  // Own tile loop, loaders scoped to the tile and no prefetch across tiles:
+  // the epilogue needs the registers. dY rows are gathered by token
+  // (straight into LDS in bf16); W2 is read mn-major in bf16, k-major
+  // (transposed codes) in FP8.
+  for (int64_t t = first_tile(); t < total; t += gridDim.x) {
+    const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
+    KLoaderD<FP8> lp;
+    if constexpr (FP8)
+      lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU, DY.scales, p.T * (H / 32));
+    else
+      lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int m = KMajorLoader::row_of_thread(i);
+      const int mc = m < rt.rows ? m : rt.rows - 1;
+      lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * KU);
+    }
+    const int ncols = min(BN, I - rt.nt * BN);
+    const float w_row = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
+    const bool active = wave_m() * WTM < rt.rows;
+    Acc acc;
+    acc.zero();
+    if constexpr (FP8) {
+      // rows i of W2^T past the (partial) last n-tile reuse row I-1; their
+      // columns are never stored
+      KMajorLoader8 lq;
+      lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * I + int64_t(rt.nt) * BN) * KU,
+                  int64_t(ncols) * KU, W.scales + (int64_t(rt.e) * I + int64_t(rt.nt) * BN) * (H / 32),
+                  int64_t(ncols) * (H / 32));
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        lq.set_row(i, int64_t(min(KMajorLoader::row_of_thread(i), ncols - 1)) * KU);
+      mainloop_fp8<F32S>(lp, lq, KU / 64, acc, active);
+    } else {
+      MNMajorLoaderD<DirectRows> lq;
+      lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN,
+                  int64_t(H) * I - int64_t(rt.nt) * BN);
+      lq.fn.ld = I;
+      lq.fn.nrows = H;
+      lq.nchunks = ncols / 8;
+      lq.prime(0);
+      mainloop_direct<false, true>(lp, lq, KU / 64, acc, active);
+    }
+    TileState st;
+    st.rt = rt;
+    st.w = w_row;
+    dh_epilogue(st, acc, I, nparts, s_w, h13, dh13, dwpart);
   }
 }
 
