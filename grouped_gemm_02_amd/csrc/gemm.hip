@@ -165,56 +165,6 @@ struct KMajorLoaderT {
 using KMajorLoader = KMajorLoaderT<false>;
 using KMajorLoaderD = KMajorLoaderT<true>;
 
-// mn-major operand: 64 k-rows per slab, each holding the tile's 256 entities
-// contiguously. Thread t copies chunk (t % 32) of k-rows t/32 + 16*i.
-// RowFn::index(k) gives the memory row of absolute k, always a real row, and
-// RowFn::valid(k) whether k contributes (k-rows past the end are loaded from
-// a real row and replaced by zero when stored); rows are RowFn::ld elements
-// apart. Loads go through a buffer resource over the tile's entity 0 of
-// row 0. Slabs are fetched in order; each fetch also works out the rows of
-// the next slab, since they may come from an index array.
-template <class RowFn>
-struct MNMajorLoader {
-  static constexpr bool kDirect = false;
-  RowFn fn;
-  __amdgpu_buffer_rsrc_t data;
-  int nchunks = 32;  // 16-byte chunks of the tile that exist (partial last n-tile)
-  uint32_t nxt[kPer];  // byte offsets of the next slab's rows
-  uint32_t nxt_ok;     // bit i: k-row i of the next slab contributes
-
-  __device__ __forceinline__ void set_base(const uint16_t* base, int64_t units) {
-    data = make_rsrc(base, units > 0 ? units * 2 : 0);
-  }
-  __device__ __forceinline__ void prime(int kt) {
-    uint32_t ok = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int k = kt * BK + (threadIdx.x >> 5) + 16 * i;
-      nxt[i] = uint32_t(fn.index(k)) * uint32_t(fn.ld) * 2u;
-      ok |= uint32_t(fn.valid(k)) << i;
-    }
-    nxt_ok = ok;
-  }
-  __device__ __forceinline__ void fetch(int kt, Stage& st) {
-    const int c = threadIdx.x & 31;
-    const bool col_ok = c < nchunks;
-    const uint32_t cc = col_ok ? uint32_t(c) * 16u : 0u;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) st.r[i] = __builtin_amdgcn_raw_buffer_load_b128(data, nxt[i] + cc, 0, 0);
-    st.ok = col_ok ? nxt_ok : 0u;
-    prime(kt + 1);
-  }
-  // The zero-fill is applied when the stage is written to LDS, after the
-  // MFMAs, so that nothing right after the loads waits for them.
-  __device__ __forceinline__ void store(uint16_t* lds, const Stage& st) const {
-    const int r0 = threadIdx.x >> 5, c = threadIdx.x & 31;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<u32x4*>(lds + (r0 + 16 * i) * LDN + c * 8) =
-          ((st.ok >> i) & 1u) ? st.r[i] : u32x4{0u, 0u, 0u, 0u};
-  }
-};
-
 // mn-major operand in an unpadded, swizzled layout that loads straight into
 // LDS can write: k-row k of the slab at k * 256 elements (512 bytes, the
 // tile's 256 entities), its 16-byte chunk c (entities 8c .. 8c+7) at slot
@@ -306,26 +256,12 @@ __device__ __forceinline__ bf16x8 frag_k(const uint16_t* lds, int ent0, int kk) 
   return *reinterpret_cast<const bf16x8*>(lds + e * LDK + c * 8);
 }
 
-// The same fragment from an mn-major tile with two transpose reads. In each
-// 16-lane group, ds_read_b64_tr_b16 gives lane p element (p % 4) of the
-// 8-byte chunk addressed by lane 4j + p/4, for j = 0..3. Lane p therefore
-// addresses k-row k0 + p/4 at entities n0 + 4*(p % 4), and receives the
-// 4 consecutive k of entity n0 + p.
-__device__ __forceinline__ bf16x8 frag_mn(const uint16_t* lds, int ent0, int kk) {
-  const int lane = lane_id();
-  const int g = lane >> 4, p = lane & 15;
-  const int n = ent0 + 16 * (g & 1) + 4 * (p & 3);
-  const int k = kk * 16 + 8 * (g >> 1) + (p >> 2);
-  const uint16_t* a = lds + k * LDN + n;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 4 * LDN));
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
-  const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 // The same fragment from the swizzled unpadded mn-major layout of
-// MNMajorLoaderD. Rows k and k + 4, and k + 16 kk, have the same k % 4, so
+// MNMajorLoaderD, with two transpose reads. In each 16-lane group,
+// ds_read_b64_tr_b16 gives lane p element (p % 4) of the 8-byte chunk
+// addressed by lane 4j + p/4, for j = 0..3. Lane p therefore addresses k-row
+// k0 + p/4 at entities n0 + 4*(p % 4), and receives the 4 consecutive k of
+// entity n0 + p. Rows k and k + 4, and k + 16 kk, have the same k % 4, so
 // all of a sub-tile's reads share one lane offset and differ by constants.
 // That offset is passed through an empty asm operand: otherwise the
 // optimizer splits the address into a chain of pointer steps too long for
@@ -386,7 +322,8 @@ __device__ __forceinline__ int lane_col(int tn, int g) {
 // MNMajorLoaderD); otherwise the padded layouts.
 template <bool MN, bool SWZ>
 __device__ __forceinline__ bf16x8 frag(const uint16_t* lds, int ent0, int kk) {
-  if constexpr (MN) return SWZ ? frag_ms(lds, ent0, kk) : frag_mn(lds, ent0, kk);
+  static_assert(!MN || SWZ, "mn-major operands are staged only in the swizzled layout");
+  if constexpr (MN) return frag_ms(lds, ent0, kk);
   return frag_k<SWZ>(lds, ent0, kk);
 }
 
@@ -428,11 +365,8 @@ __device__ __forceinline__ void mma_slab(const uint16_t* ldsP, const uint16_t* l
 
 // Slab kt of both operands into stage buffer `buf`: when both loaders can,
 // straight into LDS now; otherwise into registers (stored by store_next after
-// the MFMAs). Only both or neither here: the compiler cannot tell the LDS
-// transpose reads of an mn-major operand from loads into LDS in flight, and
-// would wait for those loads before the slab's first fragment read (the
-// mixed case, a straight k-major operand with an mn-major one, has its own
-// slab order: mixed_slab).
+// the MFMAs). Both or neither: a slab mixing the two would need its own order
+// of loads and fragment reads.
 template <class LP, class LQ>
 constexpr bool kBothDirect = LP::kDirect && LQ::kDirect;
 
@@ -458,42 +392,6 @@ __device__ __forceinline__ void store_next(const LP& lp, const LQ& lq, uint16_t*
     lp.store(buf, sp);
     lq.store(buf + kOperandLds, sq);
   }
-}
-
-// A slab whose k-major operand P is loaded straight into LDS while the
-// mn-major operand Q goes through registers (the dX and dH GEMMs). The
-// compiler cannot tell Q's transpose reads from loads into LDS in flight and
-// would wait for P's loads before any of them that follows; so Q's fragments
-// of the whole slab (32 registers) are read first, then slab kt+1 is
-// requested, then P's fragments are read step by step between the MFMAs.
-template <class LP, class LQ>
-__device__ __forceinline__ void mixed_slab(LP& lp, LQ& lq, int kt, int nk, uint16_t* cur, uint16_t* nxt, Acc& acc,
-                                           bool active, Stage& sq) {
-  const bool more = kt + 1 < nk;
-  bf16x8 qf[BK / 16][TN];
-  const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
-  if (active) {
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) qf[kk][j] = frag_mn(cur + kOperandLds, qn0 + 32 * j, kk);
-  }
-  if (more) {
-    lp.dma(kt + 1, nxt);
-    lq.fetch(kt + 1, sq);
-  }
-  if (active) {
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 pf[TM];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) pf[i] = frag_k<true>(cur, pm0 + 32 * i, kk);
-      mma_step(pf, qf[kk], acc);
-    }
-  }
-  if (more) lq.store(nxt + kOperandLds, sq);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // P's loads into LDS have landed (vmcnt(0))
-  __syncthreads();
 }
 
 // One slab kt of the k loop out of stage `cur`; slab kt+1 (if any) goes to
@@ -556,11 +454,8 @@ __device__ __forceinline__ void mainloop_staged(LP& lp, LQ& lq, int nk, Acc& acc
       lq.advance(1);
     }
   }
-  if constexpr (LP::kDirect && !LQ::kDirect) {
-    static_assert(!P_MN && Q_MN, "mixed slabs: P k-major and loaded straight into LDS, Q mn-major");
-    for (int kt = 0; kt < nk; ++kt)
-      mixed_slab(lp, lq, kt, nk, stage_buf(kt & 1), stage_buf((kt + 1) & 1), acc, active, sq);
-  } else if constexpr (!kBothDirect<LP, LQ>) {
+  static_assert(LP::kDirect == LQ::kDirect, "both operands or neither load straight into LDS");
+  if constexpr (!kBothDirect<LP, LQ>) {
     // slabs through registers: one loop body (unrolled by two it would not
     // fit the registers of the weight-gradient GEMMs)
     for (int kt = 0; kt < nk; ++kt)
@@ -1305,14 +1200,15 @@ int dh_num_parts(int64_t I) { return int((I + BN - 1) / BN) * 2; }
 // In the FP8 variant W2 arrives transposed, [E, I, H] (k-major rows i).
 // The dH epilogue of one row tile: dA_u (the accumulators) with the saved
 // [g | u] rows gives dh13 = [dg | du] and the routing-weight partials.
-// Rows per batch of the dH epilogue (8 rows a thread in all): fewer rows
-// leave registers for the k loop.
-constexpr int kDhRows = 1;
-constexpr int kDhBatches = 8 / kDhRows;
-
+// The dH epilogue of one row tile: dA_u (the accumulators) with the saved
+// [g | u] rows gives dh13 = [dg | du] and the routing-weight partials. A
+// thread handles 8 rows in batches of kDhRows (fewer rows per batch leave
+// more registers to the k loop).
+template <int kDhRows>
 __device__ __forceinline__ void dh_epilogue(const TileState& st, const Acc& acc, int I, int nparts, float* s_w,
                                             const uint16_t* __restrict__ h13, uint16_t* __restrict__ dh13,
                                             float* __restrict__ dwpart) {
+  constexpr int kDhBatches = 8 / kDhRows;
     const RowTile& rt = st.rt;
     const int ncols = min(BN, I - rt.nt * BN);
     if (threadIdx.x < BM) s_w[threadIdx.x] = st.w;
@@ -1381,7 +1277,9 @@ __device__ __forceinline__ void dh_epilogue(const TileState& st, const Acc& acc,
   }
 
 // The FP8 dH (W2 arrives as transposed codes): k loop through registers.
-template <bool F32S, bool FP8 = true>
+// Its epilogue is the one of dh_epilogue with four rows per batch, written
+// inline: called as that function the FP8 kernels spill 34-35 registers.
+template <bool F32S, bool FP8 = true>  // FP8 stays a template parameter for row_units<FP8>
 __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand& DY, const Operand& W,
                                              const uint16_t* __restrict__ h13, uint16_t* __restrict__ dh13,
                                              float* __restrict__ dwpart) {
@@ -1395,10 +1293,7 @@ __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
     const int KU = row_units<FP8>(H);
     KLoader<FP8> lp;
-    if constexpr (FP8)
-      lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU, DY.scales, p.T * (H / 32));
-    else
-      lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU);
+    lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU, DY.scales, p.T * (H / 32));
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
@@ -1409,7 +1304,7 @@ __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand
     const float w_row = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
     Acc acc;
     acc.zero();
-    if constexpr (FP8) {
+    {
       // rows i of W2^T past the (partial) last n-tile reuse row I-1; their
       // columns are never stored
       KMajorLoader8 lq;
@@ -1420,15 +1315,6 @@ __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand
       for (int i = 0; i < kPer; ++i)
         lq.set_row(i, int64_t(min(KMajorLoader::row_of_thread(i), ncols - 1)) * KU);
       mainloop_fp8<F32S>(lp, lq, KU / 64, acc, wave_m() * WTM < rt.rows);
-    } else {
-      MNMajorLoader<DirectRows> lq;
-      lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN,
-                  int64_t(H) * I - int64_t(rt.nt) * BN);
-      lq.fn.ld = I;
-      lq.fn.nrows = H;
-      lq.nchunks = ncols / 8;
-      lq.prime(0);
-      mainloop<false, true>(lp, lq, KU / 64, acc, wave_m() * WTM < rt.rows);
     }
     if (threadIdx.x < BM) s_w[threadIdx.x] = w_row;
     // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
@@ -1496,7 +1382,6 @@ __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand
   }
 }
 
-
 template <bool FP8, bool F32S = false>
 __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operand DY, Operand W,
                                                            const uint16_t* __restrict__ h13,
@@ -1559,7 +1444,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operan
     TileState st;
     st.rt = rt;
     st.w = w_row;
-    dh_epilogue(st, acc, I, nparts, s_w, h13, dh13, dwpart);
+    dh_epilogue<1>(st, acc, I, nparts, s_w, h13, dh13, dwpart);
   }
 }
 
