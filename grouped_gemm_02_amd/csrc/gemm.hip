@@ -552,10 +552,53 @@ struct KMajorLoader8 : KMajorLoader {
   }
 };
 
+// An E4M3 operand loaded straight into LDS: the codes in the swizzled
+// k-major layout of KMajorLoaderD (a row's slab is 128 codes, the 128 bytes
+// of a bf16 slab), the slab's scale words (4 bytes per row: four E8M0 bytes,
+// or one fp32 block scale) after them, at kScaleWords8, in thread order:
+// thread t moves the word of row (t / 8) + 64 (t % 4), whose code offsets it
+// already holds, to word t (each row twice), so row e's word is word
+// 8 (e % 64) + e / 64. Slab 0 of a row tile may go through registers
+// (fetch, store) when the persistent walk prefetches it.
+constexpr int kScaleWords8 = 16384;  // 16-bit units: byte 32768 of an operand region
+static_assert(2 * kScaleWords8 + 4 * kThreads <= 2 * kOperandLds, "codes and scale words fit an operand region");
+
+struct KMajorLoader8D : KMajorLoaderD {
+  __amdgpu_buffer_rsrc_t scale;
+  uint32_t soff;  // byte offset of the scale word this thread moves (slab 0)
+
+  __device__ __forceinline__ void set_base(const uint16_t* base, int64_t units, const uint8_t* sbase,
+                                           int64_t sbytes) {
+    KMajorLoaderD::set_base(base, units);
+    scale = make_rsrc(sbase, sbytes);
+  }
+  __device__ __forceinline__ void set_row(int i, int64_t row_off) {
+    KMajorLoaderD::set_row(i, row_off);
+    if (int(threadIdx.x & 3) == i) soff = uint32_t(row_off * 2) >> 5;
+  }
+  __device__ __forceinline__ void fetch(int kt, Stage8& st) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) st.r[i] = __builtin_amdgcn_raw_buffer_load_b128(data, off[i], kt * 2 * BK, 0);
+    st.s = __builtin_amdgcn_raw_buffer_load_b32(scale, soff, kt * 4, 0);
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, const Stage8& st) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4*>(lds + (int(threadIdx.x) + 512 * i) * 8) = st.r[i];
+    *reinterpret_cast<uint32_t*>(lds + kScaleWords8 + 2 * int(threadIdx.x)) = st.s;
+  }
+  __device__ __forceinline__ void dma(int kt, uint16_t* lds) const {
+    KMajorLoaderD::dma(kt, lds);
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        scale, (__attribute__((address_space(3))) void*)(lds + kScaleWords8 + w * 128), 4, soff, kt * 4, 0, 0);
+  }
+};
+
 template <bool FP8>
 using KLoader = typename std::conditional<FP8, KMajorLoader8, KMajorLoader>::type;
-// the same, with bf16 in the swizzled layout moved straight into LDS (for
-// GEMMs whose two operands are both k-major)
+// the bf16 operand moved straight into LDS (swizzled layout); E4M3 operands
+// of the row-tile walks stay on the register path (straight into LDS, their
+// kernels spill 6-14 registers and measured 1.4-7 % slower)
 template <bool FP8>
 using KLoaderD = typename std::conditional<FP8, KMajorLoader8, KMajorLoaderD>::type;
 
@@ -604,15 +647,31 @@ struct KMajorLoader4 {
 
 template <class L> struct StageOf { using type = Stage; };
 template <> struct StageOf<KMajorLoader8> { using type = Stage8; };
+template <> struct StageOf<KMajorLoader8D> { using type = Stage8; };
 template <> struct StageOf<KMajorLoader4> { using type = Stage4; };
 
+// SWZ: the operand was moved by KMajorLoader8D (swizzled codes, scale
+// words in thread order); otherwise by KMajorLoader8 (padded rows, scale
+// word in the row's padding).
+template <bool SWZ = false>
 __device__ __forceinline__ i32x8 frag8(const uint16_t* lds, int ent0, int s) {
   const int lane = lane_id();
-  const uint16_t* p = lds + (ent0 + (lane & 31)) * LDK + s * 32 + (lane >> 5) * 8;
-  const u32x4 a = *reinterpret_cast<const u32x4*>(p);       // codes 16h .. 16h+15 of the step
-  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);  // codes 32+16h .. 32+16h+15
+  u32x4 a, b;
+  if constexpr (SWZ) {
+    // 16-byte chunks 4s + h and 4s + 2 + h of the row
+    const int e = ent0 + (lane & 31), h = lane >> 5;
+    a = *reinterpret_cast<const u32x4*>(lds + e * BK + (((4 * s + h) ^ kswz(e)) << 3));
+    b = *reinterpret_cast<const u32x4*>(lds + e * BK + (((4 * s + 2 + h) ^ kswz(e)) << 3));
+  } else {
+    const uint16_t* p = lds + (ent0 + (lane & 31)) * LDK + s * 32 + (lane >> 5) * 8;
+    a = *reinterpret_cast<const u32x4*>(p);       // codes 16h .. 16h+15 of the step
+    b = *reinterpret_cast<const u32x4*>(p + 16);  // codes 32+16h .. 32+16h+15
+  }
   return i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(b[0]), int(b[1]), int(b[2]), int(b[3])};
 }
+
+// where KMajorLoader8D put row e's scale word (16-bit units from the operand)
+__device__ __forceinline__ int scale_pos8(int e) { return kScaleWords8 + 2 * (8 * (e & 63) + (e >> 6)); }
 
 // scale byte of k-block 2s + lane/32 (codes 64s + 32h .. +31) of this lane's row
 __device__ __forceinline__ int scale8(const uint16_t* lds, int ent0, int s) {
@@ -633,8 +692,10 @@ __device__ __forceinline__ i32x8 frag4(const uint16_t* lds, int ent0, int s) {
 // fp32 scale of this lane's row for the slab: with fp32 block scales
 // (kRuleF32) the slab's 4 scale bytes of a row are one float, the scale of
 // its 128-code block
+template <bool SWZ = false>
 __device__ __forceinline__ float fscale8(const uint16_t* lds, int ent0) {
-  return *reinterpret_cast<const float*>(lds + (ent0 + (lane_id() & 31)) * LDK + BK);
+  const int e = ent0 + (lane_id() & 31);
+  return *reinterpret_cast<const float*>(lds + (SWZ ? scale_pos8(e) : e * LDK + BK));
 }
 
 // s = m * 2^e with m in [1, 2) and e in E8M0's range [-127, 127]; a
@@ -660,14 +721,15 @@ __device__ __forceinline__ void split_scale(float s, int& e, float& m) {
 // the current block's m_P m_Q (bounded, [1, 4)): each slab first rescales
 // them by the previous block's m_P m_Q over this one's, and after the last
 // slab mainloop_staged_fp8 multiplies by the last m_P m_Q.
+template <bool SWZ = false>
 __device__ __forceinline__ void mma_slab_fp8_f32s(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
   const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
   int pe[TM], qe[TN];
   float pmant[TM], qmant[TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) split_scale(fscale8(ldsP, pm0 + 32 * i), pe[i], pmant[i]);
+  for (int i = 0; i < TM; ++i) split_scale(fscale8<SWZ>(ldsP, pm0 + 32 * i), pe[i], pmant[i]);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) split_scale(fscale8(ldsQ, qn0 + 32 * j), qe[j], qmant[j]);
+  for (int j = 0; j < TN; ++j) split_scale(fscale8<SWZ>(ldsQ, qn0 + 32 * j), qe[j], qmant[j]);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -684,10 +746,10 @@ __device__ __forceinline__ void mma_slab_fp8_f32s(const uint16_t* ldsP, const ui
   for (int s = 0; s < 2; ++s) {
     i32x8 qf[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) qf[j] = frag8(ldsQ, qn0 + 32 * j, s);
+    for (int j = 0; j < TN; ++j) qf[j] = frag8<SWZ>(ldsQ, qn0 + 32 * j, s);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const i32x8 pf = frag8(ldsP, pm0 + 32 * i, s);
+      const i32x8 pf = frag8<SWZ>(ldsP, pm0 + 32 * i, s);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[j], pf, acc.c[i][j], 0, 0, 0, qe[j] + 127,
@@ -710,39 +772,56 @@ __device__ __forceinline__ void finish_f32s(Acc& acc) {
 
 // The slab's 4 scale bytes of this lane's row, one LDS word (byte 2s + h is
 // the scale of k-block h of step s)
+template <bool SWZ = false>
 __device__ __forceinline__ uint32_t scale_word8(const uint16_t* lds, int ent0) {
-  return *reinterpret_cast<const uint32_t*>(lds + (ent0 + (lane_id() & 31)) * LDK + BK);
+  const int e = ent0 + (lane_id() & 31);
+  return *reinterpret_cast<const uint32_t*>(lds + (SWZ ? scale_pos8(e) : e * LDK + BK));
 }
 __device__ __forceinline__ int scale_byte8(uint32_t w, int s) {
   return int((w >> (8 * (2 * s + (lane_id() >> 5)))) & 0xFFu);
 }
 
-template <bool W4 = false, bool F32S = false>
+template <bool W4 = false, bool F32S = false, bool SWZ = false>
 __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_t* ldsQ, Acc& acc) {
+  static_assert(!(W4 && SWZ), "FP4 weights go through registers");
   if constexpr (F32S) {
     static_assert(!W4, "fp32 block scales are for E4M3 operands");
-    mma_slab_fp8_f32s(ldsP, ldsQ, acc);
+    mma_slab_fp8_f32s<SWZ>(ldsP, ldsQ, acc);
     return;
   }
   const int pm0 = wave_m() * WTM, qn0 = wave_n() * WTN;
   // scale words of the slab: one LDS read per row block
   uint32_t qsw[TN], psw[TM];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) qsw[j] = scale_word8(ldsQ, qn0 + 32 * j);
+  for (int j = 0; j < TN; ++j) qsw[j] = scale_word8<SWZ>(ldsQ, qn0 + 32 * j);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) psw[i] = scale_word8(ldsP, pm0 + 32 * i);
+  for (int i = 0; i < TM; ++i) psw[i] = scale_word8<SWZ>(ldsP, pm0 + 32 * i);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     i32x8 qf[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) qf[j] = W4 ? frag4(ldsQ, qn0 + 32 * j, s) : frag8(ldsQ, qn0 + 32 * j, s);
+    for (int j = 0; j < TN; ++j) qf[j] = W4 ? frag4(ldsQ, qn0 + 32 * j, s) : frag8<SWZ>(ldsQ, qn0 + 32 * j, s);
+    if constexpr (SWZ) {
+      // straight-to-LDS slabs: the compiler's own order (the pipelined form
+      // below costs registers these k loops do not have)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const i32x8 pf = frag8<SWZ>(ldsP, pm0 + 32 * i, s);
+        const int ps = scale_byte8(psw[i], s);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[j], pf, acc.c[i][j], 0, 0, 0,
+                                                                        scale_byte8(qsw[j], s), 0, ps);
+      }
+      continue;
+    }
     // the P fragments are software-pipelined: row block i+1's read is issued
     // before row block i's MFMAs, so its LDS latency hides behind them
-    i32x8 pf = frag8(ldsP, pm0, s);
+    i32x8 pf = frag8<SWZ>(ldsP, pm0, s);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       i32x8 pn;
-      if (i + 1 < TM) pn = frag8(ldsP, pm0 + 32 * (i + 1), s);
+      if (i + 1 < TM) pn = frag8<SWZ>(ldsP, pm0 + 32 * (i + 1), s);
       __builtin_amdgcn_sched_barrier(0);
       const int ps = scale_byte8(psw[i], s);
 #pragma unroll
@@ -755,41 +834,83 @@ __device__ __forceinline__ void mma_slab_fp8(const uint16_t* ldsP, const uint16_
   }
 }
 
-template <bool F32S = false, class LQ = KMajorLoader8>
-__device__ __forceinline__ void mainloop_staged_fp8(KMajorLoader8& lp, LQ& lq, int nk, Acc& acc, bool active,
-                                                    Stage8& sp, typename StageOf<LQ>::type& sq) {
+// One FP8 slab loaded straight into LDS (both operands KMajorLoader8D): slab
+// kt out of stage `cur`, slab kt+1 into `nxt` (both compile-time objects).
+template <bool F32S, class LP, class LQ>
+__device__ __forceinline__ void fp8_direct_slab(LP& lp, LQ& lq, int kt, int nk, uint16_t* cur, uint16_t* nxt,
+                                                Acc& acc, bool active) {
+  if (kt + 1 < nk) {
+    lp.dma(kt + 1, nxt);
+    lq.dma(kt + 1, nxt + kOperandLds);
+  }
+  if (active) mma_slab_fp8<false, F32S, true>(cur, cur + kOperandLds, acc);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the slab's loads into LDS have landed (vmcnt(0))
+  __syncthreads();
+}
+
+// Straight-to-LDS FP8 slabs 0 .. nk-1, slab 0 in stage 0, in whole pairs
+// and a last odd slab (as direct_pairs).
+template <bool F32S, class LP, class LQ>
+__device__ __forceinline__ void fp8_direct_pairs(LP& lp, LQ& lq, int nk, Acc& acc, bool active) {
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    fp8_direct_slab<F32S>(lp, lq, kt, nk, g_stage0, g_stage1, acc, active);
+    fp8_direct_slab<F32S>(lp, lq, kt + 1, nk, g_stage1, g_stage0, acc, active);
+  }
+  if (kt < nk) fp8_direct_slab<F32S>(lp, lq, kt, nk, g_stage0, g_stage1, acc, active);
+}
+
+// The FP8 k loop with slab 0 already fetched into sp, sq (row-tile walks).
+template <bool F32S = false, class LP = KMajorLoader8, class LQ = KMajorLoader8>
+__device__ __forceinline__ void mainloop_staged_fp8(LP& lp, LQ& lq, int nk, Acc& acc, bool active,
+                                                    typename StageOf<LP>::type& sp,
+                                                    typename StageOf<LQ>::type& sq) {
   constexpr bool W4 = std::is_same<LQ, KMajorLoader4>::value;
+  static_assert(LP::kDirect == LQ::kDirect, "both operands or neither load straight into LDS");
   if (nk <= 0) return;
   lp.store(g_stage0, sp);
   lq.store(g_stage0 + kOperandLds, sq);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    uint16_t* cur = stage_buf(kt & 1);
-    uint16_t* nxt = stage_buf((kt + 1) & 1);
-    const bool more = kt + 1 < nk;
-    if (more) {
-      lp.fetch(kt + 1, sp);
-      lq.fetch(kt + 1, sq);
+  if constexpr (kBothDirect<LP, LQ>) {
+    fp8_direct_pairs<F32S>(lp, lq, nk, acc, active);
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      uint16_t* cur = stage_buf(kt & 1);
+      uint16_t* nxt = stage_buf((kt + 1) & 1);
+      const bool more = kt + 1 < nk;
+      if (more) {
+        lp.fetch(kt + 1, sp);
+        lq.fetch(kt + 1, sq);
+      }
+      if (active) mma_slab_fp8<W4, F32S>(cur, cur + kOperandLds, acc);
+      // unconditional (after the last slab it rewrites stale data into the idle
+      // buffer): a conditional block here lets the compiler sink the MFMAs
+      // below it, with every fragment of the slab live at once
+      lp.store(nxt, sp);
+      lq.store(nxt + kOperandLds, sq);
+      __syncthreads();
     }
-    if (active) mma_slab_fp8<W4, F32S>(cur, cur + kOperandLds, acc);
-    // unconditional (after the last slab it rewrites stale data into the idle
-    // buffer): a conditional block here lets the compiler sink the MFMAs
-    // below it, with every fragment of the slab live at once
-    lp.store(nxt, sp);
-    lq.store(nxt + kOperandLds, sq);
-    __syncthreads();
   }
   if constexpr (F32S) finish_f32s(acc);
 }
 
-template <bool F32S = false>
-__device__ __forceinline__ void mainloop_fp8(KMajorLoader8& lp, KMajorLoader8& lq, int nk, Acc& acc,
-                                             bool active = true) {
+// The FP8 k loop of a tile that loads its own slab 0.
+template <bool F32S = false, class LP, class LQ>
+__device__ __forceinline__ void mainloop_fp8(LP& lp, LQ& lq, int nk, Acc& acc, bool active = true) {
   if (nk <= 0) return;
-  Stage8 sp, sq;
-  lp.fetch(0, sp);
-  lq.fetch(0, sq);
-  mainloop_staged_fp8<F32S>(lp, lq, nk, acc, active, sp, sq);
+  if constexpr (kBothDirect<LP, LQ>) {
+    lp.dma(0, g_stage0);
+    lq.dma(0, g_stage0 + kOperandLds);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    fp8_direct_pairs<F32S>(lp, lq, nk, acc, active);
+    if constexpr (F32S) finish_f32s(acc);
+  } else {
+    Stage8 sp, sq;
+    lp.fetch(0, sp);
+    lq.fetch(0, sq);
+    mainloop_staged_fp8<F32S>(lp, lq, nk, acc, active, sp, sq);
+  }
 }
 
 // ------------------------------------------------------------------ LDS-staged epilogue
@@ -1276,7 +1397,8 @@ __device__ __forceinline__ void dh_epilogue(const TileState& st, const Acc& acc,
     }
   }
 
-// The FP8 dH (W2 arrives as transposed codes): k loop through registers.
+// The FP8 dH (W2 arrives as transposed codes), both operands straight into
+// LDS; its own tile loop, no prefetch across tiles.
 // Its epilogue is the one of dh_epilogue with four rows per batch, written
 // inline: called as that function the FP8 kernels spill 34-35 registers.
 template <bool F32S, bool FP8 = true>  // FP8 stays a template parameter for row_units<FP8>
@@ -1292,7 +1414,7 @@ __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
     const int KU = row_units<FP8>(H);
-    KLoader<FP8> lp;
+    KMajorLoader8D lp;
     lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU, DY.scales, p.T * (H / 32));
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -1307,7 +1429,7 @@ __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand
     {
       // rows i of W2^T past the (partial) last n-tile reuse row I-1; their
       // columns are never stored
-      KMajorLoader8 lq;
+      KMajorLoader8D lq;
       lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * I + int64_t(rt.nt) * BN) * KU,
                   int64_t(ncols) * KU, W.scales + (int64_t(rt.e) * I + int64_t(rt.nt) * BN) * (H / 32),
                   int64_t(ncols) * (H / 32));
@@ -1382,70 +1504,55 @@ __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand
   }
 }
 
-template <bool FP8, bool F32S = false>
-__global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operand DY, Operand W,
-                                                           const uint16_t* __restrict__ h13,
-                                                           uint16_t* __restrict__ dh13,
-                                                           float* __restrict__ dwpart) {
-  if constexpr (FP8) {
-    dh_fp8_tiles<F32S>(p, DY, W, h13, dh13, dwpart);
-    return;
-  }
+// The bf16 dH: own tile loop, the loaders scoped to the tile and no prefetch
+// across tiles (the epilogue needs the registers); the gathered dY rows and
+// the mn-major W2 load straight into LDS.
+__device__ __forceinline__ void dh_bf16_tiles(const GemmProblem& p, const Operand& DY, const Operand& W,
+                                              const uint16_t* __restrict__ h13, uint16_t* __restrict__ dh13,
+                                              float* __restrict__ dwpart) {
   __shared__ float s_w[BM];
   const int E = int(p.E), H = int(p.H), I = int(p.I), k = int(p.k);
   MOE_ROW_SCHED
   const int NT = (I + BN - 1) / BN;  // the last n-tile may hold 128 columns
   const int nparts = 2 * NT;
   const int64_t total = int64_t(s_pref[E]) * NT;
-  const int KU = row_units<FP8>(H);
-  // Own tile loop, loaders scoped to the tile and no prefetch across tiles:
-  // the epilogue needs the registers. dY rows are gathered by token
-  // (straight into LDS in bf16); W2 is read mn-major in bf16, k-major
-  // (transposed codes) in FP8.
   for (int64_t t = first_tile(); t < total; t += gridDim.x) {
     const RowTile rt = decode_row_tile(t, NT, s_pref, E, p.counts, p.offsets);
-    KLoaderD<FP8> lp;
-    if constexpr (FP8)
-      lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU, DY.scales, p.T * (H / 32));
-    else
-      lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * KU);
+    KMajorLoaderD lp;
+    lp.set_base(static_cast<const uint16_t*>(DY.data), p.T * H);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = KMajorLoader::row_of_thread(i);
       const int mc = m < rt.rows ? m : rt.rows - 1;
-      lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * KU);
+      lp.set_row(i, int64_t(p.src_of[rt.row0 + mc] / k) * H);
     }
     const int ncols = min(BN, I - rt.nt * BN);
-    const float w_row = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
-    const bool active = wave_m() * WTM < rt.rows;
-    Acc acc;
-    acc.zero();
-    if constexpr (FP8) {
-      // rows i of W2^T past the (partial) last n-tile reuse row I-1; their
-      // columns are never stored
-      KMajorLoader8 lq;
-      lq.set_base(static_cast<const uint16_t*>(W.data) + (int64_t(rt.e) * I + int64_t(rt.nt) * BN) * KU,
-                  int64_t(ncols) * KU, W.scales + (int64_t(rt.e) * I + int64_t(rt.nt) * BN) * (H / 32),
-                  int64_t(ncols) * (H / 32));
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        lq.set_row(i, int64_t(min(KMajorLoader::row_of_thread(i), ncols - 1)) * KU);
-      mainloop_fp8<F32S>(lp, lq, KU / 64, acc, active);
-    } else {
-      MNMajorLoaderD<DirectRows> lq;
-      lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN,
-                  int64_t(H) * I - int64_t(rt.nt) * BN);
-      lq.fn.ld = I;
-      lq.fn.nrows = H;
-      lq.nchunks = ncols / 8;
-      lq.prime(0);
-      mainloop_direct<false, true>(lp, lq, KU / 64, acc, active);
-    }
+    MNMajorLoaderD<DirectRows> lq;
+    lq.set_base(static_cast<const uint16_t*>(W.data) + int64_t(rt.e) * H * I + int64_t(rt.nt) * BN,
+                int64_t(H) * I - int64_t(rt.nt) * BN);
+    lq.fn.ld = I;
+    lq.fn.nrows = H;
+    lq.nchunks = ncols / 8;
+    lq.prime(0);
     TileState st;
     st.rt = rt;
-    st.w = w_row;
+    st.w = threadIdx.x < BM ? p.wrow[rt.row0 + min(int(threadIdx.x), rt.rows - 1)] : 0.f;
+    Acc acc;
+    acc.zero();
+    mainloop_direct<false, true>(lp, lq, H / 64, acc, wave_m() * WTM < rt.rows);
     dh_epilogue<1>(st, acc, I, nparts, s_w, h13, dh13, dwpart);
   }
+}
+
+template <bool FP8, bool F32S = false>
+__global__ __launch_bounds__(kThreads) void gemm_dh_kernel(GemmProblem p, Operand DY, Operand W,
+                                                           const uint16_t* __restrict__ h13,
+                                                           uint16_t* __restrict__ dh13,
+                                                           float* __restrict__ dwpart) {
+  if constexpr (FP8)
+    dh_fp8_tiles<F32S>(p, DY, W, h13, dh13, dwpart);
+  else
+    dh_bf16_tiles(p, DY, W, h13, dh13, dwpart);
 }
 
 // ================================================================== backward dX
@@ -1897,7 +2004,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw_fp8_kernel(GemmProblem p, co
     const int ncols = min(BN, NQ - nt * BN);
     const int64_t pb = int64_t(MP) * poff + int64_t(mt) * BM * kp + it.k0;  // byte of P row 0, code k0
     const int64_t qb = int64_t(NQ) * poff + int64_t(nt) * BN * kp + it.k0;
-    KMajorLoader8 lp, lq;
+    KMajorLoader8 lp, lq;  // through registers: straight into LDS this kernel spills 67 VGPRs
     lp.set_base(reinterpret_cast<const uint16_t*>(pcodes + pb), int64_t(BM) * KU - it.k0 / 2, pscales + pb / 32,
                 int64_t(BM) * kp / 32 - it.k0 / 32);
     lq.set_base(reinterpret_cast<const uint16_t*>(qcodes + qb), int64_t(ncols) * KU - it.k0 / 2, qscales + qb / 32,
