@@ -1298,16 +1298,29 @@ struct DirectRows {  // memory row k of a row-major tensor
   __device__ __forceinline__ int32_t row(Raw r) const { return r; }
 };
 
+// floor(2^32 / k) (2^32 - 1 for k = 1): with it, n / k for 0 <= n < 2^31 is
+// q = mulhi(n, m) or q + 1. m is short of 2^32 / k by less than 1, so n m / 2^32
+// is short of n / k by less than n / 2^32 < 1/2 and q is the quotient or one less;
+// one comparison of the remainder fixes it.
+__host__ __device__ inline uint32_t div_magic(uint32_t k) {
+  return k == 1 ? 0xFFFFFFFFu : uint32_t((uint64_t(1) << 32) / k);
+}
+__device__ __forceinline__ uint32_t div_by(uint32_t n, uint32_t k, uint32_t m) {
+  const uint32_t q = uint32_t((uint64_t(n) * m) >> 32);
+  return q + (n - q * k >= k ? 1u : 0u);
+}
+
 struct TokenRows {  // k-th row of an expert segment -> its token's row
   using Raw = int32_t;
   int32_t ld;            // elements between token rows
   const int32_t* src;    // src_of + segment start
   int rows;              // segment length (>= 1)
   int kk;                // experts per token
-  __device__ __forceinline__ int32_t index(int k) const { return src[k < rows ? k : rows - 1] / kk; }
+  uint32_t kmagic;       // div_magic(kk)
   __device__ __forceinline__ bool valid(int k) const { return k < rows; }
   __device__ __forceinline__ Raw load(int k) const { return src[k < rows ? k : rows - 1]; }
-  __device__ __forceinline__ int32_t row(Raw r) const { return r / kk; }
+  // a pair index (>= 0) -> its token
+  __device__ __forceinline__ int32_t row(Raw r) const { return int32_t(div_by(uint32_t(r), uint32_t(kk), kmagic)); }
 };
 
 // ================================================================== backward dH
@@ -1873,6 +1886,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
   MOE_DW_SMEM
   const int H = int(p.H), I = int(p.I);
   const int MT = (2 * I) / BM, NT = H / BN;
+  const uint32_t kmagic = div_magic(uint32_t(p.k));
   dw_for_each_item(p.counts, int(p.E), MT * NT, queue, plan_out, s_cnt, s_order, &s_flag, &s_next, &s_plan,
                    [&](const DwItem& it) {
     const int nt = it.local % NT;
@@ -1889,6 +1903,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw13_kernel(GemmProblem p, cons
     lq.fn.src = p.src_of + off;
     lq.fn.rows = rows;
     lq.fn.kk = int(p.k);
+    lq.fn.kmagic = kmagic;
     if (rows > 0) {  // an empty expert runs no k loop and stores zeros
       lp.prime(0);
       lq.prime(0);
@@ -1907,6 +1922,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
   MOE_DW_SMEM
   const int H = int(p.H), I = int(p.I);
   const int MT = H / BM, NT = (I + BN - 1) / BN;  // the last n-tile may hold 128 columns
+  const uint32_t kmagic = div_magic(uint32_t(p.k));
   dw_for_each_item(p.counts, int(p.E), MT * NT, queue, plan_out, s_cnt, s_order, &s_flag, &s_next, &s_plan,
                    [&](const DwItem& it) {
     const int nt = it.local % NT;
@@ -1919,6 +1935,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dw2_kernel(GemmProblem p, const
     lp.fn.src = p.src_of + off;
     lp.fn.rows = rows;
     lp.fn.kk = int(p.k);
+    lp.fn.kmagic = kmagic;
     MNMajorLoaderD<DirectRows> lq;
     lq.set_base(act + off * I + int64_t(nt) * BN, int64_t(rows) * I - int64_t(nt) * BN);
     lq.fn.ld = I;
