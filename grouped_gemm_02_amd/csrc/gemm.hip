@@ -213,8 +213,11 @@ struct MNMajorLoaderD {
       const int kr = krow(i);
       const int c = p ^ (4 * (kr & 3));
       const int k = kt * BK + kr;
-      nxt[i] = (fn.valid(k) && c < nchunks) ? uint32_t(fn.row(raw[i])) * uint32_t(fn.ld) * 2u + uint32_t(c) * 16u
-                                            : kPastExtent;
+      // computed for every lane (row() of a clamped index is a real row, so the
+      // offset is inside the extent, below 2^31) and pushed past the extent
+      // where the k-row or the chunk does not exist: no branch, one select
+      const uint32_t off = uint32_t(fn.row(raw[i])) * uint32_t(fn.ld) * 2u + uint32_t(c) * 16u;
+      nxt[i] = off | ((fn.valid(k) && c < nchunks) ? 0u : kPastExtent);
     }
   }
   __device__ __forceinline__ void prime(int kt) {
