@@ -1686,12 +1686,13 @@ __device__ bool dw_expert_order(const int32_t* counts, int E, int32_t* s_cnt, in
 // the plan for that kernel.
 constexpr int kMaxSplit = 4;
 constexpr int kMaxSplitExperts = 16;
-constexpr int kSplitSlots = 256;  // fp32 partial tiles of 256 x 256
+constexpr int kSplitSlots = 320;  // fp32 partial tiles of 256 x 256
 constexpr int kSplitMinRows = 1024;
 constexpr int kNominalWGs = 256;
 
 struct DwPlan {
   int nsplit;                      // split experts: queue ranks 0 .. nsplit-1
+  int split_last;                  // 1: their items after the unsplit ones (tail split)
   int e[kMaxSplitExperts];         // their expert ids
   int S[kMaxSplitExperts];         // their split counts
   int chunk[kMaxSplitExperts];     // rows per split
@@ -1735,27 +1736,102 @@ __device__ void dw_plan(const int32_t* s_cnt, const int32_t* s_order, int E, int
     ++n;
   }
   plan->nsplit = n;
+  plan->split_last = 0;
+}
+
+// Split for the last round under balanced routing. The n = E * per_expert
+// tiles cost about the same, so the walk takes ceil(n / G) tile times on G
+// workgroups, with the last round only x / G full (x = n mod G). Cutting x
+// tiles into two row halves and running the whole tiles first (longest
+// first) finishes in floor(n / G) + 1/2 tile times when x <= G / 2. The
+// tiles of the ceil(x / per_expert) heaviest experts are cut (each half a
+// multiple of 128 rows, at least kSplitMinRows); only when floor(n / G) is 1
+// to 3 (a saving of an eighth to a quarter) and every cut expert has the
+// rows. G is the nominal 256, as in dw_plan. nsplit = 0: no split.
+__device__ void dw_tail_plan(const int32_t* s_cnt, const int32_t* s_order, int E, int per_expert, DwPlan* plan) {
+  if (threadIdx.x != 0) return;
+  plan->nsplit = 0;
+  plan->split_last = 1;
+  plan->item0[0] = 0;
+  const int n = E * per_expert;
+  const int r = n / kNominalWGs, x = n - r * kNominalWGs;
+  if (r < 1 || r > 3 || x == 0 || 2 * x > kNominalWGs) return;
+  const int nexp = (x + per_expert - 1) / per_expert;
+  if (nexp > kMaxSplitExperts || nexp > E || nexp * per_expert * 2 > kSplitSlots) return;
+  for (int j = 0; j < nexp; ++j) {
+    const int e = s_order[j];
+    const int rows = s_cnt[e];
+    const int chunk = ((rows + 1) / 2 + 127) / 128 * 128;
+    if (chunk < kSplitMinRows || (rows + chunk - 1) / chunk != 2) return;
+    plan->e[j] = e;
+    plan->S[j] = 2;
+    plan->chunk[j] = chunk;
+    plan->slot0[j] = j * per_expert * 2;
+    plan->item0[j + 1] = (j + 1) * per_expert * 2;
+  }
+  plan->nsplit = nexp;
 }
 
 // Runs body(item) over every work item of a weight-gradient GEMM with
 // per_expert tiles per expert. Balanced routing: the static walk over
-// (expert, tile), no splits. Skewed: the queue, heaviest expert first, the
-// split experts' items first. s_flag and s_next are distinct LDS words.
-// Workgroup 0 writes the plan (no split experts when balanced) to plan_out.
+// (expert, tile), unless dw_tail_plan cuts the last round's tiles. Skewed:
+// workgroups take items from one queue (queue[0]), the split experts' items
+// first, then the other experts heaviest first. Tail split: the whole tiles
+// and then the halves are dealt out in eight contiguous shares, XCD x
+// (= blockIdx % 8) taking items from its own share through queue[x], so
+// that the tiles one XCD runs at the same time share expert rows in its L2
+// (the static walk's locality, which a single queue loses); a workgroup
+// whose share is done takes items from the next XCDs' shares. s_flag and
+// s_next are distinct LDS words. Workgroup 0 writes the plan (nsplit = 0:
+// no split tiles) to plan_out.
 template <class Body>
 __device__ __forceinline__ void dw_for_each_item(const int32_t* counts, int E, int per_expert, int32_t* queue,
                                                  int32_t* plan_out, int32_t* s_cnt, int32_t* s_order,
                                                  int32_t* s_flag, int32_t* s_next, DwPlan* plan, Body&& body) {
-  if (dw_expert_order(counts, E, s_cnt, s_order, s_flag)) {
+  const bool skewed = dw_expert_order(counts, E, s_cnt, s_order, s_flag);
+  if (skewed)
     dw_plan(s_cnt, s_order, E, per_expert, plan);
-    __syncthreads();
-    if (blockIdx.x == 0) {
-      const int32_t* w = reinterpret_cast<const int32_t*>(plan);
-      for (int i = threadIdx.x; i < int(sizeof(DwPlan) / sizeof(int32_t)); i += kThreads) plan_out[i] = w[i];
+  else
+    dw_tail_plan(s_cnt, s_order, E, per_expert, plan);
+  __syncthreads();
+  const int nsplit = __builtin_amdgcn_readfirstlane(plan->nsplit);
+  if (blockIdx.x == 0) {
+    const int32_t* w = reinterpret_cast<const int32_t*>(plan);
+    for (int i = threadIdx.x; i < int(sizeof(DwPlan) / sizeof(int32_t)); i += kThreads) plan_out[i] = w[i];
+  }
+  const int split_items = __builtin_amdgcn_readfirstlane(plan->item0[nsplit]);
+  const int whole_items = (E - nsplit) * per_expert;
+  // split item us (us < split_items) or whole item v
+  auto run = [&](bool split, int idx) {
+    DwItem it;
+    if (split) {
+      int r = 0;
+      while (r + 1 < nsplit && plan->item0[r + 1] <= idx) ++r;
+      r = __builtin_amdgcn_readfirstlane(r);
+      const int S = __builtin_amdgcn_readfirstlane(plan->S[r]);
+      const int within = idx - __builtin_amdgcn_readfirstlane(plan->item0[r]);
+      it.e = __builtin_amdgcn_readfirstlane(plan->e[r]);
+      it.local = within / S;
+      it.s = within % S;
+      it.S = S;
+      it.chunk = __builtin_amdgcn_readfirstlane(plan->chunk[r]);
+      it.k0 = it.s * it.chunk;
+      it.klen = min(it.chunk, __builtin_amdgcn_readfirstlane(counts[it.e]) - it.k0);
+      it.slot = __builtin_amdgcn_readfirstlane(plan->slot0[r]) + it.local * S + it.s;
+    } else {
+      it.e = __builtin_amdgcn_readfirstlane(s_order[nsplit + idx / per_expert]);
+      it.local = idx % per_expert;
+      it.s = 0;
+      it.S = 1;
+      it.k0 = 0;
+      it.klen = __builtin_amdgcn_readfirstlane(counts[it.e]);
+      it.chunk = it.klen;
+      it.slot = 0;
     }
-    const int nsplit = __builtin_amdgcn_readfirstlane(plan->nsplit);
-    const int split_items = __builtin_amdgcn_readfirstlane(plan->item0[nsplit]);
-    const int total = split_items + (E - nsplit) * per_expert;
+    body(it);
+  };
+  if (skewed) {
+    const int total = split_items + whole_items;
     int32_t ticket = 0;  // thread 0 only
     if (threadIdx.x == 0) ticket = atomicAdd(queue, 1);
     for (;;) {
@@ -1765,48 +1841,31 @@ __device__ __forceinline__ void dw_for_each_item(const int32_t* counts, int E, i
       __syncthreads();
       if (u >= total) break;
       if (threadIdx.x == 0) ticket = atomicAdd(queue, 1);
-      DwItem it;
-      if (u < split_items) {
-        int r = 0;
-        while (r + 1 < nsplit && plan->item0[r + 1] <= u) ++r;
-        r = __builtin_amdgcn_readfirstlane(r);
-        const int S = __builtin_amdgcn_readfirstlane(plan->S[r]);
-        const int within = u - __builtin_amdgcn_readfirstlane(plan->item0[r]);
-        it.e = __builtin_amdgcn_readfirstlane(plan->e[r]);
-        it.local = within / S;
-        it.s = within % S;
-        it.S = S;
-        it.chunk = __builtin_amdgcn_readfirstlane(plan->chunk[r]);
-        it.k0 = it.s * it.chunk;
-        it.klen = min(it.chunk, __builtin_amdgcn_readfirstlane(counts[it.e]) - it.k0);
-        it.slot = __builtin_amdgcn_readfirstlane(plan->slot0[r]) + it.local * S + it.s;
-      } else {
-        const int v = u - split_items;
-        it.e = __builtin_amdgcn_readfirstlane(s_order[nsplit + v / per_expert]);
-        it.local = v % per_expert;
-        it.s = 0;
-        it.S = 1;
-        it.k0 = 0;
-        it.klen = __builtin_amdgcn_readfirstlane(counts[it.e]);
-        it.chunk = it.klen;
-        it.slot = 0;
+      run(u < split_items, u < split_items ? u : u - split_items);
+    }
+  } else if (nsplit > 0) {
+    // share x: whole items [W x / 8, W (x+1) / 8), then split items [S x / 8, S (x+1) / 8)
+    int x = int(blockIdx.x & 7), tries = 0;
+    int32_t ticket = 0;  // thread 0 only
+    if (threadIdx.x == 0) ticket = atomicAdd(queue + x, 1);
+    for (;;) {
+      if (threadIdx.x == 0) *s_next = ticket;
+      __syncthreads();
+      const int j = __builtin_amdgcn_readfirstlane(*s_next);
+      __syncthreads();
+      const int w0 = whole_items * x / 8, w1 = whole_items * (x + 1) / 8;
+      const int s0 = split_items * x / 8, s1 = split_items * (x + 1) / 8;
+      if (j >= (w1 - w0) + (s1 - s0)) {  // share x is done: the next one
+        if (++tries == 8) break;
+        x = (x + 1) & 7;
+        if (threadIdx.x == 0) ticket = atomicAdd(queue + x, 1);
+        continue;
       }
-      body(it);
+      if (threadIdx.x == 0) ticket = atomicAdd(queue + x, 1);
+      run(j >= w1 - w0, j < w1 - w0 ? w0 + j : s0 + j - (w1 - w0));
     }
   } else {
-    if (blockIdx.x == 0 && threadIdx.x == 0) plan_out[0] = 0;  // nsplit
-    for (int t = int(first_tile()); t < E * per_expert; t += gridDim.x) {
-      DwItem it;
-      it.e = t / per_expert;
-      it.local = t % per_expert;
-      it.s = 0;
-      it.S = 1;
-      it.k0 = 0;
-      it.klen = __builtin_amdgcn_readfirstlane(counts[it.e]);
-      it.chunk = it.klen;
-      it.slot = 0;
-      body(it);
-    }
+    for (int t = int(first_tile()); t < E * per_expert; t += gridDim.x) run(false, t);
   }
 }
 

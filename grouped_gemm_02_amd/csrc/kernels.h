@@ -89,15 +89,16 @@ hipError_t launch_gemm_dh(const GemmProblem& p, GemmOperand dy, GemmOperand W2, 
                           uint16_t* dh13, float* dwpart, hipStream_t st, KernelTimer* timer);
 hipError_t launch_gemm_dx(const GemmProblem& p, GemmOperand dh13, GemmOperand W13, uint16_t* dx_rows,
                           hipStream_t st, KernelTimer* timer);
-// weight gradients; each takes one zeroed queue word (tile counter), the
+// weight gradients; each takes kQueuesPerGemm zeroed queue words (tile counters), the
 // fp32 partial tiles of split items (kSplitFloats floats, shared: the
 // weight-gradient GEMMs run one after the other) and kSplitWords words of its
 // own for the split plan, which the GEMM writes and its split-sum kernel
 // (launched right after it by the same call) reads
-constexpr int kNumQueues = 2;
+constexpr int kQueuesPerGemm = 8;  // one per XCD (the tail split); the skew queue is the first
+constexpr int kNumQueues = 2 * kQueuesPerGemm;
 constexpr int kSplitWords = 256;
 constexpr int kQueueWords = kNumQueues + 2 * kSplitWords;  // queues, then the plan words of both GEMMs
-constexpr int64_t kSplitFloats = int64_t(256) * 256 * 256;
+constexpr int64_t kSplitFloats = int64_t(320) * 256 * 256;
 hipError_t launch_zero_queues(int32_t* queues, hipStream_t st, KernelTimer* timer);
 hipError_t launch_gemm_dw13(const GemmProblem& p, const uint16_t* dh13, const uint16_t* x, uint16_t* dW13,
                             int32_t* queue, float* partial, int32_t* plan, hipStream_t st, KernelTimer* timer);

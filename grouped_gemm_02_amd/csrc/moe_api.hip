@@ -628,14 +628,14 @@ moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int3
     if ((e = launch_quant_tokens(act, I, I, counts, offsets, E, Tk, nullptr, 1, wga, wgas, rule, hs, tm,
                                  "quant_wg_act")) != hipSuccess)
       return MOE_ERR_LAUNCH;
-    e = launch_gemm_dw_fp8(gp, wgy, wgys, H, wga, wgas, I, static_cast<uint16_t*>(dW2), queues + 1, partial,
+    e = launch_gemm_dw_fp8(gp, wgy, wgys, H, wga, wgas, I, static_cast<uint16_t*>(dW2), queues + kQueuesPerGemm, partial,
                            plan2, hs, tm, "gemm_dw2_fp8", "dw2_split_sum");
     return launch_status(e);
   }
   if ((e = launch_gemm_dw13(gp, dh13, x16, static_cast<uint16_t*>(dW13), queues, partial, plan13, hs, tm)) !=
       hipSuccess)
     return MOE_ERR_LAUNCH;
-  e = launch_gemm_dw2(gp, dy16, act, static_cast<uint16_t*>(dW2), queues + 1, partial, plan2, hs, tm);
+  e = launch_gemm_dw2(gp, dy16, act, static_cast<uint16_t*>(dW2), queues + kQueuesPerGemm, partial, plan2, hs, tm);
   return launch_status(e);
 }
 

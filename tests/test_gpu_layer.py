@@ -165,6 +165,40 @@ def test_split_weight_gradients_deterministic_bitwise(B):
         assert torch.equal(a[k], b[k]), k
 
 
+# Balanced routing whose weight-gradient tiles leave the last round of the
+# nominal 256 workgroups partly empty: dW2 has 10 * 8 * 4 = 320 tiles (one
+# round and a quarter), dW13 640 (two and a half); the tiles of the two
+# heaviest experts (about 2000 rows each) are cut into two row ranges of 1024
+# and the rest, and the whole tiles run first.
+TAIL = inputs.LayerConfig("tail", 10000, 2048, 1024, 10, 2, "uniform", "bf16", 23)
+
+
+def _assert_tail_routing(d, cfg):
+    c = np.bincount(d["topk_idx"].cpu().numpy().ravel(), minlength=cfg.E)
+    assert int(c.max()) * cfg.E <= 2 * int(c.sum()), "balanced (no skew split)"
+    assert np.sort(c)[-2] > 1024, np.sort(c)[-4:]
+    for per_expert in ((cfg.H // 256) * ((cfg.I + 255) // 256), (2 * cfg.I // 256) * (cfg.H // 256)):
+        n = cfg.E * per_expert
+        assert 1 <= n // 256 <= 3 and 0 < 2 * (n % 256) <= 256, n
+
+
+def test_tail_split_weight_gradients_elementwise(B):
+    d = inputs.make_layer_inputs(TAIL, "cpu")
+    _assert_tail_routing(d, TAIL)
+    del d
+    _full_size_check(B, TAIL)
+
+
+def test_tail_split_weight_gradients_deterministic_bitwise(B):
+    cfg = TAIL
+    _say(f"case tail-split dW determinism {inputs.describe(cfg)}")
+    d = inputs.make_layer_inputs(cfg, DEV)
+    a = run_layer(B, cfg, d)
+    b = run_layer(B, cfg, d, num_cus=37)
+    for k in ("dW13", "dW2"):
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_layer_deterministic_bitwise(B):
     cfg = SMALL[1]
     _say(f"case determinism {inputs.describe(cfg)}")
