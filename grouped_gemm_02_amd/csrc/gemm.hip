@@ -1335,83 +1335,91 @@ struct TokenRows {  // k-th row of an expert segment -> its token's row
 int dh_num_parts(int64_t I) { return int((I + BN - 1) / BN) * 2; }
 
 // In the FP8 variant W2 arrives transposed, [E, I, H] (k-major rows i).
-// The dH epilogue of one row tile: dA_u (the accumulators) with the saved
-// [g | u] rows gives dh13 = [dg | du] and the routing-weight partials.
+
 // The dH epilogue of one row tile: dA_u (the accumulators) with the saved
 // [g | u] rows gives dh13 = [dg | du] and the routing-weight partials. A
 // thread handles 8 rows in batches of kDhRows (fewer rows per batch leave
-// more registers to the k loop).
+// more registers to the k loop); the [g | u] loads of the next batch go out
+// before the current batch's math, so their latency hides behind it.
 template <int kDhRows>
 __device__ __forceinline__ void dh_epilogue(const TileState& st, const Acc& acc, int I, int nparts, float* s_w,
                                             const uint16_t* __restrict__ h13, uint16_t* __restrict__ dh13,
                                             float* __restrict__ dwpart) {
   constexpr int kDhBatches = 8 / kDhRows;
-    const RowTile& rt = st.rt;
-    const int ncols = min(BN, I - rt.nt * BN);
-    if (threadIdx.x < BM) s_w[threadIdx.x] = st.w;
-    // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
-    // Thread t works on 8 of them (c) for tile rows t/16 + 32*j, j < 8, in
-    // batches of kDhRows rows; each batch's [g | u] pieces are requested
-    // together (the first batch's before the staging barrier).
-    const int c = (threadIdx.x & 15) * 8;
-    for (int h = 0; h < 2; ++h) {
-      const bool col_ok = h * 128 + c < ncols;
-      const int i = rt.nt * BN + h * 128 + (col_ok ? c : 0);
-      stage_half(acc, h);
-      for (int bt = 0; bt < kDhBatches; ++bt) {
-        u32x4 gq[kDhRows], uq[kDhRows];
+  const RowTile& rt = st.rt;
+  const int ncols = min(BN, I - rt.nt * BN);
+  if (threadIdx.x < BM) s_w[threadIdx.x] = st.w;
+  // half h holds dA_u of intermediate indices nt*256 + h*128 + [0, 128).
+  // Thread t works on 8 of them (c) for tile rows t/16 + 32*j, j < 8.
+  const int c = (threadIdx.x & 15) * 8;
+  for (int h = 0; h < 2; ++h) {
+    const bool col_ok = h * 128 + c < ncols;
+    const int i = rt.nt * BN + h * 128 + (col_ok ? c : 0);
+    auto request = [&](int bt, u32x4 (&gq)[kDhRows], u32x4 (&uq)[kDhRows]) {
 #pragma unroll
-        for (int j = 0; j < kDhRows; ++j) {
-          const int m = min((int(threadIdx.x) >> 4) + kRowPass * (kDhRows * bt + j), rt.rows - 1);
-          const uint16_t* src = h13 + (rt.row0 + m) * 2 * I + i;
-          gq[j] = *reinterpret_cast<const u32x4*>(src);
-          uq[j] = *reinterpret_cast<const u32x4*>(src + I);
-        }
-        if (bt == 0) __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kDhRows; ++j) {
-          const int m = (threadIdx.x >> 4) + kRowPass * (kDhRows * bt + j);
-          const bool row_ok = m < rt.rows;
-          float dws = 0.f;
-          if (row_ok && col_ok) {
-            const int64_t r = rt.row0 + m;
-            const float w = s_w[m];
-            const f32x4 d0 = *reinterpret_cast<const f32x4*>(frow(m) + c);
-            const f32x4 d1 = *reinterpret_cast<const f32x4*>(frow(m) + c + 4);
-            u32x4 dgq, duq;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float dgp[2], dup[2];
-#pragma unroll
-              for (int hh = 0; hh < 2; ++hh) {
-                const float gv = hh ? bf16_hi(gq[j][q]) : bf16_lo(gq[j][q]);
-                const float uv = hh ? bf16_hi(uq[j][q]) : bf16_lo(uq[j][q]);
-                const int e8 = 2 * q + hh;
-                const float dau = e8 < 4 ? d0[e8] : d1[e8 - 4];
-                const float sg_ = sigmoidf_fast(gv);
-                const float sl = gv * sg_;  // silu(g)
-                dws += dau * sl * uv;
-                const float da = w * dau;
-                dgp[hh] = da * uv * sg_ * (1.f + gv * (1.f - sg_));
-                dup[hh] = da * sl;
-              }
-              dgq[q] = pack_bf16x2(dgp[0], dgp[1]);
-              duq[q] = pack_bf16x2(dup[0], dup[1]);
-            }
-            *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i) = dgq;
-            *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i) = duq;
-          }
-          // sum over the 16 threads of this row (lanes 16g .. 16g+15)
-          dws += __shfl_xor(dws, 8);
-          dws += __shfl_xor(dws, 4);
-          dws += __shfl_xor(dws, 2);
-          dws += __shfl_xor(dws, 1);
-          if (row_ok && (threadIdx.x & 15) == 0) dwpart[(rt.row0 + m) * nparts + 2 * rt.nt + h] = dws;
-        }
+      for (int j = 0; j < kDhRows; ++j) {
+        const int m = min((int(threadIdx.x) >> 4) + kRowPass * (kDhRows * bt + j), rt.rows - 1);
+        const uint16_t* src = h13 + (rt.row0 + m) * 2 * I + i;
+        gq[j] = *reinterpret_cast<const u32x4*>(src);
+        uq[j] = *reinterpret_cast<const u32x4*>(src + I);
       }
-      __syncthreads();
+    };
+    stage_half(acc, h);
+    u32x4 gn[kDhRows], un[kDhRows];
+    request(0, gn, un);
+    __syncthreads();
+    for (int bt = 0; bt < kDhBatches; ++bt) {
+      u32x4 gq[kDhRows], uq[kDhRows];
+#pragma unroll
+      for (int j = 0; j < kDhRows; ++j) {
+        gq[j] = gn[j];
+        uq[j] = un[j];
+      }
+      if (bt + 1 < kDhBatches) request(bt + 1, gn, un);
+#pragma unroll
+      for (int j = 0; j < kDhRows; ++j) {
+        const int m = (threadIdx.x >> 4) + kRowPass * (kDhRows * bt + j);
+        const bool row_ok = m < rt.rows;
+        float dws = 0.f;
+        if (row_ok && col_ok) {
+          const int64_t r = rt.row0 + m;
+          const float w = s_w[m];
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(frow(m) + c);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(frow(m) + c + 4);
+          u32x4 dgq, duq;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float dgp[2], dup[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const float gv = hh ? bf16_hi(gq[j][q]) : bf16_lo(gq[j][q]);
+              const float uv = hh ? bf16_hi(uq[j][q]) : bf16_lo(uq[j][q]);
+              const int e8 = 2 * q + hh;
+              const float dau = e8 < 4 ? d0[e8] : d1[e8 - 4];
+              const float sg_ = sigmoidf_fast(gv);
+              const float sl = gv * sg_;  // silu(g)
+              dws += dau * sl * uv;
+              const float da = w * dau;
+              dgp[hh] = da * uv * sg_ * (1.f + gv * (1.f - sg_));
+              dup[hh] = da * sl;
+            }
+            dgq[q] = pack_bf16x2(dgp[0], dgp[1]);
+            duq[q] = pack_bf16x2(dup[0], dup[1]);
+          }
+          *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i) = dgq;
+          *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i) = duq;
+        }
+        // sum over the 16 threads of this row (lanes 16g .. 16g+15)
+        dws += __shfl_xor(dws, 8);
+        dws += __shfl_xor(dws, 4);
+        dws += __shfl_xor(dws, 2);
+        dws += __shfl_xor(dws, 1);
+        if (row_ok && (threadIdx.x & 15) == 0) dwpart[(rt.row0 + m) * nparts + 2 * rt.nt + h] = dws;
+      }
     }
+    __syncthreads();
   }
+}
 
 // The FP8 dH (W2 arrives as transposed codes), both operands straight into
 // LDS; its own tile loop, no prefetch across tiles.
