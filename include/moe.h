@@ -351,9 +351,10 @@ moe_status moe_fwd_logits(const moe_shape* s, const void* x, const float* logits
  * dY and w*silu(g)*u quantized along each expert's rows (moe_quantize_tokens
  * layout; [dg | du], and dY when k == 1, are quantized along both axes in
  * one pass). Under skewed routing the weight-gradient tiles of the hottest
- * experts are cut along the expert's rows into fp32 partials (in bwd_ws)
- * that a second kernel adds in a fixed order: results are deterministic and
- * do not depend on num_cus. */
+ * experts, and under balanced routing the tiles of a last round of
+ * workgroups that would be at most half full, are cut along the expert's
+ * rows into fp32 partials (in bwd_ws) that a second kernel adds in a fixed
+ * order: results are deterministic and do not depend on num_cus. */
 moe_status moe_bwd(const moe_shape* s, const void* dy, const void* x, const int32_t* topk_idx,
                    const float* topk_w, const void* W13, const void* W2, const void* wq,
                    const void* saved, void* dx, float* d_topk_w, void* dW13, void* dW2, void* ws,
