@@ -1,10 +1,11 @@
 """Pins for the oracle's FP8 emulation (oracle/moe_fp8.py).
 
-Independent references: E4M3 values observed on the MI355X matrix cores
-(code 0x38 multiplies as 1.0, 0x40 as 2.0, and the scale byte 127 + 1
-doubles a product), the defining properties of the scale rules and of
-round-to-nearest-even, and a per-token loop implementation of the quantized
-layer with its own scalar rounding (math.frexp based) on tiny inputs.
+Independent references: E4M3 values fixed by the format's bit fields (OCP
+8-bit floating point, E4M3 with exponent bias 7: code 0x38 is 1.0, 0x40 is
+2.0, 0x7E is 448; an E8M0 scale byte b is 2^(b - 127)), the defining
+properties of the scale rules and of round-to-nearest-even, and a per-token
+loop implementation of the quantized layer with its own scalar rounding
+(math.frexp based) on tiny inputs.
 """
 import math
 import struct
@@ -18,7 +19,7 @@ from oracle import moe_oracle as orc
 
 def test_e4m3_anchor_values():
     t = f8.e4m3_decode_table()
-    assert t[0x38] == 1.0 and t[0x40] == 2.0          # as multiplied by the MI355X MFMA
+    assert t[0x38] == 1.0 and t[0x40] == 2.0          # exponent field 7 and 8, bias 7
     assert t[0x7E] == 448.0 and t[0xFE] == -448.0     # largest finite magnitude
     assert t[0x08] == 2.0 ** -6                       # smallest normal
     assert t[0x01] == 2.0 ** -9                       # smallest subnormal
