@@ -194,9 +194,10 @@ def test_tail_split_weight_gradients_deterministic_bitwise(B):
     _say(f"case tail-split dW determinism {inputs.describe(cfg)}")
     d = inputs.make_layer_inputs(cfg, DEV)
     a = run_layer(B, cfg, d)
-    b = run_layer(B, cfg, d, num_cus=37)
-    for k in ("dW13", "dW2"):
-        assert torch.equal(a[k], b[k]), k
+    for cus in (37, 3):  # 3 workgroups: most XCD shares are taken over by other workgroups
+        b = run_layer(B, cfg, d, num_cus=cus)
+        for k in ("dW13", "dW2"):
+            assert torch.equal(a[k], b[k]), (k, cus)
 
 
 def test_layer_deterministic_bitwise(B):
