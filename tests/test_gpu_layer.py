@@ -318,6 +318,14 @@ def test_qwen3_30b_shape_zipf_routing_bf16_elementwise(B):
     _full_size_check(B, cfg)
 
 
+def test_ep8_share_bf16_elementwise(B):
+    """One EP=8 rank's share in bf16 (131,072 rows, 16 experts, top-1): the
+    down and dX GEMMs write rows straight to their tokens, and dW2's 384
+    tiles take the last-round split."""
+    cfg = inputs.CONFIGS["ep8_share"].scaled(name="ep8_share_bf16", precision="bf16")
+    _full_size_check(B, cfg)
+
+
 # --------------------------------------------------------------- duplicate experts
 
 def _with_duplicates(d, every=3):
