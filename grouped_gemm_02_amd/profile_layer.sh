@@ -67,4 +67,9 @@ timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/pmc_
 python3 -m grouped_gemm_02_amd.profile_summary traffic "$OUT/pmc_fetch/pmc_counter_collection.csv" \
   "$OUT/pmc_write/pmc_counter_collection.csv" "$PROF/gemm_traffic_qwen3_30b_bf16.json" --workload qwen3_30b/bf16 \
   --cmd "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline ; rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o pmc -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline"
+# bf16 (the 30B layer): LDS bank conflicts
+pmc qwen3_30b_bf16 lds "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS" --config qwen3_30b
+python3 -m grouped_gemm_02_amd.profile_summary lds "$OUT/pmc_qwen3_30b_bf16_lds/pmc_counter_collection.csv" \
+  "$PROF/lds_bank_conflicts_qwen3_30b_bf16.txt" --title "Qwen3-30B-A3B-shaped layer, bf16" \
+  --cmd "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS --output-format csv -d $OUT/pmc_qwen3_30b_bf16_lds -o pmc -- python3 bench.py --config qwen3_30b --steps 2 --warmup 1 --no-cpu-baseline"
 echo "profiles written"

@@ -5,6 +5,8 @@
         <write_counter_collection.csv> <out.json> --cmd "<command>"
     python -m grouped_gemm_02_amd.profile_summary mfma <counter_collection.csv> <out.txt> --cmd "<command>" \
         --title "<workload>"
+    python -m grouped_gemm_02_amd.profile_summary lds <counter_collection.csv> <out.txt> --cmd "<command>" \
+        --title "<workload>" [--config qwen3_30b]
 
 `stats` turns the --kernel-trace --stats table into a short text table.
 `traffic` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE, both in KiB per
@@ -125,6 +127,49 @@ def mfma(csv_path: str, out_path: str, cmd: str, title: str, simds: int = 1024, 
         f.write("\n".join(lines) + "\n")
 
 
+def _tiles_per_launch(config: str) -> dict:
+    """Output tiles of each GEMM launch for the seeded routing of `config`
+    (256 x 256 tiles; the row-tile GEMMs have sum_e ceil(rows_e / 256) m-tiles)."""
+    import torch
+    from grouped_gemm_02_amd import inputs
+    cfg = inputs.CONFIGS[config]
+    d = inputs.make_layer_inputs(cfg, "cpu", with_dy=False)
+    counts = torch.bincount(d["topk_idx"].flatten(), minlength=cfg.E)
+    mt = int(((counts + 255) // 256).sum())
+    n_i = (cfg.I + 255) // 256
+    return {"gemm1_swiglu": mt * (2 * cfg.I // 256), "gemm2": mt * (cfg.H // 256), "gemm_dh": mt * n_i,
+            "gemm_dx": mt * (cfg.H // 256), "gemm_dw13": cfg.E * (2 * cfg.I // 256) * (cfg.H // 256),
+            "gemm_dw2": cfg.E * (cfg.H // 256) * n_i}
+
+
+def lds(csv_path: str, out_path: str, cmd: str, title: str, config: str) -> None:
+    """SQ_LDS_BANK_CONFLICT and SQ_ACTIVE_INST_LDS per dispatch of each GEMM,
+    and the conflict cycles per output tile."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = r["Dispatch_Id"]
+        vals[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    agg = collections.defaultdict(list)
+    for d, v in vals.items():
+        if "moe::gemm" in names[d]:
+            agg[short_name(names[d])].append((v.get("SQ_LDS_BANK_CONFLICT", 0.0), v.get("SQ_ACTIVE_INST_LDS", 0.0)))
+    tiles = _tiles_per_launch(config)
+    lines = [f"# rocprofv3 LDS counters, {title} (one pass, two SQ counters)", f"# command: {cmd}",
+             "# values: average per dispatch, summed over the chip; tiles per launch from the seeded routing",
+             "#", f"{'kernel':36s} {'bank_conflict_cycles':>21s} {'active_lds_inst_cycles':>23s} {'tiles':>6s} "
+             f"{'conflict_cycles_per_tile':>25s}"]
+    for k in sorted(agg):
+        bc = sum(a for a, _ in agg[k]) / len(agg[k])
+        ai = sum(b for _, b in agg[k]) / len(agg[k])
+        n = next((v for key, v in tiles.items() if k.startswith(key)), 0)
+        per = f"{bc / n:25.0f}" if n else f"{'-':>25s}"
+        lines.append(f"{k:36s} {bc:21.0f} {ai:23.0f} {n:6d} {per}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -144,9 +189,17 @@ def main():
     m.add_argument("out")
     m.add_argument("--cmd", required=True)
     m.add_argument("--title", required=True)
+    ls = sub.add_parser("lds")
+    ls.add_argument("csv")
+    ls.add_argument("out")
+    ls.add_argument("--cmd", required=True)
+    ls.add_argument("--title", required=True)
+    ls.add_argument("--config", default="qwen3_30b")
     a = ap.parse_args()
     if a.what == "stats":
         stats(a.csv, a.out, a.cmd)
+    elif a.what == "lds":
+        lds(a.csv, a.out, a.cmd, a.title, a.config)
     elif a.what == "mfma":
         mfma(a.csv, a.out, a.cmd, a.title)
     else:
