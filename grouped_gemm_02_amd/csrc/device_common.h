@@ -19,7 +19,6 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
-__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
 // Two floats -> two bf16 (round to nearest even, hardware v_cvt_pk_bf16_f32),
 // `a` in the low half.
@@ -27,10 +26,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2 v = {a, b};
   bf16x2 r = __builtin_convertvector(v, bf16x2);
   return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float a) {
-  return static_cast<uint16_t>(pack_bf16x2(a, 0.f) & 0xffffu);
 }
 
 // logistic function; exp2 of a scaled argument keeps it on the hardware

@@ -676,12 +676,6 @@ __device__ __forceinline__ i32x8 frag8(const uint16_t* lds, int ent0, int s) {
 // where KMajorLoader8D put row e's scale word (16-bit units from the operand)
 __device__ __forceinline__ int scale_pos8(int e) { return kScaleWords8 + 2 * (8 * (e & 63) + (e >> 6)); }
 
-// scale byte of k-block 2s + lane/32 (codes 64s + 32h .. +31) of this lane's row
-__device__ __forceinline__ int scale8(const uint16_t* lds, int ent0, int s) {
-  const int lane = lane_id();
-  return reinterpret_cast<const uint8_t*>(lds + (ent0 + (lane & 31)) * LDK + BK)[2 * s + (lane >> 5)];
-}
-
 // An E2M1 operand of the same MFMA (measured on gfx950): a lane of half h
 // holds k = 32h .. 32h+31 of its row as 32 nibbles in registers 0-3, value
 // 2j in the low nibble of byte j, i.e. 16 consecutive bytes of the row; its
