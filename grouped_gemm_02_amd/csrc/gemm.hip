@@ -74,6 +74,7 @@ __shared__ __attribute__((aligned(16))) uint16_t g_stage1[kStageLds];
 __device__ __forceinline__ uint16_t* stage_buf(int s) { return s ? g_stage1 : g_stage0; }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // ------------------------------------------------------------------ loaders
@@ -1648,25 +1649,33 @@ __global__ __launch_bounds__(kThreads) void gemm_dx_kernel(GemmProblem p, Operan
 // Fills s_order (experts by descending count) and returns whether the
 // routing is skewed. Same result in every workgroup.
 __device__ bool dw_expert_order(const int32_t* counts, int E, int32_t* s_cnt, int32_t* s_order, int32_t* s_flag) {
-  for (int e = threadIdx.x; e < E; e += kThreads) s_cnt[e] = counts[e];
+  // s_cnt padded to a multiple of 4 with -1, which ranks below every count
+  const int E4 = (E + 3) >> 2;
+  for (int e = threadIdx.x; e < 4 * E4; e += kThreads) s_cnt[e] = e < E ? counts[e] : -1;
   __syncthreads();
+  const i32x4* c4 = reinterpret_cast<const i32x4*>(s_cnt);
   for (int e = threadIdx.x; e < E; e += kThreads) {
     const int c = s_cnt[e];
     int r = 0;
-    for (int j = 0; j < E; ++j) {
-      const int cj = s_cnt[j];
-      r += (cj > c || (cj == c && j < e)) ? 1 : 0;
+    for (int q = 0; q < E4; ++q) {
+      const i32x4 v = c4[q];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r += (v[u] > c || (v[u] == c && 4 * q + u < e)) ? 1 : 0;
     }
     s_order[r] = e;
   }
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {  // wave 0: the total and the largest count
     int64_t sum = 0;
     int mx = 0;
-    for (int j = 0; j < E; ++j) {
+    for (int j = threadIdx.x; j < E; j += 64) {
       sum += s_cnt[j];
       mx = max(mx, s_cnt[j]);
     }
-    *s_flag = (int64_t(mx) * E > 2 * sum) ? 1 : 0;
+    for (int o = 32; o > 0; o >>= 1) {
+      sum += __shfl_xor(sum, o);
+      mx = max(mx, __shfl_xor(mx, o));
+    }
+    if (threadIdx.x == 0) *s_flag = (int64_t(mx) * E > 2 * sum) ? 1 : 0;
   }
   __syncthreads();
   return __builtin_amdgcn_readfirstlane(*s_flag) != 0;
@@ -1937,7 +1946,7 @@ __global__ __launch_bounds__(kSumThreads) void dw_split_sum_kernel(const int32_t
 }
 
 #define MOE_DW_SMEM                                                            \
-  __shared__ int32_t s_cnt[1024];                                              \
+  __shared__ __attribute__((aligned(16))) int32_t s_cnt[1024];                 \
   __shared__ int32_t s_order[1024];                                            \
   __shared__ int32_t s_flag;                                                   \
   __shared__ int32_t s_next;                                                   \
