@@ -334,9 +334,11 @@ def main():
     if B.moe_read_status(buf.fwd_ws) != 0:
         raise RuntimeError("routing status word set")
 
+    # The timed steps: events only around each step and its forward and
+    # backward halves. Events around every kernel put gaps between the
+    # kernels (~2-3 % of the step), so the kernels' own durations are taken
+    # over the next `steps` steps, the same work with per-kernel events.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    B.moe_kernel_timing_collect()          # drop anything recorded before
-    B.moe_set_kernel_timing(True)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -346,10 +348,19 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    B.moe_kernel_timing_collect()          # drop anything recorded before
+    B.moe_set_kernel_timing(True)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for i in range(args.steps):
+        step()
+    k1.record()
+    torch.cuda.synchronize()
     B.moe_set_kernel_timing(False)
     kt = B.moe_kernel_timing_collect()
-
-    ms_step = start.elapsed_time(stop) / args.steps
+    ms_step_kernel_events = k0.elapsed_time(k1) / args.steps
     fwd_ms = [e[3].elapsed_time(e[1]) for e in evs]
     wq_ms = [e[0].elapsed_time(e[3]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
@@ -429,6 +440,10 @@ def main():
         "gemm_tflops": round((flops) / (gemm_ms * 1e-3) / 1e12, 1),
         "hbm_copy_gbps": round(copy_gbs, 1),
         "wall_s": round(wall, 3),
+        # per-kernel durations (kernels, roofline) come from a second run of
+        # the same number of steps with an event pair around every kernel;
+        # its step time, gaps for the events included:
+        "ms_per_step_with_kernel_events": round(ms_step_kernel_events, 4),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": kernel_peak(dom),
                      "unit": "TFLOP/s", "frac": round(achieved / kernel_peak(dom), 4),
