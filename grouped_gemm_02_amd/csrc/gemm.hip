@@ -1350,13 +1350,14 @@ __device__ __forceinline__ void dh_epilogue(const TileState& st, const Acc& acc,
   for (int h = 0; h < 2; ++h) {
     const bool col_ok = h * 128 + c < ncols;
     const int i = rt.nt * BN + h * 128 + (col_ok ? c : 0);
+    // [g | u] is read once: streaming (nontemporal) loads keep it out of the caches
     auto request = [&](int bt, u32x4 (&gq)[kDhRows], u32x4 (&uq)[kDhRows]) {
 #pragma unroll
       for (int j = 0; j < kDhRows; ++j) {
         const int m = min((int(threadIdx.x) >> 4) + kRowPass * (kDhRows * bt + j), rt.rows - 1);
         const uint16_t* src = h13 + (rt.row0 + m) * 2 * I + i;
-        gq[j] = *reinterpret_cast<const u32x4*>(src);
-        uq[j] = *reinterpret_cast<const u32x4*>(src + I);
+        gq[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+        uq[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + I));
       }
     };
     stage_half(acc, h);
@@ -1473,8 +1474,8 @@ __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand
         for (int j = 0; j < 4; ++j) {
           const int m = min((int(threadIdx.x) >> 4) + kRowPass * (4 * bt + j), rt.rows - 1);
           const uint16_t* src = h13 + (rt.row0 + m) * 2 * I + i;
-          gq[j] = *reinterpret_cast<const u32x4*>(src);
-          uq[j] = *reinterpret_cast<const u32x4*>(src + I);
+          gq[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+          uq[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + I));
         }
         if (bt == 0) __syncthreads();
 #pragma unroll

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 #pragma unroll
     for (int u = 0; u < kQItems; ++u) {
       const int64_t g = g0 + u * stride;
-      raw[u] = g < total ? *reinterpret_cast<const u32x4*>(in + g * 8) : u32x4{0u, 0u, 0u, 0u};
+      raw[u] = g < total ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in + g * 8)) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kQItems; ++u) {
