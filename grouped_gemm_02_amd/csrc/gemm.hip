@@ -976,6 +976,11 @@ __device__ __forceinline__ void stage_image(const Acc& acc, int64_t row0, int ro
   __syncthreads();
 }
 
+// The image's rows out to global memory with streaming (nontemporal) stores:
+// every output of these GEMMs (the down GEMM's and dX's rows, summed by a
+// combine; the weight gradients) is written once and not read again by the
+// next tiles, and cached stores displaced the operand rows that the
+// concurrent tiles share in L2 (the weight-gradient GEMMs ran 6 % slower).
 __device__ __forceinline__ void copy_image(uint16_t* out, int64_t ld, int64_t row0,
                                            int64_t col0, int rows, int cols, const int32_t* rowmap,
                                            const int32_t* s_map) {
@@ -983,7 +988,8 @@ __device__ __forceinline__ void copy_image(uint16_t* out, int64_t ld, int64_t ro
   if (c < cols) {
     for (int m = threadIdx.x >> 5; m < rows; m += kThreads / 32) {
       const int64_t orow = rowmap ? int64_t(s_map[m]) : row0 + m;
-      *reinterpret_cast<u32x4*>(out + orow * ld + col0 + c) = *reinterpret_cast<const u32x4*>(img_row(m) + c);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(img_row(m) + c),
+                                  reinterpret_cast<u32x4*>(out + orow * ld + col0 + c));
     }
   }
   __syncthreads();
@@ -1076,6 +1082,11 @@ __device__ __forceinline__ RowTile decode_row_tile(int64_t t, int NT, const int3
 __device__ __forceinline__ void store4_bf16(uint16_t* p, float a, float b, float c, float d) {
   u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
   *reinterpret_cast<u32x2*>(p) = v;
+}
+// the same as a streaming (nontemporal) store: for data no later kernel of
+// the step reads soon, which then does not displace operands in the caches
+__device__ __forceinline__ void store4_bf16_nt(uint16_t* p, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)}, reinterpret_cast<u32x2*>(p));
 }
 
 
@@ -1217,9 +1228,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_kernel(GemmProblem p, O
         float av[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) av[q] = w * (gv[q] * sigmoidf_fast(gv[q]) * uv[q]);
-        if (h13) {
-          store4_bf16(h13 + r * 2 * I + i, gv[0], gv[1], gv[2], gv[3]);
-          store4_bf16(h13 + r * 2 * I + I + i, uv[0], uv[1], uv[2], uv[3]);
+        if (h13) {  // read again only by the backward's dH epilogue
+          store4_bf16_nt(h13 + r * 2 * I + i, gv[0], gv[1], gv[2], gv[3]);
+          store4_bf16_nt(h13 + r * 2 * I + I + i, uv[0], uv[1], uv[2], uv[3]);
         }
         store4_bf16(act + r * I + i, av[0], av[1], av[2], av[3]);
       }
@@ -1402,8 +1413,8 @@ __device__ __forceinline__ void dh_epilogue(const TileState& st, const Acc& acc,
             dgq[q] = pack_bf16x2(dgp[0], dgp[1]);
             duq[q] = pack_bf16x2(dup[0], dup[1]);
           }
-          *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i) = dgq;
-          *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i) = duq;
+          __builtin_nontemporal_store(dgq, reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i));
+          __builtin_nontemporal_store(duq, reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i));
         }
         // sum over the 16 threads of this row (lanes 16g .. 16g+15)
         dws += __shfl_xor(dws, 8);
@@ -1508,8 +1519,8 @@ __device__ __forceinline__ void dh_fp8_tiles(const GemmProblem& p, const Operand
               dgq[q] = pack_bf16x2(dgp[0], dgp[1]);
               duq[q] = pack_bf16x2(dup[0], dup[1]);
             }
-            *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i) = dgq;
-            *reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i) = duq;
+            __builtin_nontemporal_store(dgq, reinterpret_cast<u32x4*>(dh13 + r * 2 * I + i));
+            __builtin_nontemporal_store(duq, reinterpret_cast<u32x4*>(dh13 + r * 2 * I + I + i));
           }
           // sum over the 16 threads of this row (lanes 16g .. 16g+15)
           dws += __shfl_xor(dws, 8);
